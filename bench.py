@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the Ladder Residual Transformer forward step on one MI355X.
+
+Default workload: one tensor-parallel rank's shard of a 70B-shape model (TP=8: 80 ladder
+layers, hidden 8192, 8 query heads + 1 kv head of 128, ffn 3584, vocab 16032, bf16),
+batch 1, 1024-token prompt, decode steps at positions 1024.. .  One "step" is one
+decode step: every module of every layer (RMSNorm, QKV + RoPE + KV append, GQA
+attention, O projection, SwiGLU MLP, ladder residual adds), then the LM head and the
+greedy argmax.  Weights are random N(0, 0.02) from a fixed seed and the prompt is
+uniform random ids (synthetic data of the workload's shape).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s + % HBM roofline, 70B-shape TP8 one-rank shard, batch 1"
+HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15      # FLOP/s, dense bf16
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_gemv_70b_b1.json")
+KERNEL_SOURCES = ("ladder_residual_transformer_amd/csrc/gemv.hip", "ladder_residual_transformer_amd/csrc/common.hpp")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(cfg, B, pos):
+    """Algorithmic HBM bytes of one decode step at position pos: every weight once, the
+    KV rows 0..pos read and row pos written."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    kv_row = B * cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * esz
+    return cfg.weight_bytes() + kv_row * (pos + 1) + kv_row
+
+
+def prefill_flops(cfg, B, T):
+    H, F, hd = cfg.hidden, cfg.ffn, cfg.head_dim
+    q, kv = cfg.n_q_heads * hd, cfg.n_kv_heads * hd
+    proj = 2 * cfg.n_layers * (H * (q + 2 * kv) + q * H + 3 * H * F) * B * T
+    attn = cfg.n_layers * B * cfg.n_q_heads * 4 * hd * (T * (T + 1) // 2)
+    head = 2 * cfg.vocab * H * B
+    return proj + attn + head
+
+
+def gateup_bytes(cfg, B):
+    esz = 2 if cfg.dtype == "bf16" else 4
+    return 2 * cfg.ffn * cfg.hidden * esz + cfg.hidden * esz + B * cfg.hidden * 4 + B * cfg.ffn * 4
+
+
+def cpu_baseline(cfg, w, prompt, sample_layers, steps):
+    """The oracle (numpy float32) on a bounded sample: `sample_layers` real-width layers
+    plus the LM head; decode time per token extrapolated to the full depth."""
+    import numpy as np
+    import synth
+    from oracle import LadderOracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    sub = synth.scaled_config(cfg, sample_layers)
+    ws = synth.ModelWeights(w.dtype, w.tok_embed, w.final_norm, w.lm_head, w.layers[:sample_layers])
+    o = LadderOracle(sub, ws, dtype=np.float32, cache_weights=True)
+    cache = o.new_cache()
+    B, T = prompt.shape
+    t0 = time.perf_counter()
+    r = o.forward(prompt, cache, 0, logits="last")
+    t_prefill = time.perf_counter() - t0
+    tok = np.argmax(r.logits[:, -1], axis=-1)
+    o.forward(tok[:, None], cache, T, logits="last")          # warm (weights cached)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        r = o.forward(tok[:, None], cache, T + 1 + k, logits=None)
+    t_layers = (time.perf_counter() - t0) / steps
+    hd = o.head()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        from oracle import rms_norm
+        np.matmul(rms_norm(r.hidden[:, -1], hd["final_norm"], cfg.norm_eps), hd["lm_head"].T)
+    t_head = (time.perf_counter() - t0) / steps
+    per_token = t_layers * cfg.n_layers / sample_layers + t_head
+    return {"value": B / per_token, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"numpy float32 oracle, {sample_layers} of {cfg.n_layers} layers at full width plus the LM "
+                       f"head, {steps} decode steps at KV length {T + 1}, per-token time scaled by "
+                       f"{cfg.n_layers}/{sample_layers} for the layer stack; prefill of the {T}-token prompt "
+                       f"over the sample took {t_prefill:.1f} s"),
+            "prefill_tok_s_extrapolated": B * T / (t_prefill * cfg.n_layers / sample_layers)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="70b_tp8_shard")
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--schedule", choices=("serial", "side", "dual"), default="dual")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--prefill-reps", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-layers", type=int, default=8)
+    ap.add_argument("--cpu-steps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs one GPU's share of the model (one tensor-parallel rank's shard); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from ladder_residual_transformer_amd import DeviceWeights, LadderModel, load
+
+    load()
+    wl = synth.WORKLOADS[args.workload]
+    cfg = wl.model
+    B, P = args.batch, wl.prompt_len
+    if args.steps < 1 or args.warmup < 0 or max(args.steps, args.warmup) > wl.decode_len:
+        sys.exit(f"steps and warmup must be within the {wl.decode_len} decode positions")
+    torch.cuda.set_device(0)
+    t = time.time()
+    w = synth.gen_weights(cfg, seed=0)
+    log(f"[bench] generated {cfg.weight_bytes() / 1e9:.2f} GB of {cfg.name} weights in {time.time() - t:.1f} s")
+    t = time.time()
+    dw = DeviceWeights(w)
+    model = LadderModel(cfg, dw, B, wl.max_seq)
+    sched = {"serial": 0, "side": 1, "dual": 2}[args.schedule]
+    model.set_schedule(sched, not args.no_graph)
+    torch.cuda.synchronize()
+    log(f"[bench] uploaded weights and built the context in {time.time() - t:.1f} s "
+        f"(workspace {model.workspace_bytes() / 1e6:.0f} MB)")
+    prompt = synth.gen_ids(B, P, cfg.vocab, seed=1)
+    ids = torch.from_numpy(prompt).cuda()
+
+    # ---- prefill
+    _, first, _ = model.prefill(ids, logits=False, hidden=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.prefill_reps):
+        _, first, _ = model.prefill(ids, logits=False, hidden=False)
+    torch.cuda.synchronize()
+    prefill_s = (time.perf_counter() - t0) / args.prefill_reps
+    pflops = prefill_flops(cfg, B, P)
+    log(f"[bench] prefill {B}x{P}: {prefill_s * 1e3:.1f} ms, {B * P / prefill_s:.0f} tok/s, "
+        f"{pflops / prefill_s / 1e12:.1f} TFLOP/s")
+
+    # ---- decode: W untimed steps, then exactly K timed steps (positions P..)
+    bufs = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(2)]
+    bufs[0].copy_(first)
+    cur = bufs[0]
+    for k in range(args.warmup):
+        model.decode_step(cur, P + k, out=(None, bufs[(k + 1) % 2], None))
+        cur = bufs[(k + 1) % 2]
+    torch.cuda.synchronize()
+    bufs[0].copy_(first)
+    cur = bufs[0]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for k in range(args.steps):
+        model.decode_step(cur, P + k, out=(None, bufs[(k + 1) % 2], None))
+        cur = bufs[(k + 1) % 2]
+    e1.record()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    toks = cur.cpu().numpy()
+    assert np.all((toks >= 0) & (toks < cfg.vocab)), "decode produced an out-of-range token id"
+    tok_s = B * args.steps / dt
+    total_bytes = sum(decode_bytes(cfg, B, P + k) for k in range(args.steps))
+    hbm_frac = total_bytes / dt / HBM_PEAK
+    log(f"[bench] decode {args.steps} steps: {dt * 1e3 / args.steps:.3f} ms/step (events {gpu_ms / args.steps:.3f}), "
+        f"{tok_s:.1f} tok/s, {total_bytes / args.steps / 1e9:.2f} GB/step, {100 * hbm_frac:.1f}% of HBM peak")
+
+    # ---- dominant kernel (gate/up GEMV, ~55% of the bytes), timed on its stream
+    ku = model.time_kernels(B, reps=3)
+    gu_bytes = gateup_bytes(cfg, B)
+    achieved = gu_bytes / (ku["gateup"] * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sha") == kernel_sha() and tr.get("batch") == B and tr.get("workload") == cfg.name:
+            traffic = tr.get("bytes_per_launch")
+    log(f"[bench] kernel us/launch: " + ", ".join(f"{k} {v:.2f}" for k, v in ku.items()))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t = time.time()
+        cpu = cpu_baseline(cfg, w, prompt, min(args.cpu_sample_layers, cfg.n_layers), args.cpu_steps)
+        log(f"[bench] cpu baseline {cpu['value']:.4f} tok/s on {cpu['cores']} threads ({time.time() - t:.1f} s)")
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dt * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}, batch {B}, prompt {P}, decode positions {P}..{P + args.steps - 1}",
+                   "batch": B, "prompt_len": P, "layers": cfg.n_layers, "hidden": cfg.hidden,
+                   "schedule": args.schedule, "hip_graph": not args.no_graph},
+        "decode_hbm_frac": round(hbm_frac, 4),
+        "decode_bytes_per_step": total_bytes // args.steps,
+        "prefill_tok_s": round(B * P / prefill_s, 1),
+        "prefill_mfma_frac": round(pflops / prefill_s / MFMA_BF16_PEAK, 4),
+        "roofline": {"bound": "hbm", "kernel": "gateup GEMV (RMSNorm + [Wgate,Wup] + SwiGLU)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": traffic,
+                     "bytes_per_launch": gu_bytes, "us_per_launch": round(ku["gateup"], 3)},
+        "kernels_us": {k: round(v, 3) for k, v in ku.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    model.free()
+
+
+if __name__ == "__main__":
+    main()

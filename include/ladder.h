@@ -1,0 +1,178 @@
+/*
+ * ladder.h -- C ABI of libladder: the per-token forward step of a Ladder Residual
+ * Transformer (attention and SwiGLU-MLP modules, Llama-3.1 shaped) on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (arXiv 2501.06589; Paper-Notes page "Ladder Residual:
+ * Parallelism-Aware Architecture for Accelerating Large Model Inference",
+ * sections "core idea" and "method details / key design"): every attention and
+ * every MLP is one module h; the standard residual update x_{i+1} = h_{i+1}(x_i) + x_i
+ * becomes x_{i+1} = h_{i+1}(x_{i-1}) + x_i, so a module reads the residual stream
+ * from one step earlier while the stream itself still accumulates every module's
+ * output (section "overall framework").  A module therefore never waits for the
+ * previous module's result; the pages use this to overlap the tensor-parallel
+ * all-reduce with compute (section "asynchronous AllReduce implementation").
+ * Layers can be mixed: standard lower layers, ladder upper layers (section
+ * "hybrid Ladder adaptation").
+ *
+ * This library runs one tensor-parallel rank's shard of such a model with the
+ * cross-GPU all-reduce replaced by identity.  Module numbering: m = 0..2L-1,
+ * m = 2l is layer l's attention, m = 2l+1 its MLP; x_0 is the token embedding,
+ * x_{m+1} = x_m + out_m; a ladder module reads x_{m-1} (x_{-1} taken as x_0), a
+ * standard module reads x_m.  The final hidden state is x_{2L}; logits are
+ * RMSNorm(x_{2L}) . W_lm^T and the next token is their argmax (lowest index on
+ * exact ties).
+ *
+ * Conventions for every entry point
+ *   - Pointers named d_* and every pointer inside ladder_weights / ladder_kv are
+ *     device pointers on the GPU that was current at ladder_init; others are host.
+ *   - Matrices are row-major [out][in] (the nn.Linear layout), 16-byte aligned.
+ *   - bf16 tensors hold raw bfloat16 bit patterns (uint16).
+ *   - The caller owns weights, KV cache, ids and outputs and keeps them alive and
+ *     unmodified until ladder_free; the context owns its workspace, streams,
+ *     events and graphs.
+ *   - Work is enqueued asynchronously on the stream given to ladder_init; the
+ *     context's internal streams are joined back into it before each call returns.
+ *   - Argument errors are reported synchronously and leave the context usable;
+ *     LADDER_ERR_HIP is sticky (the context must then be freed).
+ *   - A context is not thread-safe.
+ */
+#ifndef LADDER_H
+#define LADDER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ladder_status;
+#define LADDER_OK 0
+#define LADDER_ERR_ARG (-1)      /* null pointer, unknown enum, non-positive size */
+#define LADDER_ERR_SHAPE (-2)    /* dimensions this build does not support */
+#define LADDER_ERR_CAPACITY (-3) /* B > max_batch, or positions beyond max_seq */
+#define LADDER_ERR_STATE (-4)    /* reads KV positions that were never written */
+#define LADDER_ERR_HIP (-5)      /* a HIP runtime call failed (sticky) */
+#define LADDER_ERR_OOM (-6)      /* workspace allocation failed */
+
+#define LADDER_F32 0             /* weights and KV cache fp32 */
+#define LADDER_BF16 1            /* weights and KV cache bf16; residual and accumulation fp32 */
+
+/* Execution schedule of the module loop.  All three give bitwise identical results. */
+#define LADDER_SCHED_SERIAL 0    /* one stream, modules and residual adds in program order */
+#define LADDER_SCHED_SIDE 1      /* residual adds on a side stream: module m+1 starts on its
+                                    stale input while x_{m+1} = x_m + out_m completes */
+#define LADDER_SCHED_DUAL 2      /* attention and MLP modules on two streams, residual add
+                                    fused into each module's output projection; a ladder
+                                    module overlaps the previous module (default) */
+
+typedef struct ladder_config {
+  int32_t n_layers;
+  int32_t hidden;          /* H */
+  int32_t n_q_heads;       /* per-rank query heads */
+  int32_t n_kv_heads;      /* per-rank key/value heads; n_q_heads % n_kv_heads == 0 */
+  int32_t head_dim;        /* 64 or 128 */
+  int32_t ffn;             /* per-rank SwiGLU width F */
+  int32_t vocab;           /* per-rank vocabulary rows of embedding and LM head */
+  double rope_theta;       /* pair j of a head rotates by p * theta^(-2j/head_dim) */
+  float norm_eps;          /* RMSNorm epsilon (1e-5) */
+  int32_t dtype;           /* LADDER_F32 or LADDER_BF16 */
+  int32_t max_batch;       /* 1..16 */
+  int32_t max_seq;         /* KV capacity per sequence */
+  int32_t max_prefill_tokens; /* rows per prefill chunk (B * tokens); 0 = 8192 */
+  int32_t kv_filled;       /* KV positions already valid at init (resume on an existing cache) */
+  const uint8_t* ladder_mask; /* host, n_layers bytes: 1 = ladder layer, 0 = standard; copied */
+} ladder_config;
+
+typedef struct ladder_layer_weights {
+  const void* attn_norm;   /* [H] */
+  const void* wq;          /* [n_q_heads*head_dim][H] */
+  const void* wk;          /* [n_kv_heads*head_dim][H] */
+  const void* wv;          /* [n_kv_heads*head_dim][H] */
+  const void* wo;          /* [H][n_q_heads*head_dim] */
+  const void* mlp_norm;    /* [H] */
+  const void* w_gate;      /* [F][H] */
+  const void* w_up;        /* [F][H] */
+  const void* w_down;      /* [H][F] */
+} ladder_layer_weights;
+
+typedef struct ladder_weights {
+  const void* tok_embed;   /* [vocab][H] */
+  const void* final_norm;  /* [H] */
+  const void* lm_head;     /* [vocab][H] */
+  const ladder_layer_weights* layers; /* host array of n_layers entries; copied at init */
+} ladder_weights;
+
+typedef struct ladder_kv {
+  void* k;                 /* [n_layers][max_batch][n_kv_heads][max_seq][head_dim], dtype */
+  void* v;                 /* same layout */
+} ladder_kv;
+
+typedef struct ladder_ctx ladder_ctx;
+
+/* Validate the configuration, copy the weight/KV pointers and the mask, allocate
+ * the workspace and build the RoPE table (fp64 on the host, stored fp32).
+ * stream: a hipStream_t of the current device (NULL = the null stream).
+ * On success *out receives the context; on error *out is NULL. */
+ladder_status ladder_init(const ladder_config* cfg, const ladder_weights* w, const ladder_kv* kv,
+                          void* stream, ladder_ctx** out);
+
+/* Prompt processing: d_ids [B][T] int32 at positions start_pos..start_pos+T-1 for
+ * sequences (cache slots) 0..B-1.  Writes K/V rows of those positions.  Requires
+ * start_pos <= positions already filled and start_pos + T <= max_seq.
+ * Outputs (each nullable) are for the last position: d_logits [B][vocab] fp32,
+ * d_next [B] int32 (greedy), d_hidden [B][H] fp32 (x_{2L}). */
+ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t T, int32_t start_pos,
+                             float* d_logits, int32_t* d_next, float* d_hidden);
+
+/* One decode step: d_ids [B] int32 at position pos (pos <= positions filled,
+ * pos < max_seq).  Same outputs as ladder_prefill.  d_ids may alias d_next of the
+ * previous step, so a generation loop needs no host synchronisation.  Replays a
+ * captured HIP graph per (B, schedule) when graphs are enabled. */
+ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t pos,
+                                 float* d_logits, int32_t* d_next, float* d_hidden);
+
+/* Select the schedule (LADDER_SCHED_*) and whether decode steps use HIP graphs. */
+ladder_status ladder_set_schedule(ladder_ctx* ctx, int32_t schedule, int32_t use_graph);
+
+/* Number of KV positions the context regards as filled. */
+ladder_status ladder_filled(const ladder_ctx* ctx, int32_t* out);
+
+/* Device bytes the context allocated for its workspace. */
+ladder_status ladder_workspace_bytes(const ladder_ctx* ctx, size_t* out);
+
+/* Wait for all work of the context (its stream and internal streams). */
+ladder_status ladder_sync(ladder_ctx* ctx);
+
+/* Decode kernel kinds, for ladder_time_kernels. */
+#define LADDER_KERNEL_QKV 0      /* RMSNorm + [Wq;Wk;Wv] GEMV + RoPE + KV append */
+#define LADDER_KERNEL_ATTN 1     /* split-KV GQA decode attention (+ chunk merge) */
+#define LADDER_KERNEL_OPROJ 2    /* Wo GEMV + fused residual add */
+#define LADDER_KERNEL_GATEUP 3   /* RMSNorm + [Wgate,Wup] GEMV + SwiGLU */
+#define LADDER_KERNEL_DOWN 4     /* Wdown GEMV + fused residual add */
+#define LADDER_KERNEL_LMHEAD 5   /* final RMSNorm + LM head GEMV + greedy argmax */
+#define LADDER_N_KERNELS 6
+
+/* Profiling aid.  For each kernel kind, enqueue it on the context's stream exactly as
+ * a decode step at batch B launches it (once per layer; the LM head once), reps times,
+ * between two HIP events, and store the mean duration of one launch in microseconds
+ * in us_out[kind] (host array of LADDER_N_KERNELS floats).  Works on the context's
+ * current buffers and the position of the last decode step, whose KV row it
+ * overwrites; requires at least one filled position.  Blocks until done. */
+ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, float* us_out);
+
+/* Release the context (NULL is a no-op).  Does not free caller buffers. */
+void ladder_free(ladder_ctx* ctx);
+
+/* Static description of a status code. */
+const char* ladder_status_string(ladder_status s);
+
+/* Text of the last error recorded by the context (empty if none). */
+const char* ladder_last_error(const ladder_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LADDER_H */

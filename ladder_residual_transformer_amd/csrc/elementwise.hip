@@ -1,0 +1,138 @@
+// Small memory-bound kernels of the prefill path and the decode step prologue.
+#include "common.hpp"
+#include "kernels.h"
+
+namespace ladder {
+
+// x[m][:] = E[ids[m]][:] in fp32.  Ids outside [0, V) are clamped so a bad id cannot
+// read outside the table.
+template <typename WT>
+__global__ __launch_bounds__(256) void embed_kernel(const WT* table, int V, int H, const int* ids, float* x) {
+  const int m = blockIdx.x;
+  int id = ids[m];
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  const WT* row = table + (size_t)id * H;
+  for (int i = threadIdx.x; i < H; i += 256) x[(size_t)m * H + i] = load_w<WT>(row + i);
+}
+
+template <typename WT>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int ldx, const WT* gain, float eps, int H,
+                                                      void* out, int out_bf16) {
+  __shared__ float part[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float* xr = x + (size_t)m * ldx;
+  float s = 0.f;
+  for (int i = tid; i < H; i += 256) s = fmaf(xr[i], xr[i], s);
+  s = wave_sum(s);
+  if ((tid & 63) == 0) part[tid >> 6] = s;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int i = tid; i < H; i += 256) {
+    const float v = xr[i] * inv * load_w<WT>(gain + i);
+    if (out_bf16) ((uint16_t*)out)[(size_t)m * H + i] = f32_to_bf16(v);
+    else ((float*)out)[(size_t)m * H + i] = v;
+  }
+}
+
+// Row m = b*T + t of qkv holds token t of sequence b at position start_pos + t.
+template <typename WT>
+__global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int T, int start_pos, int nq, int nkv, int hd,
+                                                      const float* rope_cos, const float* rope_sin, float* q_out,
+                                                      WT* k_cache, WT* v_cache, int max_seq) {
+  const int m = blockIdx.x;
+  const int b = m / T, t = m % T, pos = start_pos + t;
+  const int qr = nq * hd, kr = nkv * hd, half = hd / 2;
+  const float* row = qkv + (size_t)m * (qr + 2 * kr);
+  for (int i = threadIdx.x; i < (qr + kr) / 2; i += 256) {
+    const int n = 2 * i;
+    const int d = (n < qr ? n : n - qr) % hd;
+    const float c = rope_cos[(size_t)pos * half + d / 2], s = rope_sin[(size_t)pos * half + d / 2];
+    const float y0 = row[n], y1 = row[n + 1];
+    const float r0 = y0 * c - y1 * s, r1 = y0 * s + y1 * c;
+    if (n < qr) {
+      q_out[(size_t)m * qr + n] = r0;
+      q_out[(size_t)m * qr + n + 1] = r1;
+    } else {
+      const int kvh = (n - qr) / hd;
+      WT* dst = k_cache + (((size_t)b * nkv + kvh) * max_seq + pos) * hd + d;
+      store_w<WT>(dst, r0);
+      store_w<WT>(dst + 1, r1);
+    }
+  }
+  for (int i = threadIdx.x; i < kr; i += 256) {
+    const int kvh = i / hd, d = i % hd;
+    store_w<WT>(v_cache + (((size_t)b * nkv + kvh) * max_seq + pos) * hd + d, row[qr + kr + i]);
+  }
+}
+
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* gu, size_t total, int F, void* a, int a_bf16) {
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+    const size_t m = i / F, n = i % F;
+    const float g = gu[m * 2 * F + 2 * n], u = gu[m * 2 * F + 2 * n + 1];
+    const float v = silu(g) * u;
+    if (a_bf16) ((uint16_t*)a)[i] = f32_to_bf16(v);
+    else ((float*)a)[i] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void add_kernel(const float* x, const float* y, float* out, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) out[i] = x[i] + y[i];
+}
+
+__global__ void decode_prologue_kernel(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos) {
+  const int i = threadIdx.x;
+  if (i < B) ids_dst[i] = ids_src[i];
+  if (i == 0) *d_pos = pos;
+}
+
+static unsigned grid_for(size_t n) {
+  size_t g = (n + 255) / 256;
+  if (g > 4096) g = 4096;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+hipError_t launch_embed(int wdtype, const void* table, int V, int H, const int* ids, int M, float* x, hipStream_t s) {
+  if (wdtype == W_BF16) hipLaunchKernelGGL(embed_kernel<uint16_t>, dim3(M), dim3(256), 0, s, (const uint16_t*)table, V, H, ids, x);
+  else hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, s, (const float*)table, V, H, ids, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int wdtype, const float* x, int ldx, const void* gain, float eps, int M, int H,
+                          void* out, int out_bf16, hipStream_t s) {
+  if (wdtype == W_BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<uint16_t>, dim3(M), dim3(256), 0, s, x, ldx, (const uint16_t*)gain, eps, H, out, out_bf16);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, s, x, ldx, (const float*)gain, eps, H, out, out_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_kv(int wdtype, const float* qkv, int B, int T, int start_pos, int nq, int nkv, int hd,
+                          const float* rope_cos, const float* rope_sin, float* q_out,
+                          void* k_cache, void* v_cache, int max_seq, hipStream_t s) {
+  if (wdtype == W_BF16)
+    hipLaunchKernelGGL(rope_kv_kernel<uint16_t>, dim3(B * T), dim3(256), 0, s, qkv, T, start_pos, nq, nkv, hd,
+                       rope_cos, rope_sin, q_out, (uint16_t*)k_cache, (uint16_t*)v_cache, max_seq);
+  else
+    hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(B * T), dim3(256), 0, s, qkv, T, start_pos, nq, nkv, hd,
+                       rope_cos, rope_sin, q_out, (float*)k_cache, (float*)v_cache, max_seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const float* gu, int M, int F, void* a, int a_bf16, hipStream_t s) {
+  const size_t total = (size_t)M * F;
+  hipLaunchKernelGGL(swiglu_kernel, dim3(grid_for(total)), dim3(256), 0, s, gu, total, F, a, a_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_add(const float* x, const float* y, float* out, size_t n, hipStream_t s) {
+  hipLaunchKernelGGL(add_kernel, dim3(grid_for(n)), dim3(256), 0, s, x, y, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_prologue(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, hipStream_t s) {
+  hipLaunchKernelGGL(decode_prologue_kernel, dim3(1), dim3(64), 0, s, ids_src, ids_dst, B, d_pos, pos);
+  return hipGetLastError();
+}
+
+}  // namespace ladder

@@ -1,0 +1,106 @@
+// Host-side launchers of the gfx950 kernels (internal to libladder; not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ladder {
+
+enum WDtype { W_F32 = 0, W_BF16 = 1 };
+
+// Rows of a (virtual) weight matrix [N][K] gathered from up to three stored
+// matrices, each row-major [rows][K]:
+//   interleave == 0: rows [0,n0) from m[0], [n0,n1) from m[1], [n1,N) from m[2];
+//   interleave == 1: row r is row r/2 of m[r & 1] (gate/up pairs side by side).
+struct RowSrc {
+  const void* m[3];
+  int n0, n1;
+  int interleave;
+};
+
+// ---------------------------------------------------------------- decode GEMV
+enum GemvEpi {
+  EPI_STORE = 0,        // out[b][n] = y
+  EPI_ADD = 1,          // out[b][n] = xres[b][n] + y   (ladder residual add, fused)
+  EPI_QKV_ROPE = 2,     // q -> out (fp32, rotated); k (rotated), v -> KV cache at pos
+  EPI_GATEUP_SWIGLU = 3,// out[b][n] = silu(y[2n]) * y[2n+1]
+  EPI_LOGITS = 4,       // out[b][n] = y; greedy argmax -> next_out[b]
+};
+
+struct GemvParams {
+  int wdtype;
+  RowSrc rows;
+  int N, K, B;
+  const float* x; int ldx;        // input rows [B][ldx] (fp32)
+  const void* gain; float eps;    // RMSNorm gain of the input (nullptr: no norm)
+  int epi;
+  float* out; int ldo;
+  const float* xres; int ldr;     // EPI_ADD
+  // EPI_QKV_ROPE
+  void* k_cache; void* v_cache;   // this layer: [max_batch][n_kv][max_seq][head_dim]
+  int q_rows, kv_rows, head_dim, max_seq, n_kv;
+  const float* rope_cos; const float* rope_sin;   // [max_seq][head_dim/2]
+  const int* d_pos;
+  // EPI_LOGITS
+  float* best_val; int* best_idx; int* arg_counter; int* next_out;
+  // split-K workspace (used when B is large enough that K is split)
+  float* part; float* part_sq; int* counters;
+};
+
+struct GemvWorkspaceReq { size_t part_floats, part_sq_floats, counters, best; };
+// Workspace a decode GEMV of this shape needs at batch B (upper bounds).
+GemvWorkspaceReq gemv_workspace(int wdtype, int N, int K, int B);
+hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
+
+// ----------------------------------------------------------- decode attention
+struct AttnDecodeParams {
+  int wdtype;                          // KV cache element type
+  const float* q;                      // [B][nq*hd], rotated
+  const void* k_cache; const void* v_cache;  // this layer's base
+  int max_seq, nq, nkv, hd, B;
+  const int* d_pos;                    // keys 0..pos
+  int n_split;
+  float* part;                         // [B][nq][n_split][hd+2]
+  int* counters;                       // [B][nkv]
+  float* out;                          // [B][nq*hd]
+};
+int attn_decode_splits(int max_seq);
+hipError_t launch_attn_decode(const AttnDecodeParams& p, hipStream_t s);
+
+// ---------------------------------------------------------- prefill attention
+struct AttnPrefillParams {
+  int wdtype;
+  const float* q;                      // [B*T][nq*hd] rotated, fp32
+  const void* k_cache; const void* v_cache;
+  int max_seq, nq, nkv, hd, B, T, start_pos;
+  void* out; int out_bf16;             // [B*T][nq*hd]
+};
+hipError_t launch_attn_prefill(const AttnPrefillParams& p, hipStream_t s);
+
+// ----------------------------------------------------------------- GEMM (prefill)
+// C[M][N] (fp32, ldc) = (res ? res[M][N] : 0) + A[M][K] . B^T, B rows from RowSrc.
+struct GemmParams {
+  int wdtype;                          // W_BF16: A bf16 (lda), MFMA; W_F32: A fp32, VALU
+  const void* A; int lda;
+  RowSrc rows;
+  int M, N, K;
+  float* C; int ldc;
+  const float* res; int ldr;
+};
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------ elementwise
+hipError_t launch_embed(int wdtype, const void* table, int V, int H, const int* ids, int M, float* x, hipStream_t s);
+// out[m][:] = RMSNorm(x[m*ldx + :]) * gain, as bf16 (out_bf16) or fp32
+hipError_t launch_rmsnorm(int wdtype, const float* x, int ldx, const void* gain, float eps, int M, int H,
+                          void* out, int out_bf16, hipStream_t s);
+// qkv [B*T][q_rows + 2 kv_rows] -> q (rotated, fp32) and KV cache rows start_pos..start_pos+T-1
+hipError_t launch_rope_kv(int wdtype, const float* qkv, int B, int T, int start_pos, int nq, int nkv, int hd,
+                          const float* rope_cos, const float* rope_sin, float* q_out,
+                          void* k_cache, void* v_cache, int max_seq, hipStream_t s);
+// gu [M][2F] interleaved (gate, up) -> a [M][F] as bf16 or fp32
+hipError_t launch_swiglu(const float* gu, int M, int F, void* a, int a_bf16, hipStream_t s);
+hipError_t launch_add(const float* x, const float* y, float* out, size_t n, hipStream_t s);
+hipError_t launch_decode_prologue(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, hipStream_t s);
+
+}  // namespace ladder

@@ -1,0 +1,842 @@
+// libladder runtime: context, workspace, module schedule and the C ABI of include/ladder.h.
+//
+// Module loop (decode and prefill).  Modules m = 0..2L-1 alternate attention / MLP;
+// module m reads x_src with src = m-1 for a ladder layer (x_{-1} = x_0) and src = m for
+// a standard one, and the stream advances as x_{m+1} = x_m + out_m.  Because a ladder
+// module never reads the output of the module right before it, module m+1 can start
+// before x_{m+1} exists.  Three schedules realise this on one GPU:
+//   SERIAL: everything on one stream in program order (the reference order);
+//   SIDE:   modules on the main stream, each residual add on a side stream; module m+1
+//           waits only for the add that produced its own (stale) input;
+//   DUAL:   attention modules on stream A, MLP modules on stream B, each residual add
+//           fused into the module's output projection.  A module waits for its input
+//           residual, and its output projection waits for x_m, produced by the other
+//           stream.  Ladder modules overlap the previous module (attention of layer l+1
+//           runs beside the MLP of layer l).
+// All three compute every value with the same kernels and the same arithmetic, so
+// their results are bitwise identical (the race check of the test suite).
+//
+// Two residual buffers are in flight (x_{m-1} and x_m while x_{m+1} is formed into the
+// slot of x_{m-1}); the ordering argument for each schedule is in the comments of
+// run_modules().
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "ladder.h"
+#include "kernels.h"
+
+using namespace ladder;
+
+namespace {
+
+struct StreamScratch {
+  // decode
+  float* q = nullptr;
+  float* attn_part = nullptr;
+  int* attn_cnt = nullptr;
+  float* o = nullptr;
+  float* a = nullptr;
+  float* gpart = nullptr;
+  float* gpart_sq = nullptr;
+  int* gcnt = nullptr;
+  // prefill
+  void* u = nullptr;
+  float* qkv = nullptr;
+  float* qr = nullptr;
+  void* ob = nullptr;
+  float* gu = nullptr;
+  void* ab = nullptr;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Carver {
+  size_t off = 0;
+  char* base = nullptr;
+  template <typename T>
+  T* take(size_t count) {
+    const size_t bytes = align_up(count * sizeof(T) + 16, 256);
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+}  // namespace
+
+struct ladder_ctx {
+  ladder_config cfg{};
+  std::vector<uint8_t> mask;
+  std::vector<ladder_layer_weights> layers;
+  ladder_weights w{};
+  ladder_kv kv{};
+  int dev = 0;
+  int esz = 2;               // bytes per weight / KV element
+  int wdt = W_BF16;
+  int qrows = 0, kvrows = 0; // n_q_heads*head_dim, n_kv_heads*head_dim
+  int n_split = 1;
+  int mmax = 0;              // prefill rows per chunk
+  size_t layer_kv_elems = 0;
+
+  hipStream_t user = nullptr;   // caller's stream
+  hipStream_t s0 = nullptr;     // origin stream of every call (graph capture happens here)
+  hipStream_t sa = nullptr, sb = nullptr, side = nullptr;
+  std::vector<hipEvent_t> ev_x, ev_out;
+  hipEvent_t ev_fork = nullptr, ev_in = nullptr, ev_done = nullptr;
+
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+  float* dx[2] = {nullptr, nullptr};     // decode residual ring [max_batch][H]
+  float* dout[2] = {nullptr, nullptr};   // decode module outputs (SERIAL / SIDE)
+  float* px[2] = {nullptr, nullptr};     // prefill residual ring [mmax][H]
+  float* pout[2] = {nullptr, nullptr};
+  int* ids_dev = nullptr;
+  int* pos_dev = nullptr;
+  int* ids_chunk = nullptr;
+  float* logits = nullptr;
+  int* next = nullptr;
+  float* best_val = nullptr;
+  int* best_idx = nullptr;
+  int* arg_cnt = nullptr;
+  StreamScratch sc[2];
+
+  int sched = LADDER_SCHED_DUAL;
+  int use_graph = 1;
+  std::map<int, hipGraphExec_t> graphs;
+  int filled = 0;
+  bool broken = false;
+  std::string err;
+};
+
+namespace {
+
+ladder_status fail(ladder_ctx* c, ladder_status s, const char* fmt, const char* what = "") {
+  if (c) {
+    char buf[512];
+    snprintf(buf, sizeof buf, fmt, what);
+    c->err = buf;
+  }
+  return s;
+}
+
+#define HIPCHK(call)                                                                    \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess) {                                                             \
+      ctx->broken = true;                                                               \
+      return fail(ctx, LADDER_ERR_HIP, "%s", (std::string(#call) + ": " + hipGetErrorString(e_)).c_str()); \
+    }                                                                                   \
+  } while (0)
+
+bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+ladder_status validate(const ladder_config* c, const ladder_weights* w, const ladder_kv* kv) {
+  if (!c || !w || !kv || !c->ladder_mask || !w->layers) return LADDER_ERR_ARG;
+  if (c->n_layers < 1 || c->hidden < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 ||
+      c->ffn < 1 || c->vocab < 1 || c->max_batch < 1 || c->max_seq < 1 || c->max_prefill_tokens < 0)
+    return LADDER_ERR_ARG;
+  if (c->dtype != LADDER_F32 && c->dtype != LADDER_BF16) return LADDER_ERR_ARG;
+  if (!(c->rope_theta > 0.0) || !(c->norm_eps >= 0.0f)) return LADDER_ERR_ARG;
+  if (c->kv_filled < 0 || c->kv_filled > c->max_seq) return LADDER_ERR_ARG;
+  if (c->max_batch > 16) return LADDER_ERR_SHAPE;
+  if (c->n_q_heads % c->n_kv_heads != 0 || c->n_q_heads / c->n_kv_heads > 16) return LADDER_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return LADDER_ERR_SHAPE;
+  const int vec = c->dtype == LADDER_BF16 ? 8 : 4;
+  if (c->hidden % vec || c->ffn % vec) return LADDER_ERR_SHAPE;
+  if (c->dtype == LADDER_BF16 &&
+      (c->hidden % 64 || c->ffn % 64 || (c->n_q_heads * c->head_dim) % 64))
+    return LADDER_ERR_SHAPE;   // K of every prefill contraction is a whole number of 64-wide MFMA steps
+  for (int l = 0; l < c->n_layers; ++l)
+    if (c->ladder_mask[l] > 1) return LADDER_ERR_ARG;
+  if (!aligned16(w->tok_embed) || !aligned16(w->final_norm) || !aligned16(w->lm_head)) return LADDER_ERR_ARG;
+  for (int l = 0; l < c->n_layers; ++l) {
+    const ladder_layer_weights& L = w->layers[l];
+    const void* ps[] = {L.attn_norm, L.wq, L.wk, L.wv, L.wo, L.mlp_norm, L.w_gate, L.w_up, L.w_down};
+    for (const void* p : ps)
+      if (!aligned16(p)) return LADDER_ERR_ARG;
+  }
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return LADDER_ERR_ARG;
+  return LADDER_OK;
+}
+
+// Lay the workspace out (base == nullptr: only measure).
+void carve(ladder_ctx* c, Carver& cv) {
+  const ladder_config& g = c->cfg;
+  const int H = g.hidden, F = g.ffn, V = g.vocab, B = g.max_batch;
+  const int qkv = c->qrows + 2 * c->kvrows;
+  c->rope_cos = cv.take<float>((size_t)g.max_seq * g.head_dim / 2);
+  c->rope_sin = cv.take<float>((size_t)g.max_seq * g.head_dim / 2);
+  for (int i = 0; i < 2; ++i) {
+    c->dx[i] = cv.take<float>((size_t)B * H);
+    c->dout[i] = cv.take<float>((size_t)B * H);
+    c->px[i] = cv.take<float>((size_t)c->mmax * H);
+    c->pout[i] = cv.take<float>((size_t)c->mmax * H);
+  }
+  c->ids_dev = cv.take<int>(B);
+  c->pos_dev = cv.take<int>(1);
+  c->ids_chunk = cv.take<int>(c->mmax);
+  c->logits = cv.take<float>((size_t)B * V);
+  c->next = cv.take<int>(B);
+  // GEMV split-K / argmax scratch: the largest need over every decode GEMV shape and batch
+  GemvWorkspaceReq need{};
+  const int shapes[5][2] = {{qkv, H}, {H, c->qrows}, {2 * F, H}, {H, F}, {V, H}};
+  for (int b = 1; b <= B; ++b)
+    for (auto& sh : shapes) {
+      GemvWorkspaceReq r = gemv_workspace(c->wdt, sh[0], sh[1], b);
+      need.part_floats = std::max(need.part_floats, r.part_floats);
+      need.part_sq_floats = std::max(need.part_sq_floats, r.part_sq_floats);
+      need.counters = std::max(need.counters, r.counters);
+      need.best = std::max(need.best, r.best);
+    }
+  c->best_val = cv.take<float>(need.best);
+  c->best_idx = cv.take<int>(need.best);
+  c->arg_cnt = cv.take<int>(1);
+  const size_t ue = c->wdt == W_BF16 ? 2 : 4;
+  for (int s = 0; s < 2; ++s) {
+    StreamScratch& sc = c->sc[s];
+    sc.q = cv.take<float>((size_t)B * c->qrows);
+    sc.attn_part = cv.take<float>((size_t)B * g.n_q_heads * c->n_split * (g.head_dim + 2));
+    sc.attn_cnt = cv.take<int>((size_t)B * g.n_kv_heads);
+    sc.o = cv.take<float>((size_t)B * c->qrows);
+    sc.a = cv.take<float>((size_t)B * F);
+    sc.gpart = cv.take<float>(need.part_floats);
+    sc.gpart_sq = cv.take<float>(need.part_sq_floats);
+    sc.gcnt = cv.take<int>(need.counters);
+    sc.u = cv.take<char>((size_t)c->mmax * H * ue);
+    sc.qkv = cv.take<float>((size_t)c->mmax * qkv);
+    sc.qr = cv.take<float>((size_t)c->mmax * c->qrows);
+    sc.ob = cv.take<char>((size_t)c->mmax * c->qrows * ue);
+    sc.gu = cv.take<float>((size_t)c->mmax * 2 * F);
+    sc.ab = cv.take<char>((size_t)c->mmax * F * ue);
+  }
+}
+
+inline int module_src(const ladder_ctx* c, int m) {
+  return c->mask[m / 2] ? (m > 0 ? m - 1 : 0) : m;
+}
+
+void* layer_k(const ladder_ctx* c, int l) { return (char*)c->kv.k + (size_t)l * c->layer_kv_elems * c->esz; }
+void* layer_v(const ladder_ctx* c, int l) { return (char*)c->kv.v + (size_t)l * c->layer_kv_elems * c->esz; }
+
+// Stream running module m under the current schedule.
+hipStream_t module_stream(const ladder_ctx* c, int m) {
+  if (c->sched == LADDER_SCHED_DUAL) return (m % 2 == 0) ? c->sa : c->sb;
+  return c->s0;
+}
+
+StreamScratch& module_scratch(ladder_ctx* c, int m) {
+  return c->sc[(c->sched == LADDER_SCHED_DUAL && m % 2 == 1) ? 1 : 0];
+}
+
+// ---------------------------------------------------------------- decode module
+// Parameter builders of the decode kernels (shared by the module loop and the
+// per-kernel timing entry point, so both launch exactly the same configuration).
+GemvParams gemv_base(const ladder_ctx* ctx, int B, const StreamScratch& sc) {
+  GemvParams p{};
+  p.wdtype = ctx->wdt;
+  p.B = B;
+  p.eps = ctx->cfg.norm_eps;
+  p.part = sc.gpart;
+  p.part_sq = sc.gpart_sq;
+  p.counters = sc.gcnt;
+  return p;
+}
+
+// RMSNorm + [Wq;Wk;Wv] + RoPE + KV append of layer l
+GemvParams qkv_params(const ladder_ctx* ctx, int l, int B, const float* xin, const StreamScratch& sc) {
+  const ladder_config& g = ctx->cfg;
+  const ladder_layer_weights& L = ctx->layers[l];
+  GemvParams p = gemv_base(ctx, B, sc);
+  p.rows = RowSrc{{L.wq, L.wk, L.wv}, ctx->qrows, ctx->qrows + ctx->kvrows, 0};
+  p.N = ctx->qrows + 2 * ctx->kvrows;
+  p.K = g.hidden;
+  p.x = xin;
+  p.ldx = g.hidden;
+  p.gain = L.attn_norm;
+  p.epi = EPI_QKV_ROPE;
+  p.out = sc.q;
+  p.ldo = ctx->qrows;
+  p.k_cache = layer_k(ctx, l);
+  p.v_cache = layer_v(ctx, l);
+  p.q_rows = ctx->qrows;
+  p.kv_rows = ctx->kvrows;
+  p.head_dim = g.head_dim;
+  p.max_seq = g.max_seq;
+  p.n_kv = g.n_kv_heads;
+  p.rope_cos = ctx->rope_cos;
+  p.rope_sin = ctx->rope_sin;
+  p.d_pos = ctx->pos_dev;
+  return p;
+}
+
+AttnDecodeParams attn_params(const ladder_ctx* ctx, int l, int B, const StreamScratch& sc) {
+  const ladder_config& g = ctx->cfg;
+  AttnDecodeParams a{};
+  a.wdtype = ctx->wdt;
+  a.q = sc.q;
+  a.k_cache = layer_k(ctx, l);
+  a.v_cache = layer_v(ctx, l);
+  a.max_seq = g.max_seq;
+  a.nq = g.n_q_heads;
+  a.nkv = g.n_kv_heads;
+  a.hd = g.head_dim;
+  a.B = B;
+  a.d_pos = ctx->pos_dev;
+  a.n_split = ctx->n_split;
+  a.part = sc.attn_part;
+  a.counters = sc.attn_cnt;
+  a.out = sc.o;
+  return a;
+}
+
+// RMSNorm + [Wgate,Wup] (row pairs) + SwiGLU of layer l
+GemvParams gateup_params(const ladder_ctx* ctx, int l, int B, const float* xin, const StreamScratch& sc) {
+  const ladder_config& g = ctx->cfg;
+  const ladder_layer_weights& L = ctx->layers[l];
+  GemvParams p = gemv_base(ctx, B, sc);
+  p.rows = RowSrc{{L.w_gate, L.w_up, nullptr}, 0, 0, 1};
+  p.N = 2 * g.ffn;
+  p.K = g.hidden;
+  p.x = xin;
+  p.ldx = g.hidden;
+  p.gain = L.mlp_norm;
+  p.epi = EPI_GATEUP_SWIGLU;
+  p.out = sc.a;
+  p.ldo = g.ffn;
+  return p;
+}
+
+// Output projection (Wo for attention, Wdown for the MLP) of module m: with the residual
+// add fused (out_x = x_m + out_m) or storing out_m.
+GemvParams outproj_params(const ladder_ctx* ctx, int m, int B, const StreamScratch& sc, const float* xm,
+                          float* out_x, float* out_store) {
+  const ladder_config& g = ctx->cfg;
+  const ladder_layer_weights& L = ctx->layers[m / 2];
+  const bool attn = m % 2 == 0;
+  GemvParams o = gemv_base(ctx, B, sc);
+  o.rows = RowSrc{{attn ? L.wo : L.w_down, nullptr, nullptr}, g.hidden, g.hidden, 0};
+  o.N = g.hidden;
+  o.K = attn ? ctx->qrows : g.ffn;
+  o.x = attn ? sc.o : sc.a;
+  o.ldx = o.K;
+  o.gain = nullptr;
+  if (out_x) {
+    o.epi = EPI_ADD;
+    o.xres = xm;
+    o.ldr = g.hidden;
+    o.out = out_x;
+  } else {
+    o.epi = EPI_STORE;
+    o.out = out_store;
+  }
+  o.ldo = g.hidden;
+  return o;
+}
+
+GemvParams lmhead_params(const ladder_ctx* ctx, const float* x, int ldx, int B) {
+  const ladder_config& g = ctx->cfg;
+  GemvParams p = gemv_base(ctx, B, ctx->sc[0]);
+  p.rows = RowSrc{{ctx->w.lm_head, nullptr, nullptr}, g.vocab, g.vocab, 0};
+  p.N = g.vocab;
+  p.K = g.hidden;
+  p.x = x;
+  p.ldx = ldx;
+  p.gain = ctx->w.final_norm;
+  p.epi = EPI_LOGITS;
+  p.out = ctx->logits;
+  p.ldo = g.vocab;
+  p.best_val = ctx->best_val;
+  p.best_idx = ctx->best_idx;
+  p.arg_counter = ctx->arg_cnt;
+  p.next_out = ctx->next;
+  return p;
+}
+
+// Enqueue module m of one decode step.  out_x != nullptr: fused residual add
+// (out_x = x_m + out_m); else out_m goes to out_store.
+ladder_status decode_module(ladder_ctx* ctx, int m, int B, const float* xin, const float* xm, float* out_x,
+                            float* out_store, hipStream_t s, bool wait_xm, hipEvent_t ev_xm) {
+  const int l = m / 2;
+  StreamScratch& sc = module_scratch(ctx, m);
+  if (m % 2 == 0) {
+    HIPCHK(launch_gemv(qkv_params(ctx, l, B, xin, sc), s));
+    HIPCHK(launch_attn_decode(attn_params(ctx, l, B, sc), s));
+  } else {
+    HIPCHK(launch_gemv(gateup_params(ctx, l, B, xin, sc), s));
+  }
+  if (out_x && wait_xm) HIPCHK(hipStreamWaitEvent(s, ev_xm, 0));
+  HIPCHK(launch_gemv(outproj_params(ctx, m, B, sc, xm, out_x, out_store), s));
+  return LADDER_OK;
+}
+
+// ---------------------------------------------------------------- prefill module
+ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos, const float* xin,
+                             const float* xm, float* out_x, float* out_store, hipStream_t s, bool wait_xm,
+                             hipEvent_t ev_xm) {
+  const ladder_config& g = ctx->cfg;
+  const int l = m / 2, M = B * T;
+  const ladder_layer_weights& L = ctx->layers[l];
+  StreamScratch& sc = module_scratch(ctx, m);
+  const int bf = ctx->wdt == W_BF16;
+  GemmParams gp{};
+  gp.wdtype = ctx->wdt;
+  gp.M = M;
+  const void* proj_in;
+  int proj_k;
+  const void* proj_w;
+  if (m % 2 == 0) {
+    HIPCHK(launch_rmsnorm(ctx->wdt, xin, g.hidden, L.attn_norm, g.norm_eps, M, g.hidden, sc.u, bf, s));
+    const int nqkv = ctx->qrows + 2 * ctx->kvrows;
+    gp.A = sc.u;
+    gp.lda = g.hidden;
+    gp.rows = RowSrc{{L.wq, L.wk, L.wv}, ctx->qrows, ctx->qrows + ctx->kvrows, 0};
+    gp.N = nqkv;
+    gp.K = g.hidden;
+    gp.C = sc.qkv;
+    gp.ldc = nqkv;
+    HIPCHK(launch_gemm(gp, s));
+    HIPCHK(launch_rope_kv(ctx->wdt, sc.qkv, B, T, start_pos, g.n_q_heads, g.n_kv_heads, g.head_dim, ctx->rope_cos,
+                          ctx->rope_sin, sc.qr, layer_k(ctx, l), layer_v(ctx, l), g.max_seq, s));
+    AttnPrefillParams ap{};
+    ap.wdtype = ctx->wdt;
+    ap.q = sc.qr;
+    ap.k_cache = layer_k(ctx, l);
+    ap.v_cache = layer_v(ctx, l);
+    ap.max_seq = g.max_seq;
+    ap.nq = g.n_q_heads;
+    ap.nkv = g.n_kv_heads;
+    ap.hd = g.head_dim;
+    ap.B = B;
+    ap.T = T;
+    ap.start_pos = start_pos;
+    ap.out = sc.ob;
+    ap.out_bf16 = bf;
+    HIPCHK(launch_attn_prefill(ap, s));
+    proj_in = sc.ob;
+    proj_k = ctx->qrows;
+    proj_w = L.wo;
+  } else {
+    HIPCHK(launch_rmsnorm(ctx->wdt, xin, g.hidden, L.mlp_norm, g.norm_eps, M, g.hidden, sc.u, bf, s));
+    gp.A = sc.u;
+    gp.lda = g.hidden;
+    gp.rows = RowSrc{{L.w_gate, L.w_up, nullptr}, 0, 0, 1};
+    gp.N = 2 * g.ffn;
+    gp.K = g.hidden;
+    gp.C = sc.gu;
+    gp.ldc = 2 * g.ffn;
+    HIPCHK(launch_gemm(gp, s));
+    HIPCHK(launch_swiglu(sc.gu, M, g.ffn, sc.ab, bf, s));
+    proj_in = sc.ab;
+    proj_k = g.ffn;
+    proj_w = L.w_down;
+  }
+  GemmParams op{};
+  op.wdtype = ctx->wdt;
+  op.A = proj_in;
+  op.lda = proj_k;
+  op.rows = RowSrc{{proj_w, nullptr, nullptr}, g.hidden, g.hidden, 0};
+  op.M = M;
+  op.N = g.hidden;
+  op.K = proj_k;
+  op.ldc = g.hidden;
+  if (out_x) {
+    if (wait_xm) HIPCHK(hipStreamWaitEvent(s, ev_xm, 0));
+    op.C = out_x;
+    op.res = xm;
+    op.ldr = g.hidden;
+  } else {
+    op.C = out_store;
+  }
+  HIPCHK(launch_gemm(op, s));
+  return LADDER_OK;
+}
+
+// Enqueue the module loop on the context's streams, starting from x_0 in X[0] and
+// finishing with x_{2L} in X[(2L) % 2] and every stream joined into s0.
+//
+// Ordering (two residual slots: x_j lives in X[j % 2]):
+//   SERIAL - program order on s0.
+//   SIDE   - module m (s0) waits ev_x[src] recorded by the add that produced x_src; the
+//            add m (side) waits ev_out[m], i.e. module m is complete, which also means
+//            every earlier reader of X[(m+1) % 2] (module m's own input x_{m-1}, the add
+//            m-1) is done before x_{m+1} overwrites it.  out_m alternates two buffers;
+//            module m+2 overwrites OUT[m % 2] only after waiting for an input produced by
+//            add m or later.
+//   DUAL   - module m runs on stream m % 2.  Its input x_src was produced by module
+//            src-1: on the same stream for a ladder module, else waited for via
+//            ev_x[src].  Its output projection adds x_m, produced by module m-1 on the
+//            other stream, so it waits for ev_x[m] first; that wait also orders the
+//            overwrite of X[(m+1) % 2] (x_{m-1}) after module m-1's last read of it.
+template <typename ModuleFn>
+ladder_status run_modules(ladder_ctx* ctx, float* const X[2], float* const OUT[2], size_t add_elems,
+                          ModuleFn&& module) {
+  const int NM = 2 * ctx->cfg.n_layers;
+  const int sched = ctx->sched;
+  if (sched == LADDER_SCHED_DUAL) {
+    HIPCHK(hipEventRecord(ctx->ev_fork, ctx->s0));
+    HIPCHK(hipStreamWaitEvent(ctx->sa, ctx->ev_fork, 0));
+    HIPCHK(hipStreamWaitEvent(ctx->sb, ctx->ev_fork, 0));
+  }
+  for (int m = 0; m < NM; ++m) {
+    const int src = module_src(ctx, m);
+    const float* xin = X[src % 2];
+    const float* xm = X[m % 2];
+    float* xn = X[(m + 1) % 2];
+    hipStream_t s = module_stream(ctx, m);
+    ladder_status st;
+    if (sched == LADDER_SCHED_SERIAL) {
+      st = module(m, xin, xm, nullptr, OUT[m % 2], s, false, nullptr);
+      if (st) return st;
+      HIPCHK(launch_add(xm, OUT[m % 2], xn, add_elems, s));
+    } else if (sched == LADDER_SCHED_SIDE) {
+      if (src > 0) HIPCHK(hipStreamWaitEvent(s, ctx->ev_x[src], 0));
+      st = module(m, xin, xm, nullptr, OUT[m % 2], s, false, nullptr);
+      if (st) return st;
+      HIPCHK(hipEventRecord(ctx->ev_out[m], s));
+      HIPCHK(hipStreamWaitEvent(ctx->side, ctx->ev_out[m], 0));
+      HIPCHK(launch_add(xm, OUT[m % 2], xn, add_elems, ctx->side));
+      HIPCHK(hipEventRecord(ctx->ev_x[m + 1], ctx->side));
+    } else {
+      // producer of x_j (j >= 1) is module j-1, on stream (j-1) % 2; x_0 precedes the fork
+      const bool src_other = src > 0 && ((src - 1) % 2) != (m % 2);
+      if (src_other) HIPCHK(hipStreamWaitEvent(s, ctx->ev_x[src], 0));
+      const bool xm_other = m > 0 && ((m - 1) % 2) != (m % 2) && !(src_other && src == m);
+      st = module(m, xin, xm, xn, nullptr, s, xm_other, m > 0 ? ctx->ev_x[m] : nullptr);
+      if (st) return st;
+      HIPCHK(hipEventRecord(ctx->ev_x[m + 1], s));
+    }
+  }
+  if (sched == LADDER_SCHED_SIDE) {
+    HIPCHK(hipStreamWaitEvent(ctx->s0, ctx->ev_x[NM], 0));
+  } else if (sched == LADDER_SCHED_DUAL) {
+    HIPCHK(hipStreamWaitEvent(ctx->s0, ctx->ev_x[NM], 0));       // last MLP (stream B)
+    HIPCHK(hipStreamWaitEvent(ctx->s0, ctx->ev_x[NM - 1], 0));   // last attention (stream A)
+  }
+  return LADDER_OK;
+}
+
+ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream_t s) {
+  HIPCHK(launch_gemv(lmhead_params(ctx, x, ldx, B), s));
+  return LADDER_OK;
+}
+
+// One decode step reading ids_dev / pos_dev, leaving logits/next in the context and
+// x_{2L} in dx[(2L) % 2].  Enqueued on s0 (possibly under graph capture).
+ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
+  const ladder_config& g = ctx->cfg;
+  HIPCHK(launch_embed(ctx->wdt, ctx->w.tok_embed, g.vocab, g.hidden, ctx->ids_dev, B, ctx->dx[0], ctx->s0));
+  auto mod = [&](int m, const float* xin, const float* xm, float* xn, float* store, hipStream_t s, bool wait,
+                 hipEvent_t ev) { return decode_module(ctx, m, B, xin, xm, xn, store, s, wait, ev); };
+  ladder_status st = run_modules(ctx, ctx->dx, ctx->dout, (size_t)B * g.hidden, mod);
+  if (st) return st;
+  return lm_head(ctx, ctx->dx[(2 * g.n_layers) % 2], g.hidden, B, ctx->s0);
+}
+
+ladder_status begin_call(ladder_ctx* ctx) {
+  HIPCHK(hipSetDevice(ctx->dev));
+  HIPCHK(hipEventRecord(ctx->ev_in, ctx->user));
+  HIPCHK(hipStreamWaitEvent(ctx->s0, ctx->ev_in, 0));
+  return LADDER_OK;
+}
+
+ladder_status end_call(ladder_ctx* ctx) {
+  HIPCHK(hipEventRecord(ctx->ev_done, ctx->s0));
+  HIPCHK(hipStreamWaitEvent(ctx->user, ctx->ev_done, 0));
+  return LADDER_OK;
+}
+
+ladder_status copy_outputs(ladder_ctx* ctx, int B, const float* x_last, size_t x_pitch, float* d_logits,
+                           int32_t* d_next, float* d_hidden) {
+  const ladder_config& g = ctx->cfg;
+  if (d_logits)
+    HIPCHK(hipMemcpyAsync(d_logits, ctx->logits, (size_t)B * g.vocab * 4, hipMemcpyDeviceToDevice, ctx->s0));
+  if (d_next) HIPCHK(hipMemcpyAsync(d_next, ctx->next, (size_t)B * 4, hipMemcpyDeviceToDevice, ctx->s0));
+  if (d_hidden)
+    HIPCHK(hipMemcpy2DAsync(d_hidden, (size_t)g.hidden * 4, x_last, x_pitch, (size_t)g.hidden * 4, B,
+                            hipMemcpyDeviceToDevice, ctx->s0));
+  return LADDER_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+const char* ladder_status_string(ladder_status s) {
+  switch (s) {
+    case LADDER_OK: return "ok";
+    case LADDER_ERR_ARG: return "invalid argument";
+    case LADDER_ERR_SHAPE: return "unsupported shape";
+    case LADDER_ERR_CAPACITY: return "capacity exceeded (batch or sequence length)";
+    case LADDER_ERR_STATE: return "KV positions read before they were written";
+    case LADDER_ERR_HIP: return "HIP runtime error";
+    case LADDER_ERR_OOM: return "out of device memory";
+    default: return "unknown status";
+  }
+}
+
+const char* ladder_last_error(const ladder_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+void ladder_free(ladder_ctx* ctx) {
+  if (!ctx) return;
+  (void)hipSetDevice(ctx->dev);
+  if (ctx->s0) (void)hipStreamSynchronize(ctx->s0);
+  for (auto& kv : ctx->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (hipEvent_t e : ctx->ev_x) if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : ctx->ev_out) if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : {ctx->ev_fork, ctx->ev_in, ctx->ev_done}) if (e) (void)hipEventDestroy(e);
+  for (hipStream_t s : {ctx->sa, ctx->sb, ctx->side}) {
+    if (s) { (void)hipStreamSynchronize(s); (void)hipStreamDestroy(s); }
+  }
+  if (ctx->s0) (void)hipStreamDestroy(ctx->s0);
+  if (ctx->ws) (void)hipFree(ctx->ws);
+  delete ctx;
+}
+
+ladder_status ladder_init(const ladder_config* cfg, const ladder_weights* w, const ladder_kv* kv, void* stream,
+                          ladder_ctx** out) {
+  if (!out) return LADDER_ERR_ARG;
+  *out = nullptr;
+  ladder_status v = validate(cfg, w, kv);
+  if (v != LADDER_OK) return v;
+  ladder_ctx* ctx = new ladder_ctx();
+  ctx->cfg = *cfg;
+  ctx->mask.assign(cfg->ladder_mask, cfg->ladder_mask + cfg->n_layers);
+  ctx->cfg.ladder_mask = ctx->mask.data();
+  ctx->layers.assign(w->layers, w->layers + cfg->n_layers);
+  ctx->w = *w;
+  ctx->w.layers = ctx->layers.data();
+  ctx->kv = *kv;
+  ctx->wdt = cfg->dtype == LADDER_BF16 ? W_BF16 : W_F32;
+  ctx->esz = cfg->dtype == LADDER_BF16 ? 2 : 4;
+  ctx->qrows = cfg->n_q_heads * cfg->head_dim;
+  ctx->kvrows = cfg->n_kv_heads * cfg->head_dim;
+  ctx->n_split = attn_decode_splits(cfg->max_seq);
+  ctx->layer_kv_elems = (size_t)cfg->max_batch * cfg->n_kv_heads * cfg->max_seq * cfg->head_dim;
+  {
+    long long mm = cfg->max_prefill_tokens > 0 ? cfg->max_prefill_tokens : 8192;
+    const long long cap = (long long)cfg->max_batch * cfg->max_seq;
+    if (mm > cap) mm = cap;
+    if (mm < cfg->max_batch) mm = cfg->max_batch;
+    ctx->mmax = (int)mm;
+  }
+  ctx->filled = cfg->kv_filled;
+  ctx->user = (hipStream_t)stream;
+
+  auto bail = [&](ladder_status s) {
+    ladder_free(ctx);
+    return s;
+  };
+  hipError_t e = hipGetDevice(&ctx->dev);
+  if (e != hipSuccess) { fail(ctx, LADDER_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e)); return bail(LADDER_ERR_HIP); }
+#define INITCHK(call)                                                            \
+  do {                                                                           \
+    hipError_t e_ = (call);                                                      \
+    if (e_ != hipSuccess) return bail(e_ == hipErrorOutOfMemory ? LADDER_ERR_OOM : LADDER_ERR_HIP); \
+  } while (0)
+  INITCHK(hipStreamCreateWithFlags(&ctx->s0, hipStreamNonBlocking));
+  INITCHK(hipStreamCreateWithFlags(&ctx->sa, hipStreamNonBlocking));
+  INITCHK(hipStreamCreateWithFlags(&ctx->sb, hipStreamNonBlocking));
+  INITCHK(hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking));
+  const int NM = 2 * cfg->n_layers;
+  ctx->ev_x.assign(NM + 1, nullptr);
+  ctx->ev_out.assign(NM, nullptr);
+  for (auto& ev : ctx->ev_x) INITCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+  for (auto& ev : ctx->ev_out) INITCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+  INITCHK(hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming));
+  INITCHK(hipEventCreateWithFlags(&ctx->ev_in, hipEventDisableTiming));
+  INITCHK(hipEventCreateWithFlags(&ctx->ev_done, hipEventDisableTiming));
+
+  Carver measure;
+  carve(ctx, measure);
+  ctx->ws_bytes = measure.off;
+  INITCHK(hipMalloc((void**)&ctx->ws, ctx->ws_bytes));
+  Carver real;
+  real.base = ctx->ws;
+  carve(ctx, real);
+  INITCHK(hipMemsetAsync(ctx->ws, 0, ctx->ws_bytes, ctx->s0));
+
+  // RoPE table: pair j at position p rotates by p * theta^(-2j/hd), computed in fp64
+  {
+    const int half = cfg->head_dim / 2;
+    std::vector<float> cs((size_t)cfg->max_seq * half), sn((size_t)cfg->max_seq * half);
+    for (int j = 0; j < half; ++j) {
+      const double inv_freq = std::pow(cfg->rope_theta, -2.0 * j / cfg->head_dim);
+      for (int p = 0; p < cfg->max_seq; ++p) {
+        const double a = (double)p * inv_freq;
+        cs[(size_t)p * half + j] = (float)std::cos(a);
+        sn[(size_t)p * half + j] = (float)std::sin(a);
+      }
+    }
+    INITCHK(hipMemcpyAsync(ctx->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, ctx->s0));
+    INITCHK(hipMemcpyAsync(ctx->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, ctx->s0));
+    INITCHK(hipStreamSynchronize(ctx->s0));
+  }
+#undef INITCHK
+  *out = ctx;
+  return LADDER_OK;
+}
+
+ladder_status ladder_set_schedule(ladder_ctx* ctx, int32_t schedule, int32_t use_graph) {
+  if (!ctx) return LADDER_ERR_ARG;
+  if (schedule < LADDER_SCHED_SERIAL || schedule > LADDER_SCHED_DUAL) return LADDER_ERR_ARG;
+  ctx->sched = schedule;
+  ctx->use_graph = use_graph ? 1 : 0;
+  return LADDER_OK;
+}
+
+ladder_status ladder_filled(const ladder_ctx* ctx, int32_t* out) {
+  if (!ctx || !out) return LADDER_ERR_ARG;
+  *out = ctx->filled;
+  return LADDER_OK;
+}
+
+ladder_status ladder_workspace_bytes(const ladder_ctx* ctx, size_t* out) {
+  if (!ctx || !out) return LADDER_ERR_ARG;
+  *out = ctx->ws_bytes;
+  return LADDER_OK;
+}
+
+ladder_status ladder_sync(ladder_ctx* ctx) {
+  if (!ctx) return LADDER_ERR_ARG;
+  HIPCHK(hipSetDevice(ctx->dev));
+  HIPCHK(hipStreamSynchronize(ctx->s0));
+  HIPCHK(hipStreamSynchronize(ctx->user));
+  return LADDER_OK;
+}
+
+ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, float* us_out) {
+  if (!ctx || !us_out || reps < 1) return LADDER_ERR_ARG;
+  if (ctx->broken) return LADDER_ERR_HIP;
+  const ladder_config& g = ctx->cfg;
+  if (B < 1 || B > g.max_batch) return fail(ctx, LADDER_ERR_CAPACITY, "batch beyond capacity%s");
+  if (ctx->filled < 1) return fail(ctx, LADDER_ERR_STATE, "no decode position to time at%s");
+  ladder_status st = begin_call(ctx);
+  if (st) return st;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  HIPCHK(hipEventCreate(&e0));
+  HIPCHK(hipEventCreate(&e1));
+  const StreamScratch& sc = ctx->sc[0];
+  hipStream_t s = ctx->s0;
+  for (int kind = 0; kind < LADDER_N_KERNELS; ++kind) {
+    int launches = 0;
+    HIPCHK(hipEventRecord(e0, s));
+    for (int r = 0; r < reps; ++r) {
+      if (kind == LADDER_KERNEL_LMHEAD) {
+        HIPCHK(launch_gemv(lmhead_params(ctx, ctx->dx[0], g.hidden, B), s));
+        ++launches;
+        continue;
+      }
+      for (int l = 0; l < g.n_layers; ++l, ++launches) {
+        switch (kind) {
+          case LADDER_KERNEL_QKV: HIPCHK(launch_gemv(qkv_params(ctx, l, B, ctx->dx[0], sc), s)); break;
+          case LADDER_KERNEL_ATTN: HIPCHK(launch_attn_decode(attn_params(ctx, l, B, sc), s)); break;
+          case LADDER_KERNEL_OPROJ:
+            HIPCHK(launch_gemv(outproj_params(ctx, 2 * l, B, sc, ctx->dx[0], ctx->dx[1], nullptr), s));
+            break;
+          case LADDER_KERNEL_GATEUP: HIPCHK(launch_gemv(gateup_params(ctx, l, B, ctx->dx[0], sc), s)); break;
+          default:
+            HIPCHK(launch_gemv(outproj_params(ctx, 2 * l + 1, B, sc, ctx->dx[0], ctx->dx[1], nullptr), s));
+            break;
+        }
+      }
+    }
+    HIPCHK(hipEventRecord(e1, s));
+    HIPCHK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, e0, e1));
+    us_out[kind] = 1000.f * ms / (float)launches;
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return end_call(ctx);
+}
+
+ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t T, int32_t start_pos,
+                             float* d_logits, int32_t* d_next, float* d_hidden) {
+  if (!ctx || !d_ids) return LADDER_ERR_ARG;
+  if (ctx->broken) return LADDER_ERR_HIP;
+  const ladder_config& g = ctx->cfg;
+  if (B < 1 || T < 1 || start_pos < 0) return fail(ctx, LADDER_ERR_ARG, "bad B/T/start_pos%s");
+  if (B > g.max_batch || (long long)start_pos + T > g.max_seq)
+    return fail(ctx, LADDER_ERR_CAPACITY, "batch or positions beyond capacity%s");
+  if (start_pos > ctx->filled) return fail(ctx, LADDER_ERR_STATE, "prefill starts after unfilled positions%s");
+  ladder_status st = begin_call(ctx);
+  if (st) return st;
+  const int tc_max = std::max(1, ctx->mmax / B);
+  const int NM = 2 * g.n_layers;
+  for (int t0 = 0; t0 < T; t0 += tc_max) {
+    const int Tc = std::min(tc_max, T - t0);
+    const int M = B * Tc;
+    HIPCHK(hipMemcpy2DAsync(ctx->ids_chunk, (size_t)Tc * 4, d_ids + t0, (size_t)T * 4, (size_t)Tc * 4, B,
+                            hipMemcpyDeviceToDevice, ctx->s0));
+    HIPCHK(launch_embed(ctx->wdt, ctx->w.tok_embed, g.vocab, g.hidden, ctx->ids_chunk, M, ctx->px[0], ctx->s0));
+    const int sp = start_pos + t0;
+    auto mod = [&](int m, const float* xin, const float* xm, float* xn, float* store, hipStream_t s, bool wait,
+                   hipEvent_t ev) { return prefill_module(ctx, m, B, Tc, sp, xin, xm, xn, store, s, wait, ev); };
+    st = run_modules(ctx, ctx->px, ctx->pout, (size_t)M * g.hidden, mod);
+    if (st) return st;
+    if (t0 + Tc == T) {
+      const float* xl = ctx->px[NM % 2] + (size_t)(Tc - 1) * g.hidden;
+      st = lm_head(ctx, xl, Tc * g.hidden, B, ctx->s0);
+      if (st) return st;
+      st = copy_outputs(ctx, B, xl, (size_t)Tc * g.hidden * 4, d_logits, d_next, d_hidden);
+      if (st) return st;
+    }
+  }
+  ctx->filled = std::max(ctx->filled, start_pos + T);
+  return end_call(ctx);
+}
+
+ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t pos, float* d_logits,
+                                 int32_t* d_next, float* d_hidden) {
+  if (!ctx || !d_ids) return LADDER_ERR_ARG;
+  if (ctx->broken) return LADDER_ERR_HIP;
+  const ladder_config& g = ctx->cfg;
+  if (B < 1 || pos < 0) return fail(ctx, LADDER_ERR_ARG, "bad B/pos%s");
+  if (B > g.max_batch || pos >= g.max_seq) return fail(ctx, LADDER_ERR_CAPACITY, "batch or position beyond capacity%s");
+  if (pos > ctx->filled) return fail(ctx, LADDER_ERR_STATE, "decode position after unfilled positions%s");
+  ladder_status st = begin_call(ctx);
+  if (st) return st;
+  HIPCHK(launch_decode_prologue(d_ids, ctx->ids_dev, B, ctx->pos_dev, pos, ctx->s0));
+  if (ctx->use_graph) {
+    const int key = B * 8 + ctx->sched;
+    auto it = ctx->graphs.find(key);
+    if (it == ctx->graphs.end()) {
+      hipGraph_t graph = nullptr;
+      HIPCHK(hipStreamBeginCapture(ctx->s0, hipStreamCaptureModeThreadLocal));
+      st = enqueue_decode(ctx, B);
+      hipError_t ce = hipStreamEndCapture(ctx->s0, &graph);
+      if (st) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+      }
+      HIPCHK(ce);
+      hipGraphExec_t exec = nullptr;
+      hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      HIPCHK(ie);
+      it = ctx->graphs.emplace(key, exec).first;
+    }
+    HIPCHK(hipGraphLaunch(it->second, ctx->s0));
+  } else {
+    st = enqueue_decode(ctx, B);
+    if (st) return st;
+  }
+  st = copy_outputs(ctx, B, ctx->dx[(2 * g.n_layers) % 2], (size_t)g.hidden * 4, d_logits, d_next, d_hidden);
+  if (st) return st;
+  ctx->filled = std::max(ctx->filled, pos + 1);
+  return end_call(ctx);
+}
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+"""HIP path vs the oracle on small models: every kernel, schedule, mask and edge case.
+
+All calls go through the C ABI (libladder.so via ctypes); inputs are the seeded synth
+arrays, expected values come from oracle/ only.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import (TOL, check_against_oracle, gpu_free_running, gpu_teacher_forced, log, make_model,
+                         oracle_record, rel_err, small_config)
+from oracle import LadderOracle, teacher_forced
+
+pytestmark = pytest.mark.gpu
+
+SERIAL, SIDE, DUAL = 0, 1, 2
+
+# bf16 model with ragged shapes: H = 2112 (264 vectors: two K slices at batch > 4, the
+# second one short), 6 query / 2 kv heads of 64, F = 1344, vocab 1001 (ragged row
+# tiles), standard layer 0 then ladder layers 1-2.
+EDGE = synth.ModelConfig("edge", 3, 2112, 6, 2, 64, 1344, 1001, 1e4, "bf16", (0, 1, 1))
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = synth.CONFIGS["tiny"]
+    return cfg, synth.gen_weights(cfg, seed=0)
+
+
+def test_tiny_fp32_matches_oracle_and_greedy_is_identical(tiny):
+    cfg, w = tiny
+    wl = synth.WORKLOADS["tiny"]
+    prompt = synth.gen_ids(1, wl.prompt_len, cfg.vocab, seed=1)
+    log("tiny fp32: B=1 prompt", wl.prompt_len, "decode", wl.decode_len)
+    ref = oracle_record(cfg, w, prompt, wl.decode_len)
+    model = make_model(cfg, w, 1, wl.max_seq)
+    gl, gh, gt = gpu_teacher_forced(model, prompt, ref["tokens"][:, :-1])
+    check_against_oracle(cfg, gl, gh, gt, ref, TOL["f32"], "tiny teacher-forced")
+    assert np.array_equal(gt, ref["tokens"])
+    free = gpu_free_running(model, prompt, wl.decode_len)
+    assert np.array_equal(free, ref["tokens"]), (free, ref["tokens"])
+    model.free()
+
+
+@pytest.mark.parametrize("mask", [(0, 0), (0, 1), (1, 0)])
+def test_tiny_every_mask(tiny, mask):
+    cfg, w = tiny
+    cfg = cfg.with_mask(mask)
+    prompt = synth.gen_ids(1, 9, cfg.vocab, seed=2)
+    log("tiny mask", mask)
+    ref = oracle_record(cfg, w, prompt, 6)
+    model = make_model(cfg, w, 1, 16)
+    gl, gh, gt = gpu_teacher_forced(model, prompt, ref["tokens"][:, :-1])
+    check_against_oracle(cfg, gl, gh, gt, ref, TOL["f32"], f"tiny {mask}")
+    assert np.array_equal(gt, ref["tokens"])
+    model.free()
+
+
+def test_single_key_prompt(tiny):
+    """A one-token prompt: attention sees exactly one key (position 0)."""
+    cfg, w = tiny
+    prompt = synth.gen_ids(2, 1, cfg.vocab, seed=3)
+    ref = oracle_record(cfg, w, prompt, 3)
+    model = make_model(cfg, w, 2, 8)
+    gl, gh, gt = gpu_teacher_forced(model, prompt, ref["tokens"][:, :-1])
+    check_against_oracle(cfg, gl, gh, gt, ref, TOL["f32"], "single key")
+    model.free()
+
+
+@pytest.fixture(scope="module")
+def edge():
+    return EDGE, synth.gen_weights(EDGE, seed=5)
+
+
+@pytest.mark.parametrize("B, T, chunk", [(1, 37, 0), (5, 37, 64), (3, 20, 0)])
+def test_edge_shapes_bf16(edge, B, T, chunk):
+    """Ragged tiles everywhere; B=5 splits K of the 2112-wide projections; chunk=64
+    cuts the 5x37 prompt into 12-token prefill chunks."""
+    cfg, w = edge
+    prompt = synth.gen_ids(B, T, cfg.vocab, seed=6)
+    log(f"edge bf16 B={B} T={T} chunk={chunk}")
+    ref = oracle_record(cfg, w, prompt, 5, dtype=np.float64)
+    model = make_model(cfg, w, B, T + 8, max_prefill_tokens=chunk)
+    gl, gh, gt = gpu_teacher_forced(model, prompt, ref["tokens"][:, :-1])
+    check_against_oracle(cfg, gl, gh, gt, ref, TOL["bf16"], f"edge B={B}")
+    model.free()
+
+
+@pytest.mark.parametrize("use_graph", [False, True])
+def test_schedules_are_bitwise_identical(edge, use_graph):
+    """Race check: the two-stream and side-stream schedules must reproduce the serial
+    one bit for bit (any missing wait would read a stale or half-written residual)."""
+    cfg, w = edge
+    prompt = synth.gen_ids(5, 21, cfg.vocab, seed=7)
+    cont = synth.gen_ids(5, 4, cfg.vocab, seed=7, stream=1)
+    outs = {}
+    for sched in (SERIAL, SIDE, DUAL):
+        model = make_model(cfg, w, 5, 32)
+        model.set_schedule(sched, use_graph)
+        outs[sched] = gpu_teacher_forced(model, prompt, cont)
+        model.free()
+    for sched in (SIDE, DUAL):
+        for a, b in zip(outs[SERIAL], outs[sched]):
+            assert np.array_equal(a, b), f"schedule {sched} differs from serial"
+
+
+def test_graph_replay_matches_eager(edge):
+    cfg, w = edge
+    prompt = synth.gen_ids(2, 11, cfg.vocab, seed=8)
+    cont = synth.gen_ids(2, 6, cfg.vocab, seed=8, stream=1)
+    res = []
+    for g in (False, True):
+        model = make_model(cfg, w, 2, 24)
+        model.set_schedule(DUAL, g)
+        res.append(gpu_teacher_forced(model, prompt, cont))
+        model.free()
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
+
+
+def test_chunked_prefill_equals_prefill_then_decode(edge):
+    """prefill(n) followed by single decode steps equals prefill(n+k) at the last position
+    (both against the oracle), and a prefill that starts at start_pos > 0 continues the cache."""
+    cfg, w = edge
+    ids = synth.gen_ids(1, 24, cfg.vocab, seed=9)
+    o = LadderOracle(cfg, w)
+    ref = o.forward(ids)
+    model = make_model(cfg, w, 1, 32)
+    t = torch.from_numpy(ids).cuda()
+    model.prefill(t[:, :16].contiguous())
+    lg, nx, hd = model.prefill(t[:, 16:24].contiguous(), start_pos=16)
+    torch.cuda.synchronize()
+    assert rel_err(lg.cpu().numpy(), ref.logits[:, 23]) <= TOL["bf16"]
+    assert rel_err(hd.cpu().numpy(), ref.hidden[:, 23]) <= TOL["bf16"]
+    model.free()
+
+
+def test_resume_on_existing_cache_is_bitwise(edge):
+    """Prefill and two decode steps in one context, then a fresh context on the same KV
+    cache (kv_filled) continues exactly like the uninterrupted one."""
+    cfg, w = edge
+    prompt = synth.gen_ids(1, 12, cfg.vocab, seed=10)
+    cont = synth.gen_ids(1, 5, cfg.vocab, seed=10, stream=1)
+    a = make_model(cfg, w, 1, 24)
+    full = gpu_teacher_forced(a, prompt, cont)
+    a.free()
+    b = make_model(cfg, w, 1, 24)
+    gpu_teacher_forced(b, prompt, cont[:, :2])
+    kv = (b.k_cache, b.v_cache)
+    c = make_model(cfg, w, 1, 24, kv=kv, kv_filled=12 + 2)
+    outs = []
+    for k in range(2, 5):
+        lg, nx, hd = c.decode_step(torch.from_numpy(cont[:, k].copy()).cuda(), 12 + k)
+        outs.append(lg)
+    torch.cuda.synchronize()
+    for k, lg in zip(range(2, 5), outs):
+        assert np.array_equal(lg.cpu().numpy(), full[0][:, k + 1])
+    b.free()
+    c.free()
+
+
+def test_error_paths_on_device(edge):
+    from ladder_residual_transformer_amd import LadderError, abi
+    cfg, w = edge
+    m = make_model(cfg, w, 2, 16)
+    ids1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(LadderError) as e:
+        m.decode_step(ids1, 3)                    # nothing prefilled yet
+    assert e.value.status == abi.LADDER_ERR_STATE
+    with pytest.raises(LadderError) as e:
+        m.decode_step(torch.zeros(3, dtype=torch.int32, device="cuda"), 0)
+    assert e.value.status == abi.LADDER_ERR_CAPACITY
+    with pytest.raises(LadderError) as e:
+        m.prefill(torch.zeros((1, 17), dtype=torch.int32, device="cuda"))
+    assert e.value.status == abi.LADDER_ERR_CAPACITY
+    m.prefill(torch.zeros((1, 16), dtype=torch.int32, device="cuda"))
+    with pytest.raises(LadderError) as e:
+        m.decode_step(ids1, 16)                   # pos == max_seq
+    assert e.value.status == abi.LADDER_ERR_CAPACITY
+    assert m.filled() == 16
+    m.decode_step(ids1, 15)                       # rewriting the last position is allowed
+    torch.cuda.synchronize()
+    m.free()
+
+
+def test_batch_rows_match_single_sequence(edge):
+    cfg, w = edge
+    prompt = synth.gen_ids(3, 10, cfg.vocab, seed=11)
+    cont = synth.gen_ids(3, 3, cfg.vocab, seed=11, stream=1)
+    m3 = make_model(cfg, w, 3, 16)
+    l3 = gpu_teacher_forced(m3, prompt, cont)[0]
+    m3.free()
+    for b in range(3):
+        m1 = make_model(cfg, w, 1, 16)
+        l1 = gpu_teacher_forced(m1, prompt[b:b + 1], cont[b:b + 1])[0]
+        m1.free()
+        assert rel_err(l3[b], l1[0]) <= 2e-3
