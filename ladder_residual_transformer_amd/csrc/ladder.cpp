@@ -8,7 +8,8 @@
 //   SERIAL: everything on one stream in program order (the reference order);
 //   SIDE:   modules on the main stream, each residual add on a side stream; module m+1
 //           waits only for the add that produced its own (stale) input;
-//   DUAL:   attention modules on stream A, MLP modules on stream B, each residual add
+//   DUAL:   attention modules on the origin stream (A), MLP modules on a second stream
+//           (B), each residual add
 //           fused into the module's output projection.  A module waits for its input
 //           residual, and its output projection waits for x_m, produced by the other
 //           stream.  Ladder modules overlap the previous module (attention of layer l+1
@@ -87,7 +88,7 @@ struct ladder_ctx {
 
   hipStream_t user = nullptr;   // caller's stream
   hipStream_t s0 = nullptr;     // origin stream of every call (graph capture happens here)
-  hipStream_t sa = nullptr, sb = nullptr, side = nullptr;
+  hipStream_t sb = nullptr, side = nullptr;   // MLP stream of DUAL, add stream of SIDE
   std::vector<hipEvent_t> ev_x, ev_out;
   hipEvent_t ev_fork = nullptr, ev_in = nullptr, ev_done = nullptr;
 
@@ -229,7 +230,7 @@ void* layer_v(const ladder_ctx* c, int l) { return (char*)c->kv.v + (size_t)l * 
 
 // Stream running module m under the current schedule.
 hipStream_t module_stream(const ladder_ctx* c, int m) {
-  if (c->sched == LADDER_SCHED_DUAL) return (m % 2 == 0) ? c->sa : c->sb;
+  if (c->sched == LADDER_SCHED_DUAL) return (m % 2 == 0) ? c->s0 : c->sb;
   return c->s0;
 }
 
@@ -483,7 +484,6 @@ ladder_status run_modules(ladder_ctx* ctx, float* const X[2], float* const OUT[2
   const int sched = ctx->sched;
   if (sched == LADDER_SCHED_DUAL) {
     HIPCHK(hipEventRecord(ctx->ev_fork, ctx->s0));
-    HIPCHK(hipStreamWaitEvent(ctx->sa, ctx->ev_fork, 0));
     HIPCHK(hipStreamWaitEvent(ctx->sb, ctx->ev_fork, 0));
   }
   for (int m = 0; m < NM; ++m) {
@@ -519,7 +519,6 @@ ladder_status run_modules(ladder_ctx* ctx, float* const X[2], float* const OUT[2
     HIPCHK(hipStreamWaitEvent(ctx->s0, ctx->ev_x[NM], 0));
   } else if (sched == LADDER_SCHED_DUAL) {
     HIPCHK(hipStreamWaitEvent(ctx->s0, ctx->ev_x[NM], 0));       // last MLP (stream B)
-    HIPCHK(hipStreamWaitEvent(ctx->s0, ctx->ev_x[NM - 1], 0));   // last attention (stream A)
   }
   return LADDER_OK;
 }
@@ -595,7 +594,7 @@ void ladder_free(ladder_ctx* ctx) {
   for (hipEvent_t e : ctx->ev_x) if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : ctx->ev_out) if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : {ctx->ev_fork, ctx->ev_in, ctx->ev_done}) if (e) (void)hipEventDestroy(e);
-  for (hipStream_t s : {ctx->sa, ctx->sb, ctx->side}) {
+  for (hipStream_t s : {ctx->sb, ctx->side}) {
     if (s) { (void)hipStreamSynchronize(s); (void)hipStreamDestroy(s); }
   }
   if (ctx->s0) (void)hipStreamDestroy(ctx->s0);
@@ -645,7 +644,6 @@ ladder_status ladder_init(const ladder_config* cfg, const ladder_weights* w, con
     if (e_ != hipSuccess) return bail(e_ == hipErrorOutOfMemory ? LADDER_ERR_OOM : LADDER_ERR_HIP); \
   } while (0)
   INITCHK(hipStreamCreateWithFlags(&ctx->s0, hipStreamNonBlocking));
-  INITCHK(hipStreamCreateWithFlags(&ctx->sa, hipStreamNonBlocking));
   INITCHK(hipStreamCreateWithFlags(&ctx->sb, hipStreamNonBlocking));
   INITCHK(hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking));
   const int NM = 2 * cfg->n_layers;
