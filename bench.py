@@ -25,8 +25,9 @@ if ROOT not in sys.path:
 METRIC = "decode tok/s + % HBM roofline, 70B-shape TP8 one-rank shard, batch 1"
 HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15      # FLOP/s, dense bf16
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_gemv_70b_b1.json")
-KERNEL_SOURCES = ("ladder_residual_transformer_amd/csrc/gemv.hip", "ladder_residual_transformer_amd/csrc/common.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qkv_gateup_70b_b1.json")
+KERNEL_SOURCES = ("ladder_residual_transformer_amd/csrc/gemv_rw.hip", "ladder_residual_transformer_amd/csrc/attn_decode.hpp",
+                  "ladder_residual_transformer_amd/csrc/common.hpp")
 
 
 def log(*a):
@@ -58,9 +59,15 @@ def prefill_flops(cfg, B, T):
     return proj + attn + head
 
 
-def gateup_bytes(cfg, B):
+def qkv_gateup_bytes(cfg, B):
+    """Algorithmic bytes of one fused [QKV | gate/up] launch: both weight blocks and norm
+    gains once, the two input residual rows, q and the SwiGLU output written, one K and
+    one V row appended per kv head."""
     esz = 2 if cfg.dtype == "bf16" else 4
-    return 2 * cfg.ffn * cfg.hidden * esz + cfg.hidden * esz + B * cfg.hidden * 4 + B * cfg.ffn * 4
+    H, F, hd = cfg.hidden, cfg.ffn, cfg.head_dim
+    q, kv = cfg.n_q_heads * hd, cfg.n_kv_heads * hd
+    weights = (H * (q + 2 * kv) + 2 * F * H + 2 * H) * esz
+    return weights + 2 * B * H * 4 + B * q * 4 + B * F * 4 + 2 * B * kv * esz
 
 
 def cpu_baseline(cfg, w, prompt, sample_layers, steps):
@@ -110,12 +117,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="70b_tp8_shard")
     ap.add_argument("--batch", type=int, default=1)
-    ap.add_argument("--schedule", choices=("serial", "side", "dual"), default="dual")
+    ap.add_argument("--schedule", choices=("serial", "side", "dual", "fused"), default="fused")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--prefill-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-layers", type=int, default=8)
-    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--cpu-sample-layers", type=int, default=16)
+    ap.add_argument("--cpu-steps", type=int, default=6)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs one GPU's share of the model (one tensor-parallel rank's shard); "
@@ -141,7 +148,7 @@ def main():
     t = time.time()
     dw = DeviceWeights(w)
     model = LadderModel(cfg, dw, B, wl.max_seq)
-    sched = {"serial": 0, "side": 1, "dual": 2}[args.schedule]
+    sched = {"serial": 0, "side": 1, "dual": 2, "fused": 3}[args.schedule]
     model.set_schedule(sched, not args.no_graph)
     torch.cuda.synchronize()
     log(f"[bench] uploaded weights and built the context in {time.time() - t:.1f} s "
@@ -190,10 +197,11 @@ def main():
     log(f"[bench] decode {args.steps} steps: {dt * 1e3 / args.steps:.3f} ms/step (events {gpu_ms / args.steps:.3f}), "
         f"{tok_s:.1f} tok/s, {total_bytes / args.steps / 1e9:.2f} GB/step, {100 * hbm_frac:.1f}% of HBM peak")
 
-    # ---- dominant kernel (gate/up GEMV, ~55% of the bytes), timed on its stream
+    # ---- dominant kernel: the fused [QKV | gate/up] launch (~65% of the bytes), timed
+    # on the stream it runs on
     ku = model.time_kernels(B, reps=3)
-    gu_bytes = gateup_bytes(cfg, B)
-    achieved = gu_bytes / (ku["gateup"] * 1e-6) / 1e9
+    gu_bytes = qkv_gateup_bytes(cfg, B)
+    achieved = gu_bytes / (ku["qkv_gateup"] * 1e-6) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -219,10 +227,10 @@ def main():
         "decode_bytes_per_step": total_bytes // args.steps,
         "prefill_tok_s": round(B * P / prefill_s, 1),
         "prefill_mfma_frac": round(pflops / prefill_s / MFMA_BF16_PEAK, 4),
-        "roofline": {"bound": "hbm", "kernel": "gateup GEMV (RMSNorm + [Wgate,Wup] + SwiGLU)",
+        "roofline": {"bound": "hbm", "kernel": "fused ladder launch [RMSNorm+QKV+RoPE+KV | RMSNorm+gate/up+SwiGLU]",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": traffic,
-                     "bytes_per_launch": gu_bytes, "us_per_launch": round(ku["gateup"], 3)},
+                     "bytes_per_launch": gu_bytes, "us_per_launch": round(ku["qkv_gateup"], 3)},
         "kernels_us": {k: round(v, 3) for k, v in ku.items()},
         "cpu_baseline": cpu,
     }

@@ -65,7 +65,12 @@ typedef int32_t ladder_status;
                                     stale input while x_{m+1} = x_m + out_m completes */
 #define LADDER_SCHED_DUAL 2      /* attention and MLP modules on two streams, residual add
                                     fused into each module's output projection; a ladder
-                                    module overlaps the previous module (default) */
+                                    module overlaps the previous module */
+#define LADDER_SCHED_FUSED 3     /* one stream; a ladder layer's attention and MLP run side
+                                    by side: [QKV | gate/up] in one launch (they read
+                                    x_{2l-1} and x_{2l}), [attention | down projection] in
+                                    one launch, then the O projection adds both residual
+                                    updates (default) */
 
 typedef struct ladder_config {
   int32_t n_layers;
@@ -152,10 +157,14 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 #define LADDER_KERNEL_GATEUP 3   /* RMSNorm + [Wgate,Wup] GEMV + SwiGLU */
 #define LADDER_KERNEL_DOWN 4     /* Wdown GEMV + fused residual add */
 #define LADDER_KERNEL_LMHEAD 5   /* final RMSNorm + LM head GEMV + greedy argmax */
-#define LADDER_N_KERNELS 6
+#define LADDER_KERNEL_QKV_GATEUP 6  /* fused ladder launch: QKV (+RoPE/KV) | gate/up (+SwiGLU) */
+#define LADDER_KERNEL_ATTN_DOWN 7   /* fused ladder launch: decode attention | down projection */
+#define LADDER_KERNEL_OPROJ_ADD2 8  /* fused ladder launch: O projection + both residual adds */
+#define LADDER_N_KERNELS 9
 
 /* Profiling aid.  For each kernel kind, enqueue it on the context's stream exactly as
  * a decode step at batch B launches it (once per layer; the LM head once), reps times,
+ * (the fused kinds use each layer as if it were a ladder layer),
  * between two HIP events, and store the mean duration of one launch in microseconds
  * in us_out[kind] (host array of LADDER_N_KERNELS floats).  Works on the context's
  * current buffers and the position of the last decode step, whose KV row it

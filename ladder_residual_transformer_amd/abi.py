@@ -29,12 +29,13 @@ LADDER_BF16 = 1
 LADDER_SCHED_SERIAL = 0
 LADDER_SCHED_SIDE = 1
 LADDER_SCHED_DUAL = 2
+LADDER_SCHED_FUSED = 3
 
 EXPORTED = ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_filled",
             "ladder_workspace_bytes", "ladder_sync", "ladder_free", "ladder_status_string", "ladder_last_error",
             "ladder_time_kernels")
 
-KERNEL_KINDS = ("qkv", "attn", "oproj", "gateup", "down", "lmhead")
+KERNEL_KINDS = ("qkv", "attn", "oproj", "gateup", "down", "lmhead", "qkv_gateup", "attn_down", "oproj_add2")
 
 
 class ladder_config(ctypes.Structure):

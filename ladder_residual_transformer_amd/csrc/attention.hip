@@ -1,23 +1,17 @@
 // Grouped-query causal softmax attention over the KV cache.
 //
-// Decode (one new token per sequence): the keys 0..pos of one (sequence, kv head)
-// are split into n_split contiguous chunks, one workgroup each.  A workgroup stages
-// 64-key tiles of K and V in LDS once and serves all G = nq/nkv query heads that
-// share that kv head (the GQA map: query head h reads kv head h / G), keeping a
-// running max / sum / accumulator per head (online softmax).  The last workgroup of
-// a (sequence, kv head) merges the chunks with their log-sum-exp weights, in chunk
-// order, so results do not depend on scheduling.
+// Decode (one new token per sequence): split-KV workgroups of attn_decode.hpp.
 //
 // Prefill (T tokens per sequence starting at start_pos): one workgroup per 32-query
 // tile of one head walks the causally visible 64-key tiles with the same online
 // softmax.
+#include "attn_decode.hpp"
 #include "common.hpp"
 #include "kernels.h"
 
 namespace ladder {
 
-constexpr int kKeyTile = 64;
-constexpr int kMaxGroup = 16;
+constexpr int kKeyTile = 64;      // prefill key tile
 
 template <typename WT, int HD>
 __device__ __forceinline__ void stage_rows(float (*dst)[HD + 4], const WT* src, int n_rows, int tid) {
@@ -37,141 +31,38 @@ __device__ __forceinline__ void stage_rows(float (*dst)[HD + 4], const WT* src, 
   }
 }
 
-template <typename WT, int HD>
+template <typename WT, int HD, int HPW>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeParams p) {
-  __shared__ float qs[kMaxGroup][HD];
-  __shared__ float ks[kKeyTile][HD + 4];
-  __shared__ float vs[kKeyTile][HD + 4];
-  __shared__ float ps[kMaxGroup][kKeyTile];
-  __shared__ float alpha[kMaxGroup];
-  __shared__ float m_run[kMaxGroup];
-  __shared__ float l_run[kMaxGroup];
-  __shared__ int is_last;
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int G = p.nq / p.nkv;
-  const int len = *p.d_pos + 1;
-  const int chunk = (len + p.n_split - 1) / p.n_split;
-  const int start = s * chunk;
-  const int end = min(len, start + chunk);
-  const float scale = 1.0f / sqrtf((float)HD);
-  const size_t kv_base = ((size_t)b * p.nkv + kvh) * p.max_seq * HD;
-  const WT* kc = (const WT*)p.k_cache + kv_base;
-  const WT* vc = (const WT*)p.v_cache + kv_base;
-
-  for (int i = tid; i < G * HD; i += 256) {
-    const int h = i / HD, d = i % HD;
-    qs[h][d] = p.q[(size_t)b * p.nq * HD + (size_t)(kvh * G + h) * HD + d];
-  }
-  if (tid < G) { m_run[tid] = -INFINITY; l_run[tid] = 0.f; }
-  constexpr int kMaxOwn = kMaxGroup * HD / 256;
-  float acc[kMaxOwn];
-#pragma unroll
-  for (int k = 0; k < kMaxOwn; ++k) acc[k] = 0.f;
-  __syncthreads();
-
-  for (int t0 = start; t0 < end; t0 += kKeyTile) {
-    const int n = min(kKeyTile, end - t0);
-    stage_rows<WT, HD>(ks, kc + (size_t)t0 * HD, n, tid);
-    stage_rows<WT, HD>(vs, vc + (size_t)t0 * HD, n, tid);
-    __syncthreads();
-    for (int i = tid; i < G * kKeyTile; i += 256) {
-      const int h = i / kKeyTile, j = i % kKeyTile;
-      float dot = 0.f;
-      if (j < n) {
-#pragma unroll 8
-        for (int d = 0; d < HD; ++d) dot = fmaf(qs[h][d], ks[j][d], dot);
-        ps[h][j] = dot * scale;
-      } else {
-        ps[h][j] = -INFINITY;
-      }
-    }
-    __syncthreads();
-    for (int h = wid; h < G; h += 4) {
-      const float sc = ps[h][lane];
-      const float m_new = fmaxf(m_run[h], wave_max(sc));
-      const float e = lane < n ? expf(sc - m_new) : 0.f;
-      const float sum = wave_sum(e);
-      ps[h][lane] = e;
-      if (lane == 0) {
-        const float a = expf(m_run[h] - m_new);
-        alpha[h] = a;
-        l_run[h] = l_run[h] * a + sum;
-        m_run[h] = m_new;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kMaxOwn; ++k) {
-      const int i = tid + k * 256;
-      if (i < G * HD) {
-        const int h = i / HD, d = i % HD;
-        float a = acc[k] * alpha[h];
-        for (int j = 0; j < n; ++j) a = fmaf(ps[h][j], vs[j][d], a);
-        acc[k] = a;
-      }
-    }
-    __syncthreads();
-  }
-
-  // this chunk's (max, sum, unnormalised accumulator) per query head
-  const size_t stride = HD + 2;
-#pragma unroll
-  for (int k = 0; k < kMaxOwn; ++k) {
-    const int i = tid + k * 256;
-    if (i < G * HD) {
-      const int h = i / HD, d = i % HD;
-      float* dst = p.part + (((size_t)b * p.nq + kvh * G + h) * p.n_split + s) * stride;
-      dst[2 + d] = acc[k];
-      if (d == 0) { dst[0] = m_run[h]; dst[1] = l_run[h]; }
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  int* counter = p.counters + (size_t)b * p.nkv + kvh;
-  if (tid == 0) is_last = (atomicAdd(counter, 1) == p.n_split - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int i = tid; i < G * HD; i += 256) {
-    const int h = i / HD, d = i % HD;
-    const float* src = p.part + (((size_t)b * p.nq + kvh * G + h) * p.n_split) * stride;
-    float M = -INFINITY;
-    for (int q = 0; q < p.n_split; ++q) M = fmaxf(M, src[q * stride]);
-    float L = 0.f, o = 0.f;
-    if (M != -INFINITY) {
-      for (int q = 0; q < p.n_split; ++q) {
-        const float w = expf(src[q * stride] - M);
-        L = fmaf(src[q * stride + 1], w, L);
-        o = fmaf(src[q * stride + 2 + d], w, o);
-      }
-    }
-    p.out[(size_t)b * p.nq * HD + (size_t)(kvh * G + h) * HD + d] = L > 0.f ? o / L : 0.f;
-  }
-  if (tid == 0) *counter = 0;
+  __shared__ AttnLds<WT, HD> L;
+  attn_decode_block<WT, HD, HPW>(p, blockIdx.x, L);
 }
 
+// Chunks per (sequence, kv head): one 64-key tile each at full length, at most 16 (the
+// merge then reads every chunk of a head slice in one round of loads).
 int attn_decode_splits(int max_seq) {
-  int n = (max_seq + kKeyTile - 1) / kKeyTile;
+  int n = (max_seq + kAttnKeyTile - 1) / kAttnKeyTile;
   if (n < 1) n = 1;
-  if (n > 32) n = 32;
+  if (n > 16) n = 16;
   return n;
 }
 
-hipError_t launch_attn_decode(const AttnDecodeParams& p, hipStream_t s) {
-  if (p.nkv < 1 || p.nq % p.nkv != 0 || p.nq / p.nkv > kMaxGroup) return hipErrorInvalidValue;
-  dim3 grid(p.n_split, p.nkv, p.B);
-  if (p.hd == 128) {
-    if (p.wdtype == W_BF16) hipLaunchKernelGGL((attn_decode_kernel<uint16_t, 128>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((attn_decode_kernel<float, 128>), grid, dim3(256), 0, s, p);
-  } else if (p.hd == 64) {
-    if (p.wdtype == W_BF16) hipLaunchKernelGGL((attn_decode_kernel<uint16_t, 64>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((attn_decode_kernel<float, 64>), grid, dim3(256), 0, s, p);
-  } else {
-    return hipErrorInvalidValue;
+template <typename WT, int HD>
+hipError_t attn_decode_go(const AttnDecodeParams& p, hipStream_t s) {
+  dim3 grid(p.n_split * p.nkv * p.B);
+  switch (attn_hpw(p.nq / p.nkv)) {
+    case 1: hipLaunchKernelGGL((attn_decode_kernel<WT, HD, 1>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((attn_decode_kernel<WT, HD, 2>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((attn_decode_kernel<WT, HD, 4>), grid, dim3(256), 0, s, p); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const AttnDecodeParams& p, hipStream_t s) {
+  if (p.nkv < 1 || p.nq % p.nkv != 0 || p.nq / p.nkv > kAttnMaxGroup || p.n_split > kAttnMaxSplits)
+    return hipErrorInvalidValue;
+  if (p.hd == 128) return p.wdtype == W_BF16 ? attn_decode_go<uint16_t, 128>(p, s) : attn_decode_go<float, 128>(p, s);
+  if (p.hd == 64) return p.wdtype == W_BF16 ? attn_decode_go<uint16_t, 64>(p, s) : attn_decode_go<float, 64>(p, s);
+  return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------------ prefill

@@ -57,6 +57,16 @@ __device__ void gemv_epilogue(const GemvParams& p, int row0, const float* fin, c
       }
       break;
     }
+    case EPI_ADD2: {
+      for (int i = tid; i < ROWS * BT; i += nt) {
+        const int r = i / BT, b = i % BT, n = row0 + r;
+        if (n >= p.N || b >= B) continue;
+        const float t = p.xres[(size_t)b * p.ldr + n] + fin[i] * inv[b];
+        p.out[(size_t)b * p.ldo + n] = t;
+        p.out2[(size_t)b * p.ldo + n] = t + p.add2[(size_t)b * p.ldo + n];
+      }
+      break;
+    }
     case EPI_GATEUP_SWIGLU: {
       for (int i = tid; i < (ROWS / 2) * BT; i += nt) {
         const int r = 2 * (i / BT), b = i % BT, n = row0 + r;
@@ -125,7 +135,6 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
   const int ntiles = (p.N + ROWS - 1) / ROWS;
   const bool norm = p.gain != nullptr;
 
-  // ---- prologue: this thread's slice of u = x (* g), and sum of squares
   int koff[VPT];
   bool kvalid[VPT];
 #pragma unroll
@@ -133,6 +142,25 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
     koff[v] = k0 + (tid + v * NT) * VEC;
     kvalid[v] = koff[v] < p.K;
   }
+  // Weight loads do not depend on the input, so the first tile's are issued before
+  // the prologue and every later tile's right after the previous tile's FMAs: the
+  // prologue, the cross-wave reduction and the epilogue run under their latency.
+  uint4 w[ROWS][VPT];
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int n = tile * ROWS + r;
+      const WT* rp = row_ptr<WT>(p.rows, n < p.N ? n : p.N - 1, p.K);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        if (kvalid[v] && n < p.N) w[r][v] = *(const uint4*)(rp + koff[v]);
+        else w[r][v] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+  if (blockIdx.x < ntiles) load_tile(blockIdx.x);
+
+  // ---- prologue: this thread's slice of u = x (* g), and sum of squares
   float u[BT][VPT][VEC];
   float sq[BT];
 #pragma unroll
@@ -173,7 +201,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
   if (tid < BT) {
     float t = 0.f;
     if (norm)
-      for (int w = 0; w < NW; ++w) t += sqw[w][tid];
+      for (int q = 0; q < NW; ++q) t += sqw[q][tid];
     slice_sq[tid] = t;
     inv[tid] = norm ? 1.0f / sqrtf(t / (float)p.K + p.eps) : 1.0f;
   }
@@ -182,17 +210,6 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
   // ---- stream row tiles
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int row0 = tile * ROWS;
-    uint4 w[ROWS][VPT];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const int n = row0 + r;
-      const WT* rp = row_ptr<WT>(p.rows, n < p.N ? n : p.N - 1, p.K);
-#pragma unroll
-      for (int v = 0; v < VPT; ++v) {
-        if (kvalid[v] && n < p.N) w[r][v] = *(const uint4*)(rp + koff[v]);
-        else w[r][v] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
     float acc[ROWS][BT];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r)
@@ -210,6 +227,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
           for (int e = 0; e < VEC; ++e) acc[r][b] = fmaf(wf[e], u[b][v][e], acc[r][b]);
       }
     }
+    if (tile + (int)gridDim.x < ntiles) load_tile(tile + gridDim.x);
 #pragma unroll
     for (int r = 0; r < ROWS; ++r)
 #pragma unroll
@@ -272,15 +290,32 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
     __syncthreads();
     if (is_last) {
       __threadfence();
-      if (tid < BT && tid < p.B) {
+      // each thread scans a strided subset of the block results, then a tree in LDS;
+      // ties resolve to the lower index at every level, so the result is the global
+      // first maximum whatever the scan order
+      __shared__ float rv[NT];
+      __shared__ int ri[NT];
+      for (int b = 0; b < p.B && b < BT; ++b) {
         float best = -INFINITY;
         int idx = INT_MAX;
-        for (int q = 0; q < nblk; ++q) {
-          const float v = p.best_val[(size_t)q * BT + tid];
-          const int i = p.best_idx[(size_t)q * BT + tid];
+        for (int q = tid; q < nblk; q += NT) {
+          const float v = p.best_val[(size_t)q * BT + b];
+          const int i = p.best_idx[(size_t)q * BT + b];
           if (v > best || (v == best && i < idx)) { best = v; idx = i; }
         }
-        p.next_out[tid] = idx == INT_MAX ? 0 : idx;
+        rv[tid] = best;
+        ri[tid] = idx;
+        __syncthreads();
+        for (int o = NT / 2; o > 0; o >>= 1) {
+          if (tid < o) {
+            const float v = rv[tid + o];
+            const int i = ri[tid + o];
+            if (v > rv[tid] || (v == rv[tid] && i < ri[tid])) { rv[tid] = v; ri[tid] = i; }
+          }
+          __syncthreads();
+        }
+        if (tid == 0) p.next_out[b] = ri[0] == INT_MAX ? 0 : ri[0];
+        __syncthreads();
       }
       if (tid == 0) *p.arg_counter = 0;
     }

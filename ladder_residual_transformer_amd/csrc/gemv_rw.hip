@@ -1,0 +1,503 @@
+// Decode projections for batch 1..4, one wave per row pair, and horizontal fusion of
+// independent projections (and decode attention) into one launch.
+//
+// A workgroup (4 waves) owns a contiguous range of row pairs of one problem.  It first
+// stages its input u = x (* RMSNorm gain) for all batch rows in LDS as fp32 together
+// with inv_rms = 1/sqrt(mean(x^2)+eps); every wave then streams whole row pairs: lane l
+// reads the 16-byte vectors l, l+64, ... of both rows (coalesced, each weight byte read
+// once), multiplies them with u from LDS in fp32, and a wave reduction gives the two
+// dot products.  There is no barrier inside the row loop, and the next pair's weight
+// loads are issued before the current pair's reduction and epilogue, so their latency
+// overlaps.  A row's result depends only on K and the lane mapping, never on which
+// workgroup computed it, so every launch shape gives bitwise identical values.
+//
+// One launch can carry two problems (blocks split in proportion to their bytes) and,
+// in front of them, the workgroups of a split-KV decode attention: with ladder
+// residuals a layer's QKV and gate/up projections read x_{2l-1} and x_{2l}, which are
+// both ready before the layer starts, and the down projection does not depend on the
+// attention, so each pair runs side by side in one kernel.
+#include <climits>
+
+#include "attn_decode.hpp"
+#include "common.hpp"
+#include "kernels.h"
+
+namespace ladder {
+
+template <typename WT>
+__device__ __forceinline__ const WT* rw_row_ptr(const RowSrc& s, int r, int K) {
+  if (s.interleave) return (const WT*)s.m[r & 1] + (size_t)(r >> 1) * K;
+  if (r < s.n0) return (const WT*)s.m[0] + (size_t)r * K;
+  if (r < s.n1) return (const WT*)s.m[1] + (size_t)(r - s.n0) * K;
+  return (const WT*)s.m[2] + (size_t)(r - s.n1) * K;
+}
+
+// Epilogue of one row pair (rows n0 = 2*pair, n0+1) for batch row b.
+template <typename WT>
+__device__ __forceinline__ void rw_epilogue(const GemvParams& p, int pair, int b, float y0, float y1, float inv,
+                                            float& best, int& bidx) {
+  const int n0 = 2 * pair, n1 = n0 + 1;
+  const bool v1 = n1 < p.N;
+  switch (p.epi) {
+    case EPI_STORE:
+    case EPI_LOGITS: {
+      y0 *= inv;
+      y1 *= inv;
+      p.out[(size_t)b * p.ldo + n0] = y0;
+      if (v1) p.out[(size_t)b * p.ldo + n1] = y1;
+      if (p.epi == EPI_LOGITS) {
+        if (y0 > best) { best = y0; bidx = n0; }
+        if (v1 && y1 > best) { best = y1; bidx = n1; }
+      }
+      break;
+    }
+    case EPI_ADD: {
+      p.out[(size_t)b * p.ldo + n0] = p.xres[(size_t)b * p.ldr + n0] + y0 * inv;
+      if (v1) p.out[(size_t)b * p.ldo + n1] = p.xres[(size_t)b * p.ldr + n1] + y1 * inv;
+      break;
+    }
+    case EPI_ADD2: {
+      const float t0 = p.xres[(size_t)b * p.ldr + n0] + y0 * inv;
+      p.out[(size_t)b * p.ldo + n0] = t0;
+      p.out2[(size_t)b * p.ldo + n0] = t0 + p.add2[(size_t)b * p.ldo + n0];
+      if (v1) {
+        const float t1 = p.xres[(size_t)b * p.ldr + n1] + y1 * inv;
+        p.out[(size_t)b * p.ldo + n1] = t1;
+        p.out2[(size_t)b * p.ldo + n1] = t1 + p.add2[(size_t)b * p.ldo + n1];
+      }
+      break;
+    }
+    case EPI_GATEUP_SWIGLU:
+      p.out[(size_t)b * p.ldo + pair] = silu(y0 * inv) * (y1 * inv);
+      break;
+    case EPI_QKV_ROPE: {
+      y0 *= inv;
+      y1 *= inv;
+      const int pos = *p.d_pos;
+      if (n0 < p.q_rows + p.kv_rows) {              // q or k: rotate the adjacent pair
+        const int d = (n0 < p.q_rows ? n0 : n0 - p.q_rows) % p.head_dim;
+        const int half = p.head_dim >> 1;
+        const float c = p.rope_cos[(size_t)pos * half + (d >> 1)];
+        const float s = p.rope_sin[(size_t)pos * half + (d >> 1)];
+        const float r0 = y0 * c - y1 * s;
+        const float r1 = y0 * s + y1 * c;
+        y0 = r0;
+        y1 = r1;
+      }
+      if (n0 < p.q_rows) {
+        p.out[(size_t)b * p.ldo + n0] = y0;
+        p.out[(size_t)b * p.ldo + n1] = y1;
+      } else {
+        const bool isk = n0 < p.q_rows + p.kv_rows;
+        const int rr = isk ? n0 - p.q_rows : n0 - p.q_rows - p.kv_rows;
+        const int kvh = rr / p.head_dim, d = rr % p.head_dim;
+        WT* cache = (WT*)(isk ? p.k_cache : p.v_cache);
+        const size_t off = (((size_t)b * p.n_kv + kvh) * p.max_seq + pos) * p.head_dim + d;
+        store_w<WT>(cache + off, y0);
+        store_w<WT>(cache + off + 1, y1);
+      }
+      break;
+    }
+    default:
+      break;
+  }
+}
+
+template <typename WT, int BT, int VPL, int HDA, int HPW>
+__global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  if constexpr (HDA != 0) {
+    if ((int)blockIdx.x < mp.n_attn) {
+      attn_decode_block<WT, HDA, HPW>(mp.attn, blockIdx.x, *reinterpret_cast<AttnLds<WT, HDA>*>(lds_raw));
+      return;
+    }
+  }
+  constexpr int VEC = Vec<WT>::N;
+  constexpr int CHUNK = 64 * VPL;                 // vectors of a row one wave covers per step
+  __shared__ float sqw[4][BT];
+  __shared__ float inv_sh[BT];
+  __shared__ float wbv[4][BT];
+  __shared__ int wbi[4][BT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int blk = (int)blockIdx.x - mp.n_attn;
+  const int pi = (mp.np > 1 && blk >= mp.blk_begin[1]) ? 1 : 0;
+  const GemvParams& p = mp.prob[pi];
+  const int lb = blk - mp.blk_begin[pi];
+  const int nb = mp.blk_begin[pi + 1] - mp.blk_begin[pi];
+  const int K = p.K, B = p.B;
+  const int nvec = K / VEC;
+  const int nchunk = (nvec + CHUNK - 1) / CHUNK;
+  const int P = (p.N + 1) / 2;
+  const int pr0 = (int)((long long)lb * P / nb);
+  const int pr1 = (int)((long long)(lb + 1) * P / nb);
+  float* u = reinterpret_cast<float*>(lds_raw);   // [B][K]
+
+  // This wave's work is a sequence of units: unit i is chunk (i % nchunk) of its pair
+  // number (i / nchunk); its pairs are pr0 + wid, pr0 + wid + 4, ...  Two register
+  // buffers form a pipeline: the loads of unit i+1 are in flight while unit i is
+  // multiplied.  Loads are unconditional (addresses clamped into the matrix) so that no
+  // branch separates a load from its use; lanes past the end of a row read the zero
+  // pad of u instead, and a missing odd row is discarded by the epilogue.
+  const int my_pairs = pr1 > pr0 + wid ? (pr1 - pr0 - wid + 3) / 4 : 0;
+  const int n_units = my_pairs * nchunk;
+  uint4 wa[2][VPL], wb[2][VPL];
+  auto load_unit = [&](uint4 (&w)[2][VPL], int unit) {
+    const int pair = pr0 + wid + 4 * (unit / nchunk), c = unit % nchunk;
+    const int n0 = 2 * pair;
+    const WT* r0 = rw_row_ptr<WT>(p.rows, n0, K);
+    const WT* r1 = rw_row_ptr<WT>(p.rows, min(n0 + 1, p.N - 1), K);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = min(c * CHUNK + lane + 64 * v, nvec - 1);
+      w[0][v] = *(const uint4*)(r0 + (size_t)vi * VEC);
+      w[1][v] = *(const uint4*)(r1 + (size_t)vi * VEC);
+    }
+  };
+  const int ustride = K + VEC;                     // u rows carry a zero pad of VEC floats
+
+  // ---- prologue: u = x (* g) for every batch row, and inv_rms.  For one batch row
+  // and K <= 256*4*VEC the input loads are issued before the first weight unit, so the
+  // in-order completion of loads does not make the prologue wait for the weights.
+  const bool norm = p.gain != nullptr;
+  if (tid < B * VEC) u[(tid / VEC) * ustride + K + tid % VEC] = 0.f;
+  if (BT == 1 && nvec <= 256 * 4) {
+    float4 xr[4][VEC / 4];
+    uint4 gr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = min(tid + 256 * i, nvec - 1);
+#pragma unroll
+      for (int e = 0; e < VEC / 4; ++e) xr[i][e] = *(const float4*)(p.x + (size_t)v * VEC + 4 * e);
+      gr[i] = norm ? *(const uint4*)((const WT*)p.gain + (size_t)v * VEC) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (n_units > 0) load_unit(wa, 0);
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = tid + 256 * i;
+      if (v < nvec) {
+        float xv[VEC], g[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC / 4; ++e) {
+          xv[4 * e] = xr[i][e].x; xv[4 * e + 1] = xr[i][e].y; xv[4 * e + 2] = xr[i][e].z; xv[4 * e + 3] = xr[i][e].w;
+        }
+        if (norm) {
+          unpack16(gr[i], g);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            sq = fmaf(xv[e], xv[e], sq);
+            xv[e] *= g[e];
+          }
+        }
+        float* up = u + (size_t)v * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) *(float4*)(up + e) = make_float4(xv[e], xv[e + 1], xv[e + 2], xv[e + 3]);
+      }
+    }
+    sq = wave_sum(sq);
+    if (lane == 0) sqw[wid][0] = sq;
+  } else {
+    if (n_units > 0) load_unit(wa, 0);
+    for (int b = 0; b < BT; ++b) {
+      float sq = 0.f;
+      if (b < B) {
+        for (int v = tid; v < nvec; v += 256) {
+          const float* xp = p.x + (size_t)b * p.ldx + (size_t)v * VEC;
+          float xv[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4) {
+            const float4 t = *(const float4*)(xp + e);
+            xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
+          }
+          if (norm) {
+            float g[VEC];
+            unpack16(*(const uint4*)((const WT*)p.gain + (size_t)v * VEC), g);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+              sq = fmaf(xv[e], xv[e], sq);
+              xv[e] *= g[e];
+            }
+          }
+          float* up = u + (size_t)b * ustride + (size_t)v * VEC;
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4) *(float4*)(up + e) = make_float4(xv[e], xv[e + 1], xv[e + 2], xv[e + 3]);
+        }
+      }
+      sq = wave_sum(sq);
+      if (lane == 0) sqw[wid][b] = sq;
+    }
+  }
+  __syncthreads();
+  if (tid < BT) {
+    const float t = ((sqw[0][tid] + sqw[1][tid]) + sqw[2][tid]) + sqw[3][tid];
+    inv_sh[tid] = norm ? 1.0f / sqrtf(t / (float)K + p.eps) : 1.0f;
+  }
+  __syncthreads();
+  float inv_b[BT];
+#pragma unroll
+  for (int b = 0; b < BT; ++b) inv_b[b] = inv_sh[b];
+
+  // ---- row pairs
+  float best = -INFINITY;
+  int bidx = INT_MAX;
+  float acc[2][BT];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
+  auto compute_unit = [&](const uint4 (&w)[2][VPL], int unit) {
+    const int c = unit % nchunk;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = c * CHUNK + lane + 64 * v;
+      const int ui = (vi < nvec ? vi : nvec) * VEC;    // past the row end: the zero pad
+      float w0[VEC], w1[VEC];
+      unpack16(w[0][v], w0);
+      unpack16(w[1][v], w1);
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        if (b < B) {
+          const float* up = u + (size_t)b * ustride + ui;
+          float uv[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4) {
+            const float4 t = *(const float4*)(up + e);
+            uv[e] = t.x; uv[e + 1] = t.y; uv[e + 2] = t.z; uv[e + 3] = t.w;
+          }
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            acc[0][b] = fmaf(w0[e], uv[e], acc[0][b]);
+            acc[1][b] = fmaf(w1[e], uv[e], acc[1][b]);
+          }
+        }
+      }
+    }
+    if (c == nchunk - 1) {                      // pair complete: reduce and finish it
+      const int pair = pr0 + wid + 4 * (unit / nchunk);
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        const float y0 = wave_sum(acc[0][b]);
+        const float y1 = wave_sum(acc[1][b]);
+        if (lane == b && b < B) rw_epilogue<WT>(p, pair, b, y0, y1, inv_b[b], best, bidx);
+        acc[0][b] = 0.f;
+        acc[1][b] = 0.f;
+      }
+    }
+  };
+  for (int i = 0; i < n_units; i += 2) {
+    if (i + 1 < n_units) load_unit(wb, i + 1);
+    compute_unit(wa, i);
+    if (i + 1 < n_units) {
+      if (i + 2 < n_units) load_unit(wa, i + 2);
+      compute_unit(wb, i + 1);
+    }
+  }
+
+  if (p.epi == EPI_LOGITS) {
+    // per-block greedy candidate (lowest index among equal maxima); merged by argmax_finalize
+    if (lane < BT) { wbv[wid][lane] = best; wbi[wid][lane] = bidx; }
+    __syncthreads();
+    if (tid < BT) {
+      float bb = wbv[0][tid];
+      int ii = wbi[0][tid];
+      for (int q = 1; q < 4; ++q)
+        if (wbv[q][tid] > bb || (wbv[q][tid] == bb && wbi[q][tid] < ii)) { bb = wbv[q][tid]; ii = wbi[q][tid]; }
+      p.best_val[(size_t)lb * BT + tid] = bb;
+      p.best_idx[(size_t)lb * BT + tid] = ii;
+    }
+  }
+}
+
+// next[b] = index of the first maximum over the n per-block candidates.
+__global__ __launch_bounds__(256) void argmax_finalize_kernel(const float* bv, const int* bi, int n, int BT, int B,
+                                                              int* next) {
+  __shared__ float rv[256];
+  __shared__ int ri[256];
+  const int tid = threadIdx.x;
+  for (int b = 0; b < B; ++b) {
+    float best = -INFINITY;
+    int idx = INT_MAX;
+    for (int q = tid; q < n; q += 256) {
+      const float v = bv[(size_t)q * BT + b];
+      const int i = bi[(size_t)q * BT + b];
+      if (v > best || (v == best && i < idx)) { best = v; idx = i; }
+    }
+    rv[tid] = best;
+    ri[tid] = idx;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) {
+        const float v = rv[tid + o];
+        const int i = ri[tid + o];
+        if (v > rv[tid] || (v == rv[tid] && i < ri[tid])) { rv[tid] = v; ri[tid] = i; }
+      }
+      __syncthreads();
+    }
+    if (tid == 0) next[b] = ri[0] == INT_MAX ? 0 : ri[0];
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ host side
+namespace {
+
+constexpr int kRwTargetBlocks = 1024;  // upper bound; the launch uses what fits on the device at once
+constexpr int kRwBlocksPerCu = 2;
+
+int rw_bt(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : 4; }
+
+// Workgroups per problem in proportion to its rows, at least 4 row pairs each.
+void rw_split_blocks(MultiGemvParams& mp, int target) {
+  long long rows = 0;
+  for (int i = 0; i < mp.np; ++i) rows += mp.prob[i].N;
+  mp.blk_begin[0] = 0;
+  for (int i = 0; i < mp.np; ++i) {
+    const int P = (mp.prob[i].N + 1) / 2;
+    long long nb = (long long)target * mp.prob[i].N / rows;
+    const int cap = (P + 3) / 4;
+    if (nb > cap) nb = cap;
+    if (nb < 1) nb = 1;
+    mp.blk_begin[i + 1] = mp.blk_begin[i] + (int)nb;
+  }
+  if (mp.np == 1) mp.blk_begin[2] = mp.blk_begin[1];
+}
+
+// vectors per lane per pipeline unit: the whole row when it fits in 4 (256 vectors,
+// 4 KB of bf16), else units of 4 -- two buffers of 2 rows x 4 x 16 B stay in registers
+int rw_vpl(int nvec) {
+  for (int v : {1, 2})
+    if (64 * v >= nvec) return v;
+  return 4;
+}
+
+template <typename WT, int BT, int VPL, int HDA, int HPW>
+hipError_t rw_go(MultiGemvParams& mp, size_t lds, hipStream_t s) {
+  auto fn = gemv_rw_kernel<WT, BT, VPL, HDA, HPW>;
+  // resident workgroups of this instance at this LDS size (queried once per instance
+  // and size): the GEMV workgroups of one launch are sized to fill the device once
+  static size_t cached_lds = 0;
+  static int cached_resident = 0;
+  if (cached_lds != lds || cached_resident == 0) {
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    int per_cu = 0, dev = 0, ncu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)fn, 256, lds);
+    if (e != hipSuccess) return e;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    // two long-lived workgroups per CU (8 waves) keep ~2 x 16 KB per wave in flight
+    // and give every wave several pipeline units
+    const int want = per_cu < kRwBlocksPerCu ? per_cu : kRwBlocksPerCu;
+    cached_resident = want > 0 ? want * ncu : 256;
+    cached_lds = lds;
+  }
+  int target = cached_resident - mp.n_attn;
+  if (target < 64) target = 64;
+  if (target > kRwTargetBlocks) target = kRwTargetBlocks;
+  rw_split_blocks(mp, target);
+  const int grid = mp.n_attn + mp.blk_begin[mp.np];
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, s, mp);
+  return hipGetLastError();
+}
+
+// Attention workgroups are only fused into launches with 4 vectors per lane per unit
+// (every down projection here); the caller launches them separately otherwise.
+template <typename WT, int BT, int VPL>
+hipError_t rw_hda(MultiGemvParams& mp, int hda, size_t lds, hipStream_t s) {
+  if constexpr (VPL == 4) {
+    const int hpw = hda ? attn_hpw(mp.attn.nq / mp.attn.nkv) : 0;
+    if (hda == 128) {
+      if (hpw == 1) return rw_go<WT, BT, VPL, 128, 1>(mp, lds, s);
+      if (hpw == 2) return rw_go<WT, BT, VPL, 128, 2>(mp, lds, s);
+      return rw_go<WT, BT, VPL, 128, 4>(mp, lds, s);
+    }
+    if (hda == 64) {
+      if (hpw == 1) return rw_go<WT, BT, VPL, 64, 1>(mp, lds, s);
+      if (hpw == 2) return rw_go<WT, BT, VPL, 64, 2>(mp, lds, s);
+      return rw_go<WT, BT, VPL, 64, 4>(mp, lds, s);
+    }
+  }
+  if (hda != 0) return hipErrorInvalidValue;
+  return rw_go<WT, BT, VPL, 0, 0>(mp, lds, s);
+}
+
+template <typename WT, int BT>
+hipError_t rw_vpl_go(MultiGemvParams& mp, int vpl, int hda, size_t lds, hipStream_t s) {
+  switch (vpl) {
+    case 1: return rw_hda<WT, BT, 1>(mp, hda, lds, s);
+    case 2: return rw_hda<WT, BT, 2>(mp, hda, lds, s);
+    default: return rw_hda<WT, BT, 4>(mp, hda, lds, s);
+  }
+}
+
+template <typename WT>
+hipError_t rw_bt_go(MultiGemvParams& mp, int bt, int vpl, int hda, size_t lds, hipStream_t s) {
+  if (bt == 1) return rw_vpl_go<WT, 1>(mp, vpl, hda, lds, s);
+  if (bt == 2) return rw_vpl_go<WT, 2>(mp, vpl, hda, lds, s);
+  return rw_vpl_go<WT, 4>(mp, vpl, hda, lds, s);
+}
+
+}  // namespace
+
+bool gemv_rw_attn_fusable(int wdtype, int K) { return rw_vpl(K / (wdtype == W_BF16 ? 8 : 4)) == 4; }
+
+bool gemv_rw_supported(int wdtype, int K, int B) {
+  return B >= 1 && B <= 4 && (size_t)B * (K + (wdtype == W_BF16 ? 8 : 4)) * 4 <= 66560;
+}
+
+int gemv_rw_blocks(int wdtype, int N, int K, int B) {
+  (void)wdtype;
+  (void)K;
+  (void)B;
+  const int P = (N + 1) / 2;
+  int nb = (P + 3) / 4;
+  return nb < kRwTargetBlocks ? nb : kRwTargetBlocks;   // upper bound of a one-problem launch
+}
+
+hipError_t launch_gemv_multi(const GemvParams* probs, int np, const AttnDecodeParams* attn, hipStream_t s,
+                             int* blocks_out) {
+  if (np < 1 || np > 2) return hipErrorInvalidValue;
+  const int K = probs[0].K, B = probs[0].B, wdt = probs[0].wdtype;
+  for (int i = 0; i < np; ++i)
+    if (probs[i].K != K || probs[i].B != B || probs[i].wdtype != wdt || probs[i].N < 1) return hipErrorInvalidValue;
+  if (!gemv_rw_supported(wdt, K, B)) return hipErrorInvalidValue;
+  MultiGemvParams mp{};
+  mp.np = np;
+  for (int i = 0; i < np; ++i) mp.prob[i] = probs[i];
+  size_t lds = (size_t)B * (K + (wdt == W_BF16 ? 8 : 4)) * 4;
+  int hda = 0;
+  if (attn) {
+    if (rw_vpl(K / (wdt == W_BF16 ? 8 : 4)) != 4) return hipErrorInvalidValue;
+    if (attn->nkv < 1 || attn->nq % attn->nkv != 0 || attn->nq / attn->nkv > kAttnMaxGroup ||
+        attn->n_split > kAttnMaxSplits || (attn->hd != 64 && attn->hd != 128) || attn->wdtype != wdt)
+      return hipErrorInvalidValue;
+    mp.attn = *attn;
+    mp.n_attn = attn->n_split * attn->nkv * attn->B;
+    hda = attn->hd;
+    const size_t al = wdt == W_BF16 ? (hda == 128 ? sizeof(AttnLds<uint16_t, 128>) : sizeof(AttnLds<uint16_t, 64>))
+                                    : (hda == 128 ? sizeof(AttnLds<float, 128>) : sizeof(AttnLds<float, 64>));
+    if (al > lds) lds = al;
+  }
+  const int vpl = rw_vpl(K / (wdt == W_BF16 ? 8 : 4));
+  const int bt = rw_bt(B);
+  const hipError_t e = wdt == W_BF16 ? rw_bt_go<uint16_t>(mp, bt, vpl, hda, lds, s)
+                                     : rw_bt_go<float>(mp, bt, vpl, hda, lds, s);
+  if (blocks_out)
+    for (int i = 0; i < np; ++i) blocks_out[i] = mp.blk_begin[i + 1] - mp.blk_begin[i];
+  return e;
+}
+
+hipError_t launch_argmax_finalize(const float* best_val, const int* best_idx, int n, int BT, int B, int* next,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(256), 0, s, best_val, best_idx, n, BT, B, next);
+  return hipGetLastError();
+}
+
+int gemv_rw_bt(int B) { return rw_bt(B); }
+
+}  // namespace ladder

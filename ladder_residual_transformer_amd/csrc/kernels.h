@@ -25,6 +25,7 @@ enum GemvEpi {
   EPI_QKV_ROPE = 2,     // q -> out (fp32, rotated); k (rotated), v -> KV cache at pos
   EPI_GATEUP_SWIGLU = 3,// out[b][n] = silu(y[2n]) * y[2n+1]
   EPI_LOGITS = 4,       // out[b][n] = y; greedy argmax -> next_out[b]
+  EPI_ADD2 = 5,         // out[b][n] = xres[b][n] + y; out2[b][n] = out[b][n] + add2[b][n]
 };
 
 struct GemvParams {
@@ -35,7 +36,8 @@ struct GemvParams {
   const void* gain; float eps;    // RMSNorm gain of the input (nullptr: no norm)
   int epi;
   float* out; int ldo;
-  const float* xres; int ldr;     // EPI_ADD
+  const float* xres; int ldr;     // EPI_ADD, EPI_ADD2
+  const float* add2; float* out2; // EPI_ADD2 (same leading dimension as out)
   // EPI_QKV_ROPE
   void* k_cache; void* v_cache;   // this layer: [max_batch][n_kv][max_seq][head_dim]
   int q_rows, kv_rows, head_dim, max_seq, n_kv;
@@ -60,12 +62,33 @@ struct AttnDecodeParams {
   int max_seq, nq, nkv, hd, B;
   const int* d_pos;                    // keys 0..pos
   int n_split;
-  float* part;                         // [B][nq][n_split][hd+2]
+  float* part;                         // [B][nq][n_split][hd+4]: max, sum, -, -, acc[hd]
   int* counters;                       // [B][nkv]
   float* out;                          // [B][nq*hd]
 };
 int attn_decode_splits(int max_seq);
 hipError_t launch_attn_decode(const AttnDecodeParams& p, hipStream_t s);
+
+// ------------------------------------------- row-wave GEMV (batch <= 4), fused launches
+// Up to two GEMV problems with the same K and batch, optionally preceded by the
+// workgroups of a split-KV decode attention, in one launch.
+struct MultiGemvParams {
+  GemvParams prob[2];
+  int np;
+  int blk_begin[3];       // problem p owns blocks [blk_begin[p], blk_begin[p+1]) after the attention ones
+  int n_attn;             // leading workgroups running decode attention (0 = none)
+  AttnDecodeParams attn;
+};
+bool gemv_rw_supported(int wdtype, int K, int B);
+bool gemv_rw_attn_fusable(int wdtype, int K);   // a launch of this K can carry attention workgroups
+int gemv_rw_blocks(int wdtype, int N, int K, int B);   // workgroups of a one-problem launch
+int gemv_rw_bt(int B);
+// blocks_out (nullable): workgroups given to each problem
+hipError_t launch_gemv_multi(const GemvParams* probs, int np, const AttnDecodeParams* attn, hipStream_t s,
+                             int* blocks_out);
+// next[b] = first maximum of n per-workgroup candidates (best_val/best_idx [n][BT])
+hipError_t launch_argmax_finalize(const float* best_val, const int* best_idx, int n, int BT, int B, int* next,
+                                  hipStream_t s);
 
 // ---------------------------------------------------------- prefill attention
 struct AttnPrefillParams {

@@ -110,7 +110,7 @@ struct ladder_ctx {
   int* arg_cnt = nullptr;
   StreamScratch sc[2];
 
-  int sched = LADDER_SCHED_DUAL;
+  int sched = LADDER_SCHED_FUSED;
   int use_graph = 1;
   std::map<int, hipGraphExec_t> graphs;
   int filled = 0;
@@ -198,14 +198,15 @@ void carve(ladder_ctx* c, Carver& cv) {
       need.counters = std::max(need.counters, r.counters);
       need.best = std::max(need.best, r.best);
     }
-  c->best_val = cv.take<float>(need.best);
-  c->best_idx = cv.take<int>(need.best);
+  const size_t nbest = std::max<size_t>(need.best, 1024 * 16);
+  c->best_val = cv.take<float>(nbest);
+  c->best_idx = cv.take<int>(nbest);
   c->arg_cnt = cv.take<int>(1);
   const size_t ue = c->wdt == W_BF16 ? 2 : 4;
   for (int s = 0; s < 2; ++s) {
     StreamScratch& sc = c->sc[s];
     sc.q = cv.take<float>((size_t)B * c->qrows);
-    sc.attn_part = cv.take<float>((size_t)B * g.n_q_heads * c->n_split * (g.head_dim + 2));
+    sc.attn_part = cv.take<float>((size_t)B * g.n_q_heads * c->n_split * (g.head_dim + 4));
     sc.attn_cnt = cv.take<int>((size_t)B * g.n_kv_heads);
     sc.o = cv.take<float>((size_t)B * c->qrows);
     sc.a = cv.take<float>((size_t)B * F);
@@ -362,21 +363,72 @@ GemvParams lmhead_params(const ladder_ctx* ctx, const float* x, int ldx, int B) 
   return p;
 }
 
+// One decode GEMV: the row-wave kernel when the batch and K allow (its per-row
+// arithmetic is the same in every launch shape), else the K-sliced kernel.  Logits get
+// their greedy argmax finalised by a one-workgroup kernel in the first case (the
+// K-sliced kernel finalises in its last workgroup).
+ladder_status run_gemv(ladder_ctx* ctx, const GemvParams& p, hipStream_t s) {
+  if (gemv_rw_supported(p.wdtype, p.K, p.B)) {
+    int nb = 0;
+    HIPCHK(launch_gemv_multi(&p, 1, nullptr, s, &nb));
+    if (p.epi == EPI_LOGITS)
+      HIPCHK(launch_argmax_finalize(p.best_val, p.best_idx, nb, gemv_rw_bt(p.B), p.B, p.next_out, s));
+  } else {
+    HIPCHK(launch_gemv(p, s));
+  }
+  return LADDER_OK;
+}
+
 // Enqueue module m of one decode step.  out_x != nullptr: fused residual add
 // (out_x = x_m + out_m); else out_m goes to out_store.
 ladder_status decode_module(ladder_ctx* ctx, int m, int B, const float* xin, const float* xm, float* out_x,
                             float* out_store, hipStream_t s, bool wait_xm, hipEvent_t ev_xm) {
   const int l = m / 2;
   StreamScratch& sc = module_scratch(ctx, m);
+  ladder_status st;
   if (m % 2 == 0) {
-    HIPCHK(launch_gemv(qkv_params(ctx, l, B, xin, sc), s));
+    if ((st = run_gemv(ctx, qkv_params(ctx, l, B, xin, sc), s))) return st;
     HIPCHK(launch_attn_decode(attn_params(ctx, l, B, sc), s));
   } else {
-    HIPCHK(launch_gemv(gateup_params(ctx, l, B, xin, sc), s));
+    if ((st = run_gemv(ctx, gateup_params(ctx, l, B, xin, sc), s))) return st;
   }
   if (out_x && wait_xm) HIPCHK(hipStreamWaitEvent(s, ev_xm, 0));
-  HIPCHK(launch_gemv(outproj_params(ctx, m, B, sc, xm, out_x, out_store), s));
-  return LADDER_OK;
+  return run_gemv(ctx, outproj_params(ctx, m, B, sc, xm, out_x, out_store), s);
+}
+
+// One ladder layer l of a decode step on one stream, in three launches:
+//   [QKV_l | gate/up_l]   the attention reads x_{2l-1}, the MLP x_{2l}: both exist;
+//   [attention_l | down_l] the down projection needs only the SwiGLU output; stores d;
+//   [O_l]                 x_{2l+1} = x_{2l} + o, then x_{2l+2} = x_{2l+1} + d.
+// The values are those of the module-by-module order (same kernels per row, same adds).
+ladder_status decode_layer_fused(ladder_ctx* ctx, int l, int B) {
+  const int ma = 2 * l, mm = 2 * l + 1;
+  StreamScratch& sc = ctx->sc[0];
+  hipStream_t s = ctx->s0;
+  float* const* X = ctx->dx;
+  ladder_status st;
+  GemvParams pr[2] = {qkv_params(ctx, l, B, X[module_src(ctx, ma) % 2], sc),
+                      gateup_params(ctx, l, B, X[module_src(ctx, mm) % 2], sc)};
+  const bool rw = gemv_rw_supported(ctx->wdt, ctx->cfg.hidden, B);
+  if (rw) {
+    HIPCHK(launch_gemv_multi(pr, 2, nullptr, s, nullptr));
+  } else {
+    if ((st = run_gemv(ctx, pr[0], s))) return st;
+    if ((st = run_gemv(ctx, pr[1], s))) return st;
+  }
+  const GemvParams down = outproj_params(ctx, mm, B, sc, nullptr, nullptr, ctx->dout[0]);
+  const AttnDecodeParams at = attn_params(ctx, l, B, sc);
+  if (gemv_rw_supported(ctx->wdt, ctx->cfg.ffn, B) && gemv_rw_attn_fusable(ctx->wdt, ctx->cfg.ffn)) {
+    HIPCHK(launch_gemv_multi(&down, 1, &at, s, nullptr));
+  } else {
+    HIPCHK(launch_attn_decode(at, s));
+    if ((st = run_gemv(ctx, down, s))) return st;
+  }
+  GemvParams o = outproj_params(ctx, ma, B, sc, X[ma % 2], X[(ma + 1) % 2], nullptr);
+  o.epi = EPI_ADD2;
+  o.add2 = ctx->dout[0];
+  o.out2 = X[(ma + 2) % 2];
+  return run_gemv(ctx, o, s);
 }
 
 // ---------------------------------------------------------------- prefill module
@@ -524,8 +576,7 @@ ladder_status run_modules(ladder_ctx* ctx, float* const X[2], float* const OUT[2
 }
 
 ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream_t s) {
-  HIPCHK(launch_gemv(lmhead_params(ctx, x, ldx, B), s));
-  return LADDER_OK;
+  return run_gemv(ctx, lmhead_params(ctx, x, ldx, B), s);
 }
 
 // One decode step reading ids_dev / pos_dev, leaving logits/next in the context and
@@ -533,10 +584,26 @@ ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream
 ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
   const ladder_config& g = ctx->cfg;
   HIPCHK(launch_embed(ctx->wdt, ctx->w.tok_embed, g.vocab, g.hidden, ctx->ids_dev, B, ctx->dx[0], ctx->s0));
-  auto mod = [&](int m, const float* xin, const float* xm, float* xn, float* store, hipStream_t s, bool wait,
-                 hipEvent_t ev) { return decode_module(ctx, m, B, xin, xm, xn, store, s, wait, ev); };
-  ladder_status st = run_modules(ctx, ctx->dx, ctx->dout, (size_t)B * g.hidden, mod);
-  if (st) return st;
+  ladder_status st;
+  if (ctx->sched == LADDER_SCHED_FUSED) {
+    // ladder layers in three launches; standard layers module by module (fused adds)
+    for (int l = 0; l < g.n_layers; ++l) {
+      if (ctx->mask[l]) {
+        if ((st = decode_layer_fused(ctx, l, B))) return st;
+      } else {
+        for (int m = 2 * l; m < 2 * l + 2; ++m) {
+          st = decode_module(ctx, m, B, ctx->dx[module_src(ctx, m) % 2], ctx->dx[m % 2], ctx->dx[(m + 1) % 2],
+                             nullptr, ctx->s0, false, nullptr);
+          if (st) return st;
+        }
+      }
+    }
+  } else {
+    auto mod = [&](int m, const float* xin, const float* xm, float* xn, float* store, hipStream_t s, bool wait,
+                   hipEvent_t ev) { return decode_module(ctx, m, B, xin, xm, xn, store, s, wait, ev); };
+    st = run_modules(ctx, ctx->dx, ctx->dout, (size_t)B * g.hidden, mod);
+    if (st) return st;
+  }
   return lm_head(ctx, ctx->dx[(2 * g.n_layers) % 2], g.hidden, B, ctx->s0);
 }
 
@@ -687,7 +754,7 @@ ladder_status ladder_init(const ladder_config* cfg, const ladder_weights* w, con
 
 ladder_status ladder_set_schedule(ladder_ctx* ctx, int32_t schedule, int32_t use_graph) {
   if (!ctx) return LADDER_ERR_ARG;
-  if (schedule < LADDER_SCHED_SERIAL || schedule > LADDER_SCHED_DUAL) return LADDER_ERR_ARG;
+  if (schedule < LADDER_SCHED_SERIAL || schedule > LADDER_SCHED_FUSED) return LADDER_ERR_ARG;
   ctx->sched = schedule;
   ctx->use_graph = use_graph ? 1 : 0;
   return LADDER_OK;
@@ -726,27 +793,58 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
   HIPCHK(hipEventCreate(&e1));
   const StreamScratch& sc = ctx->sc[0];
   hipStream_t s = ctx->s0;
+  const bool rw_h = gemv_rw_supported(ctx->wdt, g.hidden, B);
+  const bool rw_f = gemv_rw_supported(ctx->wdt, g.ffn, B) && gemv_rw_attn_fusable(ctx->wdt, g.ffn);
   for (int kind = 0; kind < LADDER_N_KERNELS; ++kind) {
     int launches = 0;
     HIPCHK(hipEventRecord(e0, s));
     for (int r = 0; r < reps; ++r) {
       if (kind == LADDER_KERNEL_LMHEAD) {
-        HIPCHK(launch_gemv(lmhead_params(ctx, ctx->dx[0], g.hidden, B), s));
+        if ((st = run_gemv(ctx, lmhead_params(ctx, ctx->dx[0], g.hidden, B), s))) return st;
         ++launches;
         continue;
       }
       for (int l = 0; l < g.n_layers; ++l, ++launches) {
         switch (kind) {
-          case LADDER_KERNEL_QKV: HIPCHK(launch_gemv(qkv_params(ctx, l, B, ctx->dx[0], sc), s)); break;
+          case LADDER_KERNEL_QKV: st = run_gemv(ctx, qkv_params(ctx, l, B, ctx->dx[0], sc), s); break;
           case LADDER_KERNEL_ATTN: HIPCHK(launch_attn_decode(attn_params(ctx, l, B, sc), s)); break;
           case LADDER_KERNEL_OPROJ:
-            HIPCHK(launch_gemv(outproj_params(ctx, 2 * l, B, sc, ctx->dx[0], ctx->dx[1], nullptr), s));
+            st = run_gemv(ctx, outproj_params(ctx, 2 * l, B, sc, ctx->dx[0], ctx->dx[1], nullptr), s);
             break;
-          case LADDER_KERNEL_GATEUP: HIPCHK(launch_gemv(gateup_params(ctx, l, B, ctx->dx[0], sc), s)); break;
-          default:
-            HIPCHK(launch_gemv(outproj_params(ctx, 2 * l + 1, B, sc, ctx->dx[0], ctx->dx[1], nullptr), s));
+          case LADDER_KERNEL_GATEUP: st = run_gemv(ctx, gateup_params(ctx, l, B, ctx->dx[0], sc), s); break;
+          case LADDER_KERNEL_DOWN:
+            st = run_gemv(ctx, outproj_params(ctx, 2 * l + 1, B, sc, ctx->dx[0], ctx->dx[1], nullptr), s);
             break;
+          case LADDER_KERNEL_QKV_GATEUP: {
+            GemvParams pr[2] = {qkv_params(ctx, l, B, ctx->dx[1], sc), gateup_params(ctx, l, B, ctx->dx[0], sc)};
+            if (rw_h) {
+              HIPCHK(launch_gemv_multi(pr, 2, nullptr, s, nullptr));
+            } else if (!(st = run_gemv(ctx, pr[0], s))) {
+              st = run_gemv(ctx, pr[1], s);
+            }
+            break;
+          }
+          case LADDER_KERNEL_ATTN_DOWN: {
+            const GemvParams down = outproj_params(ctx, 2 * l + 1, B, sc, nullptr, nullptr, ctx->dout[0]);
+            const AttnDecodeParams at = attn_params(ctx, l, B, sc);
+            if (rw_f) {
+              HIPCHK(launch_gemv_multi(&down, 1, &at, s, nullptr));
+            } else {
+              HIPCHK(launch_attn_decode(at, s));
+              st = run_gemv(ctx, down, s);
+            }
+            break;
+          }
+          default: {
+            GemvParams o = outproj_params(ctx, 2 * l, B, sc, ctx->dx[0], ctx->dx[1], nullptr);
+            o.epi = EPI_ADD2;
+            o.add2 = ctx->dout[0];
+            o.out2 = ctx->dx[0];
+            st = run_gemv(ctx, o, s);
+            break;
+          }
         }
+        if (st) return st;
       }
     }
     HIPCHK(hipEventRecord(e1, s));
@@ -782,7 +880,10 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
     const int sp = start_pos + t0;
     auto mod = [&](int m, const float* xin, const float* xm, float* xn, float* store, hipStream_t s, bool wait,
                    hipEvent_t ev) { return prefill_module(ctx, m, B, Tc, sp, xin, xm, xn, store, s, wait, ev); };
+    const int saved = ctx->sched;
+    if (saved == LADDER_SCHED_FUSED) ctx->sched = LADDER_SCHED_SERIAL;   // prefill: module order
     st = run_modules(ctx, ctx->px, ctx->pout, (size_t)M * g.hidden, mod);
+    ctx->sched = saved;
     if (st) return st;
     if (t0 + Tc == T) {
       const float* xl = ctx->px[NM % 2] + (size_t)(Tc - 1) * g.hidden;
@@ -812,7 +913,7 @@ ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t 
     auto it = ctx->graphs.find(key);
     if (it == ctx->graphs.end()) {
       hipGraph_t graph = nullptr;
-      HIPCHK(hipStreamBeginCapture(ctx->s0, hipStreamCaptureModeThreadLocal));
+      HIPCHK(hipStreamBeginCapture(ctx->s0, hipStreamCaptureModeRelaxed));
       st = enqueue_decode(ctx, B);
       hipError_t ce = hipStreamEndCapture(ctx->s0, &graph);
       if (st) {

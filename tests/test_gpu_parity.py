@@ -14,7 +14,7 @@ from oracle import LadderOracle, teacher_forced
 
 pytestmark = pytest.mark.gpu
 
-SERIAL, SIDE, DUAL = 0, 1, 2
+SERIAL, SIDE, DUAL, FUSED = 0, 1, 2, 3
 
 # bf16 model with ragged shapes: H = 2112 (264 vectors: two K slices at batch > 4, the
 # second one short), 6 query / 2 kv heads of 64, F = 1344, vocab 1001 (ragged row
@@ -87,20 +87,22 @@ def test_edge_shapes_bf16(edge, B, T, chunk):
     model.free()
 
 
+@pytest.mark.parametrize("B", [2, 5])
 @pytest.mark.parametrize("use_graph", [False, True])
-def test_schedules_are_bitwise_identical(edge, use_graph):
-    """Race check: the two-stream and side-stream schedules must reproduce the serial
-    one bit for bit (any missing wait would read a stale or half-written residual)."""
+def test_schedules_are_bitwise_identical(edge, use_graph, B):
+    """Race check: the side-stream, two-stream and fused-ladder schedules must reproduce
+    the serial one bit for bit (any missing wait would read a stale or half-written
+    residual).  B=2 uses the row-wave kernels, B=5 the K-sliced ones."""
     cfg, w = edge
-    prompt = synth.gen_ids(5, 21, cfg.vocab, seed=7)
-    cont = synth.gen_ids(5, 4, cfg.vocab, seed=7, stream=1)
+    prompt = synth.gen_ids(B, 21, cfg.vocab, seed=7)
+    cont = synth.gen_ids(B, 4, cfg.vocab, seed=7, stream=1)
     outs = {}
-    for sched in (SERIAL, SIDE, DUAL):
-        model = make_model(cfg, w, 5, 32)
+    for sched in (SERIAL, SIDE, DUAL, FUSED):
+        model = make_model(cfg, w, B, 32)
         model.set_schedule(sched, use_graph)
         outs[sched] = gpu_teacher_forced(model, prompt, cont)
         model.free()
-    for sched in (SIDE, DUAL):
+    for sched in (SIDE, DUAL, FUSED):
         for a, b in zip(outs[SERIAL], outs[sched]):
             assert np.array_equal(a, b), f"schedule {sched} differs from serial"
 
@@ -112,7 +114,7 @@ def test_graph_replay_matches_eager(edge):
     res = []
     for g in (False, True):
         model = make_model(cfg, w, 2, 24)
-        model.set_schedule(DUAL, g)
+        model.set_schedule(FUSED, g)
         res.append(gpu_teacher_forced(model, prompt, cont))
         model.free()
     for a, b in zip(*res):
