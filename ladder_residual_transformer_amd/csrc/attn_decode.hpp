@@ -31,7 +31,7 @@ constexpr int kAttnMaxSplits = 32;
 template <typename WT, int HD>
 struct AttnLds {
   static constexpr int RW = HD * (int)sizeof(WT) / 4 + 1;   // dwords per staged row (odd)
-  float qs[kAttnMaxGroup][HD];
+  __attribute__((aligned(16))) float qs[kAttnMaxGroup][HD];
   uint32_t ks[kAttnKeyTile][RW];
   uint32_t vs[kAttnKeyTile][RW];
   float wsc[kAttnMaxGroup][kAttnMaxSplits];
@@ -127,10 +127,18 @@ __device__ void attn_decode_block(const AttnDecodeParams& p, int blk, AttnLds<WT
     for (int k = 0; k < HPW; ++k) sc[k] = 0.f;
     const uint32_t* krow = L.ks[lane];
 #pragma unroll
-    for (int d = 0; d < HD; ++d) {
-      const float kv = attn_elem<WT>(krow, d);
+    for (int d = 0; d < HD; d += 4) {               // 4 dims per step: one 16-byte q read per head
+      float kv[4];
 #pragma unroll
-      for (int k = 0; k < HPW; ++k) sc[k] = fmaf(L.qs[hc[k]][d], kv, sc[k]);
+      for (int e = 0; e < 4; ++e) kv[e] = attn_elem<WT>(krow, d + e);
+#pragma unroll
+      for (int k = 0; k < HPW; ++k) {
+        const float4 q4 = *reinterpret_cast<const float4*>(&L.qs[hc[k]][d]);
+        sc[k] = fmaf(q4.x, kv[0], sc[k]);
+        sc[k] = fmaf(q4.y, kv[1], sc[k]);
+        sc[k] = fmaf(q4.z, kv[2], sc[k]);
+        sc[k] = fmaf(q4.w, kv[3], sc[k]);
+      }
     }
     // online softmax per head, then P.V with lane = output dims
     float pj[HPW];
@@ -145,6 +153,7 @@ __device__ void attn_decode_block(const AttnDecodeParams& p, int blk, AttnLds<WT
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[k][e] *= a;
     }
+#pragma unroll 4
     for (int j = 0; j < n; ++j) {
       float v[DPL];
 #pragma unroll
