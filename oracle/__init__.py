@@ -14,6 +14,7 @@ from .ladder import (  # noqa: F401
     LadderOracle,
     ForwardResult,
     upcast,
+    round_to_storage,
     rms_norm,
     rope_angles,
     apply_rope,

@@ -30,7 +30,10 @@ design notes of the repository):
   * pre-norm RMSNorm with eps 1e-5, gains stored with the weights;
   * rotary pairs are adjacent elements (2j, 2j+1), angle p * theta^(-2j/hd);
   * no biases, untied LM head, greedy argmax takes the lowest index on ties;
-  * the KV cache holds unrounded values (the GPU may store it in bf16).
+  * the KV cache is model state kept in the model's storage type, like the
+    weights it is computed from: each K and V value is rounded to that type
+    (round to nearest, ties to even) when it is written, and attention reads
+    the stored values.  ``kv_store_dtype=False`` keeps them unrounded.
 
 Compute precision is float64 unless the caller asks for float32 (used only to
 time the oracle and to run the largest shards within host memory).
@@ -61,6 +64,26 @@ def upcast(w: np.ndarray, dtype=np.float64) -> np.ndarray:
     else:
         raise TypeError(f"unsupported stored dtype {w.dtype}")
     return np.asarray(f, dtype=dtype)
+
+
+def round_to_storage(x: np.ndarray, dtype_name: str) -> np.ndarray:
+    """Round ``x`` to the model's storage type, keeping the array's own dtype.
+
+    bf16 has 8 significant bits: with x = f * 2**e, 0.5 <= |f| < 1 (frexp), the
+    spacing of bf16 values around x is 2**(e - 8), and 2**-133 below the smallest
+    normal 2**-126; x / spacing is rounded half-to-even (numpy ``rint``) and scaled
+    back, which is exact in binary floating point.  fp32 storage is numpy's own
+    round-to-nearest-even conversion.  Pins: halfway cases round to the even
+    neighbour; agreement with an independent bit-pattern rounding of float32 input.
+    """
+    if dtype_name == "bf16":
+        x64 = np.asarray(x, dtype=np.float64)
+        _, e = np.frexp(x64)
+        q = np.ldexp(1.0, np.maximum(e, -125) - 8)
+        return (np.rint(x64 / q) * q).astype(x.dtype)
+    if dtype_name == "f32":
+        return np.asarray(x).astype(np.float32).astype(x.dtype)
+    raise ValueError(f"unknown storage dtype {dtype_name!r}")
 
 
 def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
@@ -171,13 +194,16 @@ class LadderOracle:
     final_norm, lm_head, layers[...] with attn_norm, wq, wk, wv, wo, mlp_norm,
     w_gate, w_up, w_down) holding the stored arrays; ``cfg`` provides the
     shapes (hidden, n_q_heads, n_kv_heads, head_dim, n_layers, rope_theta,
-    norm_eps, ladder_mask).  Weights are upcast exactly from their stored
-    values, one layer at a time unless ``cache_weights`` keeps them.
+    norm_eps, ladder_mask, dtype).  Weights are upcast exactly from their stored
+    values, one layer at a time unless ``cache_weights`` keeps them.  New K and V
+    rows are rounded to ``cfg.dtype`` before they enter the cache unless
+    ``kv_store_dtype`` is False.
     """
 
     def __init__(self, cfg, weights, dtype=np.float64, cache_weights: bool = False,
-                 ladder_mask=None):
+                 ladder_mask=None, kv_store_dtype: bool = True):
         self.cfg = cfg
+        self.kv_store_dtype = kv_store_dtype
         self.w = weights
         self.dtype = np.dtype(dtype)
         self.mask = tuple(int(v) for v in (cfg.ladder_mask if ladder_mask is None else ladder_mask))
@@ -228,6 +254,9 @@ class LadderOracle:
         pos = start_pos + np.arange(T)
         q = apply_rope(q, pos, cfg.rope_theta)
         k = apply_rope(k, pos, cfg.rope_theta)
+        if self.kv_store_dtype:
+            k = round_to_storage(k, cfg.dtype)
+            v = round_to_storage(v, cfg.dtype)
         prev_k, prev_v = cache["k"][li], cache["v"][li]
         if start_pos == 0 or prev_k is None:
             if start_pos != 0:

@@ -15,7 +15,7 @@ import torch.nn.functional as F
 
 import synth
 from oracle import (LadderOracle, apply_rope, gqa_attention, greedy_generate, module_input_index,
-                    rms_norm, rope_angles, silu, swiglu_mlp, teacher_forced, upcast)
+                    rms_norm, rope_angles, round_to_storage, silu, swiglu_mlp, teacher_forced, upcast)
 
 torch.set_default_dtype(torch.float64)
 
@@ -40,6 +40,47 @@ def test_upcast_bit_patterns():
     assert np.signbit(got[5])
     f = np.array([1.5, -3.25], dtype=np.float32)
     assert np.array_equal(upcast(f), f.astype(np.float64))
+
+
+def test_round_to_storage_bf16_halfway_cases():
+    e = 2.0 ** -8                                   # half a bf16 spacing in [1, 2)
+    x = np.array([1 + e, 1 + 3 * e, -(1 + e), 1 + e + 2.0 ** -30, 1 - e / 2, 0.0,
+                  2.0 ** -130 + 2.0 ** -134, 2.0 ** -130 + 3 * 2.0 ** -134, 3.0 * 2 ** 100])
+    want = np.array([1.0, 1 + 4 * e, -1.0, 1 + 2 * e, 1.0, 0.0,
+                     2.0 ** -130, 2.0 ** -130 + 2 * 2.0 ** -133, 3.0 * 2 ** 100])
+    got = round_to_storage(x, "bf16")
+    assert got.dtype == np.float64
+    assert np.array_equal(got, want)
+
+
+def test_round_to_storage_matches_bit_rounding_and_torch():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000))).astype(np.float32)
+    got = round_to_storage(x.astype(np.float64), "bf16")
+    assert np.array_equal(got, upcast(synth.f32_to_bf16_bits(x)))            # bit-pattern RNE
+    assert np.array_equal(got, torch.from_numpy(x).to(torch.bfloat16).double().numpy())
+    y = rng.standard_normal(1000)
+    assert np.array_equal(round_to_storage(y, "f32"), y.astype(np.float32).astype(np.float64))
+    with pytest.raises(ValueError):
+        round_to_storage(y, "fp8")
+
+
+def test_kv_cache_holds_values_of_the_storage_type():
+    """Layer 0's cached K/V are the unrounded ones rounded once; every cached value is
+    a bf16 value; attention reads the cache (rounding changes the output)."""
+    cfg = small_cfg(mask=(1, 0), dtype="bf16")
+    w = model(cfg, seed=12)
+    ids = synth.gen_ids(2, 7, cfg.vocab, seed=4)
+    ca, cb = None, None
+    oa, ob = LadderOracle(cfg, w), LadderOracle(cfg, w, kv_store_dtype=False)
+    ca, cb = oa.new_cache(), ob.new_cache()
+    ra, rb = oa.forward(ids, ca), ob.forward(ids, cb)
+    for key in ("k", "v"):
+        assert np.array_equal(ca[key][0], round_to_storage(cb[key][0], "bf16"))
+        for li in range(cfg.n_layers):
+            assert np.array_equal(ca[key][li], round_to_storage(ca[key][li], "bf16"))
+    assert not np.array_equal(ra.hidden, rb.hidden)
+    assert np.max(np.abs(ra.hidden - rb.hidden)) / np.max(np.abs(rb.hidden)) < 1e-2
 
 
 def test_rms_norm_matches_torch_and_scale_invariance():
@@ -165,7 +206,7 @@ def test_zero_ladder_equals_standard_transformer(dtype):
     cfg = small_cfg(mask=(0, 0, 0), dtype=dtype)
     w = model(cfg, seed=11)
     ids = synth.gen_ids(2, 9, cfg.vocab, seed=3)
-    r = LadderOracle(cfg, w).forward(ids)
+    r = LadderOracle(cfg, w, kv_store_dtype=False).forward(ids)
     hx, lg = torch_standard_transformer(cfg, w, ids)
     np.testing.assert_allclose(r.hidden, hx, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(r.logits, lg, rtol=1e-10, atol=1e-12)
@@ -175,7 +216,7 @@ def test_zero_ladder_equals_standard_transformer_tiny_shape():
     cfg = synth.CONFIGS["tiny"].with_mask((0, 0))
     w = synth.gen_weights(cfg, seed=0, threads=2)
     ids = synth.gen_ids(1, 16, cfg.vocab, seed=1)
-    r = LadderOracle(cfg, w).forward(ids)
+    r = LadderOracle(cfg, w, kv_store_dtype=False).forward(ids)
     hx, lg = torch_standard_transformer(cfg, w, ids)
     np.testing.assert_allclose(r.hidden, hx, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(r.logits, lg, rtol=1e-10, atol=1e-12)
