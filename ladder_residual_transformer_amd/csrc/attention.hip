@@ -2,9 +2,13 @@
 //
 // Decode (one new token per sequence): split-KV workgroups of attn_decode.hpp.
 //
-// Prefill (T tokens per sequence starting at start_pos): one workgroup per 32-query
-// tile of one head walks the causally visible 64-key tiles with the same online
-// softmax.
+// Prefill (T tokens per sequence starting at start_pos), causal, online softmax:
+//   bf16 models: matrix cores.  A workgroup owns 128 queries of one head, a wave 32 of
+//     them; S^T = K.Q^T and O^T += V^T.P^T run as v_mfma_f32_32x32x16_f16 with the
+//     stored bf16 K/V converted exactly to fp16 in LDS, and q and the probabilities p
+//     each carried as an fp16 pair (hi + lo, about 22 significant bits, two MFMAs per
+//     product); fp32 accumulation and fp32 softmax statistics.
+//   fp32 models: a VALU kernel, one workgroup per 32-query tile of one head.
 #include "attn_decode.hpp"
 #include "common.hpp"
 #include "kernels.h"
@@ -153,29 +157,241 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) 
   if (!qvalid) return;
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
   const size_t o = ((size_t)b * p.T + t) * qld + (size_t)h * HD + sub * DPT;
-  if (p.out_bf16) {
-    uint16_t* dst = (uint16_t*)p.out + o;
+  float* dst = p.out + o;
 #pragma unroll
-    for (int k = 0; k < DPT; ++k) dst[k] = f32_to_bf16(acc[k] * inv);
-  } else {
-    float* dst = (float*)p.out + o;
+  for (int k = 0; k < DPT; ++k) dst[k] = acc[k] * inv;
+}
+
+
+// ------------------------------------------------- prefill, bf16 models (MFMA)
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPqWave = 32;                  // queries per wave
+constexpr int kPqTile = 4 * kPqWave;         // queries per workgroup
+constexpr int kPkTile = 64;                  // keys per LDS tile
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// (a, b) -> fp16 pairs hi = fp16(v), lo = fp16(v - hi), two elements per word
+__device__ __forceinline__ void split_h2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 h = {(_Float16)a, (_Float16)b};
+  const h2 l = {(_Float16)(a - (float)h[0]), (_Float16)(b - (float)h[1])};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// 8 bf16 (one 16-byte chunk) -> 8 fp16, exact for |v| in [2^-17, 65504].
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& v) {
+  return make_uint4(pack_h2(bf16_lo(v.x), bf16_hi(v.x)), pack_h2(bf16_lo(v.y), bf16_hi(v.y)),
+                    pack_h2(bf16_lo(v.z), bf16_hi(v.z)), pack_h2(bf16_lo(v.w), bf16_hi(v.w)));
+}
+
+template <int HD>
+struct PrefillLds {
+  uint16_t ks[kPkTile][HD + 8];     // K tile, row = key (fp16)
+  uint16_t vt[HD][kPkTile + 8];     // V tile transposed, row = head dim (fp16)
+};
+
+// MFMA 32x32x16 operand/result layout (lane l): A row l%32, B column l%32, k-slots
+// 8*(l/32)..+8; C column l%32, rows 8*(r/4) + 4*(l/32) + r%4 for result r = 0..15.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillParams p) {
+  __shared__ __attribute__((aligned(16))) PrefillLds<HD> L;
+  constexpr int NST = HD / 16;               // 16-dim steps of S = K.Q^T
+  constexpr int NDB = HD / 32;               // 32-dim blocks of O^T
+  constexpr int CPR = HD / 8;                // 16-byte chunks per K/V row
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int n_qt = (p.T + kPqTile - 1) / kPqTile;
+  const int qt = n_qt - 1 - (int)blockIdx.x;   // longest causal ranges first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int G = p.nq / p.nkv, kvh = h / G;
+  const size_t kv_base = ((size_t)b * p.nkv + kvh) * p.max_seq * HD;
+  const uint16_t* kc = (const uint16_t*)p.k_cache + kv_base;
+  const uint16_t* vc = (const uint16_t*)p.v_cache + kv_base;
+  const size_t qld = (size_t)p.nq * HD;
+
+  // this lane's query (column of S^T); rows past T reuse the last valid token so every
+  // key they touch is written, and write nothing
+  const int t_raw = qt * kPqTile + w * kPqWave + col;
+  const int t_q = t_raw < p.T ? t_raw : p.T - 1;
+  const int qpos = p.start_pos + t_q;
+  const int wave_last = p.start_pos + min(p.T - 1, qt * kPqTile + w * kPqWave + kPqWave - 1);
+  const int n_keys = p.start_pos + min(p.T, (qt + 1) * kPqTile);   // keys of the workgroup
+  const int n_kt = (n_keys + kPkTile - 1) / kPkTile;
+
+  // Q^T operand as fp16 pairs: step s holds dims 16s + 8*half .. +8 of this lane's query
+  half8 qh[NST], ql[NST];
+  {
+    const float* qrow = p.q + ((size_t)b * p.T + t_q) * qld + (size_t)h * HD;
 #pragma unroll
-    for (int k = 0; k < DPT; ++k) dst[k] = acc[k] * inv;
+    for (int s = 0; s < NST; ++s) {
+      const float4 a = *(const float4*)(qrow + 16 * s + 8 * half);
+      const float4 c = *(const float4*)(qrow + 16 * s + 8 * half + 4);
+      uint4 hi, lo;
+      split_h2(a.x, a.y, hi.x, lo.x);
+      split_h2(a.z, a.w, hi.y, lo.y);
+      split_h2(c.x, c.y, hi.z, lo.z);
+      split_h2(c.z, c.w, hi.w, lo.w);
+      qh[s] = __builtin_bit_cast(half8, hi);
+      ql[s] = __builtin_bit_cast(half8, lo);
+    }
   }
+
+  // K/V tile loads: thread moves K chunks (row, c) and V chunk pairs (rows 2j, 2j+1)
+  constexpr int KCH = kPkTile * CPR / 256;          // K chunks per thread
+  constexpr int VPAIR = (kPkTile / 2) * CPR / 256;  // V row pairs per thread
+  uint4 kr[KCH], vr[VPAIR][2];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int e = tid + 256 * i, r = e / CPR, c = e % CPR;
+      const int kp = k0 + r;
+      kr[i] = kp < n_keys ? *(const uint4*)(kc + (size_t)kp * HD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < VPAIR; ++i) {
+      const int e = tid + 256 * i, j = e / CPR, c = e % CPR;
+      const int kp = k0 + 2 * j;
+      vr[i][0] = kp < n_keys ? *(const uint4*)(vc + (size_t)kp * HD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+      vr[i][1] = kp + 1 < n_keys ? *(const uint4*)(vc + (size_t)(kp + 1) * HD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int e = tid + 256 * i, r = e / CPR, c = e % CPR;
+      *(uint4*)&L.ks[r][c * 8] = bf16x8_to_f16x8(kr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VPAIR; ++i) {
+      const int e = tid + 256 * i, j = e / CPR, c = e % CPR;
+      const uint32_t* v0 = (const uint32_t*)&vr[i][0];
+      const uint32_t* v1 = (const uint32_t*)&vr[i][1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        *(uint32_t*)&L.vt[c * 8 + 2 * q][2 * j] = pack_h2(bf16_lo(v0[q]), bf16_lo(v1[q]));
+        *(uint32_t*)&L.vt[c * 8 + 2 * q + 1][2 * j] = pack_h2(bf16_hi(v0[q]), bf16_hi(v1[q]));
+      }
+    }
+  };
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+  const float c2 = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(hd)
+  float m_run = -INFINITY, l_run = 0.f;
+
+  load_tile(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * kPkTile;
+    __syncthreads();                 // previous tile fully consumed
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < n_kt) load_tile(k0 + kPkTile);
+    if (k0 > wave_last) continue;    // no visible key for this wave (uniform)
+
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const half8 a = *(const half8*)&L.ks[kb * 32 + col][16 * st + 8 * half];
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ql[st], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qh[st], s[kb], 0, 0, 0);
+      }
+    }
+    // causal mask, running max over this lane's 32 keys and its partner lane's 32
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kp = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (kp > qpos) s[kb][r] = -INFINITY;
+        mx = fmaxf(mx, s[kb][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);   // finite from tile 0 on: key 0 is visible to every query
+    const float alpha = exp2f((m_run - m_new) * c2);
+    m_run = m_new;
+    const float mc = m_new * c2;
+    float ls = 0.f;
+    uint32_t ph[2][8], pl[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float e0 = exp2f(fmaf(s[kb][r], c2, -mc));
+        const float e1 = exp2f(fmaf(s[kb][r + 1], c2, -mc));
+        ls += e0 + e1;
+        split_h2(e0, e1, ph[kb][r >> 1], pl[kb][r >> 1]);
+      }
+    l_run = l_run * alpha + ls;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    // O^T += V^T . P^T over 16-key steps; step t of block kb takes this lane's results
+    // 8*(t&1) .. +8, i.e. keys 16*t' + 4*half + {0..3, 8..11} with t' = 2*kb + (t&1)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kb = t >> 1, sub = t & 1;
+      const half8 pfh = __builtin_bit_cast(half8, make_uint4(ph[kb][4 * sub], ph[kb][4 * sub + 1],
+                                                             ph[kb][4 * sub + 2], ph[kb][4 * sub + 3]));
+      const half8 pfl = __builtin_bit_cast(half8, make_uint4(pl[kb][4 * sub], pl[kb][4 * sub + 1],
+                                                             pl[kb][4 * sub + 2], pl[kb][4 * sub + 3]));
+      const int kbase = 16 * t + 4 * half;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        const uint16_t* vrow = &L.vt[d * 32 + col][0];
+        const uint2 lo = *(const uint2*)(vrow + kbase);
+        const uint2 hi = *(const uint2*)(vrow + kbase + 8);
+        const half8 vf = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pfl, o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pfh, o[d], 0, 0, 0);
+      }
+    }
+  }
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (t_raw >= p.T) return;
+  const float inv = 1.0f / l_run;
+  float* dst = p.out + ((size_t)b * p.T + t_raw) * qld + (size_t)h * HD;
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dim = d * 32 + 8 * g + 4 * half;
+      *(float4*)(dst + dim) = make_float4(o[d][4 * g] * inv, o[d][4 * g + 1] * inv,
+                                          o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv);
+    }
 }
 
 hipError_t launch_attn_prefill(const AttnPrefillParams& p, hipStream_t s) {
-  if (p.nkv < 1 || p.nq % p.nkv != 0) return hipErrorInvalidValue;
-  dim3 grid((p.T + kQTile - 1) / kQTile, p.nq, p.B);
-  if (p.hd == 128) {
-    if (p.wdtype == W_BF16) hipLaunchKernelGGL((attn_prefill_kernel<uint16_t, 128>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((attn_prefill_kernel<float, 128>), grid, dim3(256), 0, s, p);
-  } else if (p.hd == 64) {
-    if (p.wdtype == W_BF16) hipLaunchKernelGGL((attn_prefill_kernel<uint16_t, 64>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((attn_prefill_kernel<float, 64>), grid, dim3(256), 0, s, p);
-  } else {
-    return hipErrorInvalidValue;
+  if (p.nkv < 1 || p.nq % p.nkv != 0 || p.T < 1) return hipErrorInvalidValue;
+  if (p.wdtype == W_BF16) {
+    dim3 grid((p.T + kPqTile - 1) / kPqTile, p.nq, p.B);
+    if (p.hd == 128) hipLaunchKernelGGL(attn_prefill_mfma_kernel<128>, grid, dim3(256), 0, s, p);
+    else if (p.hd == 64) hipLaunchKernelGGL(attn_prefill_mfma_kernel<64>, grid, dim3(256), 0, s, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
   }
+  dim3 grid((p.T + kQTile - 1) / kQTile, p.nq, p.B);
+  if (p.hd == 128) hipLaunchKernelGGL((attn_prefill_kernel<float, 128>), grid, dim3(256), 0, s, p);
+  else if (p.hd == 64) hipLaunchKernelGGL((attn_prefill_kernel<float, 64>), grid, dim3(256), 0, s, p);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

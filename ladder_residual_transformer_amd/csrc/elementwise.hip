@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const WT* table, int V, int 
 
 template <typename WT>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int ldx, const WT* gain, float eps, int H,
-                                                      void* out, int out_bf16) {
+                                                      float* out) {
   __shared__ float part[4];
   const int m = blockIdx.x, tid = threadIdx.x;
   const float* xr = x + (size_t)m * ldx;
@@ -29,9 +29,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int ldx, c
   const float tot = part[0] + part[1] + part[2] + part[3];
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
   for (int i = tid; i < H; i += 256) {
-    const float v = xr[i] * inv * load_w<WT>(gain + i);
-    if (out_bf16) ((uint16_t*)out)[(size_t)m * H + i] = f32_to_bf16(v);
-    else ((float*)out)[(size_t)m * H + i] = v;
+    out[(size_t)m * H + i] = xr[i] * inv * load_w<WT>(gain + i);
   }
 }
 
@@ -66,13 +64,11 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int T, i
   }
 }
 
-__global__ __launch_bounds__(256) void swiglu_kernel(const float* gu, size_t total, int F, void* a, int a_bf16) {
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* gu, size_t total, int F, float* a) {
   for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
     const size_t m = i / F, n = i % F;
     const float g = gu[m * 2 * F + 2 * n], u = gu[m * 2 * F + 2 * n + 1];
-    const float v = silu(g) * u;
-    if (a_bf16) ((uint16_t*)a)[i] = f32_to_bf16(v);
-    else ((float*)a)[i] = v;
+    a[i] = silu(g) * u;
   }
 }
 
@@ -99,11 +95,11 @@ hipError_t launch_embed(int wdtype, const void* table, int V, int H, const int* 
 }
 
 hipError_t launch_rmsnorm(int wdtype, const float* x, int ldx, const void* gain, float eps, int M, int H,
-                          void* out, int out_bf16, hipStream_t s) {
+                          float* out, hipStream_t s) {
   if (wdtype == W_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<uint16_t>, dim3(M), dim3(256), 0, s, x, ldx, (const uint16_t*)gain, eps, H, out, out_bf16);
+    hipLaunchKernelGGL(rmsnorm_kernel<uint16_t>, dim3(M), dim3(256), 0, s, x, ldx, (const uint16_t*)gain, eps, H, out);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, s, x, ldx, (const float*)gain, eps, H, out, out_bf16);
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, s, x, ldx, (const float*)gain, eps, H, out);
   return hipGetLastError();
 }
 
@@ -119,9 +115,9 @@ hipError_t launch_rope_kv(int wdtype, const float* qkv, int B, int T, int start_
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu(const float* gu, int M, int F, void* a, int a_bf16, hipStream_t s) {
+hipError_t launch_swiglu(const float* gu, int M, int F, float* a, hipStream_t s) {
   const size_t total = (size_t)M * F;
-  hipLaunchKernelGGL(swiglu_kernel, dim3(grid_for(total)), dim3(256), 0, s, gu, total, F, a, a_bf16);
+  hipLaunchKernelGGL(swiglu_kernel, dim3(grid_for(total)), dim3(256), 0, s, gu, total, F, a);
   return hipGetLastError();
 }
 

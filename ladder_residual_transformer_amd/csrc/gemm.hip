@@ -1,19 +1,28 @@
 // Prefill projections C[M][N] = (R) + A[M][K] . W^T with M = batch x tokens.
 //
-// bf16: a dense contraction, so it runs on the CDNA4 matrix cores
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulate).  A workgroup of 4 waves owns a
-// 128x128 tile of C (2x2 waves of 64x64, i.e. 4x4 MFMA tiles each); A and W tiles of
-// 128x64 are staged through double-buffered LDS with padded rows so the fragment
-// reads of a wave do not collide on banks; the next K step's global loads are in
-// flight while the current one is multiplied.
+// bf16 models: a dense contraction, so it runs on the CDNA4 matrix cores
+// (v_mfma_f32_16x16x32_f16, fp32 accumulation).  A arrives in fp32 and is split on
+// its way into LDS into a pair of fp16 values, hi = fp16(a) and lo = fp16(a - hi),
+// which together carry about 22 significant bits; the stored bf16 weights convert to
+// fp16 exactly (for |w| in [2^-17, 65504]).  Each product is then two MFMAs, hi.W and
+// lo.W, into one fp32 accumulator: a single fp16 or bf16 rounding of the activations
+// would perturb every module input by up to 2^-12 relative, which a deep stack of
+// modules carries into the final residual.
 //
-// fp32 (small correctness-only models): a plain LDS-tiled VALU GEMM.
+// Tiling: a workgroup of 4 waves owns a 128x128 tile of C (2x2 waves of 64x64, i.e.
+// 4x4 MFMA tiles each) and walks K in steps of 32 through double-buffered LDS with
+// padded rows; the next step's global loads are in flight during the current MFMAs.
+// Workgroups are dealt to the 8 XCDs round robin, so the tile list (M fastest) is cut
+// into 8 contiguous runs and run x goes to XCD x: workgroups that share a weight tile
+// run together on one XCD and read it once into that XCD's L2.
+//
+// fp32 models (small correctness-only models): a plain LDS-tiled VALU GEMM.
 #include "common.hpp"
 #include "kernels.h"
 
 namespace ladder {
 
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
 template <typename WT>
@@ -24,42 +33,79 @@ __device__ __forceinline__ const WT* gemm_row(const RowSrc& s, int r, int K) {
   return (const WT*)s.m[2] + (size_t)(r - s.n1) * K;
 }
 
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
+constexpr int BM = 128, BN = 128, BK = 32, LDK = BK + 8;
+constexpr int kXcds = 8;
 
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDK];
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// a -> (hi, lo) fp16 pairs of two elements each
+__device__ __forceinline__ void split_h2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 h = {(_Float16)a, (_Float16)b};
+  const h2 l = {(_Float16)(a - (float)h[0]), (_Float16)(b - (float)h[1])};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+__global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ah[2][BM][LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Al[2][BM][LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDK];
+  const int tile = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (tile >= n_tiles) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const uint16_t* A = (const uint16_t*)p.A;
+  const int m0 = (tile % n_tiles_m) * BM, n0 = (tile / n_tiles_m) * BN;
+  const float* A = (const float*)p.A;
 
-  // each thread moves 4 16-byte chunks of A and of W per K step
-  const uint16_t* arow[4];
-  const uint16_t* brow[4];
-  int srow[4], scol[4];
+  // per K step a thread moves 4 float4 of A (rows c/8, columns 4*(c%8)) and 2 16-byte
+  // chunks of W (rows c/4, columns 8*(c%4))
+  const float* arow[4];
+  const uint16_t* brow[2];
+  int ar[4], ac[4], br[2], bc[2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = tid + 256 * i;
-    srow[i] = c >> 3;
-    scol[i] = (c & 7) * 8;
-    const int m = m0 + srow[i], n = n0 + srow[i];
-    arow[i] = m < p.M ? A + (size_t)m * p.lda + scol[i] : nullptr;
-    brow[i] = n < p.N ? gemm_row<uint16_t>(p.rows, n, p.K) + scol[i] : nullptr;
+    ar[i] = c >> 3;
+    ac[i] = (c & 7) * 4;
+    const int m = m0 + ar[i];
+    arow[i] = m < p.M ? A + (size_t)m * p.lda + ac[i] : nullptr;
   }
-  uint4 ra[4], rb[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;
+    br[i] = c >> 2;
+    bc[i] = (c & 3) * 8;
+    const int n = n0 + br[i];
+    brow[i] = n < p.N ? gemm_row<uint16_t>(p.rows, n, p.K) + bc[i] : nullptr;
+  }
+  float4 ra[4];
+  uint4 rb[2];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = arow[i] ? *(const uint4*)(arow[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
-      rb[i] = brow[i] ? *(const uint4*)(brow[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int i = 0; i < 4; ++i) ra[i] = arow[i] ? *(const float4*)(arow[i] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) rb[i] = brow[i] ? *(const uint4*)(brow[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *(uint4*)&As[buf][srow[i]][scol[i]] = ra[i];
-      *(uint4*)&Bs[buf][srow[i]][scol[i]] = rb[i];
+      uint32_t h0, l0, h1, l1;
+      split_h2(ra[i].x, ra[i].y, h0, l0);
+      split_h2(ra[i].z, ra[i].w, h1, l1);
+      *(uint2*)&Ah[buf][ar[i]][ac[i]] = make_uint2(h0, h1);
+      *(uint2*)&Al[buf][ar[i]][ac[i]] = make_uint2(l0, l1);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 w = rb[i];
+      *(uint4*)&Bs[buf][br[i]][bc[i]] =
+          make_uint4(pack_h2(bf16_lo(w.x), bf16_hi(w.x)), pack_h2(bf16_lo(w.y), bf16_hi(w.y)),
+                     pack_h2(bf16_lo(w.z), bf16_hi(w.z)), pack_h2(bf16_lo(w.w), bf16_hi(w.w)));
     }
   };
 
@@ -73,23 +119,26 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
   gload(0);
   sstore(0);
   __syncthreads();
+  // 16x16x32 fragments: lane holds row (A) / column (W) lane%16, k = 8*(lane/16) .. +8
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) gload((kt + 1) * BK);
+    half8 ah[4], al[4], b[4];
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 32) {
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)&As[cur][wm * 64 + i * 16 + fr][ks + fk];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)&Bs[cur][wn * 64 + j * 16 + fr][ks + fk];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      ah[i] = *(const half8*)&Ah[cur][wm * 64 + i * 16 + fr][fk];
+      al[i] = *(const half8*)&Al[cur][wm * 64 + i * 16 + fr][fk];
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *(const half8*)&Bs[cur][wn * 64 + j * 16 + fr][fk];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], b[j], acc[i][j], 0, 0, 0);
+      }
     if (kt + 1 < nk) sstore(cur ^ 1);
     __syncthreads();
   }
@@ -164,9 +213,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.M < 1 || p.N < 1 || p.K < 1) return hipErrorInvalidValue;
   if (p.wdtype == W_BF16) {
-    if (p.K % BK != 0) return hipErrorInvalidValue;
-    dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM);
-    hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(256), 0, s, p);
+    if (p.K % BK != 0 || p.lda % 4 != 0) return hipErrorInvalidValue;
+    const int tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
+    const int tiles = tm * tn, per = (tiles + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL(gemm_f16x2_kernel, dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per);
   } else {
     dim3 grid((p.N + FT - 1) / FT, (p.M + FT - 1) / FT);
     hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, p);

@@ -96,14 +96,15 @@ struct AttnPrefillParams {
   const float* q;                      // [B*T][nq*hd] rotated, fp32
   const void* k_cache; const void* v_cache;
   int max_seq, nq, nkv, hd, B, T, start_pos;
-  void* out; int out_bf16;             // [B*T][nq*hd]
+  float* out;                          // [B*T][nq*hd]
 };
 hipError_t launch_attn_prefill(const AttnPrefillParams& p, hipStream_t s);
 
 // ----------------------------------------------------------------- GEMM (prefill)
 // C[M][N] (fp32, ldc) = (res ? res[M][N] : 0) + A[M][K] . B^T, B rows from RowSrc.
 struct GemmParams {
-  int wdtype;                          // W_BF16: A bf16 (lda), MFMA; W_F32: A fp32, VALU
+  int wdtype;                          // W_BF16: MFMA on fp16 pairs of A, W bf16 -> fp16; W_F32: VALU
+  // A: fp32 [M][lda] (lda a multiple of 4 for bf16 models)
   const void* A; int lda;
   RowSrc rows;
   int M, N, K;
@@ -114,15 +115,15 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------ elementwise
 hipError_t launch_embed(int wdtype, const void* table, int V, int H, const int* ids, int M, float* x, hipStream_t s);
-// out[m][:] = RMSNorm(x[m*ldx + :]) * gain, as bf16 (out_bf16) or fp32
+// out[m][:] = RMSNorm(x[m*ldx + :]) * gain (fp32)
 hipError_t launch_rmsnorm(int wdtype, const float* x, int ldx, const void* gain, float eps, int M, int H,
-                          void* out, int out_bf16, hipStream_t s);
+                          float* out, hipStream_t s);
 // qkv [B*T][q_rows + 2 kv_rows] -> q (rotated, fp32) and KV cache rows start_pos..start_pos+T-1
 hipError_t launch_rope_kv(int wdtype, const float* qkv, int B, int T, int start_pos, int nq, int nkv, int hd,
                           const float* rope_cos, const float* rope_sin, float* q_out,
                           void* k_cache, void* v_cache, int max_seq, hipStream_t s);
-// gu [M][2F] interleaved (gate, up) -> a [M][F] as bf16 or fp32
-hipError_t launch_swiglu(const float* gu, int M, int F, void* a, int a_bf16, hipStream_t s);
+// gu [M][2F] interleaved (gate, up) -> a [M][F] (fp32)
+hipError_t launch_swiglu(const float* gu, int M, int F, float* a, hipStream_t s);
 hipError_t launch_add(const float* x, const float* y, float* out, size_t n, hipStream_t s);
 hipError_t launch_decode_prologue(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, hipStream_t s);
 

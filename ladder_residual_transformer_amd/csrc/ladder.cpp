@@ -47,13 +47,13 @@ struct StreamScratch {
   float* gpart = nullptr;
   float* gpart_sq = nullptr;
   int* gcnt = nullptr;
-  // prefill
-  void* u = nullptr;
+  // prefill (module inputs of the projections stay fp32; the GEMM splits them)
+  float* u = nullptr;
   float* qkv = nullptr;
   float* qr = nullptr;
-  void* ob = nullptr;
+  float* ob = nullptr;
   float* gu = nullptr;
-  void* ab = nullptr;
+  float* ab = nullptr;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -202,7 +202,6 @@ void carve(ladder_ctx* c, Carver& cv) {
   c->best_val = cv.take<float>(nbest);
   c->best_idx = cv.take<int>(nbest);
   c->arg_cnt = cv.take<int>(1);
-  const size_t ue = c->wdt == W_BF16 ? 2 : 4;
   for (int s = 0; s < 2; ++s) {
     StreamScratch& sc = c->sc[s];
     sc.q = cv.take<float>((size_t)B * c->qrows);
@@ -213,12 +212,12 @@ void carve(ladder_ctx* c, Carver& cv) {
     sc.gpart = cv.take<float>(need.part_floats);
     sc.gpart_sq = cv.take<float>(need.part_sq_floats);
     sc.gcnt = cv.take<int>(need.counters);
-    sc.u = cv.take<char>((size_t)c->mmax * H * ue);
+    sc.u = cv.take<float>((size_t)c->mmax * H);
     sc.qkv = cv.take<float>((size_t)c->mmax * qkv);
     sc.qr = cv.take<float>((size_t)c->mmax * c->qrows);
-    sc.ob = cv.take<char>((size_t)c->mmax * c->qrows * ue);
+    sc.ob = cv.take<float>((size_t)c->mmax * c->qrows);
     sc.gu = cv.take<float>((size_t)c->mmax * 2 * F);
-    sc.ab = cv.take<char>((size_t)c->mmax * F * ue);
+    sc.ab = cv.take<float>((size_t)c->mmax * F);
   }
 }
 
@@ -439,7 +438,6 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
   const int l = m / 2, M = B * T;
   const ladder_layer_weights& L = ctx->layers[l];
   StreamScratch& sc = module_scratch(ctx, m);
-  const int bf = ctx->wdt == W_BF16;
   GemmParams gp{};
   gp.wdtype = ctx->wdt;
   gp.M = M;
@@ -447,7 +445,7 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
   int proj_k;
   const void* proj_w;
   if (m % 2 == 0) {
-    HIPCHK(launch_rmsnorm(ctx->wdt, xin, g.hidden, L.attn_norm, g.norm_eps, M, g.hidden, sc.u, bf, s));
+    HIPCHK(launch_rmsnorm(ctx->wdt, xin, g.hidden, L.attn_norm, g.norm_eps, M, g.hidden, sc.u, s));
     const int nqkv = ctx->qrows + 2 * ctx->kvrows;
     gp.A = sc.u;
     gp.lda = g.hidden;
@@ -472,13 +470,12 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
     ap.T = T;
     ap.start_pos = start_pos;
     ap.out = sc.ob;
-    ap.out_bf16 = bf;
     HIPCHK(launch_attn_prefill(ap, s));
     proj_in = sc.ob;
     proj_k = ctx->qrows;
     proj_w = L.wo;
   } else {
-    HIPCHK(launch_rmsnorm(ctx->wdt, xin, g.hidden, L.mlp_norm, g.norm_eps, M, g.hidden, sc.u, bf, s));
+    HIPCHK(launch_rmsnorm(ctx->wdt, xin, g.hidden, L.mlp_norm, g.norm_eps, M, g.hidden, sc.u, s));
     gp.A = sc.u;
     gp.lda = g.hidden;
     gp.rows = RowSrc{{L.w_gate, L.w_up, nullptr}, 0, 0, 1};
@@ -487,7 +484,7 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
     gp.C = sc.gu;
     gp.ldc = 2 * g.ffn;
     HIPCHK(launch_gemm(gp, s));
-    HIPCHK(launch_swiglu(sc.gu, M, g.ffn, sc.ab, bf, s));
+    HIPCHK(launch_swiglu(sc.gu, M, g.ffn, sc.ab, s));
     proj_in = sc.ab;
     proj_k = g.ffn;
     proj_w = L.w_down;

@@ -27,6 +27,11 @@ def rel_err(got, ref) -> float:
     return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
 
 
+def step_rel_err(got, ref) -> float:
+    """The parity metric per step, worst step: arrays [B, steps, X], one step = all B rows."""
+    return max(rel_err(got[:, k], ref[:, k]) for k in range(ref.shape[1]))
+
+
 def small_config(name, base: synth.ModelConfig, **changes) -> synth.ModelConfig:
     return dataclasses.replace(base, name=name, **changes)
 

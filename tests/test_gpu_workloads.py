@@ -1,0 +1,134 @@
+"""HIP path vs the oracle at the workloads' real widths (and full depth where the oracle
+finishes in well under a minute), through the C ABI in the launch configuration the
+benchmark times (fused ladder schedule, HIP graphs).  The metric is max|d|/max|ref| per
+step (all batch rows of one step), worst step.
+
+Every expected value comes from oracle/ on the same seeded synth inputs; the oracle
+runs in float32 for these bf16 models (its float32 mode is pinned to float64 by the
+CPU tests) and upcasts each layer's stored weights exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import (TOL, check_against_oracle, gpu_free_running, gpu_teacher_forced, log, make_model,
+                         step_rel_err)
+from oracle import LadderOracle, greedy_generate, teacher_forced
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _free(model):
+    model.free()
+    torch.cuda.empty_cache()
+
+
+def test_1b_full_depth_greedy():
+    """1B-shape ladder model, all 16 layers: teacher-forced logits/hidden within 1e-2 and
+    free-running greedy decoding identical to the oracle's up to its first near-tie."""
+    wl = synth.WORKLOADS["1b"]
+    cfg = wl.model
+    w = synth.gen_weights(cfg, seed=0)
+    prompt = synth.gen_ids(1, 128, cfg.vocab, seed=1)
+    n_dec = 16
+    log("1b: oracle greedy (float32), prompt 128, decode", n_dec)
+    ref = greedy_generate(LadderOracle(cfg, w, dtype=np.float32, cache_weights=True), prompt, n_dec)
+    model = make_model(cfg, w, 1, 256)
+    gl, gh, gt = gpu_teacher_forced(model, prompt, ref["tokens"][:, :-1])
+    el, _ = check_against_oracle(cfg, gl, gh, gt, ref, TOL["bf16"], "1b teacher-forced")
+    free = gpu_free_running(model, prompt, n_dec)
+    abs_err = np.max(np.abs(gl - ref["logits"]))
+    for k in range(n_dec + 1):
+        if free[0, k] != ref["tokens"][0, k]:
+            assert ref["margins"][0, k] <= 2 * abs_err, f"free-running token {k} differs outside a near-tie"
+            log(f"1b free-running: near-tie at step {k}, compared up to it")
+            break
+    _free(model)
+
+
+def test_1b_batch8_split_k():
+    """Batch 8 takes the K-sliced GEMV with the 8192-wide down projection split over K."""
+    cfg = synth.CONFIGS["1b"]
+    cfg4 = synth.scaled_config(cfg, 4)
+    w = synth.gen_weights(cfg4, seed=2)
+    prompt = synth.gen_ids(8, 32, cfg.vocab, seed=3)
+    cont = synth.gen_ids(8, 4, cfg.vocab, seed=3, stream=1)
+    ref = teacher_forced(LadderOracle(cfg4, w, dtype=np.float32), prompt, cont)
+    model = make_model(cfg4, w, 8, 64)
+    gl, gh, _ = gpu_teacher_forced(model, prompt, cont)
+    el = step_rel_err(gl, ref.logits[:, 31:])
+    eh = step_rel_err(gh, ref.hidden[:, 31:])
+    log(f"1b x4 layers batch 8: rel err logits {el:.3g} hidden {eh:.3g}")
+    assert el <= TOL["bf16"] and eh <= TOL["bf16"]
+    _free(model)
+
+
+@pytest.mark.parametrize("B, T, n_dec", [(1, 64, 8), (16, 16, 3)])
+def test_8b_hybrid_widths(B, T, n_dec):
+    """Llama-3.1-8B widths with the hybrid mask across the standard->ladder boundary
+    (layers 0-1 standard, 2-3 ladder); batch 16 uses the K-sliced kernels."""
+    base = synth.CONFIGS["8b_hybrid"]
+    cfg = synth.ModelConfig("8b_hybrid_4l", 4, base.hidden, base.n_q_heads, base.n_kv_heads, base.head_dim,
+                            base.ffn, base.vocab, base.rope_theta, "bf16", (0, 0, 1, 1))
+    w = synth.gen_weights(cfg, seed=4)
+    prompt = synth.gen_ids(B, T, cfg.vocab, seed=5)
+    cont = synth.gen_ids(B, n_dec, cfg.vocab, seed=5, stream=1)
+    ref = teacher_forced(LadderOracle(cfg, w, dtype=np.float32), prompt, cont)
+    model = make_model(cfg, w, B, T + n_dec + 4)
+    gl, gh, gt = gpu_teacher_forced(model, prompt, cont)
+    el = step_rel_err(gl, ref.logits[:, T - 1:])
+    eh = step_rel_err(gh, ref.hidden[:, T - 1:])
+    log(f"8b widths B={B}: rel err logits {el:.3g} hidden {eh:.3g}")
+    assert el <= TOL["bf16"] and eh <= TOL["bf16"]
+    _free(model)
+
+
+@pytest.mark.timeout(900)
+def test_70b_tp8_shard_full_depth_bench_configuration():
+    """The benchmark's workload: 70B-shape TP=8 one-rank shard, all 80 ladder layers,
+    batch 1, the 1024-token prompt, then three decode steps, in the fused schedule with
+    HIP graphs.  The oracle makes one float32 pass over prompt + continuation."""
+    wl = synth.WORKLOADS["70b_tp8_shard"]
+    cfg = wl.model
+    log("70b shard: generating 17.6 GB of weights")
+    w = synth.gen_weights(cfg, seed=0)
+    prompt = synth.gen_ids(1, wl.prompt_len, cfg.vocab, seed=1)
+    cont = synth.gen_ids(1, 3, cfg.vocab, seed=1, stream=1)
+    model = make_model(cfg, w, 1, wl.max_seq)
+    log("70b shard: GPU prefill + 3 decode steps")
+    gl, gh, gt = gpu_teacher_forced(model, prompt, cont)
+    _free(model)
+    log("70b shard: oracle pass over 1027 positions")
+    ref = teacher_forced(LadderOracle(cfg, w, dtype=np.float32), prompt, cont, logits="all")
+    rl = ref.logits[:, wl.prompt_len - 1:]
+    rh = ref.hidden[:, wl.prompt_len - 1:]
+    el, eh = step_rel_err(gl, rl), step_rel_err(gh, rh)
+    log(f"70b shard full depth: rel err logits {el:.3g} hidden {eh:.3g}")
+    assert el <= TOL["bf16"] and eh <= TOL["bf16"]
+    abs_err = np.max(np.abs(gl - rl))
+    srt = np.sort(rl, axis=-1)
+    margins = srt[..., -1] - srt[..., -2]
+    top = np.argmax(rl, axis=-1)
+    for k in range(rl.shape[1]):
+        if gt[0, k] != top[0, k]:
+            assert margins[0, k] <= 2 * abs_err, f"argmax differs at step {k} outside a near-tie"
+
+
+def test_405b_tp16_shard_widths():
+    """405B-shape TP=16 shard widths (hidden 16384: the staged input exceeds 64 KB of
+    LDS), four ladder layers; batch 1 and 16."""
+    base = synth.CONFIGS["405b_tp16_shard"]
+    cfg = synth.scaled_config(base, 4)
+    w = synth.gen_weights(cfg, seed=6)
+    for B, T, n_dec in ((1, 48, 4), (16, 12, 2)):
+        prompt = synth.gen_ids(B, T, cfg.vocab, seed=7)
+        cont = synth.gen_ids(B, n_dec, cfg.vocab, seed=7, stream=1)
+        ref = teacher_forced(LadderOracle(cfg, w, dtype=np.float32), prompt, cont)
+        model = make_model(cfg, w, B, T + n_dec + 4)
+        gl, gh, _ = gpu_teacher_forced(model, prompt, cont)
+        el = step_rel_err(gl, ref.logits[:, T - 1:])
+        eh = step_rel_err(gh, ref.hidden[:, T - 1:])
+        log(f"405b widths B={B}: rel err logits {el:.3g} hidden {eh:.3g}")
+        assert el <= TOL["bf16"] and eh <= TOL["bf16"]
+        _free(model)
