@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-layers", type=int, default=16)
     ap.add_argument("--cpu-steps", type=int, default=6)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="only run a plain device-to-device copy of MB megabytes 5 times (the reference "
+                         "for scaling HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs one GPU's share of the model (one tensor-parallel rank's shard); "
@@ -131,6 +134,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe * 1000 * 1000 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 5}))
+        return
 
     import synth
     from ladder_residual_transformer_amd import DeviceWeights, LadderModel, load
@@ -197,18 +210,41 @@ def main():
     log(f"[bench] decode {args.steps} steps: {dt * 1e3 / args.steps:.3f} ms/step (events {gpu_ms / args.steps:.3f}), "
         f"{tok_s:.1f} tok/s, {total_bytes / args.steps / 1e9:.2f} GB/step, {100 * hbm_frac:.1f}% of HBM peak")
 
-    # ---- dominant kernel: the fused [QKV | gate/up] launch (~65% of the bytes), timed
-    # on the stream it runs on
-    ku = model.time_kernels(B, reps=3)
+    # ---- the dominant kernel, measured live: the same K decode steps again, each fused
+    # [QKV | gate/up] launch (~80% of the step's bytes) with a pair of HIP events on the
+    # stream it runs on, taken from its dispatch's own begin/end timestamps (traced steps
+    # are launched eagerly)
+    model.trace_kernel("qkv_gateup")
+    bufs[0].copy_(first)
+    model.decode_step(bufs[0], P, out=(None, bufs[1], None))
+    torch.cuda.synchronize()
+    cur = bufs[0]
+    tot_us, n_launch = 0.0, 0
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        model.decode_step(cur, P + k, out=(None, bufs[(k + 1) % 2], None))
+        cur = bufs[(k + 1) % 2]
+        us, n = model.trace_result()                # waits for the step
+        tot_us += us * n
+        n_launch += n
+    torch.cuda.synchronize()
+    dt_traced = time.perf_counter() - t0
+    us_launch = tot_us / n_launch
+    model.trace_kernel(None)
     gu_bytes = qkv_gateup_bytes(cfg, B)
-    achieved = gu_bytes / (ku["qkv_gateup"] * 1e-6) / 1e9
+    achieved = gu_bytes / (us_launch * 1e-6) / 1e9
+    log(f"[bench] traced decode: {dt_traced * 1e3 / args.steps:.3f} ms/step (read out per step); fused [QKV | gate/up] "
+        f"launch {us_launch:.2f} us mean over {n_launch} launches, {achieved:.0f} GB/s")
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_sha") == kernel_sha() and tr.get("batch") == B and tr.get("workload") == cfg.name:
             traffic = tr.get("bytes_per_launch")
-    log(f"[bench] kernel us/launch: " + ", ".join(f"{k} {v:.2f}" for k, v in ku.items()))
+
+    # every kernel kind replayed in isolation (diagnostic)
+    ku = model.time_kernels(B, reps=3)
+    log(f"[bench] kernel us/launch in isolation: " + ", ".join(f"{k} {v:.2f}" for k, v in ku.items()))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -230,8 +266,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "fused ladder launch [RMSNorm+QKV+RoPE+KV | RMSNorm+gate/up+SwiGLU]",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": traffic,
-                     "bytes_per_launch": gu_bytes, "us_per_launch": round(ku["qkv_gateup"], 3)},
-        "kernels_us": {k: round(v, 3) for k, v in ku.items()},
+                     "bytes_per_launch": gu_bytes, "us_per_launch": round(us_launch, 3),
+                     "launches_timed": n_launch, "traced_ms_per_step": round(dt_traced * 1e3 / args.steps, 4)},
+        "kernels_us_isolated": {k: round(v, 3) for k, v in ku.items()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -150,7 +150,7 @@ ladder_status ladder_workspace_bytes(const ladder_ctx* ctx, size_t* out);
 /* Wait for all work of the context (its stream and internal streams). */
 ladder_status ladder_sync(ladder_ctx* ctx);
 
-/* Decode kernel kinds, for ladder_time_kernels. */
+/* Decode kernel kinds, for ladder_time_kernels and ladder_trace_kernel. */
 #define LADDER_KERNEL_QKV 0      /* RMSNorm + [Wq;Wk;Wv] GEMV + RoPE + KV append */
 #define LADDER_KERNEL_ATTN 1     /* split-KV GQA decode attention (+ chunk merge) */
 #define LADDER_KERNEL_OPROJ 2    /* Wo GEMV + fused residual add */
@@ -170,6 +170,20 @@ ladder_status ladder_sync(ladder_ctx* ctx);
  * current buffers and the position of the last decode step, whose KV row it
  * overwrites; requires at least one filled position.  Blocks until done. */
 ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, float* us_out);
+
+/* Measurement aid.  kind in [0, LADDER_N_KERNELS): from the next decode step on, every
+ * launch of that kernel kind gets a pair of HIP events on the stream it runs on, taken
+ * from the dispatch's own begin and end timestamps (hipExtLaunchKernelGGL; for a kind
+ * made of two kernels, the first one's begin and the last one's end).  While a kind is
+ * traced, decode steps are launched eagerly: the same kernels with the same arguments,
+ * without a HIP graph.  kind = -1 turns it off.  Creates 2 (n_layers + 1) events on
+ * first use.  LADDER_ERR_ARG for another kind. */
+ladder_status ladder_trace_kernel(ladder_ctx* ctx, int32_t kind);
+
+/* Mean duration in microseconds (*mean_us) and number (*count) of the traced launches
+ * of the most recently enqueued decode step; waits for the context's stream.
+ * LADDER_ERR_STATE if tracing is off or no decode step ran since it was turned on. */
+ladder_status ladder_trace_result(ladder_ctx* ctx, float* mean_us, int32_t* count);
 
 /* Release the context (NULL is a no-op).  Does not free caller buffers. */
 void ladder_free(ladder_ctx* ctx);

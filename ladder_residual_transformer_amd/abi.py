@@ -33,7 +33,7 @@ LADDER_SCHED_FUSED = 3
 
 EXPORTED = ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_filled",
             "ladder_workspace_bytes", "ladder_sync", "ladder_free", "ladder_status_string", "ladder_last_error",
-            "ladder_time_kernels")
+            "ladder_time_kernels", "ladder_trace_kernel", "ladder_trace_result")
 
 KERNEL_KINDS = ("qkv", "attn", "oproj", "gateup", "down", "lmhead", "qkv_gateup", "attn_down", "oproj_add2")
 
@@ -86,6 +86,8 @@ def load(path: str = LIB_PATH):
     lib.ladder_workspace_bytes.argtypes = [c_void_p, POINTER(c_size_t)]
     lib.ladder_sync.argtypes = [c_void_p]
     lib.ladder_time_kernels.argtypes = [c_void_p, c_int32, c_int32, POINTER(c_float)]
+    lib.ladder_trace_kernel.argtypes = [c_void_p, c_int32]
+    lib.ladder_trace_result.argtypes = [c_void_p, POINTER(c_float), POINTER(c_int32)]
     lib.ladder_free.argtypes = [c_void_p]
     lib.ladder_free.restype = None
     lib.ladder_status_string.argtypes = [c_int32]
@@ -93,7 +95,8 @@ def load(path: str = LIB_PATH):
     lib.ladder_last_error.argtypes = [c_void_p]
     lib.ladder_last_error.restype = ctypes.c_char_p
     for name in ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_filled",
-                 "ladder_workspace_bytes", "ladder_sync", "ladder_time_kernels"):
+                 "ladder_workspace_bytes", "ladder_sync", "ladder_time_kernels", "ladder_trace_kernel",
+                 "ladder_trace_result"):
         getattr(lib, name).restype = c_int32
     _lib = lib
     return lib
@@ -157,6 +160,18 @@ def ladder_time_kernels(ctx: int, B: int, reps: int = 3) -> dict:
     out = (c_float * len(KERNEL_KINDS))()
     _check(ctx, load().ladder_time_kernels(c_void_p(ctx), B, reps, out), "ladder_time_kernels")
     return {k: float(v) for k, v in zip(KERNEL_KINDS, out)}
+
+
+def ladder_trace_kernel(ctx: int, kind: int) -> None:
+    """Bracket every decode launch of kernel kind ``kind`` (-1: none) with HIP events."""
+    _check(ctx, load().ladder_trace_kernel(c_void_p(ctx), kind), "ladder_trace_kernel")
+
+
+def ladder_trace_result(ctx: int):
+    """(mean microseconds, launches) of the traced kind in the most recent decode step."""
+    us, n = c_float(), c_int32()
+    _check(ctx, load().ladder_trace_result(c_void_p(ctx), ctypes.byref(us), ctypes.byref(n)), "ladder_trace_result")
+    return float(us.value), int(n.value)
 
 
 def ladder_free(ctx: int) -> None:

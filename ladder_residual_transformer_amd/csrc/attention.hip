@@ -54,9 +54,9 @@ template <typename WT, int HD>
 hipError_t attn_decode_go(const AttnDecodeParams& p, hipStream_t s) {
   dim3 grid(p.n_split * p.nkv * p.B);
   switch (attn_hpw(p.nq / p.nkv)) {
-    case 1: hipLaunchKernelGGL((attn_decode_kernel<WT, HD, 1>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((attn_decode_kernel<WT, HD, 2>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((attn_decode_kernel<WT, HD, 4>), grid, dim3(256), 0, s, p); break;
+    case 1: launch_timed(attn_decode_kernel<WT, HD, 1>, grid, dim3(256), 0, s, p); break;
+    case 2: launch_timed(attn_decode_kernel<WT, HD, 2>, grid, dim3(256), 0, s, p); break;
+    default: launch_timed(attn_decode_kernel<WT, HD, 4>, grid, dim3(256), 0, s, p); break;
   }
   return hipGetLastError();
 }

@@ -1,5 +1,6 @@
 // Device-side helpers shared by the gfx950 kernels of the ladder decode/prefill path.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,5 +56,26 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Launch timing (measurement aid).  While armed, the decode-path launches go through
+// hipExtLaunchKernelGGL: the first one records `start` when its dispatch begins, every
+// one records `stop` when its dispatch ends, so the pair spans exactly the kernels
+// launched between arming and disarming.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool armed = false;
+};
+LaunchEvents& launch_events();   // this host thread's
+
+template <typename F, typename... Args>
+inline void launch_timed(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, Args... args) {
+  LaunchEvents& le = launch_events();
+  if (le.armed) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, le.start, le.stop, 0, args...);
+    le.start = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  }
+}
 
 }  // namespace ladder

@@ -4,6 +4,20 @@
 
 namespace ladder {
 
+LaunchEvents& launch_events() {
+  static thread_local LaunchEvents le;
+  return le;
+}
+
+void launch_events_arm(hipEvent_t start, hipEvent_t stop) {
+  LaunchEvents& le = launch_events();
+  le.start = start;
+  le.stop = stop;
+  le.armed = true;
+}
+
+void launch_events_disarm() { launch_events() = LaunchEvents{}; }
+
 // x[m][:] = E[ids[m]][:] in fp32.  Ids outside [0, V) are clamped so a bad id cannot
 // read outside the table.
 template <typename WT>

@@ -367,7 +367,7 @@ Pick pick(int wdtype, int N, int K, int B) {
 template <typename WT, int BT, int NT, int VPT>
 hipError_t go(const GemvParams& p, const Pick& k, hipStream_t s) {
   constexpr int ROWS = rows_for(VPT, BT);
-  hipLaunchKernelGGL((gemv_kernel<WT, BT, NT, VPT, ROWS>), dim3(k.gx, k.S), dim3(NT), 0, s, p);
+  launch_timed(gemv_kernel<WT, BT, NT, VPT, ROWS>, dim3(k.gx, k.S), dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 

@@ -103,7 +103,8 @@ __device__ __forceinline__ void rw_epilogue(const GemvParams& p, int pair, int b
   }
 }
 
-template <typename WT, int BT, int VPL, int HDA, int HPW>
+// NP: number of GEMV problems of the launch (1 or 2).
+template <typename WT, int BT, int VPL, int HDA, int HPW, int NP>
 __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   if constexpr (HDA != 0) {
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int blk = (int)blockIdx.x - mp.n_attn;
-  const int pi = (mp.np > 1 && blk >= mp.blk_begin[1]) ? 1 : 0;
+  const int pi = (NP > 1 && blk >= mp.blk_begin[1]) ? 1 : 0;
   const GemvParams& p = mp.prob[pi];
   const int lb = blk - mp.blk_begin[pi];
   const int nb = mp.blk_begin[pi + 1] - mp.blk_begin[pi];
@@ -371,9 +372,9 @@ int rw_vpl(int nvec) {
   return 4;
 }
 
-template <typename WT, int BT, int VPL, int HDA, int HPW>
+template <typename WT, int BT, int VPL, int HDA, int HPW, int NP>
 hipError_t rw_go(MultiGemvParams& mp, size_t lds, hipStream_t s) {
-  auto fn = gemv_rw_kernel<WT, BT, VPL, HDA, HPW>;
+  auto fn = gemv_rw_kernel<WT, BT, VPL, HDA, HPW, NP>;
   // resident workgroups of this instance at this LDS size (queried once per instance
   // and size): the GEMV workgroups of one launch are sized to fill the device once
   static size_t cached_lds = 0;
@@ -401,7 +402,7 @@ hipError_t rw_go(MultiGemvParams& mp, size_t lds, hipStream_t s) {
   if (target > kRwTargetBlocks) target = kRwTargetBlocks;
   rw_split_blocks(mp, target);
   const int grid = mp.n_attn + mp.blk_begin[mp.np];
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, s, mp);
+  launch_timed(fn, dim3(grid), dim3(256), (uint32_t)lds, s, mp);
   return hipGetLastError();
 }
 
@@ -411,19 +412,21 @@ template <typename WT, int BT, int VPL>
 hipError_t rw_hda(MultiGemvParams& mp, int hda, size_t lds, hipStream_t s) {
   if constexpr (VPL == 4) {
     const int hpw = hda ? attn_hpw(mp.attn.nq / mp.attn.nkv) : 0;
+    if (hda != 0 && mp.np != 1) return hipErrorInvalidValue;   // attention rides with one problem
     if (hda == 128) {
-      if (hpw == 1) return rw_go<WT, BT, VPL, 128, 1>(mp, lds, s);
-      if (hpw == 2) return rw_go<WT, BT, VPL, 128, 2>(mp, lds, s);
-      return rw_go<WT, BT, VPL, 128, 4>(mp, lds, s);
+      if (hpw == 1) return rw_go<WT, BT, VPL, 128, 1, 1>(mp, lds, s);
+      if (hpw == 2) return rw_go<WT, BT, VPL, 128, 2, 1>(mp, lds, s);
+      return rw_go<WT, BT, VPL, 128, 4, 1>(mp, lds, s);
     }
     if (hda == 64) {
-      if (hpw == 1) return rw_go<WT, BT, VPL, 64, 1>(mp, lds, s);
-      if (hpw == 2) return rw_go<WT, BT, VPL, 64, 2>(mp, lds, s);
-      return rw_go<WT, BT, VPL, 64, 4>(mp, lds, s);
+      if (hpw == 1) return rw_go<WT, BT, VPL, 64, 1, 1>(mp, lds, s);
+      if (hpw == 2) return rw_go<WT, BT, VPL, 64, 2, 1>(mp, lds, s);
+      return rw_go<WT, BT, VPL, 64, 4, 1>(mp, lds, s);
     }
   }
   if (hda != 0) return hipErrorInvalidValue;
-  return rw_go<WT, BT, VPL, 0, 0>(mp, lds, s);
+  if (mp.np == 2) return rw_go<WT, BT, VPL, 0, 0, 2>(mp, lds, s);
+  return rw_go<WT, BT, VPL, 0, 0, 1>(mp, lds, s);
 }
 
 template <typename WT, int BT>
@@ -494,7 +497,7 @@ hipError_t launch_gemv_multi(const GemvParams* probs, int np, const AttnDecodePa
 
 hipError_t launch_argmax_finalize(const float* best_val, const int* best_idx, int n, int BT, int B, int* next,
                                   hipStream_t s) {
-  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(256), 0, s, best_val, best_idx, n, BT, B, next);
+  launch_timed(argmax_finalize_kernel, dim3(1), dim3(256), 0, s, best_val, best_idx, n, BT, B, next);
   return hipGetLastError();
 }
 

@@ -113,6 +113,12 @@ struct GemmParams {
 };
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
+// ------------------------------------------------------------ launch timing
+// Arm: the decode-path kernels launched until disarm record `start` (first dispatch
+// begins) and `stop` (each dispatch ends) through hipExtLaunchKernelGGL.
+void launch_events_arm(hipEvent_t start, hipEvent_t stop);
+void launch_events_disarm();
+
 // ------------------------------------------------------------------ elementwise
 hipError_t launch_embed(int wdtype, const void* table, int V, int H, const int* ids, int M, float* x, hipStream_t s);
 // out[m][:] = RMSNorm(x[m*ldx + :]) * gain (fp32)

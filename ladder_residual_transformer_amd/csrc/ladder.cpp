@@ -112,6 +112,10 @@ struct ladder_ctx {
 
   int sched = LADDER_SCHED_FUSED;
   int use_graph = 1;
+  int trace_kind = -1;               // kernel kind timed with events during decode (-1: none)
+  std::vector<hipEvent_t> trace_ev;  // start/end pairs, one pair per traced launch
+  int trace_n = 0;                   // pairs recorded by the step being enqueued
+  int trace_count = 0;               // pairs a decode step records
   std::map<int, hipGraphExec_t> graphs;
   int filled = 0;
   bool broken = false;
@@ -220,6 +224,28 @@ void carve(ladder_ctx* c, Carver& cv) {
     sc.ab = cv.take<float>((size_t)c->mmax * F);
   }
 }
+
+// Event pair spanning the dispatches of the launches of kernel kind `kind` (traced
+// steps are eager; the events take the dispatches' own begin/end timestamps).
+ladder_status trace_mark(ladder_ctx* ctx, int kind, hipStream_t s, bool end) {
+  (void)s;
+  if (ctx->trace_kind != kind) return LADDER_OK;
+  const size_t i = 2 * (size_t)ctx->trace_n;
+  if (i + 1 >= ctx->trace_ev.size()) return LADDER_OK;
+  if (!end) {
+    launch_events_arm(ctx->trace_ev[i], ctx->trace_ev[i + 1]);
+  } else {
+    launch_events_disarm();
+    ++ctx->trace_n;
+  }
+  return LADDER_OK;
+}
+
+#define TRACE(kind, s, end)                                   \
+  do {                                                        \
+    ladder_status t_ = trace_mark(ctx, (kind), (s), (end));   \
+    if (t_) return t_;                                        \
+  } while (0)
 
 inline int module_src(const ladder_ctx* c, int m) {
   return c->mask[m / 2] ? (m > 0 ? m - 1 : 0) : m;
@@ -386,13 +412,23 @@ ladder_status decode_module(ladder_ctx* ctx, int m, int B, const float* xin, con
   StreamScratch& sc = module_scratch(ctx, m);
   ladder_status st;
   if (m % 2 == 0) {
+    TRACE(LADDER_KERNEL_QKV, s, false);
     if ((st = run_gemv(ctx, qkv_params(ctx, l, B, xin, sc), s))) return st;
+    TRACE(LADDER_KERNEL_QKV, s, true);
+    TRACE(LADDER_KERNEL_ATTN, s, false);
     HIPCHK(launch_attn_decode(attn_params(ctx, l, B, sc), s));
+    TRACE(LADDER_KERNEL_ATTN, s, true);
   } else {
+    TRACE(LADDER_KERNEL_GATEUP, s, false);
     if ((st = run_gemv(ctx, gateup_params(ctx, l, B, xin, sc), s))) return st;
+    TRACE(LADDER_KERNEL_GATEUP, s, true);
   }
   if (out_x && wait_xm) HIPCHK(hipStreamWaitEvent(s, ev_xm, 0));
-  return run_gemv(ctx, outproj_params(ctx, m, B, sc, xm, out_x, out_store), s);
+  const int kind = m % 2 == 0 ? LADDER_KERNEL_OPROJ : LADDER_KERNEL_DOWN;
+  TRACE(kind, s, false);
+  if ((st = run_gemv(ctx, outproj_params(ctx, m, B, sc, xm, out_x, out_store), s))) return st;
+  TRACE(kind, s, true);
+  return LADDER_OK;
 }
 
 // One ladder layer l of a decode step on one stream, in three launches:
@@ -409,25 +445,32 @@ ladder_status decode_layer_fused(ladder_ctx* ctx, int l, int B) {
   GemvParams pr[2] = {qkv_params(ctx, l, B, X[module_src(ctx, ma) % 2], sc),
                       gateup_params(ctx, l, B, X[module_src(ctx, mm) % 2], sc)};
   const bool rw = gemv_rw_supported(ctx->wdt, ctx->cfg.hidden, B);
+  TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
   if (rw) {
     HIPCHK(launch_gemv_multi(pr, 2, nullptr, s, nullptr));
   } else {
     if ((st = run_gemv(ctx, pr[0], s))) return st;
     if ((st = run_gemv(ctx, pr[1], s))) return st;
   }
+  TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
   const GemvParams down = outproj_params(ctx, mm, B, sc, nullptr, nullptr, ctx->dout[0]);
   const AttnDecodeParams at = attn_params(ctx, l, B, sc);
+  TRACE(LADDER_KERNEL_ATTN_DOWN, s, false);
   if (gemv_rw_supported(ctx->wdt, ctx->cfg.ffn, B) && gemv_rw_attn_fusable(ctx->wdt, ctx->cfg.ffn)) {
     HIPCHK(launch_gemv_multi(&down, 1, &at, s, nullptr));
   } else {
     HIPCHK(launch_attn_decode(at, s));
     if ((st = run_gemv(ctx, down, s))) return st;
   }
+  TRACE(LADDER_KERNEL_ATTN_DOWN, s, true);
   GemvParams o = outproj_params(ctx, ma, B, sc, X[ma % 2], X[(ma + 1) % 2], nullptr);
   o.epi = EPI_ADD2;
   o.add2 = ctx->dout[0];
   o.out2 = X[(ma + 2) % 2];
-  return run_gemv(ctx, o, s);
+  TRACE(LADDER_KERNEL_OPROJ_ADD2, s, false);
+  if ((st = run_gemv(ctx, o, s))) return st;
+  TRACE(LADDER_KERNEL_OPROJ_ADD2, s, true);
+  return LADDER_OK;
 }
 
 // ---------------------------------------------------------------- prefill module
@@ -580,6 +623,7 @@ ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream
 // x_{2L} in dx[(2L) % 2].  Enqueued on s0 (possibly under graph capture).
 ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
   const ladder_config& g = ctx->cfg;
+  ctx->trace_n = 0;
   HIPCHK(launch_embed(ctx->wdt, ctx->w.tok_embed, g.vocab, g.hidden, ctx->ids_dev, B, ctx->dx[0], ctx->s0));
   ladder_status st;
   if (ctx->sched == LADDER_SCHED_FUSED) {
@@ -601,7 +645,11 @@ ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
     st = run_modules(ctx, ctx->dx, ctx->dout, (size_t)B * g.hidden, mod);
     if (st) return st;
   }
-  return lm_head(ctx, ctx->dx[(2 * g.n_layers) % 2], g.hidden, B, ctx->s0);
+  TRACE(LADDER_KERNEL_LMHEAD, ctx->s0, false);
+  if ((st = lm_head(ctx, ctx->dx[(2 * g.n_layers) % 2], g.hidden, B, ctx->s0))) return st;
+  TRACE(LADDER_KERNEL_LMHEAD, ctx->s0, true);
+  ctx->trace_count = ctx->trace_n;
+  return LADDER_OK;
 }
 
 ladder_status begin_call(ladder_ctx* ctx) {
@@ -658,6 +706,7 @@ void ladder_free(ladder_ctx* ctx) {
   for (hipEvent_t e : ctx->ev_x) if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : ctx->ev_out) if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : {ctx->ev_fork, ctx->ev_in, ctx->ev_done}) if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : ctx->trace_ev) if (e) (void)hipEventDestroy(e);
   for (hipStream_t s : {ctx->sb, ctx->side}) {
     if (s) { (void)hipStreamSynchronize(s); (void)hipStreamDestroy(s); }
   }
@@ -774,6 +823,37 @@ ladder_status ladder_sync(ladder_ctx* ctx) {
   HIPCHK(hipSetDevice(ctx->dev));
   HIPCHK(hipStreamSynchronize(ctx->s0));
   HIPCHK(hipStreamSynchronize(ctx->user));
+  return LADDER_OK;
+}
+
+ladder_status ladder_trace_kernel(ladder_ctx* ctx, int32_t kind) {
+  if (!ctx) return LADDER_ERR_ARG;
+  if (ctx->broken) return LADDER_ERR_HIP;
+  if (kind < -1 || kind >= LADDER_N_KERNELS) return fail(ctx, LADDER_ERR_ARG, "kernel kind out of range%s");
+  if (kind >= 0 && ctx->trace_ev.empty()) {
+    HIPCHK(hipSetDevice(ctx->dev));
+    ctx->trace_ev.assign(2 * ((size_t)ctx->cfg.n_layers + 1), nullptr);
+    for (hipEvent_t& e : ctx->trace_ev) HIPCHK(hipEventCreate(&e));
+  }
+  ctx->trace_kind = kind;
+  ctx->trace_count = 0;
+  return LADDER_OK;
+}
+
+ladder_status ladder_trace_result(ladder_ctx* ctx, float* mean_us, int32_t* count) {
+  if (!ctx || !mean_us || !count) return LADDER_ERR_ARG;
+  if (ctx->broken) return LADDER_ERR_HIP;
+  if (ctx->trace_kind < 0 || ctx->trace_count < 1) return fail(ctx, LADDER_ERR_STATE, "no traced launches%s");
+  HIPCHK(hipSetDevice(ctx->dev));
+  HIPCHK(hipStreamSynchronize(ctx->s0));
+  double tot = 0.0;
+  for (int i = 0; i < ctx->trace_count; ++i) {
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, ctx->trace_ev[2 * i], ctx->trace_ev[2 * i + 1]));
+    tot += ms;
+  }
+  *mean_us = (float)(1000.0 * tot / ctx->trace_count);
+  *count = ctx->trace_count;
   return LADDER_OK;
 }
 
@@ -905,7 +985,8 @@ ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t 
   ladder_status st = begin_call(ctx);
   if (st) return st;
   HIPCHK(launch_decode_prologue(d_ids, ctx->ids_dev, B, ctx->pos_dev, pos, ctx->s0));
-  if (ctx->use_graph) {
+  // traced steps run eagerly: event records captured into a graph carry no timestamps
+  if (ctx->use_graph && ctx->trace_kind < 0) {
     const int key = B * 8 + ctx->sched;
     auto it = ctx->graphs.find(key);
     if (it == ctx->graphs.end()) {

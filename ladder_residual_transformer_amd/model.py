@@ -113,6 +113,13 @@ class LadderModel:
     def time_kernels(self, B: int, reps: int = 3) -> dict:
         return abi.ladder_time_kernels(self.ctx, B, reps)
 
+    def trace_kernel(self, kind) -> None:
+        """Time every decode launch of one kernel kind (a name of abi.KERNEL_KINDS, or None)."""
+        abi.ladder_trace_kernel(self.ctx, -1 if kind is None else abi.KERNEL_KINDS.index(kind))
+
+    def trace_result(self):
+        return abi.ladder_trace_result(self.ctx)
+
     def filled(self) -> int:
         return abi.ladder_filled(self.ctx)
 

@@ -111,6 +111,8 @@ def test_null_context_calls():
     assert lib.ladder_decode_step(None, None, 1, 0, None, None, None) == abi.LADDER_ERR_ARG
     assert lib.ladder_set_schedule(None, 0, 0) == abi.LADDER_ERR_ARG
     assert lib.ladder_sync(None) == abi.LADDER_ERR_ARG
+    assert lib.ladder_trace_kernel(None, 0) == abi.LADDER_ERR_ARG
+    assert lib.ladder_trace_result(None, None, None) == abi.LADDER_ERR_ARG
     lib.ladder_free(None)                                  # no-op
     assert lib.ladder_last_error(None) == b""
 

@@ -198,3 +198,30 @@ def test_batch_rows_match_single_sequence(edge):
         l1 = gpu_teacher_forced(m1, prompt[b:b + 1], cont[b:b + 1])[0]
         m1.free()
         assert rel_err(l3[b], l1[0]) <= 2e-3
+
+
+def test_kernel_tracing_keeps_results_and_counts_launches(edge):
+    """Event-bracketed decode graphs give the same bits as plain ones and one timed
+    launch per ladder layer for a fused kind (the standard layer 0 has none)."""
+    from ladder_residual_transformer_amd import LadderError, abi
+    cfg, w = edge
+    prompt = synth.gen_ids(1, 9, cfg.vocab, seed=12)
+    cont = synth.gen_ids(1, 3, cfg.vocab, seed=12, stream=1)
+    m = make_model(cfg, w, 1, 16)
+    plain = gpu_teacher_forced(m, prompt, cont)
+    m.free()
+    m = make_model(cfg, w, 1, 16)
+    with pytest.raises(LadderError) as e:
+        m.trace_result()
+    assert e.value.status == abi.LADDER_ERR_STATE
+    m.trace_kernel("qkv_gateup")
+    traced = gpu_teacher_forced(m, prompt, cont)
+    us, n = m.trace_result()
+    assert n == sum(cfg.ladder_mask) and us > 0.0
+    m.trace_kernel("lmhead")
+    m.decode_step(torch.from_numpy(cont[:, 0].copy()).cuda(), 9)
+    us2, n2 = m.trace_result()
+    assert n2 == 1 and us2 > 0.0
+    m.free()
+    for a, b in zip(plain, traced):
+        assert np.array_equal(a, b)
