@@ -201,6 +201,7 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    model.sync()
     gpu_ms = e0.elapsed_time(e1)
     toks = cur.cpu().numpy()
     assert np.all((toks >= 0) & (toks < cfg.vocab)), "decode produced an out-of-range token id"

@@ -147,7 +147,9 @@ ladder_status ladder_filled(const ladder_ctx* ctx, int32_t* out);
 /* Device bytes the context allocated for its workspace. */
 ladder_status ladder_workspace_bytes(const ladder_ctx* ctx, size_t* out);
 
-/* Wait for all work of the context (its stream and internal streams). */
+/* Wait for all work of the context (its stream and internal streams).  Also reports
+ * LADDER_ERR_HIP (sticky) if a decode kernel's bounded wait for another workgroup's
+ * signal ever gave up, which does not happen in a correct run. */
 ladder_status ladder_sync(ladder_ctx* ctx);
 
 /* Decode kernel kinds, for ladder_time_kernels and ladder_trace_kernel. */
@@ -158,8 +160,11 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 #define LADDER_KERNEL_DOWN 4     /* Wdown GEMV + fused residual add */
 #define LADDER_KERNEL_LMHEAD 5   /* final RMSNorm + LM head GEMV + greedy argmax */
 #define LADDER_KERNEL_QKV_GATEUP 6  /* fused ladder launch: QKV (+RoPE/KV) | gate/up (+SwiGLU) */
-#define LADDER_KERNEL_ATTN_DOWN 7   /* fused ladder launch: decode attention | down projection */
-#define LADDER_KERNEL_OPROJ_ADD2 8  /* fused ladder launch: O projection + both residual adds */
+#define LADDER_KERNEL_ATTN_DOWN 7   /* fused ladder launch: decode attention | down projection; with
+                                       bf16 weights and batch <= 4 followed, in the same launch, by
+                                       the O projection + both residual adds */
+#define LADDER_KERNEL_OPROJ_ADD2 8  /* fused ladder launch: O projection + both residual adds (three-
+                                       launch layers only) */
 #define LADDER_N_KERNELS 9
 
 /* Profiling aid.  For each kernel kind, enqueue it on the context's stream exactly as

@@ -41,12 +41,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeParams p) {
   attn_decode_block<WT, HD, HPW>(p, blockIdx.x, L);
 }
 
-// Chunks per (sequence, kv head): one 64-key tile each at full length, at most 16 (the
-// merge then reads every chunk of a head slice in one round of loads).
+// Chunks per (sequence, kv head): one 64-key tile each up to 32 tiles of context
+// (longer contexts get several tiles per chunk); the merge reads all chunks at once.
 int attn_decode_splits(int max_seq) {
   int n = (max_seq + kAttnKeyTile - 1) / kAttnKeyTile;
   if (n < 1) n = 1;
-  if (n > 16) n = 16;
+  if (n > kAttnMaxSplits) n = kAttnMaxSplits;
   return n;
 }
 
@@ -165,34 +165,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) 
 
 // ------------------------------------------------- prefill, bf16 models (MFMA)
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 constexpr int kPqWave = 32;                  // queries per wave
 constexpr int kPqTile = 4 * kPqWave;         // queries per workgroup
 constexpr int kPkTile = 64;                  // keys per LDS tile
-
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  h2 h = {(_Float16)a, (_Float16)b};
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-// (a, b) -> fp16 pairs hi = fp16(v), lo = fp16(v - hi), two elements per word
-__device__ __forceinline__ void split_h2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const h2 h = {(_Float16)a, (_Float16)b};
-  const h2 l = {(_Float16)(a - (float)h[0]), (_Float16)(b - (float)h[1])};
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, l);
-}
-
-// 8 bf16 (one 16-byte chunk) -> 8 fp16, exact for |v| in [2^-17, 65504].
-__device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& v) {
-  return make_uint4(pack_h2(bf16_lo(v.x), bf16_hi(v.x)), pack_h2(bf16_lo(v.y), bf16_hi(v.y)),
-                    pack_h2(bf16_lo(v.z), bf16_hi(v.z)), pack_h2(bf16_lo(v.w), bf16_hi(v.w)));
-}
 
 template <int HD>
 struct PrefillLds {

@@ -57,6 +57,77 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// fp16 operands of the matrix cores.  A pair hi = fp16(v), lo = fp16(v - hi) carries
+// about 22 significant bits of an fp32 value; bf16 values convert to fp16 exactly for
+// |v| in [2^-17, 65504].
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ void split_h2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 h = {(_Float16)a, (_Float16)b};
+  const h2 l = {(_Float16)(a - (float)h[0]), (_Float16)(b - (float)h[1])};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// 8 bf16 (one 16-byte chunk) -> 8 fp16
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& v) {
+  return make_uint4(pack_h2(bf16_lo(v.x), bf16_hi(v.x)), pack_h2(bf16_lo(v.y), bf16_hi(v.y)),
+                    pack_h2(bf16_lo(v.z), bf16_hi(v.z)), pack_h2(bf16_lo(v.w), bf16_hi(v.w)));
+}
+
+// Cross-workgroup synchronisation inside one kernel, with one L2 write-back or
+// invalidate per workgroup (not one per wave): every wave first waits for its own global
+// stores to complete (they are then in its XCD's L2), the workgroup meets at a barrier,
+// and one thread performs the agent-scope release (L2 write-back) or acquire (L1/L2
+// invalidate) for all of them.
+__device__ __forceinline__ void wave_stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xF70);               // vmcnt(0): this wave's stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// A producer workgroup, after its writes, counts itself; the last of `total` publishes
+// the step's epoch in *flag.
+__device__ __forceinline__ void wg_signal(int* cnt, int* flag, int total, int epoch) {
+  wave_stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (atomicAdd(cnt, 1) == total - 1) {
+      __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+      __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// A consumer waits (one thread polls, bounded) until *flag == epoch, then acquires; on a
+// poll that gives up it sets *err and goes on, so every wave still ends.
+__device__ __forceinline__ void wg_wait(const int* flag, int epoch, int* err) {
+  if (threadIdx.x == 0) {
+    unsigned spins = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins == (1u << 18)) {          // ~14 ms: far beyond any real wait
+        atomicOr(err, 1);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
 // Launch timing (measurement aid).  While armed, the decode-path launches go through
 // hipExtLaunchKernelGGL: the first one records `start` when its dispatch begins, every
 // one records `stop` when its dispatch ends, so the pair spans exactly the kernels

@@ -90,10 +90,17 @@ __global__ __launch_bounds__(256) void add_kernel(const float* x, const float* y
   for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) out[i] = x[i] + y[i];
 }
 
-__global__ void decode_prologue_kernel(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos) {
+__global__ void decode_prologue_kernel(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, int* d_epoch) {
   const int i = threadIdx.x;
   if (i < B) ids_dst[i] = ids_src[i];
-  if (i == 0) *d_pos = pos;
+  if (i == 0) {
+    *d_pos = pos;
+    if (d_epoch) *d_epoch += 1;
+  }
+}
+
+__global__ void epoch_bump_kernel(int* d_epoch) {
+  if (threadIdx.x == 0) *d_epoch += 1;
 }
 
 static unsigned grid_for(size_t n) {
@@ -135,13 +142,19 @@ hipError_t launch_swiglu(const float* gu, int M, int F, float* a, hipStream_t s)
   return hipGetLastError();
 }
 
+hipError_t launch_epoch_bump(int* d_epoch, hipStream_t s) {
+  hipLaunchKernelGGL(epoch_bump_kernel, dim3(1), dim3(64), 0, s, d_epoch);
+  return hipGetLastError();
+}
+
 hipError_t launch_add(const float* x, const float* y, float* out, size_t n, hipStream_t s) {
   hipLaunchKernelGGL(add_kernel, dim3(grid_for(n)), dim3(256), 0, s, x, y, out, n);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_prologue(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, hipStream_t s) {
-  hipLaunchKernelGGL(decode_prologue_kernel, dim3(1), dim3(64), 0, s, ids_src, ids_dst, B, d_pos, pos);
+hipError_t launch_decode_prologue(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, int* d_epoch,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(decode_prologue_kernel, dim3(1), dim3(64), 0, s, ids_src, ids_dst, B, d_pos, pos, d_epoch);
   return hipGetLastError();
 }
 

@@ -22,7 +22,6 @@
 
 namespace ladder {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
 template <typename WT>
@@ -35,21 +34,6 @@ __device__ __forceinline__ const WT* gemm_row(const RowSrc& s, int r, int K) {
 
 constexpr int BM = 128, BN = 128, BK = 32, LDK = BK + 8;
 constexpr int kXcds = 8;
-
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  h2 h = {(_Float16)a, (_Float16)b};
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-// a -> (hi, lo) fp16 pairs of two elements each
-__device__ __forceinline__ void split_h2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const h2 h = {(_Float16)a, (_Float16)b};
-  const h2 l = {(_Float16)(a - (float)h[0]), (_Float16)(b - (float)h[1])};
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, l);
-}
 
 __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd) {
   __shared__ __attribute__((aligned(16))) uint16_t Ah[2][BM][LDK];
@@ -104,8 +88,7 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
     for (int i = 0; i < 2; ++i) {
       const uint4 w = rb[i];
       *(uint4*)&Bs[buf][br[i]][bc[i]] =
-          make_uint4(pack_h2(bf16_lo(w.x), bf16_hi(w.x)), pack_h2(bf16_lo(w.y), bf16_hi(w.y)),
-                     pack_h2(bf16_lo(w.z), bf16_hi(w.z)), pack_h2(bf16_lo(w.w), bf16_hi(w.w)));
+          bf16x8_to_f16x8(w);
     }
   };
 

@@ -103,36 +103,30 @@ __device__ __forceinline__ void rw_epilogue(const GemvParams& p, int pair, int b
   }
 }
 
-// NP: number of GEMV problems of the launch (1 or 2).
-template <typename WT, int BT, int VPL, int HDA, int HPW, int NP>
-__global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
-  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-  if constexpr (HDA != 0) {
-    if ((int)blockIdx.x < mp.n_attn) {
-      attn_decode_block<WT, HDA, HPW>(mp.attn, blockIdx.x, *reinterpret_cast<AttnLds<WT, HDA>*>(lds_raw));
-      return;
-    }
-  }
+struct RwShared {
+  float sqw[4][4];
+  float inv[4];
+  float wbv[4][4];
+  int wbi[4][4];
+};
+
+// where a pass puts its rows
+enum { RW_OUT_EPI = 0, RW_OUT_LDS = 1, RW_OUT_ADD2_LDS = 2 };
+
+// One pass of the row-wave GEMV over row pairs [pr0, pr1) of problem p (this
+// workgroup's share).  OUT: the problem's own epilogue; the rows (times inv_rms) into
+// dres[row - 2*pr0][b]; or EPI_ADD2 with dres in place of add2.  wait_flag: the first
+// weight unit is issued, then the workgroup waits for the signal before it stages the
+// input.
+template <typename WT, int BT, int VPL, int OUT>
+__device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, int lb, float* u, float* dres,
+                                        const int* wait_flag, int wait_epoch, int* err, RwShared& sh) {
   constexpr int VEC = Vec<WT>::N;
   constexpr int CHUNK = 64 * VPL;                 // vectors of a row one wave covers per step
-  __shared__ float sqw[4][BT];
-  __shared__ float inv_sh[BT];
-  __shared__ float wbv[4][BT];
-  __shared__ int wbi[4][BT];
-
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int blk = (int)blockIdx.x - mp.n_attn;
-  const int pi = (NP > 1 && blk >= mp.blk_begin[1]) ? 1 : 0;
-  const GemvParams& p = mp.prob[pi];
-  const int lb = blk - mp.blk_begin[pi];
-  const int nb = mp.blk_begin[pi + 1] - mp.blk_begin[pi];
   const int K = p.K, B = p.B;
   const int nvec = K / VEC;
   const int nchunk = (nvec + CHUNK - 1) / CHUNK;
-  const int P = (p.N + 1) / 2;
-  const int pr0 = (int)((long long)lb * P / nb);
-  const int pr1 = (int)((long long)(lb + 1) * P / nb);
-  float* u = reinterpret_cast<float*>(lds_raw);   // [B][K]
 
   // This wave's work is a sequence of units: unit i is chunk (i % nchunk) of its pair
   // number (i / nchunk); its pairs are pr0 + wid, pr0 + wid + 4, ...  Two register
@@ -157,6 +151,10 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
   };
   const int ustride = K + VEC;                     // u rows carry a zero pad of VEC floats
 
+  if (wait_flag) {
+    if (n_units > 0) load_unit(wa, 0);
+    wg_wait(wait_flag, wait_epoch, err);
+  }
   // ---- prologue: u = x (* g) for every batch row, and inv_rms.  For one batch row
   // and K <= 256*4*VEC the input loads are issued before the first weight unit, so the
   // in-order completion of loads does not make the prologue wait for the weights.
@@ -172,7 +170,7 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
       for (int e = 0; e < VEC / 4; ++e) xr[i][e] = *(const float4*)(p.x + (size_t)v * VEC + 4 * e);
       gr[i] = norm ? *(const uint4*)((const WT*)p.gain + (size_t)v * VEC) : make_uint4(0u, 0u, 0u, 0u);
     }
-    if (n_units > 0) load_unit(wa, 0);
+    if (!wait_flag && n_units > 0) load_unit(wa, 0);
     float sq = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -197,9 +195,9 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
       }
     }
     sq = wave_sum(sq);
-    if (lane == 0) sqw[wid][0] = sq;
+    if (lane == 0) sh.sqw[wid][0] = sq;
   } else {
-    if (n_units > 0) load_unit(wa, 0);
+    if (!wait_flag && n_units > 0) load_unit(wa, 0);
     for (int b = 0; b < BT; ++b) {
       float sq = 0.f;
       if (b < B) {
@@ -226,18 +224,18 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
         }
       }
       sq = wave_sum(sq);
-      if (lane == 0) sqw[wid][b] = sq;
+      if (lane == 0) sh.sqw[wid][b] = sq;
     }
   }
   __syncthreads();
   if (tid < BT) {
-    const float t = ((sqw[0][tid] + sqw[1][tid]) + sqw[2][tid]) + sqw[3][tid];
-    inv_sh[tid] = norm ? 1.0f / sqrtf(t / (float)K + p.eps) : 1.0f;
+    const float t = ((sh.sqw[0][tid] + sh.sqw[1][tid]) + sh.sqw[2][tid]) + sh.sqw[3][tid];
+    sh.inv[tid] = norm ? 1.0f / sqrtf(t / (float)K + p.eps) : 1.0f;
   }
   __syncthreads();
   float inv_b[BT];
 #pragma unroll
-  for (int b = 0; b < BT; ++b) inv_b[b] = inv_sh[b];
+  for (int b = 0; b < BT; ++b) inv_b[b] = sh.inv[b];
 
   // ---- row pairs
   float best = -INFINITY;
@@ -280,7 +278,25 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
       for (int b = 0; b < BT; ++b) {
         const float y0 = wave_sum(acc[0][b]);
         const float y1 = wave_sum(acc[1][b]);
-        if (lane == b && b < B) rw_epilogue<WT>(p, pair, b, y0, y1, inv_b[b], best, bidx);
+        if (lane == b && b < B) {
+          if constexpr (OUT == RW_OUT_EPI) {
+            rw_epilogue<WT>(p, pair, b, y0, y1, inv_b[b], best, bidx);
+          } else if constexpr (OUT == RW_OUT_LDS) {
+            const int r = 2 * (pair - pr0);
+            dres[r * BT + b] = y0 * inv_b[b];
+            dres[(r + 1) * BT + b] = y1 * inv_b[b];
+          } else {                              // EPI_ADD2, second addend from dres
+            const int r = 2 * (pair - pr0), n0 = 2 * pair;
+            const float t0 = p.xres[(size_t)b * p.ldr + n0] + y0 * inv_b[b];
+            p.out[(size_t)b * p.ldo + n0] = t0;
+            p.out2[(size_t)b * p.ldo + n0] = t0 + dres[r * BT + b];
+            if (n0 + 1 < p.N) {
+              const float t1 = p.xres[(size_t)b * p.ldr + n0 + 1] + y1 * inv_b[b];
+              p.out[(size_t)b * p.ldo + n0 + 1] = t1;
+              p.out2[(size_t)b * p.ldo + n0 + 1] = t1 + dres[(r + 1) * BT + b];
+            }
+          }
+        }
         acc[0][b] = 0.f;
         acc[1][b] = 0.f;
       }
@@ -295,18 +311,55 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
     }
   }
 
-  if (p.epi == EPI_LOGITS) {
+  if (OUT == RW_OUT_EPI && p.epi == EPI_LOGITS) {
     // per-block greedy candidate (lowest index among equal maxima); merged by argmax_finalize
-    if (lane < BT) { wbv[wid][lane] = best; wbi[wid][lane] = bidx; }
+    if (lane < BT) { sh.wbv[wid][lane] = best; sh.wbi[wid][lane] = bidx; }
     __syncthreads();
     if (tid < BT) {
-      float bb = wbv[0][tid];
-      int ii = wbi[0][tid];
+      float bb = sh.wbv[0][tid];
+      int ii = sh.wbi[0][tid];
       for (int q = 1; q < 4; ++q)
-        if (wbv[q][tid] > bb || (wbv[q][tid] == bb && wbi[q][tid] < ii)) { bb = wbv[q][tid]; ii = wbi[q][tid]; }
+        if (sh.wbv[q][tid] > bb || (sh.wbv[q][tid] == bb && sh.wbi[q][tid] < ii)) { bb = sh.wbv[q][tid]; ii = sh.wbi[q][tid]; }
       p.best_val[(size_t)lb * BT + tid] = bb;
       p.best_idx[(size_t)lb * BT + tid] = ii;
     }
+  }
+}
+
+// NP: GEMV problems of the launch: 1, 2 (side by side), or 3 = the paired launch (rows
+// of prob[0], then after the signal the same rows of prob[1]).  With HDA != 0 the first
+// n_attn workgroups run decode attention.
+template <typename WT, int BT, int VPL, int HDA, int HPW, int NP>
+__global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  if constexpr (HDA != 0) {
+    if ((int)blockIdx.x < mp.n_attn) {
+      attn_decode_block<WT, HDA, HPW>(mp.attn, blockIdx.x, *reinterpret_cast<AttnLds<WT, HDA>*>(lds_raw));
+      return;
+    }
+  }
+  __shared__ RwShared sh;
+  const int blk = (int)blockIdx.x - mp.n_attn;
+  float* u = reinterpret_cast<float*>(lds_raw);   // [B][K + pad]
+  if constexpr (NP == 3) {
+    const int nb = mp.blk_begin[1];
+    const int P = (mp.prob[0].N + 1) / 2;
+    const int pr0 = (int)((long long)blk * P / nb);
+    const int pr1 = (int)((long long)(blk + 1) * P / nb);
+    float* dres = reinterpret_cast<float*>(lds_raw + mp.dres_off);
+    const int epoch = *mp.d_epoch;
+    rw_pass<WT, BT, VPL, RW_OUT_LDS>(mp.prob[0], pr0, pr1, blk, u, dres, nullptr, 0, nullptr, sh);
+    __syncthreads();                               // u is restaged by the second pass
+    rw_pass<WT, BT, VPL, RW_OUT_ADD2_LDS>(mp.prob[1], pr0, pr1, blk, u, dres, mp.wait_flag, epoch, mp.err, sh);
+  } else {
+    const int pi = (NP > 1 && blk >= mp.blk_begin[1]) ? 1 : 0;
+    const int lb = blk - mp.blk_begin[pi];
+    const int nb = mp.blk_begin[pi + 1] - mp.blk_begin[pi];
+    const GemvParams& p = mp.prob[pi];
+    const int P = (p.N + 1) / 2;
+    const int pr0 = (int)((long long)lb * P / nb);
+    const int pr1 = (int)((long long)(lb + 1) * P / nb);
+    rw_pass<WT, BT, VPL, RW_OUT_EPI>(p, pr0, pr1, lb, u, nullptr, nullptr, 0, nullptr, sh);
   }
 }
 
@@ -400,8 +453,15 @@ hipError_t rw_go(MultiGemvParams& mp, size_t lds, hipStream_t s) {
   int target = cached_resident - mp.n_attn;
   if (target < 64) target = 64;
   if (target > kRwTargetBlocks) target = kRwTargetBlocks;
-  rw_split_blocks(mp, target);
-  const int grid = mp.n_attn + mp.blk_begin[mp.np];
+  if (NP == 3) {                      // paired: the blocks split the rows of prob[0]
+    mp.np = 1;
+    rw_split_blocks(mp, target);
+    mp.np = 2;
+    mp.blk_begin[2] = mp.blk_begin[1];
+  } else {
+    rw_split_blocks(mp, target);
+  }
+  const int grid = mp.n_attn + (NP == 3 ? mp.blk_begin[1] : mp.blk_begin[mp.np]);
   launch_timed(fn, dim3(grid), dim3(256), (uint32_t)lds, s, mp);
   return hipGetLastError();
 }
@@ -411,20 +471,27 @@ hipError_t rw_go(MultiGemvParams& mp, size_t lds, hipStream_t s) {
 template <typename WT, int BT, int VPL>
 hipError_t rw_hda(MultiGemvParams& mp, int hda, size_t lds, hipStream_t s) {
   if constexpr (VPL == 4) {
-    const int hpw = hda ? attn_hpw(mp.attn.nq / mp.attn.nkv) : 0;
-    if (hda != 0 && mp.np != 1) return hipErrorInvalidValue;   // attention rides with one problem
+    // attention rides with one problem, or with a paired launch; the fp32 path needs the
+    // heads-per-wave instance, the bf16 (matrix core) path has one
+    // attention rides with one problem, or (bf16) in front of a paired launch; the fp32
+    // path needs the heads-per-wave instance, the bf16 (matrix core) path has one
+    const int hpw = hda ? (sizeof(WT) == 2 ? 1 : attn_hpw(mp.attn.nq / mp.attn.nkv)) : 0;
+    if (hda != 0 && mp.np != 1 && !(sizeof(WT) == 2 && mp.paired)) return hipErrorInvalidValue;
     if (hda == 128) {
+      if (mp.paired) return rw_go<WT, BT, VPL, 128, 1, 3>(mp, lds, s);
       if (hpw == 1) return rw_go<WT, BT, VPL, 128, 1, 1>(mp, lds, s);
       if (hpw == 2) return rw_go<WT, BT, VPL, 128, 2, 1>(mp, lds, s);
       return rw_go<WT, BT, VPL, 128, 4, 1>(mp, lds, s);
     }
     if (hda == 64) {
+      if (mp.paired) return rw_go<WT, BT, VPL, 64, 1, 3>(mp, lds, s);
       if (hpw == 1) return rw_go<WT, BT, VPL, 64, 1, 1>(mp, lds, s);
       if (hpw == 2) return rw_go<WT, BT, VPL, 64, 2, 1>(mp, lds, s);
       return rw_go<WT, BT, VPL, 64, 4, 1>(mp, lds, s);
     }
   }
   if (hda != 0) return hipErrorInvalidValue;
+  if (mp.paired) return sizeof(WT) == 2 ? rw_go<WT, BT, VPL, 0, 0, 3>(mp, lds, s) : hipErrorInvalidValue;
   if (mp.np == 2) return rw_go<WT, BT, VPL, 0, 0, 2>(mp, lds, s);
   return rw_go<WT, BT, VPL, 0, 0, 1>(mp, lds, s);
 }
@@ -448,6 +515,51 @@ hipError_t rw_bt_go(MultiGemvParams& mp, int bt, int vpl, int hda, size_t lds, h
 }  // namespace
 
 bool gemv_rw_attn_fusable(int wdtype, int K) { return rw_vpl(K / (wdtype == W_BF16 ? 8 : 4)) == 4; }
+
+namespace {
+// LDS of a paired launch: u for the wider input, then prob[0]'s rows of one workgroup
+// (a launch has at least 64 GEMV workgroups, or as many as give each 4 row pairs)
+size_t rw_pair_lds(int wdtype, int K0, int K1, int N, int B, int* dres_off) {
+  const int vec = wdtype == W_BF16 ? 8 : 4;
+  const size_t ub = (size_t)B * ((K0 > K1 ? K0 : K1) + vec) * 4;
+  const size_t off = (ub + 15) / 16 * 16;
+  const int P = (N + 1) / 2;
+  const int per = (P + 63) / 64;                   // pairs per workgroup: >= 64 workgroups,
+  const size_t rows = 2 * (size_t)(per > 4 ? per : 4);   // or at most 4 pairs each
+  if (dres_off) *dres_off = (int)off;
+  return off + rows * 4 * sizeof(float);
+}
+}  // namespace
+
+bool gemv_rw_pair_supported(int wdtype, int K_first, int K_second, int B) {
+  return wdtype == W_BF16 && gemv_rw_supported(wdtype, K_first, B) && gemv_rw_supported(wdtype, K_second, B) &&
+         gemv_rw_attn_fusable(wdtype, K_first);
+}
+
+hipError_t launch_gemv_paired(const GemvParams& first, const GemvParams& second, const AttnDecodeParams& attn,
+                              int* err, hipStream_t s) {
+  const int B = first.B, wdt = first.wdtype;
+  if (!gemv_rw_pair_supported(wdt, first.K, second.K, B) || second.B != B || second.wdtype != wdt ||
+      first.N != second.N || second.epi != EPI_ADD2 || !attn.done_flag || !attn.done_cnt || !attn.d_epoch || !err)
+    return hipErrorInvalidValue;
+  if (attn.nkv < 1 || attn.nq % attn.nkv != 0 || attn.nq / attn.nkv > kAttnMaxGroup ||
+      attn.n_split > kAttnMaxSplits || (attn.hd != 64 && attn.hd != 128) || attn.wdtype != wdt || attn.B != B)
+    return hipErrorInvalidValue;
+  MultiGemvParams mp{};
+  mp.np = 2;
+  mp.prob[0] = first;
+  mp.prob[1] = second;
+  mp.paired = 1;
+  mp.attn = attn;
+  mp.n_attn = attn.n_split * attn.nkv * attn.B;
+  mp.wait_flag = attn.done_flag;
+  mp.d_epoch = attn.d_epoch;
+  mp.err = err;
+  size_t lds = rw_pair_lds(wdt, first.K, second.K, first.N, B, &mp.dres_off);
+  const size_t al = attn.hd == 128 ? sizeof(AttnLds<uint16_t, 128>) : sizeof(AttnLds<uint16_t, 64>);
+  if (al > lds) lds = al;
+  return rw_bt_go<uint16_t>(mp, rw_bt(B), 4, attn.hd, lds, s);
+}
 
 bool gemv_rw_supported(int wdtype, int K, int B) {
   return B >= 1 && B <= 4 && (size_t)B * (K + (wdtype == W_BF16 ? 8 : 4)) * 4 <= 66560;

@@ -65,6 +65,10 @@ struct AttnDecodeParams {
   float* part;                         // [B][nq][n_split][hd+4]: max, sum, -, -, acc[hd]
   int* counters;                       // [B][nkv]
   float* out;                          // [B][nq*hd]
+  // completion signal (nullable): after the last of the B*nkv merges, done_flag = *d_epoch
+  const int* d_epoch;
+  int* done_cnt;                       // merges finished (reset to 0 by the last)
+  int* done_flag;
 };
 int attn_decode_splits(int max_seq);
 hipError_t launch_attn_decode(const AttnDecodeParams& p, hipStream_t s);
@@ -78,6 +82,14 @@ struct MultiGemvParams {
   int blk_begin[3];       // problem p owns blocks [blk_begin[p], blk_begin[p+1]) after the attention ones
   int n_attn;             // leading workgroups running decode attention (0 = none)
   AttnDecodeParams attn;
+  // paired launch: every GEMV workgroup computes rows R of prob[0] (kept in LDS), then,
+  // once *wait_flag == *d_epoch, the same rows R of prob[1], whose EPI_ADD2 epilogue
+  // adds prob[0]'s row in place of add2
+  int paired;
+  int dres_off;           // LDS byte offset of prob[0]'s rows [rows per block][BT]
+  const int* wait_flag;
+  const int* d_epoch;
+  int* err;               // set to 1 if a wait ever gives up (never expected)
 };
 bool gemv_rw_supported(int wdtype, int K, int B);
 bool gemv_rw_attn_fusable(int wdtype, int K);   // a launch of this K can carry attention workgroups
@@ -86,6 +98,13 @@ int gemv_rw_bt(int B);
 // blocks_out (nullable): workgroups given to each problem
 hipError_t launch_gemv_multi(const GemvParams* probs, int np, const AttnDecodeParams* attn, hipStream_t s,
                              int* blocks_out);
+// Paired launch [attention | first: rows, then (once the attention has signalled) second:
+// the same rows with EPI_ADD2 taking first's result as add2].  first.N == second.N; the
+// attention's completion signal (done_cnt/done_flag, epoch *d_epoch) is what the second
+// pass waits for.  err: device word set on a failed wait.
+bool gemv_rw_pair_supported(int wdtype, int K_first, int K_second, int B);
+hipError_t launch_gemv_paired(const GemvParams& first, const GemvParams& second, const AttnDecodeParams& attn,
+                              int* err, hipStream_t s);
 // next[b] = first maximum of n per-workgroup candidates (best_val/best_idx [n][BT])
 hipError_t launch_argmax_finalize(const float* best_val, const int* best_idx, int n, int BT, int B, int* next,
                                   hipStream_t s);
@@ -131,6 +150,9 @@ hipError_t launch_rope_kv(int wdtype, const float* qkv, int B, int T, int start_
 // gu [M][2F] interleaved (gate, up) -> a [M][F] (fp32)
 hipError_t launch_swiglu(const float* gu, int M, int F, float* a, hipStream_t s);
 hipError_t launch_add(const float* x, const float* y, float* out, size_t n, hipStream_t s);
-hipError_t launch_decode_prologue(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, hipStream_t s);
+hipError_t launch_epoch_bump(int* d_epoch, hipStream_t s);   // ++*d_epoch
+// ids_dst = ids_src, *d_pos = pos, ++*d_epoch (the step counter of in-kernel signals; nullable)
+hipError_t launch_decode_prologue(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, int* d_epoch,
+                                  hipStream_t s);
 
 }  // namespace ladder

@@ -108,6 +108,10 @@ struct ladder_ctx {
   float* best_val = nullptr;
   int* best_idx = nullptr;
   int* arg_cnt = nullptr;
+  int* epoch = nullptr;           // decode steps enqueued (bumped by the step's prologue)
+  int* attn_done_cnt = nullptr;   // [L] attention merges finished in the current step
+  int* attn_done_flag = nullptr;  // [L] epoch of the last step whose attention finished
+  int* err_word = nullptr;        // set by a kernel whose bounded wait gave up
   StreamScratch sc[2];
 
   int sched = LADDER_SCHED_FUSED;
@@ -206,6 +210,10 @@ void carve(ladder_ctx* c, Carver& cv) {
   c->best_val = cv.take<float>(nbest);
   c->best_idx = cv.take<int>(nbest);
   c->arg_cnt = cv.take<int>(1);
+  c->epoch = cv.take<int>(1);
+  c->attn_done_cnt = cv.take<int>((size_t)g.n_layers);
+  c->attn_done_flag = cv.take<int>((size_t)g.n_layers);
+  c->err_word = cv.take<int>(1);
   for (int s = 0; s < 2; ++s) {
     StreamScratch& sc = c->sc[s];
     sc.q = cv.take<float>((size_t)B * c->qrows);
@@ -323,6 +331,21 @@ AttnDecodeParams attn_params(const ladder_ctx* ctx, int l, int B, const StreamSc
   a.counters = sc.attn_cnt;
   a.out = sc.o;
   return a;
+}
+
+// Attention of layer l that signals its completion (to the paired down + O launch).
+AttnDecodeParams signalled(const ladder_ctx* ctx, AttnDecodeParams a, int l) {
+  a.d_epoch = ctx->epoch;
+  a.done_cnt = ctx->attn_done_cnt + l;
+  a.done_flag = ctx->attn_done_flag + l;
+  return a;
+}
+
+// Two launches per ladder layer (bf16, batch <= 4): [QKV | gate/up] and [attention |
+// down, then (once the attention has signalled) O + both residual adds].
+bool two_launch_layers(const ladder_ctx* ctx, int B) {
+  const ladder_config& g = ctx->cfg;
+  return gemv_rw_supported(ctx->wdt, g.hidden, B) && gemv_rw_pair_supported(ctx->wdt, g.ffn, ctx->qrows, B);
 }
 
 // RMSNorm + [Wgate,Wup] (row pairs) + SwiGLU of layer l
@@ -444,6 +467,23 @@ ladder_status decode_layer_fused(ladder_ctx* ctx, int l, int B) {
   ladder_status st;
   GemvParams pr[2] = {qkv_params(ctx, l, B, X[module_src(ctx, ma) % 2], sc),
                       gateup_params(ctx, l, B, X[module_src(ctx, mm) % 2], sc)};
+  if (two_launch_layers(ctx, B)) {
+    TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
+    HIPCHK(launch_gemv_multi(pr, 2, nullptr, s, nullptr));
+    TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
+    // [attention | down rows, then (once the attention has signalled) the same O rows
+    // with x_{2l+1} = x_{2l} + o and x_{2l+2} = x_{2l+1} + d]; the O weights are already
+    // in flight while the workgroup waits
+    const GemvParams down = outproj_params(ctx, mm, B, sc, nullptr, nullptr, ctx->dout[0]);
+    GemvParams o = outproj_params(ctx, ma, B, sc, X[ma % 2], X[(ma + 1) % 2], nullptr);
+    o.epi = EPI_ADD2;
+    o.add2 = nullptr;
+    o.out2 = X[(ma + 2) % 2];
+    TRACE(LADDER_KERNEL_ATTN_DOWN, s, false);
+    HIPCHK(launch_gemv_paired(down, o, signalled(ctx, attn_params(ctx, l, B, sc), l), ctx->err_word, s));
+    TRACE(LADDER_KERNEL_ATTN_DOWN, s, true);
+    return LADDER_OK;
+  }
   const bool rw = gemv_rw_supported(ctx->wdt, ctx->cfg.hidden, B);
   TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
   if (rw) {
@@ -823,6 +863,12 @@ ladder_status ladder_sync(ladder_ctx* ctx) {
   HIPCHK(hipSetDevice(ctx->dev));
   HIPCHK(hipStreamSynchronize(ctx->s0));
   HIPCHK(hipStreamSynchronize(ctx->user));
+  int err = 0;
+  HIPCHK(hipMemcpy(&err, ctx->err_word, sizeof(int), hipMemcpyDeviceToHost));
+  if (err) {
+    ctx->broken = true;
+    return fail(ctx, LADDER_ERR_HIP, "an in-kernel wait for the attention's signal gave up%s");
+  }
   return LADDER_OK;
 }
 
@@ -872,6 +918,7 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
   hipStream_t s = ctx->s0;
   const bool rw_h = gemv_rw_supported(ctx->wdt, g.hidden, B);
   const bool rw_f = gemv_rw_supported(ctx->wdt, g.ffn, B) && gemv_rw_attn_fusable(ctx->wdt, g.ffn);
+  const bool two = two_launch_layers(ctx, B);
   for (int kind = 0; kind < LADDER_N_KERNELS; ++kind) {
     int launches = 0;
     HIPCHK(hipEventRecord(e0, s));
@@ -904,7 +951,14 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
           case LADDER_KERNEL_ATTN_DOWN: {
             const GemvParams down = outproj_params(ctx, 2 * l + 1, B, sc, nullptr, nullptr, ctx->dout[0]);
             const AttnDecodeParams at = attn_params(ctx, l, B, sc);
-            if (rw_f) {
+            if (two) {                         // a new epoch per launch, as per decode step
+              GemvParams o = outproj_params(ctx, 2 * l, B, sc, ctx->dx[0], ctx->dx[1], nullptr);
+              o.epi = EPI_ADD2;
+              o.add2 = nullptr;
+              o.out2 = ctx->dx[0];
+              HIPCHK(launch_epoch_bump(ctx->epoch, s));
+              HIPCHK(launch_gemv_paired(down, o, signalled(ctx, at, l), ctx->err_word, s));
+            } else if (rw_f) {
               HIPCHK(launch_gemv_multi(&down, 1, &at, s, nullptr));
             } else {
               HIPCHK(launch_attn_decode(at, s));
@@ -984,7 +1038,7 @@ ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t 
   if (pos > ctx->filled) return fail(ctx, LADDER_ERR_STATE, "decode position after unfilled positions%s");
   ladder_status st = begin_call(ctx);
   if (st) return st;
-  HIPCHK(launch_decode_prologue(d_ids, ctx->ids_dev, B, ctx->pos_dev, pos, ctx->s0));
+  HIPCHK(launch_decode_prologue(d_ids, ctx->ids_dev, B, ctx->pos_dev, pos, ctx->epoch, ctx->s0));
   // traced steps run eagerly: event records captured into a graph carry no timestamps
   if (ctx->use_graph && ctx->trace_kind < 0) {
     const int key = B * 8 + ctx->sched;

@@ -123,6 +123,10 @@ class LadderModel:
     def filled(self) -> int:
         return abi.ladder_filled(self.ctx)
 
+    def sync(self) -> None:
+        """Wait for the context's work; raises if a kernel's bounded wait gave up."""
+        abi.ladder_sync(self.ctx)
+
     def workspace_bytes(self) -> int:
         return abi.ladder_workspace_bytes(self.ctx)
 

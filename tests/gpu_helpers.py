@@ -59,6 +59,7 @@ def gpu_teacher_forced(model, prompt: np.ndarray, cont: np.ndarray):
         hidden.append(hd)
         nxt.append(nx)
     torch.cuda.synchronize()
+    model.sync()                  # also reports a failed in-kernel wait
     return (torch.stack(logits, 1).cpu().numpy(), torch.stack(hidden, 1).cpu().numpy(),
             torch.stack(nxt, 1).cpu().numpy())
 
@@ -73,6 +74,7 @@ def gpu_free_running(model, prompt: np.ndarray, n_decode: int):
         lg, nx, hd = model.decode_step(toks[-1], T + k, logits=False, hidden=False)
         toks.append(nx)
     torch.cuda.synchronize()
+    model.sync()
     return torch.stack(toks, 1).cpu().numpy()
 
 

@@ -9,7 +9,7 @@ import torch
 
 import synth
 from gpu_helpers import (TOL, check_against_oracle, gpu_free_running, gpu_teacher_forced, log, make_model,
-                         oracle_record, rel_err, small_config)
+                         oracle_record, rel_err, small_config, step_rel_err)
 from oracle import LadderOracle, teacher_forced
 
 pytestmark = pytest.mark.gpu
@@ -225,3 +225,21 @@ def test_kernel_tracing_keeps_results_and_counts_launches(edge):
     m.free()
     for a, b in zip(plain, traced):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("B, T, max_seq, n_dec", [(2, 150, 256, 6), (1, 2100, 2200, 3)])
+def test_long_context_split_kv(edge, B, T, max_seq, n_dec):
+    """Decode attention over several key chunks (150 keys in 64-key chunks, merged across
+    chunks) and over chunks of several tiles (2100 keys: 32 chunks of two tiles)."""
+    cfg, w = edge
+    prompt = synth.gen_ids(B, T, cfg.vocab, seed=13)
+    cont = synth.gen_ids(B, n_dec, cfg.vocab, seed=13, stream=1)
+    log(f"edge long context B={B} T={T} max_seq={max_seq}")
+    ref = teacher_forced(LadderOracle(cfg, w), prompt, cont)
+    model = make_model(cfg, w, B, max_seq)
+    gl, gh, _ = gpu_teacher_forced(model, prompt, cont)
+    model.free()
+    el = step_rel_err(gl, ref.logits[:, T - 1:])
+    eh = step_rel_err(gh, ref.hidden[:, T - 1:])
+    log(f"edge long context: rel err logits {el:.3g} hidden {eh:.3g}")
+    assert el <= TOL["bf16"] and eh <= TOL["bf16"]
