@@ -36,14 +36,33 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int ldx, c
   const int m = blockIdx.x, tid = threadIdx.x;
   const float* xr = x + (size_t)m * ldx;
   float s = 0.f;
-  for (int i = tid; i < H; i += 256) s = fmaf(xr[i], xr[i], s);
+  if (H % 4 == 0 && ldx % 4 == 0) {              // 16-byte loads and stores
+    const int n4 = H / 4;
+    for (int i = tid; i < n4; i += 256) {
+      const float4 v = *(const float4*)(xr + 4 * i);
+      s = fmaf(v.x, v.x, s);
+      s = fmaf(v.y, v.y, s);
+      s = fmaf(v.z, v.z, s);
+      s = fmaf(v.w, v.w, s);
+    }
+  } else {
+    for (int i = tid; i < H; i += 256) s = fmaf(xr[i], xr[i], s);
+  }
   s = wave_sum(s);
   if ((tid & 63) == 0) part[tid >> 6] = s;
   __syncthreads();
   const float tot = part[0] + part[1] + part[2] + part[3];
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int i = tid; i < H; i += 256) {
-    out[(size_t)m * H + i] = xr[i] * inv * load_w<WT>(gain + i);
+  if (H % 4 == 0 && ldx % 4 == 0) {
+    const int n4 = H / 4;
+    for (int i = tid; i < n4; i += 256) {
+      const float4 v = *(const float4*)(xr + 4 * i);
+      *(float4*)(out + (size_t)m * H + 4 * i) =
+          make_float4(v.x * inv * load_w<WT>(gain + 4 * i), v.y * inv * load_w<WT>(gain + 4 * i + 1),
+                      v.z * inv * load_w<WT>(gain + 4 * i + 2), v.w * inv * load_w<WT>(gain + 4 * i + 3));
+    }
+  } else {
+    for (int i = tid; i < H; i += 256) out[(size_t)m * H + i] = xr[i] * inv * load_w<WT>(gain + i);
   }
 }
 

@@ -10,8 +10,10 @@
 // modules carries into the final residual.
 //
 // Tiling: a workgroup of 4 waves owns a 128x128 tile of C (2x2 waves of 64x64, i.e.
-// 4x4 MFMA tiles each) and walks K in steps of 32 through double-buffered LDS with
-// padded rows; the next step's global loads are in flight during the current MFMAs.
+// 4x4 MFMA tiles each; 64x64 tiles when 128x128 ones would leave CUs idle) and walks K
+// in steps of 32 through double-buffered LDS with padded rows; the next step's global
+// loads are in flight during the current MFMAs.  Optional epilogues: a residual add,
+// or SwiGLU over interleaved gate/up columns.
 // Workgroups are dealt to the 8 XCDs round robin, so the tile list (M fastest) is cut
 // into 8 contiguous runs and run x goes to XCD x: workgroups that share a weight tile
 // run together on one XCD and read it once into that XCD's L2.
@@ -32,27 +34,34 @@ __device__ __forceinline__ const WT* gemm_row(const RowSrc& s, int r, int K) {
   return (const WT*)s.m[2] + (size_t)(r - s.n1) * K;
 }
 
-constexpr int BM = 128, BN = 128, BK = 32, LDK = BK + 8;
+constexpr int BK = 32, LDK = BK + 8;
 constexpr int kXcds = 8;
 
+// TM x TN workgroup tile (128x128, or 64x64 when the big tiles would not fill the
+// device), 4 waves of (TM/2) x (TN/2), i.e. (TM/32) x (TN/32) MFMA tiles of 16x16 each.
+template <int TM, int TN>
 __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ah[2][BM][LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Al[2][BM][LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDK];
+  constexpr int FM = TM / 32, FN = TN / 32;       // MFMA tiles per wave
+  constexpr int AV = TM * BK / 4 / 256;           // float4 of A per thread per K step
+  constexpr int BV = TN * BK / 8 / 256;           // 16-byte W chunks per thread per K step
+  static_assert(AV >= 1 && BV >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t Ah[2][TM][LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Al[2][TM][LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TN][LDK];
   const int tile = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (tile >= n_tiles) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  const int m0 = (tile % n_tiles_m) * BM, n0 = (tile / n_tiles_m) * BN;
+  const int m0 = (tile % n_tiles_m) * TM, n0 = (tile / n_tiles_m) * TN;
   const float* A = (const float*)p.A;
 
-  // per K step a thread moves 4 float4 of A (rows c/8, columns 4*(c%8)) and 2 16-byte
+  // per K step a thread moves AV float4 of A (rows c/8, columns 4*(c%8)) and BV 16-byte
   // chunks of W (rows c/4, columns 8*(c%4))
-  const float* arow[4];
-  const uint16_t* brow[2];
-  int ar[4], ac[4], br[2], bc[2];
+  const float* arow[AV];
+  const uint16_t* brow[BV];
+  int ar[AV], ac[AV], br[BV], bc[BV];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < AV; ++i) {
     const int c = tid + 256 * i;
     ar[i] = c >> 3;
     ac[i] = (c & 7) * 4;
@@ -60,24 +69,24 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
     arow[i] = m < p.M ? A + (size_t)m * p.lda + ac[i] : nullptr;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < BV; ++i) {
     const int c = tid + 256 * i;
     br[i] = c >> 2;
     bc[i] = (c & 3) * 8;
     const int n = n0 + br[i];
     brow[i] = n < p.N ? gemm_row<uint16_t>(p.rows, n, p.K) + bc[i] : nullptr;
   }
-  float4 ra[4];
-  uint4 rb[2];
+  float4 ra[AV];
+  uint4 rb[BV];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = arow[i] ? *(const float4*)(arow[i] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < AV; ++i) ra[i] = arow[i] ? *(const float4*)(arow[i] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) rb[i] = brow[i] ? *(const uint4*)(brow[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < BV; ++i) rb[i] = brow[i] ? *(const uint4*)(brow[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < AV; ++i) {
       uint32_t h0, l0, h1, l1;
       split_h2(ra[i].x, ra[i].y, h0, l0);
       split_h2(ra[i].z, ra[i].w, h1, l1);
@@ -85,18 +94,14 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
       *(uint2*)&Al[buf][ar[i]][ac[i]] = make_uint2(l0, l1);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint4 w = rb[i];
-      *(uint4*)&Bs[buf][br[i]][bc[i]] =
-          bf16x8_to_f16x8(w);
-    }
+    for (int i = 0; i < BV; ++i) *(uint4*)&Bs[buf][br[i]][bc[i]] = bf16x8_to_f16x8(rb[i]);
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = p.K / BK;
   gload(0);
@@ -107,18 +112,18 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) gload((kt + 1) * BK);
-    half8 ah[4], al[4], b[4];
+    half8 ah[FM], al[FM], b[FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ah[i] = *(const half8*)&Ah[cur][wm * 64 + i * 16 + fr][fk];
-      al[i] = *(const half8*)&Al[cur][wm * 64 + i * 16 + fr][fk];
+    for (int i = 0; i < FM; ++i) {
+      ah[i] = *(const half8*)&Ah[cur][wm * (TM / 2) + i * 16 + fr][fk];
+      al[i] = *(const half8*)&Al[cur][wm * (TM / 2) + i * 16 + fr][fk];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *(const half8*)&Bs[cur][wn * 64 + j * 16 + fr][fk];
+    for (int j = 0; j < FN; ++j) b[j] = *(const half8*)&Bs[cur][wn * (TN / 2) + j * 16 + fr][fk];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < FN; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], b[j], acc[i][j], 0, 0, 0);
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], b[j], acc[i][j], 0, 0, 0);
       }
@@ -126,17 +131,22 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
     __syncthreads();
   }
 
-  // C fragment: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile
+  // C fragment: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile.
+  // SwiGLU: columns 2n (gate) and 2n+1 (up) sit in neighbouring lanes; the even lane
+  // writes a[row][n] = silu(gate) * up.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 64 + j * 16 + fr;
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn * (TN / 2) + j * 16 + fr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        if (row < p.M && col < p.N) {
-          float v = acc[i][j][r];
+        const int row = m0 + wm * (TM / 2) + i * 16 + (lane >> 4) * 4 + r;
+        float v = acc[i][j][r];
+        if (p.swiglu) {
+          const float up = __shfl_xor(v, 1, 64);
+          if (!(col & 1) && row < p.M && col < p.N) p.C[(size_t)row * p.ldc + (col >> 1)] = silu(v) * up;
+        } else if (row < p.M && col < p.N) {
           if (p.res) v = p.res[(size_t)row * p.ldr + col] + v;
           p.C[(size_t)row * p.ldc + col] = v;
         }
@@ -196,10 +206,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.M < 1 || p.N < 1 || p.K < 1) return hipErrorInvalidValue;
   if (p.wdtype == W_BF16) {
-    if (p.K % BK != 0 || p.lda % 4 != 0) return hipErrorInvalidValue;
-    const int tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
-    const int tiles = tm * tn, per = (tiles + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL(gemm_f16x2_kernel, dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per);
+    if (p.K % BK != 0 || p.lda % 4 != 0 || (p.swiglu && (p.N % 2 != 0 || p.res))) return hipErrorInvalidValue;
+    // 128x128 tiles when they give the device at least one round of work, else 64x64
+    const int big = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+    if (big >= 256) {
+      const int tm = (p.M + 127) / 128, tiles = big, per = (tiles + kXcds - 1) / kXcds;
+      hipLaunchKernelGGL((gemm_f16x2_kernel<128, 128>), dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per);
+    } else {
+      const int tm = (p.M + 63) / 64, tiles = tm * ((p.N + 63) / 64), per = (tiles + kXcds - 1) / kXcds;
+      hipLaunchKernelGGL((gemm_f16x2_kernel<64, 64>), dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per);
+    }
+  } else if (p.swiglu) {
+    return hipErrorInvalidValue;
   } else {
     dim3 grid((p.N + FT - 1) / FT, (p.M + FT - 1) / FT);
     hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, p);

@@ -120,7 +120,8 @@ struct AttnPrefillParams {
 hipError_t launch_attn_prefill(const AttnPrefillParams& p, hipStream_t s);
 
 // ----------------------------------------------------------------- GEMM (prefill)
-// C[M][N] (fp32, ldc) = (res ? res[M][N] : 0) + A[M][K] . B^T, B rows from RowSrc.
+// C[M][N] (fp32, ldc) = (res ? res[M][N] : 0) + A[M][K] . B^T, B rows from RowSrc; with
+// swiglu (bf16 models, N even, rows interleaved gate/up): C[M][N/2] = silu(c[2n]) * c[2n+1].
 struct GemmParams {
   int wdtype;                          // W_BF16: MFMA on fp16 pairs of A, W bf16 -> fp16; W_F32: VALU
   // A: fp32 [M][lda] (lda a multiple of 4 for bf16 models)
@@ -129,6 +130,7 @@ struct GemmParams {
   int M, N, K;
   float* C; int ldc;
   const float* res; int ldr;
+  int swiglu;
 };
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 

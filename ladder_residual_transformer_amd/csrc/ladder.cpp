@@ -564,10 +564,17 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
     gp.rows = RowSrc{{L.w_gate, L.w_up, nullptr}, 0, 0, 1};
     gp.N = 2 * g.ffn;
     gp.K = g.hidden;
-    gp.C = sc.gu;
-    gp.ldc = 2 * g.ffn;
-    HIPCHK(launch_gemm(gp, s));
-    HIPCHK(launch_swiglu(sc.gu, M, g.ffn, sc.ab, s));
+    if (ctx->wdt == W_BF16) {               // SwiGLU in the GEMM epilogue
+      gp.swiglu = 1;
+      gp.C = sc.ab;
+      gp.ldc = g.ffn;
+      HIPCHK(launch_gemm(gp, s));
+    } else {
+      gp.C = sc.gu;
+      gp.ldc = 2 * g.ffn;
+      HIPCHK(launch_gemm(gp, s));
+      HIPCHK(launch_swiglu(sc.gu, M, g.ffn, sc.ab, s));
+    }
     proj_in = sc.ab;
     proj_k = g.ffn;
     proj_w = L.w_down;
@@ -611,7 +618,7 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
 //            overwrite of X[(m+1) % 2] (x_{m-1}) after module m-1's last read of it.
 template <typename ModuleFn>
 ladder_status run_modules(ladder_ctx* ctx, float* const X[2], float* const OUT[2], size_t add_elems,
-                          ModuleFn&& module) {
+                          ModuleFn&& module, bool fused_adds = false) {
   const int NM = 2 * ctx->cfg.n_layers;
   const int sched = ctx->sched;
   if (sched == LADDER_SCHED_DUAL) {
@@ -625,7 +632,12 @@ ladder_status run_modules(ladder_ctx* ctx, float* const X[2], float* const OUT[2
     float* xn = X[(m + 1) % 2];
     hipStream_t s = module_stream(ctx, m);
     ladder_status st;
-    if (sched == LADDER_SCHED_SERIAL) {
+    if (sched == LADDER_SCHED_SERIAL && fused_adds) {
+      // module order, each output added by the producing kernel (the module has
+      // consumed its input before it writes x_{m+1}, which may share its buffer)
+      st = module(m, xin, xm, xn, nullptr, s, false, nullptr);
+      if (st) return st;
+    } else if (sched == LADDER_SCHED_SERIAL) {
       st = module(m, xin, xm, nullptr, OUT[m % 2], s, false, nullptr);
       if (st) return st;
       HIPCHK(launch_add(xm, OUT[m % 2], xn, add_elems, s));
@@ -1012,8 +1024,9 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
     auto mod = [&](int m, const float* xin, const float* xm, float* xn, float* store, hipStream_t s, bool wait,
                    hipEvent_t ev) { return prefill_module(ctx, m, B, Tc, sp, xin, xm, xn, store, s, wait, ev); };
     const int saved = ctx->sched;
-    if (saved == LADDER_SCHED_FUSED) ctx->sched = LADDER_SCHED_SERIAL;   // prefill: module order
-    st = run_modules(ctx, ctx->px, ctx->pout, (size_t)M * g.hidden, mod);
+    const bool fused = saved == LADDER_SCHED_FUSED;
+    if (fused) ctx->sched = LADDER_SCHED_SERIAL;   // prefill: module order, adds in the GEMMs
+    st = run_modules(ctx, ctx->px, ctx->pout, (size_t)M * g.hidden, mod, fused);
     ctx->sched = saved;
     if (st) return st;
     if (t0 + Tc == T) {
