@@ -25,19 +25,26 @@ if ROOT not in sys.path:
 METRIC = "decode tok/s + % HBM roofline, 70B-shape TP8 one-rank shard, batch 1"
 HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15      # FLOP/s, dense bf16
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qkv_gateup_70b_b1.json")
-KERNEL_SOURCES = ("ladder_residual_transformer_amd/csrc/gemv_rw.hip", "ladder_residual_transformer_amd/csrc/attn_decode.hpp",
-                  "ladder_residual_transformer_amd/csrc/common.hpp")
+CSRC = "ladder_residual_transformer_amd/csrc/"
+# the kernel each schedule's roofline reports: (trace kind, description, traffic file, sources)
+DOMINANT = {
+    "fused": ("qkv_gateup", "fused ladder launch [RMSNorm+QKV+RoPE+KV | RMSNorm+gate/up+SwiGLU]",
+              "traffic_qkv_gateup_70b_b1.json",
+              ("gemv_rw.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
+    "persistent": ("layer_stack", "persistent decode launch of the whole layer stack (every projection, "
+                   "attention and residual add of every layer)", "traffic_layer_stack_70b_b1.json",
+                   ("decode_step.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sha() -> str:
+def kernel_sha(sources) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    for rel in sources:
+        with open(os.path.join(ROOT, CSRC + rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -68,6 +75,20 @@ def qkv_gateup_bytes(cfg, B):
     q, kv = cfg.n_q_heads * hd, cfg.n_kv_heads * hd
     weights = (H * (q + 2 * kv) + 2 * F * H + 2 * H) * esz
     return weights + 2 * B * H * 4 + B * q * 4 + B * F * 4 + 2 * B * kv * esz
+
+
+def layer_stack_bytes(cfg, B, pos):
+    """Algorithmic bytes of the whole layer stack of one decode step at position pos:
+    every layer's weights and norm gains once, its KV rows 0..pos read and row pos
+    written, and per layer the two residual rows read and written, q, the attention
+    output and the SwiGLU output written once and read once."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    H, F, hd = cfg.hidden, cfg.ffn, cfg.head_dim
+    q, kv = cfg.n_q_heads * hd, cfg.n_kv_heads * hd
+    weights = (H * (q + 2 * kv) + q * H + 3 * F * H + 2 * H) * esz
+    kv_rows = 2 * B * kv * esz * (pos + 2)
+    acts = 4 * B * H * 4 + 2 * B * q * 4 * 2 + 2 * B * F * 4
+    return cfg.n_layers * (weights + kv_rows + acts)
 
 
 def cpu_baseline(cfg, w, prompt, sample_layers, steps):
@@ -117,7 +138,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="70b_tp8_shard")
     ap.add_argument("--batch", type=int, default=1)
-    ap.add_argument("--schedule", choices=("serial", "side", "dual", "fused"), default="fused")
+    ap.add_argument("--schedule", choices=("serial", "side", "dual", "fused", "persistent"), default="fused")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--prefill-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -161,7 +182,7 @@ def main():
     t = time.time()
     dw = DeviceWeights(w)
     model = LadderModel(cfg, dw, B, wl.max_seq)
-    sched = {"serial": 0, "side": 1, "dual": 2, "fused": 3}[args.schedule]
+    sched = {"serial": 0, "side": 1, "dual": 2, "fused": 3, "persistent": 4}[args.schedule]
     model.set_schedule(sched, not args.no_graph)
     torch.cuda.synchronize()
     log(f"[bench] uploaded weights and built the context in {time.time() - t:.1f} s "
@@ -211,16 +232,18 @@ def main():
     log(f"[bench] decode {args.steps} steps: {dt * 1e3 / args.steps:.3f} ms/step (events {gpu_ms / args.steps:.3f}), "
         f"{tok_s:.1f} tok/s, {total_bytes / args.steps / 1e9:.2f} GB/step, {100 * hbm_frac:.1f}% of HBM peak")
 
-    # ---- the dominant kernel, measured live: the same K decode steps again, each fused
-    # [QKV | gate/up] launch (~80% of the step's bytes) with a pair of HIP events on the
-    # stream it runs on, taken from its dispatch's own begin/end timestamps (traced steps
-    # are launched eagerly)
-    model.trace_kernel("qkv_gateup")
+    # ---- the dominant kernel, measured live: the same K decode steps again, each launch
+    # of that kernel with a pair of HIP events on the stream it runs on, taken from its
+    # dispatch's own begin/end timestamps (traced steps are launched eagerly).  Fused
+    # schedule: the [QKV | gate/up] launch of every layer (~80% of the step's bytes);
+    # persistent schedule: the one launch of the whole layer stack.
+    kind, kdesc, tfile, ksrc = DOMINANT["persistent" if args.schedule == "persistent" else "fused"]
+    model.trace_kernel(kind)
     bufs[0].copy_(first)
     model.decode_step(bufs[0], P, out=(None, bufs[1], None))
     torch.cuda.synchronize()
     cur = bufs[0]
-    tot_us, n_launch = 0.0, 0
+    tot_us, n_launch, tot_bytes = 0.0, 0, 0
     t0 = time.perf_counter()
     for k in range(args.steps):
         model.decode_step(cur, P + k, out=(None, bufs[(k + 1) % 2], None))
@@ -228,19 +251,21 @@ def main():
         us, n = model.trace_result()                # waits for the step
         tot_us += us * n
         n_launch += n
+        tot_bytes += n * (layer_stack_bytes(cfg, B, P + k) if kind == "layer_stack" else qkv_gateup_bytes(cfg, B))
     torch.cuda.synchronize()
     dt_traced = time.perf_counter() - t0
     us_launch = tot_us / n_launch
+    bytes_launch = tot_bytes / n_launch
     model.trace_kernel(None)
-    gu_bytes = qkv_gateup_bytes(cfg, B)
-    achieved = gu_bytes / (us_launch * 1e-6) / 1e9
-    log(f"[bench] traced decode: {dt_traced * 1e3 / args.steps:.3f} ms/step (read out per step); fused [QKV | gate/up] "
+    achieved = bytes_launch / (us_launch * 1e-6) / 1e9
+    log(f"[bench] traced decode: {dt_traced * 1e3 / args.steps:.3f} ms/step (read out per step); {kind} "
         f"launch {us_launch:.2f} us mean over {n_launch} launches, {achieved:.0f} GB/s")
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    tpath = os.path.join(ROOT, "profiles", tfile)
+    if os.path.exists(tpath):
+        with open(tpath) as f:
             tr = json.load(f)
-        if tr.get("kernel_sha") == kernel_sha() and tr.get("batch") == B and tr.get("workload") == cfg.name:
+        if tr.get("kernel_sha") == kernel_sha(ksrc) and tr.get("batch") == B and tr.get("workload") == cfg.name:
             traffic = tr.get("bytes_per_launch")
 
     # every kernel kind replayed in isolation (diagnostic)
@@ -264,10 +289,10 @@ def main():
         "decode_bytes_per_step": total_bytes // args.steps,
         "prefill_tok_s": round(B * P / prefill_s, 1),
         "prefill_mfma_frac": round(pflops / prefill_s / MFMA_BF16_PEAK, 4),
-        "roofline": {"bound": "hbm", "kernel": "fused ladder launch [RMSNorm+QKV+RoPE+KV | RMSNorm+gate/up+SwiGLU]",
+        "roofline": {"bound": "hbm", "kernel": kdesc,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": traffic,
-                     "bytes_per_launch": gu_bytes, "us_per_launch": round(us_launch, 3),
+                     "bytes_per_launch": int(bytes_launch), "us_per_launch": round(us_launch, 3),
                      "launches_timed": n_launch, "traced_ms_per_step": round(dt_traced * 1e3 / args.steps, 4)},
         "kernels_us_isolated": {k: round(v, 3) for k, v in ku.items()},
         "cpu_baseline": cpu,

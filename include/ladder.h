@@ -59,7 +59,7 @@ typedef int32_t ladder_status;
 #define LADDER_F32 0             /* weights and KV cache fp32 */
 #define LADDER_BF16 1            /* weights and KV cache bf16; residual and accumulation fp32 */
 
-/* Execution schedule of the module loop.  All three give bitwise identical results. */
+/* Execution schedule of the module loop.  All give bitwise identical results. */
 #define LADDER_SCHED_SERIAL 0    /* one stream, modules and residual adds in program order */
 #define LADDER_SCHED_SIDE 1      /* residual adds on a side stream: module m+1 starts on its
                                     stale input while x_{m+1} = x_m + out_m completes */
@@ -71,6 +71,9 @@ typedef int32_t ladder_status;
                                     x_{2l-1} and x_{2l}), [attention | down projection] in
                                     one launch, then the O projection adds both residual
                                     updates (default) */
+#define LADDER_SCHED_PERSISTENT 4 /* decode: the whole layer stack in one launch of resident
+                                    workgroups that signal each other (every layer ladder,
+                                    bf16, batch <= 4; otherwise as FUSED); prefill as FUSED */
 
 typedef struct ladder_config {
   int32_t n_layers;
@@ -165,7 +168,10 @@ ladder_status ladder_sync(ladder_ctx* ctx);
                                        the O projection + both residual adds */
 #define LADDER_KERNEL_OPROJ_ADD2 8  /* fused ladder launch: O projection + both residual adds (three-
                                        launch layers only) */
-#define LADDER_N_KERNELS 9
+#define LADDER_KERNEL_LAYER_STACK 9  /* persistent launch of a decode step's whole layer stack
+                                        (LADDER_SCHED_PERSISTENT); ladder_time_kernels stores
+                                        -1 where that launch is not available */
+#define LADDER_N_KERNELS 10
 
 /* Profiling aid.  For each kernel kind, enqueue it on the context's stream exactly as
  * a decode step at batch B launches it (once per layer; the LM head once), reps times,

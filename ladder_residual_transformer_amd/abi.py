@@ -30,12 +30,15 @@ LADDER_SCHED_SERIAL = 0
 LADDER_SCHED_SIDE = 1
 LADDER_SCHED_DUAL = 2
 LADDER_SCHED_FUSED = 3
+LADDER_SCHED_PERSISTENT = 4
 
 EXPORTED = ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_filled",
             "ladder_workspace_bytes", "ladder_sync", "ladder_free", "ladder_status_string", "ladder_last_error",
             "ladder_time_kernels", "ladder_trace_kernel", "ladder_trace_result")
 
-KERNEL_KINDS = ("qkv", "attn", "oproj", "gateup", "down", "lmhead", "qkv_gateup", "attn_down", "oproj_add2")
+LADDER_KERNEL_LAYER_STACK = 9
+LADDER_N_KERNELS = 10
+KERNEL_KINDS = ("qkv", "attn", "oproj", "gateup", "down", "lmhead", "qkv_gateup", "attn_down", "oproj_add2", "layer_stack")
 
 
 class ladder_config(ctypes.Structure):

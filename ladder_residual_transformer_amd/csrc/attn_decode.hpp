@@ -81,7 +81,9 @@ __host__ __device__ constexpr int attn_hpw(int G) { return G <= 4 ? 1 : (G <= 8 
 template <int HD> constexpr size_t attn_rec() { return HD + 4; }
 
 // Ticket and merge, after this workgroup has written its records (G heads of one chunk).
-template <int HD, typename Lds>
+// COH: records, output and signal use coherent accesses (no cache write-back or
+// invalidate is needed).
+template <int HD, bool COH = false, typename Lds>
 __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, int n_act, Lds& L) {
   const int tid = threadIdx.x;
   const size_t stride = attn_rec<HD>();
@@ -90,9 +92,9 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
   __syncthreads();
   int* counter = p.counters + (size_t)b * p.nkv + kvh;
   if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (!COH) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const bool last = atomicAdd(counter, 1) == n_act - 1;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (!COH && last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     L.is_last = last;
   }
   __syncthreads();
@@ -108,13 +110,16 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
     const int i = min(tid, n_items - 1), h = i / (HD / 4), d4 = (i % (HD / 4)) * 4;
     const float* src = base + (size_t)h * p.n_split * stride + 4 + d4;
 #pragma unroll
-    for (int q = 0; q < QG; ++q) a0[q] = *(const float4*)(src + (size_t)min(q, n_act - 1) * stride);
+    for (int q = 0; q < QG; ++q) {
+      const float* rec = src + (size_t)min(q, n_act - 1) * stride;
+      a0[q] = COH ? ld_coh4(rec) : *(const float4*)rec;
+    }
   }
   for (int i = tid; i < G * n_act; i += 256) {
     const int h = i / n_act, q = i % n_act;
-    const float2 ml = *(const float2*)(base + ((size_t)h * p.n_split + q) * stride);
-    L.wsc[h][q] = ml.x;
-    L.lsc[h][q] = ml.y;
+    const float* rec = base + ((size_t)h * p.n_split + q) * stride;
+    L.wsc[h][q] = COH ? ld_coh(rec) : rec[0];
+    L.lsc[h][q] = COH ? ld_coh(rec + 1) : rec[1];
   }
   __syncthreads();
   if (tid < G) {
@@ -136,7 +141,10 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
     for (int q0 = 0; q0 < n_act; q0 += QG) {
       if (i != tid || q0 > 0) {
 #pragma unroll
-        for (int q = 0; q < QG; ++q) a0[q] = *(const float4*)(src + (size_t)min(q0 + q, n_act - 1) * stride);
+        for (int q = 0; q < QG; ++q) {
+          const float* rec = src + (size_t)min(q0 + q, n_act - 1) * stride;
+          a0[q] = COH ? ld_coh4(rec) : *(const float4*)rec;
+        }
       }
 #pragma unroll
       for (int q = 0; q < QG; ++q) {
@@ -148,12 +156,20 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
       }
     }
     const float li = L.linv[h];
-    *(float4*)(p.out + (size_t)b * p.nq * HD + (size_t)(kvh * G + h) * HD + d4) =
-        make_float4(o.x * li, o.y * li, o.z * li, o.w * li);
+    float* dst = p.out + (size_t)b * p.nq * HD + (size_t)(kvh * G + h) * HD + d4;
+    const float4 r = make_float4(o.x * li, o.y * li, o.z * li, o.w * li);
+    if (COH) st_coh4(dst, r);
+    else *(float4*)dst = r;
   }
-  if (tid == 0) *counter = 0;
+  if (tid == 0) {
+    if (COH) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *counter = 0;
+  }
   // completion signal: the last of the B*nkv merges publishes the step's epoch
-  if (p.done_flag) wg_signal(p.done_cnt, p.done_flag, p.B * p.nkv, *p.d_epoch);
+  if (p.done_flag) {
+    if (COH) wg_arrive_coh(p.done_cnt, p.done_flag, p.B * p.nkv, *p.d_epoch);
+    else wg_signal(p.done_cnt, p.done_flag, p.B * p.nkv, *p.d_epoch);
+  }
 }
 
 // ----------------------------------------------------------------- bf16 (MFMA)
@@ -161,7 +177,7 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
 // MFMA 16x16x32 f16: lane l supplies A row l%16 and B column l%16 with k-slots
 // 8*(l/16) .. +8; 16x16x16 f16: the same rows/columns with k-slots 4*(l/16) .. +4.  The
 // result holds column l%16, rows 4*(l/16) + i, i = 0..3.
-template <int HD>
+template <int HD, bool COH = false>
 __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnLds<uint16_t, HD>& L) {
   constexpr int T = kAttnKeyTile;
   constexpr int CPR = HD / 8;                  // 16-byte chunks per K/V row
@@ -187,20 +203,30 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
   const uint16_t* kc = (const uint16_t*)p.k_cache + kv_base;
   const uint16_t* vc = (const uint16_t*)p.v_cache + kv_base;
 
-  // tile loads; rows past the chunk end repeat its last key (masked, weight 0)
+  // tile loads; rows past the chunk end repeat its last key (masked, weight 0).  COH: the
+  // newest row (position len-1) was written in this kernel and is read coherently (q is
+  // read with ordinary loads: its producer gives it an address of its own per layer).
   uint4 kr[KCH], vr[VPAIR][2];
+  auto ld_row = [&](const uint16_t* base, int r, int c) -> uint4 {
+    const uint16_t* a = base + (size_t)r * HD + c;
+    if (COH && r == len - 1) {
+      const uint32_t* w = (const uint32_t*)a;
+      return make_uint4(ld_coh(w), ld_coh(w + 1), ld_coh(w + 2), ld_coh(w + 3));
+    }
+    return *(const uint4*)a;
+  };
   auto load_tile = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int e = tid + 256 * i, r = min(t0 + e / CPR, end - 1), c = (e % CPR) * 8;
-      kr[i] = *(const uint4*)(kc + (size_t)r * HD + c);
+      kr[i] = ld_row(kc, r, c);
     }
 #pragma unroll
     for (int i = 0; i < VPAIR; ++i) {
       const int e = tid + 256 * i, j = e / CPR, c = (e % CPR) * 8;
       const int r0 = min(t0 + 2 * j, end - 1), r1 = min(t0 + 2 * j + 1, end - 1);
-      vr[i][0] = *(const uint4*)(vc + (size_t)r0 * HD + c);
-      vr[i][1] = *(const uint4*)(vc + (size_t)r1 * HD + c);
+      vr[i][0] = ld_row(vc, r0, c);
+      vr[i][1] = ld_row(vc, r1, c);
     }
   };
   load_tile(start);
@@ -310,12 +336,19 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
   if (col < G) {
     float* dst = p.part + (((size_t)b * p.nq + kvh * G + col) * p.n_split + s) * attn_rec<HD>();
 #pragma unroll
-    for (int d = 0; d < NDB; ++d)
-      *(float4*)(dst + 4 + w * DPW + 16 * d + 4 * grp) = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
+    for (int d = 0; d < NDB; ++d) {
+      const float4 v = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
+      if (COH) st_coh4(dst + 4 + w * DPW + 16 * d + 4 * grp, v);
+      else *(float4*)(dst + 4 + w * DPW + 16 * d + 4 * grp) = v;
+    }
     // the record's max is in the merge's units, score / sqrt(hd) (m_run is a raw score)
-    if (w == 0 && grp == 0) { dst[0] = m_run * (1.0f / sqrtf((float)HD)); dst[1] = l_run; }
+    if (w == 0 && grp == 0) {
+      const float mr = m_run * (1.0f / sqrtf((float)HD));
+      if (COH) { st_coh(dst, mr); st_coh(dst + 1, l_run); }
+      else { dst[0] = mr; dst[1] = l_run; }
+    }
   }
-  attn_finish<HD>(p, b, kvh, G, n_act, L);
+  attn_finish<HD, COH>(p, b, kvh, G, n_act, L);
 }
 
 // ----------------------------------------------------------------- fp32 (VALU)

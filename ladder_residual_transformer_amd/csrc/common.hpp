@@ -85,16 +85,103 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& v) {
                     pack_h2(bf16_lo(v.z), bf16_hi(v.z)), pack_h2(bf16_lo(v.w), bf16_hi(v.w)));
 }
 
+__device__ __forceinline__ void wave_stores_done_fwd() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xF70);               // vmcnt(0): this wave's stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Coherent (agent-scope) accesses for data that one workgroup writes and another reads
+// within a kernel: they bypass the per-XCD caches, so publishing them needs no L2
+// write-back, only that the stores have completed.
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_coh(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 ld_coh4(const float* p) {
+  return make_float4(ld_coh(p), ld_coh(p + 1), ld_coh(p + 2), ld_coh(p + 3));
+}
+__device__ __forceinline__ void st_coh4(float* p, float4 v) {
+  st_coh(p, v.x); st_coh(p + 1, v.y); st_coh(p + 2, v.z); st_coh(p + 3, v.w);
+}
+
+// Arrival of a workgroup whose cross-workgroup writes were all coherent stores: once
+// every wave's stores have completed it counts itself; the last of `total` resets the
+// count and publishes `epoch` in *flag.
+__device__ __forceinline__ void wg_arrive_coh(int* cnt, int* flag, int total, int epoch) {
+  wave_stores_done_fwd();
+  __syncthreads();
+  if (threadIdx.x == 0 && atomicAdd(cnt, 1) == total - 1) {
+    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Wait (one thread polls, bounded) until *flag == epoch; the data behind it is read with
+// coherent loads, so no invalidate is needed.  A poll that gives up sets *err.
+__device__ __forceinline__ void wg_wait_coh(const int* flag, int epoch, int* err) {
+  if (threadIdx.x == 0) {
+    unsigned spins = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins == (1u << 19)) {          // far beyond any real wait
+        atomicOr(err, 1);
+        break;
+      }
+      // another wait already gave up: the results are void, so do not wait again
+      if ((spins & 1023u) == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+    }
+  }
+  __syncthreads();
+}
+
+// Progress words: every producer workgroup owns one 32-bit word and stores a code that
+// only grows (step epoch, layer, phase) when it has finished a phase; "all producers
+// passed phase X" is min over the words >= code(X).  Unlike one shared counter, the
+// producers' updates are independent stores, so none waits behind the others' atomics.
+__device__ __forceinline__ void prog_publish(uint32_t* word, uint32_t code) {
+  wave_stores_done_fwd();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(word, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every word of prog[0..n) has reached `code` (wrap-safe comparison); the
+// whole workgroup polls, one word per thread and round.  Bounded: after 2^16 rounds it
+// sets *err and returns; it also returns once another wait has set *err.  Every exit is
+// taken by the whole workgroup together.
+__device__ __forceinline__ void prog_wait(const uint32_t* prog, int n, uint32_t code, int* err) {
+  unsigned rounds = 0;
+  for (;;) {
+    int ok = 1;
+    for (int i = threadIdx.x; i < n; i += blockDim.x)
+      ok &= (int)(__hip_atomic_load(prog + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - code) >= 0;
+    if (__syncthreads_and(ok)) return;
+    if ((++rounds & 255u) == 0) {
+      int bail = rounds >= (1u << 16);
+      if (threadIdx.x == 0) {
+        if (bail) atomicOr(err, 1);
+        else bail = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+      }
+      if (__syncthreads_or(bail)) return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // Cross-workgroup synchronisation inside one kernel, with one L2 write-back or
 // invalidate per workgroup (not one per wave): every wave first waits for its own global
 // stores to complete (they are then in its XCD's L2), the workgroup meets at a barrier,
 // and one thread performs the agent-scope release (L2 write-back) or acquire (L1/L2
 // invalidate) for all of them.
-__device__ __forceinline__ void wave_stores_done() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xF70);               // vmcnt(0): this wave's stores have completed
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
+__device__ __forceinline__ void wave_stores_done() { wave_stores_done_fwd(); }
 
 // A producer workgroup, after its writes, counts itself; the last of `total` publishes
 // the step's epoch in *flag.

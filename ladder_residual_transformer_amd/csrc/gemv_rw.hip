@@ -16,315 +16,9 @@
 // residuals a layer's QKV and gate/up projections read x_{2l-1} and x_{2l}, which are
 // both ready before the layer starts, and the down projection does not depend on the
 // attention, so each pair runs side by side in one kernel.
-#include <climits>
-
-#include "attn_decode.hpp"
-#include "common.hpp"
-#include "kernels.h"
+#include "gemv_rw.hpp"
 
 namespace ladder {
-
-template <typename WT>
-__device__ __forceinline__ const WT* rw_row_ptr(const RowSrc& s, int r, int K) {
-  if (s.interleave) return (const WT*)s.m[r & 1] + (size_t)(r >> 1) * K;
-  if (r < s.n0) return (const WT*)s.m[0] + (size_t)r * K;
-  if (r < s.n1) return (const WT*)s.m[1] + (size_t)(r - s.n0) * K;
-  return (const WT*)s.m[2] + (size_t)(r - s.n1) * K;
-}
-
-// Epilogue of one row pair (rows n0 = 2*pair, n0+1) for batch row b.
-template <typename WT>
-__device__ __forceinline__ void rw_epilogue(const GemvParams& p, int pair, int b, float y0, float y1, float inv,
-                                            float& best, int& bidx) {
-  const int n0 = 2 * pair, n1 = n0 + 1;
-  const bool v1 = n1 < p.N;
-  switch (p.epi) {
-    case EPI_STORE:
-    case EPI_LOGITS: {
-      y0 *= inv;
-      y1 *= inv;
-      p.out[(size_t)b * p.ldo + n0] = y0;
-      if (v1) p.out[(size_t)b * p.ldo + n1] = y1;
-      if (p.epi == EPI_LOGITS) {
-        if (y0 > best) { best = y0; bidx = n0; }
-        if (v1 && y1 > best) { best = y1; bidx = n1; }
-      }
-      break;
-    }
-    case EPI_ADD: {
-      p.out[(size_t)b * p.ldo + n0] = p.xres[(size_t)b * p.ldr + n0] + y0 * inv;
-      if (v1) p.out[(size_t)b * p.ldo + n1] = p.xres[(size_t)b * p.ldr + n1] + y1 * inv;
-      break;
-    }
-    case EPI_ADD2: {
-      const float t0 = p.xres[(size_t)b * p.ldr + n0] + y0 * inv;
-      p.out[(size_t)b * p.ldo + n0] = t0;
-      p.out2[(size_t)b * p.ldo + n0] = t0 + p.add2[(size_t)b * p.ldo + n0];
-      if (v1) {
-        const float t1 = p.xres[(size_t)b * p.ldr + n1] + y1 * inv;
-        p.out[(size_t)b * p.ldo + n1] = t1;
-        p.out2[(size_t)b * p.ldo + n1] = t1 + p.add2[(size_t)b * p.ldo + n1];
-      }
-      break;
-    }
-    case EPI_GATEUP_SWIGLU:
-      p.out[(size_t)b * p.ldo + pair] = silu(y0 * inv) * (y1 * inv);
-      break;
-    case EPI_QKV_ROPE: {
-      y0 *= inv;
-      y1 *= inv;
-      const int pos = *p.d_pos;
-      if (n0 < p.q_rows + p.kv_rows) {              // q or k: rotate the adjacent pair
-        const int d = (n0 < p.q_rows ? n0 : n0 - p.q_rows) % p.head_dim;
-        const int half = p.head_dim >> 1;
-        const float c = p.rope_cos[(size_t)pos * half + (d >> 1)];
-        const float s = p.rope_sin[(size_t)pos * half + (d >> 1)];
-        const float r0 = y0 * c - y1 * s;
-        const float r1 = y0 * s + y1 * c;
-        y0 = r0;
-        y1 = r1;
-      }
-      if (n0 < p.q_rows) {
-        p.out[(size_t)b * p.ldo + n0] = y0;
-        p.out[(size_t)b * p.ldo + n1] = y1;
-      } else {
-        const bool isk = n0 < p.q_rows + p.kv_rows;
-        const int rr = isk ? n0 - p.q_rows : n0 - p.q_rows - p.kv_rows;
-        const int kvh = rr / p.head_dim, d = rr % p.head_dim;
-        WT* cache = (WT*)(isk ? p.k_cache : p.v_cache);
-        const size_t off = (((size_t)b * p.n_kv + kvh) * p.max_seq + pos) * p.head_dim + d;
-        store_w<WT>(cache + off, y0);
-        store_w<WT>(cache + off + 1, y1);
-      }
-      break;
-    }
-    default:
-      break;
-  }
-}
-
-struct RwShared {
-  float sqw[4][4];
-  float inv[4];
-  float wbv[4][4];
-  int wbi[4][4];
-};
-
-// where a pass puts its rows
-enum { RW_OUT_EPI = 0, RW_OUT_LDS = 1, RW_OUT_ADD2_LDS = 2 };
-
-// One pass of the row-wave GEMV over row pairs [pr0, pr1) of problem p (this
-// workgroup's share).  OUT: the problem's own epilogue; the rows (times inv_rms) into
-// dres[row - 2*pr0][b]; or EPI_ADD2 with dres in place of add2.  wait_flag: the first
-// weight unit is issued, then the workgroup waits for the signal before it stages the
-// input.
-template <typename WT, int BT, int VPL, int OUT>
-__device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, int lb, float* u, float* dres,
-                                        const int* wait_flag, int wait_epoch, int* err, RwShared& sh) {
-  constexpr int VEC = Vec<WT>::N;
-  constexpr int CHUNK = 64 * VPL;                 // vectors of a row one wave covers per step
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int K = p.K, B = p.B;
-  const int nvec = K / VEC;
-  const int nchunk = (nvec + CHUNK - 1) / CHUNK;
-
-  // This wave's work is a sequence of units: unit i is chunk (i % nchunk) of its pair
-  // number (i / nchunk); its pairs are pr0 + wid, pr0 + wid + 4, ...  Two register
-  // buffers form a pipeline: the loads of unit i+1 are in flight while unit i is
-  // multiplied.  Loads are unconditional (addresses clamped into the matrix) so that no
-  // branch separates a load from its use; lanes past the end of a row read the zero
-  // pad of u instead, and a missing odd row is discarded by the epilogue.
-  const int my_pairs = pr1 > pr0 + wid ? (pr1 - pr0 - wid + 3) / 4 : 0;
-  const int n_units = my_pairs * nchunk;
-  uint4 wa[2][VPL], wb[2][VPL];
-  auto load_unit = [&](uint4 (&w)[2][VPL], int unit) {
-    const int pair = pr0 + wid + 4 * (unit / nchunk), c = unit % nchunk;
-    const int n0 = 2 * pair;
-    const WT* r0 = rw_row_ptr<WT>(p.rows, n0, K);
-    const WT* r1 = rw_row_ptr<WT>(p.rows, min(n0 + 1, p.N - 1), K);
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int vi = min(c * CHUNK + lane + 64 * v, nvec - 1);
-      w[0][v] = *(const uint4*)(r0 + (size_t)vi * VEC);
-      w[1][v] = *(const uint4*)(r1 + (size_t)vi * VEC);
-    }
-  };
-  const int ustride = K + VEC;                     // u rows carry a zero pad of VEC floats
-
-  if (wait_flag) {
-    if (n_units > 0) load_unit(wa, 0);
-    wg_wait(wait_flag, wait_epoch, err);
-  }
-  // ---- prologue: u = x (* g) for every batch row, and inv_rms.  For one batch row
-  // and K <= 256*4*VEC the input loads are issued before the first weight unit, so the
-  // in-order completion of loads does not make the prologue wait for the weights.
-  const bool norm = p.gain != nullptr;
-  if (tid < B * VEC) u[(tid / VEC) * ustride + K + tid % VEC] = 0.f;
-  if (BT == 1 && nvec <= 256 * 4) {
-    float4 xr[4][VEC / 4];
-    uint4 gr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = min(tid + 256 * i, nvec - 1);
-#pragma unroll
-      for (int e = 0; e < VEC / 4; ++e) xr[i][e] = *(const float4*)(p.x + (size_t)v * VEC + 4 * e);
-      gr[i] = norm ? *(const uint4*)((const WT*)p.gain + (size_t)v * VEC) : make_uint4(0u, 0u, 0u, 0u);
-    }
-    if (!wait_flag && n_units > 0) load_unit(wa, 0);
-    float sq = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = tid + 256 * i;
-      if (v < nvec) {
-        float xv[VEC], g[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC / 4; ++e) {
-          xv[4 * e] = xr[i][e].x; xv[4 * e + 1] = xr[i][e].y; xv[4 * e + 2] = xr[i][e].z; xv[4 * e + 3] = xr[i][e].w;
-        }
-        if (norm) {
-          unpack16(gr[i], g);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            sq = fmaf(xv[e], xv[e], sq);
-            xv[e] *= g[e];
-          }
-        }
-        float* up = u + (size_t)v * VEC;
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4) *(float4*)(up + e) = make_float4(xv[e], xv[e + 1], xv[e + 2], xv[e + 3]);
-      }
-    }
-    sq = wave_sum(sq);
-    if (lane == 0) sh.sqw[wid][0] = sq;
-  } else {
-    if (!wait_flag && n_units > 0) load_unit(wa, 0);
-    for (int b = 0; b < BT; ++b) {
-      float sq = 0.f;
-      if (b < B) {
-        for (int v = tid; v < nvec; v += 256) {
-          const float* xp = p.x + (size_t)b * p.ldx + (size_t)v * VEC;
-          float xv[VEC];
-#pragma unroll
-          for (int e = 0; e < VEC; e += 4) {
-            const float4 t = *(const float4*)(xp + e);
-            xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
-          }
-          if (norm) {
-            float g[VEC];
-            unpack16(*(const uint4*)((const WT*)p.gain + (size_t)v * VEC), g);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              sq = fmaf(xv[e], xv[e], sq);
-              xv[e] *= g[e];
-            }
-          }
-          float* up = u + (size_t)b * ustride + (size_t)v * VEC;
-#pragma unroll
-          for (int e = 0; e < VEC; e += 4) *(float4*)(up + e) = make_float4(xv[e], xv[e + 1], xv[e + 2], xv[e + 3]);
-        }
-      }
-      sq = wave_sum(sq);
-      if (lane == 0) sh.sqw[wid][b] = sq;
-    }
-  }
-  __syncthreads();
-  if (tid < BT) {
-    const float t = ((sh.sqw[0][tid] + sh.sqw[1][tid]) + sh.sqw[2][tid]) + sh.sqw[3][tid];
-    sh.inv[tid] = norm ? 1.0f / sqrtf(t / (float)K + p.eps) : 1.0f;
-  }
-  __syncthreads();
-  float inv_b[BT];
-#pragma unroll
-  for (int b = 0; b < BT; ++b) inv_b[b] = sh.inv[b];
-
-  // ---- row pairs
-  float best = -INFINITY;
-  int bidx = INT_MAX;
-  float acc[2][BT];
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
-  auto compute_unit = [&](const uint4 (&w)[2][VPL], int unit) {
-    const int c = unit % nchunk;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int vi = c * CHUNK + lane + 64 * v;
-      const int ui = (vi < nvec ? vi : nvec) * VEC;    // past the row end: the zero pad
-      float w0[VEC], w1[VEC];
-      unpack16(w[0][v], w0);
-      unpack16(w[1][v], w1);
-#pragma unroll
-      for (int b = 0; b < BT; ++b) {
-        if (b < B) {
-          const float* up = u + (size_t)b * ustride + ui;
-          float uv[VEC];
-#pragma unroll
-          for (int e = 0; e < VEC; e += 4) {
-            const float4 t = *(const float4*)(up + e);
-            uv[e] = t.x; uv[e + 1] = t.y; uv[e + 2] = t.z; uv[e + 3] = t.w;
-          }
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            acc[0][b] = fmaf(w0[e], uv[e], acc[0][b]);
-            acc[1][b] = fmaf(w1[e], uv[e], acc[1][b]);
-          }
-        }
-      }
-    }
-    if (c == nchunk - 1) {                      // pair complete: reduce and finish it
-      const int pair = pr0 + wid + 4 * (unit / nchunk);
-#pragma unroll
-      for (int b = 0; b < BT; ++b) {
-        const float y0 = wave_sum(acc[0][b]);
-        const float y1 = wave_sum(acc[1][b]);
-        if (lane == b && b < B) {
-          if constexpr (OUT == RW_OUT_EPI) {
-            rw_epilogue<WT>(p, pair, b, y0, y1, inv_b[b], best, bidx);
-          } else if constexpr (OUT == RW_OUT_LDS) {
-            const int r = 2 * (pair - pr0);
-            dres[r * BT + b] = y0 * inv_b[b];
-            dres[(r + 1) * BT + b] = y1 * inv_b[b];
-          } else {                              // EPI_ADD2, second addend from dres
-            const int r = 2 * (pair - pr0), n0 = 2 * pair;
-            const float t0 = p.xres[(size_t)b * p.ldr + n0] + y0 * inv_b[b];
-            p.out[(size_t)b * p.ldo + n0] = t0;
-            p.out2[(size_t)b * p.ldo + n0] = t0 + dres[r * BT + b];
-            if (n0 + 1 < p.N) {
-              const float t1 = p.xres[(size_t)b * p.ldr + n0 + 1] + y1 * inv_b[b];
-              p.out[(size_t)b * p.ldo + n0 + 1] = t1;
-              p.out2[(size_t)b * p.ldo + n0 + 1] = t1 + dres[(r + 1) * BT + b];
-            }
-          }
-        }
-        acc[0][b] = 0.f;
-        acc[1][b] = 0.f;
-      }
-    }
-  };
-  for (int i = 0; i < n_units; i += 2) {
-    if (i + 1 < n_units) load_unit(wb, i + 1);
-    compute_unit(wa, i);
-    if (i + 1 < n_units) {
-      if (i + 2 < n_units) load_unit(wa, i + 2);
-      compute_unit(wb, i + 1);
-    }
-  }
-
-  if (OUT == RW_OUT_EPI && p.epi == EPI_LOGITS) {
-    // per-block greedy candidate (lowest index among equal maxima); merged by argmax_finalize
-    if (lane < BT) { sh.wbv[wid][lane] = best; sh.wbi[wid][lane] = bidx; }
-    __syncthreads();
-    if (tid < BT) {
-      float bb = sh.wbv[0][tid];
-      int ii = sh.wbi[0][tid];
-      for (int q = 1; q < 4; ++q)
-        if (sh.wbv[q][tid] > bb || (sh.wbv[q][tid] == bb && sh.wbi[q][tid] < ii)) { bb = sh.wbv[q][tid]; ii = sh.wbi[q][tid]; }
-      p.best_val[(size_t)lb * BT + tid] = bb;
-      p.best_idx[(size_t)lb * BT + tid] = ii;
-    }
-  }
-}
 
 // NP: GEMV problems of the launch: 1, 2 (side by side), or 3 = the paired launch (rows
 // of prob[0], then after the signal the same rows of prob[1]).  With HDA != 0 the first
@@ -348,9 +42,13 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
     const int pr1 = (int)((long long)(blk + 1) * P / nb);
     float* dres = reinterpret_cast<float*>(lds_raw + mp.dres_off);
     const int epoch = *mp.d_epoch;
-    rw_pass<WT, BT, VPL, RW_OUT_LDS>(mp.prob[0], pr0, pr1, blk, u, dres, nullptr, 0, nullptr, sh);
+    rw_pass<WT, BT, VPL, RW_OUT_LDS>(mp.prob[0], pr0, pr1, blk, u, dres, RwWait{}, sh);
     __syncthreads();                               // u is restaged by the second pass
-    rw_pass<WT, BT, VPL, RW_OUT_ADD2_LDS>(mp.prob[1], pr0, pr1, blk, u, dres, mp.wait_flag, epoch, mp.err, sh);
+    RwWait wt;
+    wt.flag = mp.wait_flag;
+    wt.epoch = epoch;
+    wt.err = mp.err;
+    rw_pass<WT, BT, VPL, RW_OUT_ADD2_LDS>(mp.prob[1], pr0, pr1, blk, u, dres, wt, sh);
   } else {
     const int pi = (NP > 1 && blk >= mp.blk_begin[1]) ? 1 : 0;
     const int lb = blk - mp.blk_begin[pi];
@@ -359,7 +57,7 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
     const int P = (p.N + 1) / 2;
     const int pr0 = (int)((long long)lb * P / nb);
     const int pr1 = (int)((long long)(lb + 1) * P / nb);
-    rw_pass<WT, BT, VPL, RW_OUT_EPI>(p, pr0, pr1, lb, u, nullptr, nullptr, 0, nullptr, sh);
+    rw_pass<WT, BT, VPL, RW_OUT_EPI>(p, pr0, pr1, lb, u, nullptr, RwWait{}, sh);
   }
 }
 

@@ -109,6 +109,40 @@ hipError_t launch_gemv_paired(const GemvParams& first, const GemvParams& second,
 hipError_t launch_argmax_finalize(const float* best_val, const int* best_idx, int n, int BT, int B, int* next,
                                   hipStream_t s);
 
+// --------------------------------------------------- persistent decode step
+constexpr int kStepProgWords = 1024;
+// One launch for the whole layer stack of a decode step (all layers ladder, bf16 weights
+// and cache, batch <= 4).
+struct StepLayer {
+  const void* wq; const void* wk; const void* wv; const void* wo;
+  const void* wg; const void* wu; const void* wd;
+  const void* attn_norm; const void* mlp_norm;
+  void* k_cache; void* v_cache;        // this layer's [max_batch][n_kv][max_seq][hd]
+};
+struct StepParams {
+  const StepLayer* layers;             // device array [L]
+  int L, H, F, nq, nkv, hd, B, max_seq;
+  float eps;
+  const float* rope_cos; const float* rope_sin;
+  const int* d_pos; const int* d_epoch;
+  float* x0;                           // [B][H]: x_0 on entry, x_{2L} on exit
+  float* xs; size_t xstride;           // x_j (1 <= j < 2L) at xs + (j-1)*xstride, [B][H] each
+  float* qs; float* os; size_t qstride;  // q and the attention output of layer l at +l*qstride ([B][nq*hd])
+  float* as; size_t astride;           // SwiGLU output of layer l at as + l*astride ([B][F])
+  float* part; int* attn_cnt; int n_split;   // attention records [B][nq][n_split][hd+4], tickets [B][nkv]
+  int* sync;                           // [L][8] counters and flags (zero before the first step)
+  uint32_t* prog;                      // [kStepProgWords] progress word per projection workgroup
+  int* err;                            // set if a wait gives up
+  int n_attn;                          // set by the launcher
+  int dres_off;                        // set by the launcher
+  int rows_lds;                        // set by the launcher
+  int u2_off;                          // set by the launcher (0: gate/up stages its own input)
+};
+bool step_supported(int wdtype, int H, int F, int qrows, int B, int hd, int G);
+// true when every workgroup of the launch can be resident (queries the occupancy once)
+bool step_fits(const StepParams& sp);
+hipError_t launch_decode_step(const StepParams& sp, hipStream_t s);
+
 // ---------------------------------------------------------- prefill attention
 struct AttnPrefillParams {
   int wdtype;

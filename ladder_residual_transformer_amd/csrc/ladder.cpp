@@ -112,9 +112,18 @@ struct ladder_ctx {
   int* attn_done_cnt = nullptr;   // [L] attention merges finished in the current step
   int* attn_done_flag = nullptr;  // [L] epoch of the last step whose attention finished
   int* err_word = nullptr;        // set by a kernel whose bounded wait gave up
+  StepLayer* step_layers = nullptr;  // [L] per-layer pointers of the persistent decode step
+  int* step_sync = nullptr;          // [L][8] its counters and flags
+  uint32_t* step_prog = nullptr;     // [kStepProgWords] its progress words
+  float* step_x = nullptr;           // x_1 .. x_{2L-1}
+  float* step_q = nullptr;           // q per layer
+  float* step_o = nullptr;           // attention output per layer
+  float* step_a = nullptr;           // SwiGLU output per layer
+  size_t step_xstride = 0, step_qstride = 0, step_astride = 0;
+  bool all_ladder = false;           // every layer follows the ladder rule
   StreamScratch sc[2];
 
-  int sched = LADDER_SCHED_FUSED;
+  int sched = LADDER_SCHED_PERSISTENT;
   int use_graph = 1;
   int trace_kind = -1;               // kernel kind timed with events during decode (-1: none)
   std::vector<hipEvent_t> trace_ev;  // start/end pairs, one pair per traced launch
@@ -214,6 +223,20 @@ void carve(ladder_ctx* c, Carver& cv) {
   c->attn_done_cnt = cv.take<int>((size_t)g.n_layers);
   c->attn_done_flag = cv.take<int>((size_t)g.n_layers);
   c->err_word = cv.take<int>(1);
+  c->step_layers = cv.take<StepLayer>((size_t)g.n_layers);
+  c->step_sync = cv.take<int>((size_t)8 * g.n_layers);
+  c->step_prog = cv.take<uint32_t>(kStepProgWords);
+  // vectors of the persistent decode step, each at an address of its own per step
+  if (c->all_ladder && c->wdt == W_BF16) {
+    const size_t sb = std::min(B, 4);
+    c->step_xstride = align_up(sb * H, 64);
+    c->step_qstride = align_up(sb * c->qrows, 64);
+    c->step_astride = align_up(sb * F, 64);
+    c->step_x = cv.take<float>((size_t)(2 * g.n_layers - 1) * c->step_xstride);
+    c->step_q = cv.take<float>((size_t)g.n_layers * c->step_qstride);
+    c->step_o = cv.take<float>((size_t)g.n_layers * c->step_qstride);
+    c->step_a = cv.take<float>((size_t)g.n_layers * c->step_astride);
+  }
   for (int s = 0; s < 2; ++s) {
     StreamScratch& sc = c->sc[s];
     sc.q = cv.take<float>((size_t)B * c->qrows);
@@ -667,6 +690,51 @@ ladder_status run_modules(ladder_ctx* ctx, float* const X[2], float* const OUT[2
   return LADDER_OK;
 }
 
+// The persistent decode step: every layer ladder, bf16, batch <= 4, all workgroups resident.
+StepParams step_params(const ladder_ctx* ctx, int B);
+
+bool step_usable(const ladder_ctx* ctx, int B) {
+  const ladder_config& g = ctx->cfg;
+  return ctx->all_ladder && ctx->step_x && B <= 4 &&
+         step_supported(ctx->wdt, g.hidden, g.ffn, ctx->qrows, B, g.head_dim, g.n_q_heads / g.n_kv_heads) &&
+         step_fits(step_params(ctx, B));
+}
+
+StepParams step_params(const ladder_ctx* ctx, int B) {
+  const ladder_config& g = ctx->cfg;
+  const StreamScratch& sc = ctx->sc[0];
+  StepParams sp{};
+  sp.layers = ctx->step_layers;
+  sp.L = g.n_layers;
+  sp.H = g.hidden;
+  sp.F = g.ffn;
+  sp.nq = g.n_q_heads;
+  sp.nkv = g.n_kv_heads;
+  sp.hd = g.head_dim;
+  sp.B = B;
+  sp.max_seq = g.max_seq;
+  sp.eps = g.norm_eps;
+  sp.rope_cos = ctx->rope_cos;
+  sp.rope_sin = ctx->rope_sin;
+  sp.d_pos = ctx->pos_dev;
+  sp.d_epoch = ctx->epoch;
+  sp.x0 = ctx->dx[0];
+  sp.xs = ctx->step_x;
+  sp.xstride = ctx->step_xstride;
+  sp.qs = ctx->step_q;
+  sp.os = ctx->step_o;
+  sp.qstride = ctx->step_qstride;
+  sp.as = ctx->step_a;
+  sp.astride = ctx->step_astride;
+  sp.part = sc.attn_part;
+  sp.attn_cnt = sc.attn_cnt;
+  sp.n_split = ctx->n_split;
+  sp.sync = ctx->step_sync;
+  sp.prog = ctx->step_prog;
+  sp.err = ctx->err_word;
+  return sp;
+}
+
 ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream_t s) {
   return run_gemv(ctx, lmhead_params(ctx, x, ldx, B), s);
 }
@@ -678,7 +746,11 @@ ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
   ctx->trace_n = 0;
   HIPCHK(launch_embed(ctx->wdt, ctx->w.tok_embed, g.vocab, g.hidden, ctx->ids_dev, B, ctx->dx[0], ctx->s0));
   ladder_status st;
-  if (ctx->sched == LADDER_SCHED_FUSED) {
+  if (ctx->sched == LADDER_SCHED_PERSISTENT && step_usable(ctx, B)) {
+    TRACE(LADDER_KERNEL_LAYER_STACK, ctx->s0, false);
+    HIPCHK(launch_decode_step(step_params(ctx, B), ctx->s0));
+    TRACE(LADDER_KERNEL_LAYER_STACK, ctx->s0, true);
+  } else if (ctx->sched >= LADDER_SCHED_FUSED) {
     // ladder layers in three launches; standard layers module by module (fused adds)
     for (int l = 0; l < g.n_layers; ++l) {
       if (ctx->mask[l]) {
@@ -820,6 +892,8 @@ ladder_status ladder_init(const ladder_config* cfg, const ladder_weights* w, con
   INITCHK(hipEventCreateWithFlags(&ctx->ev_in, hipEventDisableTiming));
   INITCHK(hipEventCreateWithFlags(&ctx->ev_done, hipEventDisableTiming));
 
+  ctx->all_ladder = true;
+  for (int l = 0; l < cfg->n_layers; ++l) ctx->all_ladder = ctx->all_ladder && ctx->mask[l];
   Carver measure;
   carve(ctx, measure);
   ctx->ws_bytes = measure.off;
@@ -828,6 +902,17 @@ ladder_status ladder_init(const ladder_config* cfg, const ladder_weights* w, con
   real.base = ctx->ws;
   carve(ctx, real);
   INITCHK(hipMemsetAsync(ctx->ws, 0, ctx->ws_bytes, ctx->s0));
+  {
+    std::vector<StepLayer> sl(cfg->n_layers);
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      const ladder_layer_weights& L = ctx->layers[l];
+      sl[l] = StepLayer{L.wq, L.wk, L.wv, L.wo, L.w_gate, L.w_up, L.w_down, L.attn_norm, L.mlp_norm,
+                        layer_k(ctx, l), layer_v(ctx, l)};
+    }
+    INITCHK(hipMemcpyAsync(ctx->step_layers, sl.data(), sl.size() * sizeof(StepLayer), hipMemcpyHostToDevice,
+                           ctx->s0));
+    INITCHK(hipStreamSynchronize(ctx->s0));
+  }
 
   // RoPE table: pair j at position p rotates by p * theta^(-2j/hd), computed in fp64
   {
@@ -852,7 +937,7 @@ ladder_status ladder_init(const ladder_config* cfg, const ladder_weights* w, con
 
 ladder_status ladder_set_schedule(ladder_ctx* ctx, int32_t schedule, int32_t use_graph) {
   if (!ctx) return LADDER_ERR_ARG;
-  if (schedule < LADDER_SCHED_SERIAL || schedule > LADDER_SCHED_FUSED) return LADDER_ERR_ARG;
+  if (schedule < LADDER_SCHED_SERIAL || schedule > LADDER_SCHED_PERSISTENT) return LADDER_ERR_ARG;
   ctx->sched = schedule;
   ctx->use_graph = use_graph ? 1 : 0;
   return LADDER_OK;
@@ -935,6 +1020,13 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
     int launches = 0;
     HIPCHK(hipEventRecord(e0, s));
     for (int r = 0; r < reps; ++r) {
+      if (kind == LADDER_KERNEL_LAYER_STACK) {
+        if (!step_usable(ctx, B)) break;
+        HIPCHK(launch_epoch_bump(ctx->epoch, s));
+        HIPCHK(launch_decode_step(step_params(ctx, B), s));
+        ++launches;
+        continue;
+      }
       if (kind == LADDER_KERNEL_LMHEAD) {
         if ((st = run_gemv(ctx, lmhead_params(ctx, ctx->dx[0], g.hidden, B), s))) return st;
         ++launches;
@@ -994,7 +1086,7 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
     HIPCHK(hipEventSynchronize(e1));
     float ms = 0.f;
     HIPCHK(hipEventElapsedTime(&ms, e0, e1));
-    us_out[kind] = 1000.f * ms / (float)launches;
+    us_out[kind] = launches ? 1000.f * ms / (float)launches : -1.f;
   }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
@@ -1024,7 +1116,7 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
     auto mod = [&](int m, const float* xin, const float* xm, float* xn, float* store, hipStream_t s, bool wait,
                    hipEvent_t ev) { return prefill_module(ctx, m, B, Tc, sp, xin, xm, xn, store, s, wait, ev); };
     const int saved = ctx->sched;
-    const bool fused = saved == LADDER_SCHED_FUSED;
+    const bool fused = saved >= LADDER_SCHED_FUSED;
     if (fused) ctx->sched = LADDER_SCHED_SERIAL;   // prefill: module order, adds in the GEMMs
     st = run_modules(ctx, ctx->px, ctx->pout, (size_t)M * g.hidden, mod, fused);
     ctx->sched = saved;
@@ -1052,6 +1144,8 @@ ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t 
   ladder_status st = begin_call(ctx);
   if (st) return st;
   HIPCHK(launch_decode_prologue(d_ids, ctx->ids_dev, B, ctx->pos_dev, pos, ctx->epoch, ctx->s0));
+  // occupancy queries of the persistent launch happen here, not under graph capture
+  if (ctx->sched == LADDER_SCHED_PERSISTENT) (void)step_usable(ctx, B);
   // traced steps run eagerly: event records captured into a graph carry no timestamps
   if (ctx->use_graph && ctx->trace_kind < 0) {
     const int key = B * 8 + ctx->sched;

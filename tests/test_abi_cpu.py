@@ -32,7 +32,8 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ("LADDER_OK", "LADDER_ERR_ARG", "LADDER_ERR_SHAPE", "LADDER_ERR_CAPACITY", "LADDER_ERR_STATE",
                  "LADDER_ERR_HIP", "LADDER_ERR_OOM", "LADDER_F32", "LADDER_BF16", "LADDER_SCHED_SERIAL",
-                 "LADDER_SCHED_SIDE", "LADDER_SCHED_DUAL", "LADDER_SCHED_FUSED"):
+                 "LADDER_SCHED_SIDE", "LADDER_SCHED_DUAL", "LADDER_SCHED_FUSED",
+                 "LADDER_SCHED_PERSISTENT", "LADDER_KERNEL_LAYER_STACK", "LADDER_N_KERNELS"):
         m = re.search(r"#define\s+%s\s+\(?(-?\d+)\)?" % name, text)
         assert m, name
         assert int(m.group(1)) == getattr(abi, name), name
