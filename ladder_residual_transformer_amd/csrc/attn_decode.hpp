@@ -93,7 +93,7 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
   int* counter = p.counters + (size_t)b * p.nkv + kvh;
   if (tid == 0) {
     if (!COH) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const bool last = atomicAdd(counter, 1) == n_act - 1;
+    const bool last = __hip_atomic_fetch_add(gbl(counter), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_act - 1;
     if (!COH && last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     L.is_last = last;
   }
@@ -112,14 +112,14 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
 #pragma unroll
     for (int q = 0; q < QG; ++q) {
       const float* rec = src + (size_t)min(q, n_act - 1) * stride;
-      a0[q] = COH ? ld_coh4(rec) : *(const float4*)rec;
+      a0[q] = COH ? ld_coh4(rec) : ldg4(rec);
     }
   }
   for (int i = tid; i < G * n_act; i += 256) {
     const int h = i / n_act, q = i % n_act;
     const float* rec = base + ((size_t)h * p.n_split + q) * stride;
-    L.wsc[h][q] = COH ? ld_coh(rec) : rec[0];
-    L.lsc[h][q] = COH ? ld_coh(rec + 1) : rec[1];
+    L.wsc[h][q] = COH ? ld_coh(rec) : gbl(rec)[0];
+    L.lsc[h][q] = COH ? ld_coh(rec + 1) : gbl(rec)[1];
   }
   __syncthreads();
   if (tid < G) {
@@ -143,7 +143,7 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
 #pragma unroll
         for (int q = 0; q < QG; ++q) {
           const float* rec = src + (size_t)min(q0 + q, n_act - 1) * stride;
-          a0[q] = COH ? ld_coh4(rec) : *(const float4*)rec;
+          a0[q] = COH ? ld_coh4(rec) : ldg4(rec);
         }
       }
 #pragma unroll
@@ -159,16 +159,16 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
     float* dst = p.out + (size_t)b * p.nq * HD + (size_t)(kvh * G + h) * HD + d4;
     const float4 r = make_float4(o.x * li, o.y * li, o.z * li, o.w * li);
     if (COH) st_coh4(dst, r);
-    else *(float4*)dst = r;
+    else stg4(dst, r);
   }
   if (tid == 0) {
-    if (COH) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else *counter = 0;
+    if (COH) __hip_atomic_store(gbl(counter), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *gbl(counter) = 0;
   }
   // completion signal: the last of the B*nkv merges publishes the step's epoch
   if (p.done_flag) {
-    if (COH) wg_arrive_coh(p.done_cnt, p.done_flag, p.B * p.nkv, *p.d_epoch);
-    else wg_signal(p.done_cnt, p.done_flag, p.B * p.nkv, *p.d_epoch);
+    if (COH) wg_arrive_coh(p.done_cnt, p.done_flag, p.B * p.nkv, *gbl(p.d_epoch));
+    else wg_signal(p.done_cnt, p.done_flag, p.B * p.nkv, *gbl(p.d_epoch));
   }
 }
 
@@ -193,7 +193,7 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
   const int kvh = (blk / p.n_split) % p.nkv;
   const int b = blk / (p.n_split * p.nkv);
   const int G = p.nq / p.nkv;
-  const int len = *p.d_pos + 1;
+  const int len = *gbl(p.d_pos) + 1;
   const int chunk = attn_chunk(len, p.n_split);
   const int n_act = (len + chunk - 1) / chunk;             // chunks holding keys
   if (s >= n_act) return;                                  // whole workgroup: nothing to do
@@ -213,7 +213,7 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
       const uint32_t* w = (const uint32_t*)a;
       return make_uint4(ld_coh(w), ld_coh(w + 1), ld_coh(w + 2), ld_coh(w + 3));
     }
-    return *(const uint4*)a;
+    return ldg4u(a);
   };
   auto load_tile = [&](int t0) {
 #pragma unroll
@@ -239,8 +239,8 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
     const float qz = col < G ? 1.f : 0.f;
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      const float4 x = *(const float4*)(qrow + 32 * st + 8 * grp);
-      const float4 y = *(const float4*)(qrow + 32 * st + 8 * grp + 4);
+      const float4 x = ldg4(qrow + 32 * st + 8 * grp);
+      const float4 y = ldg4(qrow + 32 * st + 8 * grp + 4);
       uint4 hi, lo;
       split_h2(x.x * qz, x.y * qz, hi.x, lo.x);
       split_h2(x.z * qz, x.w * qz, hi.y, lo.y);
@@ -339,13 +339,13 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
     for (int d = 0; d < NDB; ++d) {
       const float4 v = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
       if (COH) st_coh4(dst + 4 + w * DPW + 16 * d + 4 * grp, v);
-      else *(float4*)(dst + 4 + w * DPW + 16 * d + 4 * grp) = v;
+      else stg4(dst + 4 + w * DPW + 16 * d + 4 * grp, v);
     }
     // the record's max is in the merge's units, score / sqrt(hd) (m_run is a raw score)
     if (w == 0 && grp == 0) {
       const float mr = m_run * (1.0f / sqrtf((float)HD));
       if (COH) { st_coh(dst, mr); st_coh(dst + 1, l_run); }
-      else { dst[0] = mr; dst[1] = l_run; }
+      else { gbl(dst)[0] = mr; gbl(dst)[1] = l_run; }
     }
   }
   attn_finish<HD, COH>(p, b, kvh, G, n_act, L);
@@ -365,7 +365,7 @@ __device__ void attn_decode_block_valu(const AttnDecodeParams& p, int blk, AttnL
   const int kvh = (blk / p.n_split) % p.nkv;
   const int b = blk / (p.n_split * p.nkv);
   const int G = p.nq / p.nkv;
-  const int len = *p.d_pos + 1;
+  const int len = *gbl(p.d_pos) + 1;
   const int chunk = attn_chunk(len, p.n_split);
   const int n_act = (len + chunk - 1) / chunk;
   if (s >= n_act) return;

@@ -94,17 +94,42 @@ __device__ __forceinline__ void wave_stores_done_fwd() {
 // Coherent (agent-scope) accesses for data that one workgroup writes and another reads
 // within a kernel: they bypass the per-XCD caches, so publishing them needs no L2
 // write-back, only that the stores have completed.
+// Device memory through a pointer the compiler cannot trace to a kernel argument (read
+// from a table in memory, say) would be accessed with flat instructions, which count in
+// both the vector-memory and the LDS counters, so every use of a load waits for all
+// outstanding loads.  Every pointer given to gbl() addresses device memory.
+#define LADDER_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const LADDER_GLOBAL T* gbl(const T* p) { return (const LADDER_GLOBAL T*)p; }
+template <typename T>
+__device__ __forceinline__ LADDER_GLOBAL T* gbl(T* p) { return (LADDER_GLOBAL T*)p; }
+typedef float gf32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int gu32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ldg4(const float* p) {
+  const gf32x4 v = *(const LADDER_GLOBAL gf32x4*)p;
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ldg4u(const void* p) {
+  const gu32x4 v = *(const LADDER_GLOBAL gu32x4*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void stg4(float* p, const float4& v) {
+  gf32x4 w;
+  w.x = v.x; w.y = v.y; w.z = v.z; w.w = v.w;
+  *(LADDER_GLOBAL gf32x4*)p = w;
+}
+
 __device__ __forceinline__ float ld_coh(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gbl(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t ld_coh(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gbl(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gbl(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gbl(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float4 ld_coh4(const float* p) {
   return make_float4(ld_coh(p), ld_coh(p + 1), ld_coh(p + 2), ld_coh(p + 3));
@@ -119,9 +144,9 @@ __device__ __forceinline__ void st_coh4(float* p, float4 v) {
 __device__ __forceinline__ void wg_arrive_coh(int* cnt, int* flag, int total, int epoch) {
   wave_stores_done_fwd();
   __syncthreads();
-  if (threadIdx.x == 0 && atomicAdd(cnt, 1) == total - 1) {
-    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0 && __hip_atomic_fetch_add(gbl(cnt), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1) {
+    __hip_atomic_store(gbl(cnt), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gbl(flag), epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -130,14 +155,14 @@ __device__ __forceinline__ void wg_arrive_coh(int* cnt, int* flag, int total, in
 __device__ __forceinline__ void wg_wait_coh(const int* flag, int epoch, int* err) {
   if (threadIdx.x == 0) {
     unsigned spins = 0;
-    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+    while (__hip_atomic_load(gbl(flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins == (1u << 19)) {          // far beyond any real wait
-        atomicOr(err, 1);
+        __hip_atomic_fetch_or(gbl(err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       // another wait already gave up: the results are void, so do not wait again
-      if ((spins & 1023u) == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+      if ((spins & 1023u) == 0 && __hip_atomic_load(gbl(err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
     }
   }
   __syncthreads();
@@ -150,7 +175,7 @@ __device__ __forceinline__ void wg_wait_coh(const int* flag, int epoch, int* err
 __device__ __forceinline__ void prog_publish(uint32_t* word, uint32_t code) {
   wave_stores_done_fwd();
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(word, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(gbl(word), code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait until every word of prog[0..n) has reached `code` (wrap-safe comparison); the
@@ -162,13 +187,13 @@ __device__ __forceinline__ void prog_wait(const uint32_t* prog, int n, uint32_t 
   for (;;) {
     int ok = 1;
     for (int i = threadIdx.x; i < n; i += blockDim.x)
-      ok &= (int)(__hip_atomic_load(prog + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - code) >= 0;
+      ok &= (int)(__hip_atomic_load(gbl(prog) + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - code) >= 0;
     if (__syncthreads_and(ok)) return;
     if ((++rounds & 255u) == 0) {
       int bail = rounds >= (1u << 16);
       if (threadIdx.x == 0) {
-        if (bail) atomicOr(err, 1);
-        else bail = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+        if (bail) __hip_atomic_fetch_or(gbl(err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else bail = __hip_atomic_load(gbl(err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
       }
       if (__syncthreads_or(bail)) return;
     }

@@ -8,9 +8,7 @@
 //
 //   QKV_l     (+RoPE, K/V row)  reads x_{2l-1}   waits until every workgroup finished
 //                                                 layer l-1
-//   gate/up_l (+SwiGLU)         reads x_{2l}     (copied into LDS by direct loads issued
-//                                                 with QKV_l's: both exist once layer
-//                                                 l-1 is done)
+//   gate/up_l (+SwiGLU)         reads x_{2l}     (exists once layer l-1 is done)
 //   down_l    rows kept in LDS  reads a_l        waits until every gate/up_l is done
 //   O_l       x_{2l+1} = x_{2l} + o_l,           waits for the attention of layer l
 //             x_{2l+2} = x_{2l+1} + d_l
@@ -44,7 +42,18 @@ namespace {
 constexpr int kStepBlocksPerCu = 2;
 constexpr int kStepMinGemvBlocks = 64;   // the LDS of the down rows is sized for this many
 constexpr int kStepMaxGemvBlocks = kStepProgWords;
-constexpr size_t kStepLdsPerBlock = 80 * 1024;   // two workgroups per CU
+
+// One layer's pointers, read as plain 64-bit words through a global-address-space pointer.
+__device__ __forceinline__ StepLayer load_layer(const StepLayer* p) {
+  static_assert(sizeof(StepLayer) % 8 == 0, "StepLayer holds pointers only");
+  constexpr int n = sizeof(StepLayer) / 8;
+  uint64_t w[n];
+#pragma unroll
+  for (int i = 0; i < n; ++i) w[i] = gbl((const uint64_t*)p)[i];
+  StepLayer s;
+  __builtin_memcpy(&s, w, sizeof s);
+  return s;
+}
 
 // pair range of workgroup g of NG over P row pairs
 __device__ __forceinline__ void step_share(int P, int g, int NG, int& p0, int& p1) {
@@ -54,11 +63,11 @@ __device__ __forceinline__ void step_share(int P, int g, int NG, int& p0, int& p
 
 }  // namespace
 
-template <int BT, int HD, bool PRE>
+template <int BT, int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_step_kernel(StepParams sp) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   __shared__ RwShared sh;
-  const int epoch = *sp.d_epoch;
+  const int epoch = *gbl(sp.d_epoch);
   const int n_attn = sp.n_attn;
   const bool attn = (int)blockIdx.x < n_attn;
   const int NG = (int)gridDim.x - n_attn, g = (int)blockIdx.x - n_attn;
@@ -66,7 +75,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   float* u = reinterpret_cast<float*>(lds_raw);
   float* xrows = reinterpret_cast<float*>(lds_raw + sp.dres_off);   // [rows][BT] residual rows
   float* drows = xrows + sp.rows_lds * BT;                            // [rows][BT] down rows
-  float* u2 = reinterpret_cast<float*>(lds_raw + sp.u2_off);   // x_{2l} for gate/up (PRE)
   // progress code of phase ph (QKV, gate/up, whole layer) of layer l; the codes of this
   // step exceed every code of earlier steps
   enum { PH_QKV = 0, PH_GU = 1, PH_LAYER = 2 };
@@ -81,13 +89,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int nr = 2 * (h1 - h0);
     for (int i = threadIdx.x; i < nr * BT; i += blockDim.x) {
       const int r = i / BT, b = i % BT, n = 2 * h0 + r;
-      xrows[i] = (b < sp.B && n < sp.H) ? sp.x0[(size_t)b * sp.H + n] : 0.f;
+      xrows[i] = (b < sp.B && n < sp.H) ? gbl(sp.x0)[(size_t)b * sp.H + n] : 0.f;
     }
     __syncthreads();
   }
 
   for (int l = 0; l < sp.L; ++l) {
-    const StepLayer ly = sp.layers[l];
+    const StepLayer ly = load_layer(sp.layers + l);
     int* sy = sp.sync + 8 * l;       // [4], [5]: attention merges counter and flag
     float* q_l = sp.qs + (size_t)l * sp.qstride;
     float* o_l = sp.os + (size_t)l * sp.qstride;
@@ -149,11 +157,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       wt.code = code(l - 1, PH_LAYER);
     }
     step_share((qp.N + 1) / 2, g, NG, p0, p1);
-    // after its wait the QKV pass also copies x_{2l} into LDS for gate/up (when it fits)
-    RwSecond sec;
-    sec.x = xslot(2 * l);
-    sec.u = u2;
-    rw_pass<uint16_t, BT, 4, RW_OUT_EPI, true>(qp, p0, p1, g, u, nullptr, wt, sh, nullptr, PRE ? &sec : nullptr);
+    rw_pass<uint16_t, BT, 4, RW_OUT_EPI, true>(qp, p0, p1, g, u, nullptr, wt, sh);
     prog_publish(sp.prog + g, code(l, PH_QKV));
 
     // ---- gate/up_l from x_{2l}
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     RwWait wg;
     wg.err = sp.err;
     step_share(sp.F, g, NG, p0, p1);
-    rw_pass<uint16_t, BT, 4, RW_OUT_EPI, true>(gp, p0, p1, g, PRE ? u2 : u, nullptr, wg, sh, nullptr, nullptr, PRE);
+    rw_pass<uint16_t, BT, 4, RW_OUT_EPI, true>(gp, p0, p1, g, u, nullptr, wg, sh);
     prog_publish(sp.prog + g, code(l, PH_GU));
 
     GemvParams op{};
@@ -216,32 +220,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 
 namespace {
 
-// LDS of a projection workgroup: u (the staged input), the second staged input when it
-// fits two workgroups per CU, the residual rows and the down rows of its O/down share;
-// at least the attention's LDS.
-size_t step_lds(int H, int F, int qrows, int B, int hd, int* dres_off, int* rows_lds, int* u2_off) {
+// LDS of a projection workgroup: u (the staged input), the residual rows and the down
+// rows of its O/down share; at least the attention's LDS.
+size_t step_lds(int H, int F, int qrows, int B, int hd, int* dres_off, int* rows_lds) {
   int kmax = H > F ? H : F;
   if (qrows > kmax) kmax = qrows;
   const size_t ub = (size_t)B * (kmax + 8) * 4;
   const size_t off = (ub + 15) / 16 * 16;
-  const size_t ub2 = ((size_t)B * (H + 8) * 4 + 15) / 16 * 16;
   const int P = (H + 1) / 2;
   const int per = (P + kStepMinGemvBlocks - 1) / kStepMinGemvBlocks;
   const int rows = 2 * (per > 4 ? per : 4);
-  const size_t rows_bytes = 2 * (size_t)rows * 4 * sizeof(float);   // residual rows, then down rows
-  const bool two = off + ub2 + rows_bytes <= kStepLdsPerBlock;
-  *u2_off = two ? (int)(off + rows_bytes) : 0;
   *dres_off = (int)off;
   *rows_lds = rows;
-  size_t lds = off + rows_bytes + (two ? ub2 : 0);
+  const size_t lds = off + 2 * (size_t)rows * 4 * sizeof(float);   // residual rows, then down rows
   const size_t al = hd == 128 ? sizeof(AttnLds<uint16_t, 128>) : sizeof(AttnLds<uint16_t, 64>);
   return lds > al ? lds : al;
 }
 
 // workgroups of decode_step_kernel<BT, HD> resident at once with `lds` bytes each
-template <int BT, int HD, bool PRE>
+template <int BT, int HD>
 hipError_t step_blocks(size_t lds, int* blocks) {
-  auto fn = decode_step_kernel<BT, HD, PRE>;
+  auto fn = decode_step_kernel<BT, HD>;
   static size_t cached_lds = 0;
   static int cached_blocks = 0;
   if (cached_lds != lds || cached_blocks == 0) {
@@ -271,12 +270,11 @@ int step_plan(StepParams& sp, size_t* lds_out, hipError_t* err) {
       sp.n_split < 1 || sp.n_split > kAttnMaxSplits || sp.L < 1 || !sp.layers || !sp.sync || !sp.prog || !sp.err || !sp.xs || !sp.qs || !sp.os || !sp.as)
     return 0;
   sp.n_attn = sp.n_split * sp.nkv * sp.B;
-  const size_t lds = step_lds(sp.H, sp.F, qrows, sp.B, sp.hd, &sp.dres_off, &sp.rows_lds, &sp.u2_off);
+  const size_t lds = step_lds(sp.H, sp.F, qrows, sp.B, sp.hd, &sp.dres_off, &sp.rows_lds);
   *lds_out = lds;
   const int bt = sp.B <= 1 ? 1 : sp.B <= 2 ? 2 : 4;
   int blocks = 0;
-#define STEP_BLOCKS(BT_, HD_) \
-  (sp.u2_off ? step_blocks<BT_, HD_, true>(lds, &blocks) : step_blocks<BT_, HD_, false>(lds, &blocks))
+#define STEP_BLOCKS(BT_, HD_) step_blocks<BT_, HD_>(lds, &blocks)
   if (sp.hd == 128)
     *err = bt == 1 ? STEP_BLOCKS(1, 128) : bt == 2 ? STEP_BLOCKS(2, 128) : STEP_BLOCKS(4, 128);
   else
@@ -311,9 +309,7 @@ hipError_t launch_decode_step(const StepParams& sp_in, hipStream_t s) {
   const int bt = sp.B <= 1 ? 1 : sp.B <= 2 ? 2 : 4;
   const dim3 g(grid), b(256);
   const uint32_t ls = (uint32_t)lds;
-#define STEP_GO(BT_, HD_)                                                              \
-  if (sp.u2_off) launch_timed(decode_step_kernel<BT_, HD_, true>, g, b, ls, s, sp);   \
-  else launch_timed(decode_step_kernel<BT_, HD_, false>, g, b, ls, s, sp)
+#define STEP_GO(BT_, HD_) launch_timed(decode_step_kernel<BT_, HD_>, g, b, ls, s, sp)
   if (sp.hd == 128) {
     if (bt == 1) STEP_GO(1, 128);
     else if (bt == 2) STEP_GO(2, 128);

@@ -74,12 +74,12 @@ __device__ __forceinline__ void rw_epilogue(const GemvParams& p, int pair, int b
     case EPI_QKV_ROPE: {
       y0 *= inv;
       y1 *= inv;
-      const int pos = *p.d_pos;
+      const int pos = *gbl(p.d_pos);
       if (n0 < p.q_rows + p.kv_rows) {              // q or k: rotate the adjacent pair
         const int d = (n0 < p.q_rows ? n0 : n0 - p.q_rows) % p.head_dim;
         const int half = p.head_dim >> 1;
-        const float c = p.rope_cos[(size_t)pos * half + (d >> 1)];
-        const float s = p.rope_sin[(size_t)pos * half + (d >> 1)];
+        const float c = gbl(p.rope_cos)[(size_t)pos * half + (d >> 1)];
+        const float s = gbl(p.rope_sin)[(size_t)pos * half + (d >> 1)];
         const float r0 = y0 * c - y1 * s;
         const float r1 = y0 * s + y1 * c;
         y0 = r0;
@@ -116,12 +116,12 @@ __device__ __forceinline__ void rw_epilogue_coh(const GemvParams& p, int pair, i
     case EPI_QKV_ROPE: {
       y0 *= inv;
       y1 *= inv;
-      const int pos = *p.d_pos;
+      const int pos = *gbl(p.d_pos);
       if (n0 < p.q_rows + p.kv_rows) {
         const int d = (n0 < p.q_rows ? n0 : n0 - p.q_rows) % p.head_dim;
         const int half = p.head_dim >> 1;
-        const float c = p.rope_cos[(size_t)pos * half + (d >> 1)];
-        const float s = p.rope_sin[(size_t)pos * half + (d >> 1)];
+        const float c = gbl(p.rope_cos)[(size_t)pos * half + (d >> 1)];
+        const float s = gbl(p.rope_sin)[(size_t)pos * half + (d >> 1)];
         const float r0 = y0 * c - y1 * s;
         const float r1 = y0 * s + y1 * c;
         y0 = r0;
@@ -161,14 +161,6 @@ struct RwWait {
   int* err = nullptr;
 };
 
-// A second input of the same K and batch, copied raw into LDS (row b at b * (K + VEC)
-// floats) by direct global-to-LDS loads issued right after the pass's wait, for a later
-// pass that normalises it in place (raw_staged).
-struct RwSecond {
-  const float* x = nullptr;
-  float* u = nullptr;
-};
-
 struct RwShared {
   float sqw[4][4];
   float inv[4];
@@ -191,8 +183,7 @@ enum { RW_OUT_EPI = 0, RW_OUT_LDS = 1, RW_OUT_ADD2_LDS = 2, RW_OUT_ADD2_LDSRES =
 // producers' signal (a cached copy would be stale).
 template <typename WT, int BT, int VPL, int OUT, bool COH = false>
 __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, int lb, float* u, float* dres,
-                                        const RwWait& wt, RwShared& sh, float* res = nullptr,
-                                        const RwSecond* second = nullptr, bool raw_staged = false) {
+                                        const RwWait& wt, RwShared& sh, float* res = nullptr) {
   constexpr int VEC = Vec<WT>::N;
   constexpr int CHUNK = 64 * VPL;                 // vectors of a row one wave covers per step
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -217,8 +208,8 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = min(c * CHUNK + lane + 64 * v, nvec - 1);
-      w[0][v] = *(const uint4*)(r0 + (size_t)vi * VEC);
-      w[1][v] = *(const uint4*)(r1 + (size_t)vi * VEC);
+      w[0][v] = ldg4u(r0 + (size_t)vi * VEC);
+      w[1][v] = ldg4u(r1 + (size_t)vi * VEC);
     }
   };
   const int ustride = K + VEC;                     // u rows carry a zero pad of VEC floats
@@ -233,17 +224,6 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
   // ---- prologue: u = x (* g) for every batch row, and inv_rms.  For one batch row and
   // K <= 256*4*VEC the input loads are issued before the first weight unit, so the
   // in-order completion of loads does not make the prologue wait for the weights.
-  // raw_staged: u already holds x (raw) and is normalised in place, in the same order.
-  if (second) {                                    // raw copy of the second input
-    const int nc = K / 4;                          // 16-byte chunks per row
-    for (int b = 0; b < B; ++b)
-      for (int c0 = wid * 64; c0 < nc; c0 += 256) {
-        if (c0 + lane < nc)
-          __builtin_amdgcn_global_load_lds((const void*)(second->x + (size_t)b * p.ldx + (size_t)(c0 + lane) * 4),
-                                           (__attribute__((address_space(3))) void*)(second->u + (size_t)b * ustride + c0 * 4),
-                                           16, 0, 0);
-      }
-  }
   const bool norm = p.gain != nullptr;
   if (tid < B * VEC) u[(tid / VEC) * ustride + K + tid % VEC] = 0.f;
   if (BT == 1 && nvec <= 256 * 4) {
@@ -254,11 +234,10 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
       const int v = min(tid + 256 * i, nvec - 1);
 #pragma unroll
       for (int e = 0; e < VEC / 4; ++e)
-        xr[i][e] = raw_staged ? *(const float4*)(u + (size_t)v * VEC + 4 * e) : *(const float4*)(p.x + (size_t)v * VEC + 4 * e);
-      gr[i] = norm ? *(const uint4*)((const WT*)p.gain + (size_t)v * VEC) : make_uint4(0u, 0u, 0u, 0u);
+        xr[i][e] = ldg4(p.x + (size_t)v * VEC + 4 * e);
+      gr[i] = norm ? ldg4u((const WT*)p.gain + (size_t)v * VEC) : make_uint4(0u, 0u, 0u, 0u);
     }
     if (!waits && n_units > 0) load_unit(wa, 0);
-    if (raw_staged) __syncthreads();               // every raw element read before it is overwritten
     float sq = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -286,21 +265,20 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
     if (lane == 0) sh.sqw[wid][0] = sq;
   } else {
     if (!waits && n_units > 0) load_unit(wa, 0);
-    // each thread reads and rewrites only its own elements, so raw_staged needs no barrier
     for (int b = 0; b < BT; ++b) {
       float sq = 0.f;
       if (b < B) {
         for (int v = tid; v < nvec; v += 256) {
-          const float* xp = (raw_staged ? u + (size_t)b * ustride : p.x + (size_t)b * p.ldx) + (size_t)v * VEC;
+          const float* xg = p.x + (size_t)b * p.ldx + (size_t)v * VEC;
           float xv[VEC];
 #pragma unroll
           for (int e = 0; e < VEC; e += 4) {
-            const float4 t = *(const float4*)(xp + e);
+            const float4 t = ldg4(xg + e);
             xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
           }
           if (norm) {
             float g[VEC];
-            unpack16(*(const uint4*)((const WT*)p.gain + (size_t)v * VEC), g);
+            unpack16(ldg4u((const WT*)p.gain + (size_t)v * VEC), g);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
               sq = fmaf(xv[e], xv[e], sq);
@@ -416,11 +394,15 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
       }
     }
   };
+  // the scheduling barriers keep the next unit's loads issued ahead of the current
+  // unit's arithmetic (under register pressure the scheduler would sink them)
   for (int i = 0; i < n_units; i += 2) {
     if (i + 1 < n_units) load_unit(wb, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
     compute_unit(wa, i);
     if (i + 1 < n_units) {
       if (i + 2 < n_units) load_unit(wa, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
       compute_unit(wb, i + 1);
     }
   }

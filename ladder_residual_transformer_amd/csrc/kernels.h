@@ -136,7 +136,6 @@ struct StepParams {
   int n_attn;                          // set by the launcher
   int dres_off;                        // set by the launcher
   int rows_lds;                        // set by the launcher
-  int u2_off;                          // set by the launcher (0: gate/up stages its own input)
 };
 bool step_supported(int wdtype, int H, int F, int qrows, int B, int hd, int G);
 // true when every workgroup of the launch can be resident (queries the occupancy once)
