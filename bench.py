@@ -138,7 +138,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="70b_tp8_shard")
     ap.add_argument("--batch", type=int, default=1)
-    ap.add_argument("--schedule", choices=("serial", "side", "dual", "fused", "persistent"), default="persistent")
+    ap.add_argument("--schedule", choices=("serial", "side", "dual", "fused", "persistent"), default="fused")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--prefill-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -70,7 +70,8 @@ typedef int32_t ladder_status;
                                     by side: [QKV | gate/up] in one launch (they read
                                     x_{2l-1} and x_{2l}), [attention | down projection] in
                                     one launch, then the O projection adds both residual
-                                    updates (default) */
+                                    updates (with bf16 weights and batch <= 4 in the same
+                                    launch as the down projection) (default) */
 #define LADDER_SCHED_PERSISTENT 4 /* decode: the whole layer stack in one launch of resident
                                     workgroups that signal each other (every layer ladder,
                                     bf16, batch <= 4; otherwise as FUSED); prefill as FUSED */

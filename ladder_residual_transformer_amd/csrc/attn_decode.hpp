@@ -148,11 +148,13 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
       }
 #pragma unroll
       for (int q = 0; q < QG; ++q) {
-        const float w = q0 + q < n_act ? L.wsc[h][q0 + q] : 0.f;
-        o.x = fmaf(a0[q].x, w, o.x);
-        o.y = fmaf(a0[q].y, w, o.y);
-        o.z = fmaf(a0[q].z, w, o.z);
-        o.w = fmaf(a0[q].w, w, o.w);
+        if (q0 + q < n_act) {
+          const float w = L.wsc[h][q0 + q];
+          o.x = fmaf(a0[q].x, w, o.x);
+          o.y = fmaf(a0[q].y, w, o.y);
+          o.z = fmaf(a0[q].z, w, o.z);
+          o.w = fmaf(a0[q].w, w, o.w);
+        }
       }
     }
     const float li = L.linv[h];

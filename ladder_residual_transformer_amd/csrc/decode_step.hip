@@ -75,6 +75,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   float* u = reinterpret_cast<float*>(lds_raw);
   float* xrows = reinterpret_cast<float*>(lds_raw + sp.dres_off);   // [rows][BT] residual rows
   float* drows = xrows + sp.rows_lds * BT;                            // [rows][BT] down rows
+  float* part = reinterpret_cast<float*>(lds_raw + sp.part_off);      // partial sums of a pass
   // progress code of phase ph (QKV, gate/up, whole layer) of layer l; the codes of this
   // step exceed every code of earlier steps
   enum { PH_QKV = 0, PH_GU = 1, PH_LAYER = 2 };
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       wt.code = code(l - 1, PH_LAYER);
     }
     step_share((qp.N + 1) / 2, g, NG, p0, p1);
-    rw_pass<uint16_t, BT, 4, RW_OUT_EPI, true>(qp, p0, p1, g, u, nullptr, wt, sh);
+    rw_pass<uint16_t, BT, kRwVpl, RW_OUT_EPI, true>(qp, p0, p1, g, u, nullptr, wt, sh, part);
     prog_publish(sp.prog + g, code(l, PH_QKV));
 
     // ---- gate/up_l from x_{2l}
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     RwWait wg;
     wg.err = sp.err;
     step_share(sp.F, g, NG, p0, p1);
-    rw_pass<uint16_t, BT, 4, RW_OUT_EPI, true>(gp, p0, p1, g, u, nullptr, wg, sh);
+    rw_pass<uint16_t, BT, kRwVpl, RW_OUT_EPI, true>(gp, p0, p1, g, u, nullptr, wg, sh, part);
     prog_publish(sp.prog + g, code(l, PH_GU));
 
     GemvParams op{};
@@ -210,10 +211,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     wd.code = code(l, PH_GU);
     wd.err = sp.err;
     // down_l rows into LDS; then O_l: x_{2l+1} = x_{2l} + o_l, x_{2l+2} = x_{2l+1} + d_l
-    rw_pass<uint16_t, BT, 4, RW_OUT_LDS, true>(dp, h0, h1, g, u, drows, wd, sh);
+    rw_pass<uint16_t, BT, kRwVpl, RW_OUT_LDS, true>(dp, h0, h1, g, u, drows, wd, sh, part);
     __syncthreads();
     op.out2 = xslot(2 * l + 2);
-    rw_pass<uint16_t, BT, 4, RW_OUT_ADD2_LDSRES, true>(op, h0, h1, g, u, drows, wa, sh, xrows);
+    rw_pass<uint16_t, BT, kRwVpl, RW_OUT_ADD2_LDSRES, true>(op, h0, h1, g, u, drows, wa, sh, part, xrows);
     prog_publish(sp.prog + g, code(l, PH_LAYER));
   }
 }
@@ -222,7 +223,7 @@ namespace {
 
 // LDS of a projection workgroup: u (the staged input), the residual rows and the down
 // rows of its O/down share; at least the attention's LDS.
-size_t step_lds(int H, int F, int qrows, int B, int hd, int* dres_off, int* rows_lds) {
+size_t step_lds(int H, int F, int qrows, int kvrows, int B, int hd, int* dres_off, int* rows_lds, int* part_off) {
   int kmax = H > F ? H : F;
   if (qrows > kmax) kmax = qrows;
   const size_t ub = (size_t)B * (kmax + 8) * 4;
@@ -232,7 +233,20 @@ size_t step_lds(int H, int F, int qrows, int B, int hd, int* dres_off, int* rows
   const int rows = 2 * (per > 4 ? per : 4);
   *dres_off = (int)off;
   *rows_lds = rows;
-  const size_t lds = off + 2 * (size_t)rows * 4 * sizeof(float);   // residual rows, then down rows
+  size_t lds = off + 2 * (size_t)rows * 4 * sizeof(float);   // residual rows, then down rows
+  // partial sums: the most pairs a workgroup gets in any pass (at least 64 projection
+  // workgroups), times the chunks of that pass's K
+  const int BT = B <= 1 ? 1 : B <= 2 ? 2 : 4;
+  auto share = [](int pairs) { return (pairs + kStepMinGemvBlocks - 1) / kStepMinGemvBlocks; };
+  size_t pf = rw_part_floats(share((qrows + 2 * kvrows + 1) / 2), H, 8, BT);
+  const size_t f_gu = rw_part_floats(share(F), H, 8, BT);
+  const size_t f_d = rw_part_floats(share(P), F, 8, BT);
+  const size_t f_o = rw_part_floats(share(P), qrows, 8, BT);
+  if (f_gu > pf) pf = f_gu;
+  if (f_d > pf) pf = f_d;
+  if (f_o > pf) pf = f_o;
+  *part_off = (int)((lds + 15) / 16 * 16);
+  lds = (size_t)*part_off + pf * sizeof(float);
   const size_t al = hd == 128 ? sizeof(AttnLds<uint16_t, 128>) : sizeof(AttnLds<uint16_t, 64>);
   return lds > al ? lds : al;
 }
@@ -270,7 +284,7 @@ int step_plan(StepParams& sp, size_t* lds_out, hipError_t* err) {
       sp.n_split < 1 || sp.n_split > kAttnMaxSplits || sp.L < 1 || !sp.layers || !sp.sync || !sp.prog || !sp.err || !sp.xs || !sp.qs || !sp.os || !sp.as)
     return 0;
   sp.n_attn = sp.n_split * sp.nkv * sp.B;
-  const size_t lds = step_lds(sp.H, sp.F, qrows, sp.B, sp.hd, &sp.dres_off, &sp.rows_lds);
+  const size_t lds = step_lds(sp.H, sp.F, qrows, sp.nkv * sp.hd, sp.B, sp.hd, &sp.dres_off, &sp.rows_lds, &sp.part_off);
   *lds_out = lds;
   const int bt = sp.B <= 1 ? 1 : sp.B <= 2 ? 2 : 4;
   int blocks = 0;

@@ -41,14 +41,15 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
     const int pr0 = (int)((long long)blk * P / nb);
     const int pr1 = (int)((long long)(blk + 1) * P / nb);
     float* dres = reinterpret_cast<float*>(lds_raw + mp.dres_off);
-    const int epoch = *mp.d_epoch;
-    rw_pass<WT, BT, VPL, RW_OUT_LDS>(mp.prob[0], pr0, pr1, blk, u, dres, RwWait{}, sh);
+    const int epoch = mp.d_epoch ? *gbl(mp.d_epoch) : 0;
+    float* part = reinterpret_cast<float*>(lds_raw + mp.part_off);
+    rw_pass<WT, BT, VPL, RW_OUT_LDS>(mp.prob[0], pr0, pr1, blk, u, dres, RwWait{}, sh, part);
     __syncthreads();                               // u is restaged by the second pass
     RwWait wt;
     wt.flag = mp.wait_flag;
     wt.epoch = epoch;
     wt.err = mp.err;
-    rw_pass<WT, BT, VPL, RW_OUT_ADD2_LDS>(mp.prob[1], pr0, pr1, blk, u, dres, wt, sh);
+    rw_pass<WT, BT, VPL, RW_OUT_ADD2_LDS>(mp.prob[1], pr0, pr1, blk, u, dres, wt, sh, part);
   } else {
     const int pi = (NP > 1 && blk >= mp.blk_begin[1]) ? 1 : 0;
     const int lb = blk - mp.blk_begin[pi];
@@ -57,7 +58,8 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
     const int P = (p.N + 1) / 2;
     const int pr0 = (int)((long long)lb * P / nb);
     const int pr1 = (int)((long long)(lb + 1) * P / nb);
-    rw_pass<WT, BT, VPL, RW_OUT_EPI>(p, pr0, pr1, lb, u, nullptr, RwWait{}, sh);
+    rw_pass<WT, BT, VPL, RW_OUT_EPI>(p, pr0, pr1, lb, u, nullptr, RwWait{}, sh,
+                                     reinterpret_cast<float*>(lds_raw + mp.part_off));
   }
 }
 
@@ -115,17 +117,13 @@ void rw_split_blocks(MultiGemvParams& mp, int target) {
   if (mp.np == 1) mp.blk_begin[2] = mp.blk_begin[1];
 }
 
-// vectors per lane per pipeline unit: the whole row when it fits in 4 (256 vectors,
-// 4 KB of bf16), else units of 4 -- two buffers of 2 rows x 4 x 16 B stay in registers
-int rw_vpl(int nvec) {
-  for (int v : {1, 2})
-    if (64 * v >= nvec) return v;
-  return 4;
-}
 
+// gemv_lds: LDS of a GEMV workgroup before its partial sums; attn_lds: of an attention
+// workgroup (0 if none).  The partial sums go after gemv_lds, sized for the split.
 template <typename WT, int BT, int VPL, int HDA, int HPW, int NP>
-hipError_t rw_go(MultiGemvParams& mp, size_t lds, hipStream_t s) {
+hipError_t rw_go(MultiGemvParams& mp, size_t gemv_lds, size_t attn_lds, hipStream_t s) {
   auto fn = gemv_rw_kernel<WT, BT, VPL, HDA, HPW, NP>;
+  const size_t lds = gemv_lds > attn_lds ? gemv_lds : attn_lds;
   // resident workgroups of this instance at this LDS size (queried once per instance
   // and size): the GEMV workgroups of one launch are sized to fill the device once
   static size_t cached_lds = 0;
@@ -159,15 +157,38 @@ hipError_t rw_go(MultiGemvParams& mp, size_t lds, hipStream_t s) {
   } else {
     rw_split_blocks(mp, target);
   }
+  // partial sums: the most pairs any workgroup of a problem gets, times its chunks
+  const int vec = sizeof(WT) == 2 ? 8 : 4;
+  size_t part = 0;
+  for (int i = 0; i < (NP == 3 ? 1 : mp.np); ++i) {
+    const int nb = mp.blk_begin[i + 1] - mp.blk_begin[i];
+    const int P = (mp.prob[i].N + 1) / 2;
+    const int pairs = (P + nb - 1) / nb;
+    size_t f = rw_part_floats(pairs, mp.prob[i].K, vec, BT);
+    if (NP == 3) {
+      const size_t f1 = rw_part_floats(pairs, mp.prob[1].K, vec, BT);
+      if (f1 > f) f = f1;
+    }
+    if (f > part) part = f;
+  }
+  mp.part_off = (int)((gemv_lds + 15) / 16 * 16);
+  size_t total = (size_t)mp.part_off + part * sizeof(float);
+  if (attn_lds > total) total = attn_lds;
+  static size_t attr_lds = 65536;
+  if (total > attr_lds) {
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)total);
+    if (e != hipSuccess) return e;
+    attr_lds = total;
+  }
   const int grid = mp.n_attn + (NP == 3 ? mp.blk_begin[1] : mp.blk_begin[mp.np]);
-  launch_timed(fn, dim3(grid), dim3(256), (uint32_t)lds, s, mp);
+  launch_timed(fn, dim3(grid), dim3(256), (uint32_t)total, s, mp);
   return hipGetLastError();
 }
 
 // Attention workgroups are only fused into launches with 4 vectors per lane per unit
 // (every down projection here); the caller launches them separately otherwise.
 template <typename WT, int BT, int VPL>
-hipError_t rw_hda(MultiGemvParams& mp, int hda, size_t lds, hipStream_t s) {
+hipError_t rw_hda(MultiGemvParams& mp, int hda, size_t lds, size_t alds, hipStream_t s) {
   if constexpr (VPL == 4) {
     // attention rides with one problem, or with a paired launch; the fp32 path needs the
     // heads-per-wave instance, the bf16 (matrix core) path has one
@@ -176,43 +197,38 @@ hipError_t rw_hda(MultiGemvParams& mp, int hda, size_t lds, hipStream_t s) {
     const int hpw = hda ? (sizeof(WT) == 2 ? 1 : attn_hpw(mp.attn.nq / mp.attn.nkv)) : 0;
     if (hda != 0 && mp.np != 1 && !(sizeof(WT) == 2 && mp.paired)) return hipErrorInvalidValue;
     if (hda == 128) {
-      if (mp.paired) return rw_go<WT, BT, VPL, 128, 1, 3>(mp, lds, s);
-      if (hpw == 1) return rw_go<WT, BT, VPL, 128, 1, 1>(mp, lds, s);
-      if (hpw == 2) return rw_go<WT, BT, VPL, 128, 2, 1>(mp, lds, s);
-      return rw_go<WT, BT, VPL, 128, 4, 1>(mp, lds, s);
+      if (mp.paired) return rw_go<WT, BT, VPL, 128, 1, 3>(mp, lds, alds, s);
+      if (hpw == 1) return rw_go<WT, BT, VPL, 128, 1, 1>(mp, lds, alds, s);
+      if (hpw == 2) return rw_go<WT, BT, VPL, 128, 2, 1>(mp, lds, alds, s);
+      return rw_go<WT, BT, VPL, 128, 4, 1>(mp, lds, alds, s);
     }
     if (hda == 64) {
-      if (mp.paired) return rw_go<WT, BT, VPL, 64, 1, 3>(mp, lds, s);
-      if (hpw == 1) return rw_go<WT, BT, VPL, 64, 1, 1>(mp, lds, s);
-      if (hpw == 2) return rw_go<WT, BT, VPL, 64, 2, 1>(mp, lds, s);
-      return rw_go<WT, BT, VPL, 64, 4, 1>(mp, lds, s);
+      if (mp.paired) return rw_go<WT, BT, VPL, 64, 1, 3>(mp, lds, alds, s);
+      if (hpw == 1) return rw_go<WT, BT, VPL, 64, 1, 1>(mp, lds, alds, s);
+      if (hpw == 2) return rw_go<WT, BT, VPL, 64, 2, 1>(mp, lds, alds, s);
+      return rw_go<WT, BT, VPL, 64, 4, 1>(mp, lds, alds, s);
     }
   }
   if (hda != 0) return hipErrorInvalidValue;
-  if (mp.paired) return sizeof(WT) == 2 ? rw_go<WT, BT, VPL, 0, 0, 3>(mp, lds, s) : hipErrorInvalidValue;
-  if (mp.np == 2) return rw_go<WT, BT, VPL, 0, 0, 2>(mp, lds, s);
-  return rw_go<WT, BT, VPL, 0, 0, 1>(mp, lds, s);
-}
-
-template <typename WT, int BT>
-hipError_t rw_vpl_go(MultiGemvParams& mp, int vpl, int hda, size_t lds, hipStream_t s) {
-  switch (vpl) {
-    case 1: return rw_hda<WT, BT, 1>(mp, hda, lds, s);
-    case 2: return rw_hda<WT, BT, 2>(mp, hda, lds, s);
-    default: return rw_hda<WT, BT, 4>(mp, hda, lds, s);
-  }
+  if (mp.paired) return sizeof(WT) == 2 ? rw_go<WT, BT, VPL, 0, 0, 3>(mp, lds, 0, s) : hipErrorInvalidValue;
+  if (mp.np == 2) return rw_go<WT, BT, VPL, 0, 0, 2>(mp, lds, 0, s);
+  return rw_go<WT, BT, VPL, 0, 0, 1>(mp, lds, 0, s);
 }
 
 template <typename WT>
-hipError_t rw_bt_go(MultiGemvParams& mp, int bt, int vpl, int hda, size_t lds, hipStream_t s) {
-  if (bt == 1) return rw_vpl_go<WT, 1>(mp, vpl, hda, lds, s);
-  if (bt == 2) return rw_vpl_go<WT, 2>(mp, vpl, hda, lds, s);
-  return rw_vpl_go<WT, 4>(mp, vpl, hda, lds, s);
+hipError_t rw_bt_go(MultiGemvParams& mp, int bt, int hda, size_t lds, size_t alds, hipStream_t s) {
+  if (bt == 1) return rw_hda<WT, 1, kRwVpl>(mp, hda, lds, alds, s);
+  if (bt == 2) return rw_hda<WT, 2, kRwVpl>(mp, hda, lds, alds, s);
+  return rw_hda<WT, 4, kRwVpl>(mp, hda, lds, alds, s);
 }
 
 }  // namespace
 
-bool gemv_rw_attn_fusable(int wdtype, int K) { return rw_vpl(K / (wdtype == W_BF16 ? 8 : 4)) == 4; }
+bool gemv_rw_attn_fusable(int wdtype, int K) {
+  (void)wdtype;
+  (void)K;
+  return true;
+}
 
 namespace {
 // LDS of a paired launch: u for the wider input, then prob[0]'s rows of one workgroup
@@ -253,10 +269,9 @@ hipError_t launch_gemv_paired(const GemvParams& first, const GemvParams& second,
   mp.wait_flag = attn.done_flag;
   mp.d_epoch = attn.d_epoch;
   mp.err = err;
-  size_t lds = rw_pair_lds(wdt, first.K, second.K, first.N, B, &mp.dres_off);
+  const size_t lds = rw_pair_lds(wdt, first.K, second.K, first.N, B, &mp.dres_off);
   const size_t al = attn.hd == 128 ? sizeof(AttnLds<uint16_t, 128>) : sizeof(AttnLds<uint16_t, 64>);
-  if (al > lds) lds = al;
-  return rw_bt_go<uint16_t>(mp, rw_bt(B), 4, attn.hd, lds, s);
+  return rw_bt_go<uint16_t>(mp, rw_bt(B), attn.hd, lds, al, s);
 }
 
 bool gemv_rw_supported(int wdtype, int K, int B) {
@@ -282,24 +297,22 @@ hipError_t launch_gemv_multi(const GemvParams* probs, int np, const AttnDecodePa
   MultiGemvParams mp{};
   mp.np = np;
   for (int i = 0; i < np; ++i) mp.prob[i] = probs[i];
-  size_t lds = (size_t)B * (K + (wdt == W_BF16 ? 8 : 4)) * 4;
+  const size_t lds = (size_t)B * (K + (wdt == W_BF16 ? 8 : 4)) * 4;
+  size_t al = 0;
   int hda = 0;
   if (attn) {
-    if (rw_vpl(K / (wdt == W_BF16 ? 8 : 4)) != 4) return hipErrorInvalidValue;
     if (attn->nkv < 1 || attn->nq % attn->nkv != 0 || attn->nq / attn->nkv > kAttnMaxGroup ||
         attn->n_split > kAttnMaxSplits || (attn->hd != 64 && attn->hd != 128) || attn->wdtype != wdt)
       return hipErrorInvalidValue;
     mp.attn = *attn;
     mp.n_attn = attn->n_split * attn->nkv * attn->B;
     hda = attn->hd;
-    const size_t al = wdt == W_BF16 ? (hda == 128 ? sizeof(AttnLds<uint16_t, 128>) : sizeof(AttnLds<uint16_t, 64>))
-                                    : (hda == 128 ? sizeof(AttnLds<float, 128>) : sizeof(AttnLds<float, 64>));
-    if (al > lds) lds = al;
+    al = wdt == W_BF16 ? (hda == 128 ? sizeof(AttnLds<uint16_t, 128>) : sizeof(AttnLds<uint16_t, 64>))
+                       : (hda == 128 ? sizeof(AttnLds<float, 128>) : sizeof(AttnLds<float, 64>));
   }
-  const int vpl = rw_vpl(K / (wdt == W_BF16 ? 8 : 4));
   const int bt = rw_bt(B);
-  const hipError_t e = wdt == W_BF16 ? rw_bt_go<uint16_t>(mp, bt, vpl, hda, lds, s)
-                                     : rw_bt_go<float>(mp, bt, vpl, hda, lds, s);
+  const hipError_t e = wdt == W_BF16 ? rw_bt_go<uint16_t>(mp, bt, hda, lds, al, s)
+                                     : rw_bt_go<float>(mp, bt, hda, lds, al, s);
   if (blocks_out)
     for (int i = 0; i < np; ++i) blocks_out[i] = mp.blk_begin[i + 1] - mp.blk_begin[i];
   return e;

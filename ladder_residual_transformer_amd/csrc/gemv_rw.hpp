@@ -173,9 +173,21 @@ struct RwShared {
 // LDS) becomes out2; coherent stores.
 enum { RW_OUT_EPI = 0, RW_OUT_LDS = 1, RW_OUT_ADD2_LDS = 2, RW_OUT_ADD2_LDSRES = 3 };
 
+// Vectors of 16 bytes per lane per unit of the row-wave GEMV; a unit covers 64 * kRwVpl
+// vectors of two rows.  Fixed, because the chunking is part of the arithmetic.
+constexpr int kRwVpl = 4;
+
+// LDS floats of the partial sums of a pass over n_pairs row pairs of K inputs.
+__host__ __device__ inline size_t rw_part_floats(int n_pairs, int K, int vec, int BT) {
+  const int nvec = K / vec;
+  const int nchunk = (nvec + 64 * kRwVpl - 1) / (64 * kRwVpl);
+  return (size_t)(n_pairs > 0 ? n_pairs : 0) * nchunk * 2 * BT;
+}
+
 // One pass of the row-wave GEMV over row pairs [pr0, pr1) of problem p (this
 // workgroup's share).  OUT: the problem's own epilogue; the rows (times inv_rms) into
-// dres[row - 2*pr0][b]; or EPI_ADD2 with dres in place of add2.  wt: if it names a flag
+// dres[row - 2*pr0][b]; or EPI_ADD2 with dres in place of add2.  part: LDS scratch of
+// rw_part_floats(pr1 - pr0, p.K, ...) floats.  wt: if it names a flag
 // or progress words, the first weight unit is issued, then the workgroup waits for the
 // signal before it stages the input.  COH: the outputs are read by other workgroups of
 // the same kernel (coherent stores, coherent waits); the input is read with ordinary
@@ -183,7 +195,7 @@ enum { RW_OUT_EPI = 0, RW_OUT_LDS = 1, RW_OUT_ADD2_LDS = 2, RW_OUT_ADD2_LDSRES =
 // producers' signal (a cached copy would be stale).
 template <typename WT, int BT, int VPL, int OUT, bool COH = false>
 __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, int lb, float* u, float* dres,
-                                        const RwWait& wt, RwShared& sh, float* res = nullptr) {
+                                        const RwWait& wt, RwShared& sh, float* part, float* res = nullptr) {
   constexpr int VEC = Vec<WT>::N;
   constexpr int CHUNK = 64 * VPL;                 // vectors of a row one wave covers per step
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -191,17 +203,23 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
   const int nvec = K / VEC;
   const int nchunk = (nvec + CHUNK - 1) / CHUNK;
 
-  // This wave's work is a sequence of units: unit i is chunk (i % nchunk) of its pair
-  // number (i / nchunk); its pairs are pr0 + wid, pr0 + wid + 4, ...  Two register
-  // buffers form a pipeline: the loads of unit i+1 are in flight while unit i is
-  // multiplied.  Loads are unconditional (addresses clamped into the matrix) so that no
-  // branch separates a load from its use; lanes past the end of a row read the zero
-  // pad of u instead, and a missing odd row is discarded by the epilogue.
-  const int my_pairs = pr1 > pr0 + wid ? (pr1 - pr0 - wid + 3) / 4 : 0;
-  const int n_units = my_pairs * nchunk;
+  // The workgroup's work is (pair, chunk) units, unit j*nchunk + c being chunk c (CHUNK
+  // vectors of 16 bytes) of pair pr0 + j; wave w takes units w, w+4, w+8, ... so that
+  // its share differs from the others' by at most one unit.  Two register buffers form
+  // a pipeline: the loads of the wave's next unit are in flight while its current one is
+  // multiplied.  Each unit's two partial dot products per batch row go to part[] (LDS);
+  // after a barrier every (pair, batch row) sums its chunks in chunk order and runs the
+  // epilogue.  The sums depend only on K and CHUNK, so every launch shape and schedule
+  // gives the same bits.  Loads are unconditional (addresses clamped into the matrix) so
+  // that no branch separates a load from its use; lanes past the end of a row read the
+  // zero pad of u instead, and a missing odd row is discarded by the epilogue.
+  const int n_pairs = pr1 > pr0 ? pr1 - pr0 : 0;
+  const int total_units = n_pairs * nchunk;
+  const int n_units = total_units > wid ? (total_units - wid + 3) / 4 : 0;
   uint4 wa[2][VPL], wb[2][VPL];
-  auto load_unit = [&](uint4 (&w)[2][VPL], int unit) {
-    const int pair = pr0 + wid + 4 * (unit / nchunk), c = unit % nchunk;
+  auto load_unit = [&](uint4 (&w)[2][VPL], int i) {
+    const int un = wid + 4 * i;
+    const int pair = pr0 + un / nchunk, c = un % nchunk;
     const int n0 = 2 * pair;
     const WT* r0 = rw_row_ptr<WT>(p.rows, n0, K);
     const WT* r1 = rw_row_ptr<WT>(p.rows, min(n0 + 1, p.N - 1), K);
@@ -304,16 +322,15 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
 #pragma unroll
   for (int b = 0; b < BT; ++b) inv_b[b] = sh.inv[b];
 
-  // ---- row pairs
-  float best = -INFINITY;
-  int bidx = INT_MAX;
-  float acc[2][BT];
+  // ---- units
+  auto compute_unit = [&](const uint4 (&w)[2][VPL], int i) {
+    const int un = wid + 4 * i;
+    const int c = un % nchunk;
+    float acc[2][BT];
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
-  auto compute_unit = [&](const uint4 (&w)[2][VPL], int unit) {
-    const int c = unit % nchunk;
+      for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = c * CHUNK + lane + 64 * v;
@@ -339,76 +356,89 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
         }
       }
     }
-    if (c == nchunk - 1) {                      // pair complete: reduce and finish it
-      const int pair = pr0 + wid + 4 * (unit / nchunk);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int b = 0; b < BT; ++b) {
-        const float y0 = wave_sum(acc[0][b]);
-        const float y1 = wave_sum(acc[1][b]);
-        if (lane == b && b < B) {
-          if constexpr (OUT == RW_OUT_EPI) {
-            if constexpr (COH) rw_epilogue_coh<WT>(p, pair, b, y0, y1, inv_b[b]);
-            else rw_epilogue<WT>(p, pair, b, y0, y1, inv_b[b], best, bidx);
-          } else if constexpr (OUT == RW_OUT_LDS) {
-            const int r = 2 * (pair - pr0);
-            dres[r * BT + b] = y0 * inv_b[b];
-            dres[(r + 1) * BT + b] = y1 * inv_b[b];
-          } else if constexpr (OUT == RW_OUT_ADD2_LDSRES) {
-            const int r = 2 * (pair - pr0), n0 = 2 * pair;
-            const float t0 = res[r * BT + b] + y0 * inv_b[b];
-            const float s0 = t0 + dres[r * BT + b];
-            res[r * BT + b] = s0;
-            st_coh(p.out + (size_t)b * p.ldo + n0, t0);
-            st_coh(p.out2 + (size_t)b * p.ldo + n0, s0);
-            if (n0 + 1 < p.N) {
-              const float t1 = res[(r + 1) * BT + b] + y1 * inv_b[b];
-              const float s1 = t1 + dres[(r + 1) * BT + b];
-              res[(r + 1) * BT + b] = s1;
-              st_coh(p.out + (size_t)b * p.ldo + n0 + 1, t1);
-              st_coh(p.out2 + (size_t)b * p.ldo + n0 + 1, s1);
-            }
-          } else if constexpr (COH) {           // EPI_ADD2, second addend from dres
-            const int r = 2 * (pair - pr0), n0 = 2 * pair;
-            const float t0 = ld_coh(p.xres + (size_t)b * p.ldr + n0) + y0 * inv_b[b];
-            st_coh(p.out + (size_t)b * p.ldo + n0, t0);
-            st_coh(p.out2 + (size_t)b * p.ldo + n0, t0 + dres[r * BT + b]);
-            if (n0 + 1 < p.N) {
-              const float t1 = ld_coh(p.xres + (size_t)b * p.ldr + n0 + 1) + y1 * inv_b[b];
-              st_coh(p.out + (size_t)b * p.ldo + n0 + 1, t1);
-              st_coh(p.out2 + (size_t)b * p.ldo + n0 + 1, t1 + dres[(r + 1) * BT + b]);
-            }
-          } else {
-            const int r = 2 * (pair - pr0), n0 = 2 * pair;
-            const float t0 = p.xres[(size_t)b * p.ldr + n0] + y0 * inv_b[b];
-            p.out[(size_t)b * p.ldo + n0] = t0;
-            p.out2[(size_t)b * p.ldo + n0] = t0 + dres[r * BT + b];
-            if (n0 + 1 < p.N) {
-              const float t1 = p.xres[(size_t)b * p.ldr + n0 + 1] + y1 * inv_b[b];
-              p.out[(size_t)b * p.ldo + n0 + 1] = t1;
-              p.out2[(size_t)b * p.ldo + n0 + 1] = t1 + dres[(r + 1) * BT + b];
-            }
-          }
-        }
-        acc[0][b] = 0.f;
-        acc[1][b] = 0.f;
+        const float y = wave_sum(acc[r][b]);
+        if (lane == 0) part[((size_t)un * 2 + r) * BT + b] = y;
       }
-    }
   };
-  // the scheduling barriers keep the next unit's loads issued ahead of the current
-  // unit's arithmetic (under register pressure the scheduler would sink them)
   for (int i = 0; i < n_units; i += 2) {
     if (i + 1 < n_units) load_unit(wb, i + 1);
-    __builtin_amdgcn_sched_barrier(0);
     compute_unit(wa, i);
     if (i + 1 < n_units) {
       if (i + 2 < n_units) load_unit(wa, i + 2);
-      __builtin_amdgcn_sched_barrier(0);
       compute_unit(wb, i + 1);
+    }
+  }
+  __syncthreads();
+
+  // ---- epilogues: thread t finishes pair pr0 + t / BT for batch row t % BT
+  float best = -INFINITY;
+  int bidx = INT_MAX;
+  for (int t = tid; t < n_pairs * BT; t += 256) {
+    const int j = t / BT, b = t % BT;
+    if (b >= B) continue;
+    const int pair = pr0 + j;
+    float y0 = 0.f, y1 = 0.f;
+    for (int c = 0; c < nchunk; ++c) {
+      y0 += part[((size_t)(j * nchunk + c) * 2 + 0) * BT + b];
+      y1 += part[((size_t)(j * nchunk + c) * 2 + 1) * BT + b];
+    }
+    if constexpr (OUT == RW_OUT_EPI) {
+      if constexpr (COH) rw_epilogue_coh<WT>(p, pair, b, y0, y1, inv_b[b]);
+      else rw_epilogue<WT>(p, pair, b, y0, y1, inv_b[b], best, bidx);
+    } else if constexpr (OUT == RW_OUT_LDS) {
+      const int r = 2 * j;
+      dres[r * BT + b] = y0 * inv_b[b];
+      dres[(r + 1) * BT + b] = y1 * inv_b[b];
+    } else if constexpr (OUT == RW_OUT_ADD2_LDSRES) {
+      const int r = 2 * j, n0 = 2 * pair;
+      const float t0 = res[r * BT + b] + y0 * inv_b[b];
+      const float s0 = t0 + dres[r * BT + b];
+      res[r * BT + b] = s0;
+      st_coh(p.out + (size_t)b * p.ldo + n0, t0);
+      st_coh(p.out2 + (size_t)b * p.ldo + n0, s0);
+      if (n0 + 1 < p.N) {
+        const float t1 = res[(r + 1) * BT + b] + y1 * inv_b[b];
+        const float s1 = t1 + dres[(r + 1) * BT + b];
+        res[(r + 1) * BT + b] = s1;
+        st_coh(p.out + (size_t)b * p.ldo + n0 + 1, t1);
+        st_coh(p.out2 + (size_t)b * p.ldo + n0 + 1, s1);
+      }
+    } else if constexpr (COH) {                    // EPI_ADD2, second addend from dres
+      const int r = 2 * j, n0 = 2 * pair;
+      const float t0 = ld_coh(p.xres + (size_t)b * p.ldr + n0) + y0 * inv_b[b];
+      st_coh(p.out + (size_t)b * p.ldo + n0, t0);
+      st_coh(p.out2 + (size_t)b * p.ldo + n0, t0 + dres[r * BT + b]);
+      if (n0 + 1 < p.N) {
+        const float t1 = ld_coh(p.xres + (size_t)b * p.ldr + n0 + 1) + y1 * inv_b[b];
+        st_coh(p.out + (size_t)b * p.ldo + n0 + 1, t1);
+        st_coh(p.out2 + (size_t)b * p.ldo + n0 + 1, t1 + dres[(r + 1) * BT + b]);
+      }
+    } else {
+      const int r = 2 * j, n0 = 2 * pair;
+      const float t0 = p.xres[(size_t)b * p.ldr + n0] + y0 * inv_b[b];
+      p.out[(size_t)b * p.ldo + n0] = t0;
+      p.out2[(size_t)b * p.ldo + n0] = t0 + dres[r * BT + b];
+      if (n0 + 1 < p.N) {
+        const float t1 = p.xres[(size_t)b * p.ldr + n0 + 1] + y1 * inv_b[b];
+        p.out[(size_t)b * p.ldo + n0 + 1] = t1;
+        p.out2[(size_t)b * p.ldo + n0 + 1] = t1 + dres[(r + 1) * BT + b];
+      }
     }
   }
 
   if (OUT == RW_OUT_EPI && p.epi == EPI_LOGITS) {
-    // per-block greedy candidate (lowest index among equal maxima); merged by argmax_finalize
+    // per-block greedy candidate (lowest index among equal maxima), merged by
+    // argmax_finalize: lanes l and l ^ o (o a multiple of BT) hold the same batch row
+#pragma unroll
+    for (int o = 32; o >= BT; o >>= 1) {
+      const float ov = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bidx, o, 64);
+      if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+    }
     if (lane < BT) { sh.wbv[wid][lane] = best; sh.wbi[wid][lane] = bidx; }
     __syncthreads();
     if (tid < BT) {

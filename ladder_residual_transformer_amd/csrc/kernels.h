@@ -90,6 +90,7 @@ struct MultiGemvParams {
   const int* wait_flag;
   const int* d_epoch;
   int* err;               // set to 1 if a wait ever gives up (never expected)
+  int part_off;           // LDS byte offset of the partial sums (set by the launcher)
 };
 bool gemv_rw_supported(int wdtype, int K, int B);
 bool gemv_rw_attn_fusable(int wdtype, int K);   // a launch of this K can carry attention workgroups
@@ -136,6 +137,7 @@ struct StepParams {
   int n_attn;                          // set by the launcher
   int dres_off;                        // set by the launcher
   int rows_lds;                        // set by the launcher
+  int part_off;                        // set by the launcher
 };
 bool step_supported(int wdtype, int H, int F, int qrows, int B, int hd, int G);
 // true when every workgroup of the launch can be resident (queries the occupancy once)

@@ -123,7 +123,7 @@ struct ladder_ctx {
   bool all_ladder = false;           // every layer follows the ladder rule
   StreamScratch sc[2];
 
-  int sched = LADDER_SCHED_PERSISTENT;
+  int sched = LADDER_SCHED_FUSED;
   int use_graph = 1;
   int trace_kind = -1;               // kernel kind timed with events during decode (-1: none)
   std::vector<hipEvent_t> trace_ev;  // start/end pairs, one pair per traced launch
