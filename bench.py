@@ -272,6 +272,11 @@ def main():
     ku = model.time_kernels(B, reps=3)
     log(f"[bench] kernel us/launch in isolation: " + ", ".join(f"{k} {v:.2f}" for k, v in ku.items()))
 
+    # the part's measured streaming-read ceiling (a plain read kernel over 4 GiB)
+    from ladder_residual_transformer_amd import abi
+    ceiling = abi.ladder_read_probe(torch.cuda.current_stream().cuda_stream, 4 << 30, 5)
+    log(f"[bench] streaming-read ceiling {ceiling:.0f} GB/s ({100 * ceiling * 1e9 / HBM_PEAK:.1f}% of the 8 TB/s peak)")
+
     cpu = None
     if not args.no_cpu_baseline:
         t = time.time()
@@ -293,7 +298,9 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": traffic,
                      "bytes_per_launch": int(bytes_launch), "us_per_launch": round(us_launch, 3),
-                     "launches_timed": n_launch, "traced_ms_per_step": round(dt_traced * 1e3 / args.steps, 4)},
+                     "launches_timed": n_launch, "traced_ms_per_step": round(dt_traced * 1e3 / args.steps, 4),
+                     "read_ceiling_gbs": round(ceiling, 1),
+                     "frac_of_read_ceiling": round(achieved / ceiling, 4)},
         "kernels_us_isolated": {k: round(v, 3) for k, v in ku.items()},
         "cpu_baseline": cpu,
     }

@@ -183,6 +183,13 @@ ladder_status ladder_sync(ladder_ctx* ctx);
  * overwrites; requires at least one filled position.  Blocks until done. */
 ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, float* us_out);
 
+/* Measurement aid: the HBM streaming-read ceiling of the current device.  Reads a
+ * bytes-sized device buffer (allocated and freed here; >= 1 MiB) with plain 16-byte
+ * loads, reps times for each of 2, 4 and 8 workgroups per CU, on `stream` (a
+ * hipStream_t, NULL = the null stream), and stores the best rate in GB/s (1e9 B/s) in
+ * *gbs_out.  Blocks until done.  LADDER_ERR_OOM if the buffer cannot be allocated. */
+ladder_status ladder_read_probe(void* stream, size_t bytes, int32_t reps, float* gbs_out);
+
 /* Measurement aid.  kind in [0, LADDER_N_KERNELS): from the next decode step on, every
  * launch of that kernel kind gets a pair of HIP events on the stream it runs on, taken
  * from the dispatch's own begin and end timestamps (hipExtLaunchKernelGGL; for a kind

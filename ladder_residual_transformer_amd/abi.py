@@ -34,7 +34,7 @@ LADDER_SCHED_PERSISTENT = 4
 
 EXPORTED = ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_filled",
             "ladder_workspace_bytes", "ladder_sync", "ladder_free", "ladder_status_string", "ladder_last_error",
-            "ladder_time_kernels", "ladder_trace_kernel", "ladder_trace_result")
+            "ladder_time_kernels", "ladder_trace_kernel", "ladder_trace_result", "ladder_read_probe")
 
 LADDER_KERNEL_LAYER_STACK = 9
 LADDER_N_KERNELS = 10
@@ -92,6 +92,7 @@ def load(path: str = LIB_PATH):
     lib.ladder_trace_kernel.argtypes = [c_void_p, c_int32]
     lib.ladder_trace_result.argtypes = [c_void_p, POINTER(c_float), POINTER(c_int32)]
     lib.ladder_free.argtypes = [c_void_p]
+    lib.ladder_read_probe.argtypes = [c_void_p, c_size_t, c_int32, POINTER(c_float)]
     lib.ladder_free.restype = None
     lib.ladder_status_string.argtypes = [c_int32]
     lib.ladder_status_string.restype = ctypes.c_char_p
@@ -99,7 +100,7 @@ def load(path: str = LIB_PATH):
     lib.ladder_last_error.restype = ctypes.c_char_p
     for name in ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_filled",
                  "ladder_workspace_bytes", "ladder_sync", "ladder_time_kernels", "ladder_trace_kernel",
-                 "ladder_trace_result"):
+                 "ladder_trace_result", "ladder_read_probe"):
         getattr(lib, name).restype = c_int32
     _lib = lib
     return lib
@@ -175,6 +176,13 @@ def ladder_trace_result(ctx: int):
     us, n = c_float(), c_int32()
     _check(ctx, load().ladder_trace_result(c_void_p(ctx), ctypes.byref(us), ctypes.byref(n)), "ladder_trace_result")
     return float(us.value), int(n.value)
+
+
+def ladder_read_probe(stream: int, nbytes: int, reps: int) -> float:
+    """Streaming-read ceiling of the current device in GB/s (allocates nbytes of device memory)."""
+    g = c_float()
+    _check(0, load().ladder_read_probe(c_void_p(stream or None), nbytes, reps, ctypes.byref(g)), "ladder_read_probe")
+    return float(g.value)
 
 
 def ladder_free(ctx: int) -> None:

@@ -21,12 +21,40 @@ void launch_events_disarm() { launch_events() = LaunchEvents{}; }
 // x[m][:] = E[ids[m]][:] in fp32.  Ids outside [0, V) are clamped so a bad id cannot
 // read outside the table.
 template <typename WT>
-__global__ __launch_bounds__(256) void embed_kernel(const WT* table, int V, int H, const int* ids, float* x) {
-  const int m = blockIdx.x;
-  int id = ids[m];
+__device__ __forceinline__ void embed_row(const WT* table, int V, int H, int id, float* x) {
   id = id < 0 ? 0 : (id >= V ? V - 1 : id);
   const WT* row = table + (size_t)id * H;
-  for (int i = threadIdx.x; i < H; i += 256) x[(size_t)m * H + i] = load_w<WT>(row + i);
+  constexpr int VEC = Vec<WT>::N;                   // 16-byte vectors: 8 bf16 or 4 fp32
+  if (H % VEC == 0) {
+    const int nv = H / VEC;
+    for (int v0 = threadIdx.x; v0 < nv; v0 += 4 * 256) {
+      uint4 r[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {                 // the four loads in flight together
+        const int v = v0 + 256 * k;
+        r[k] = v < nv ? *(const uint4*)(row + (size_t)v * VEC) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int v = v0 + 256 * k;
+        if (v < nv) {
+          float f[VEC];
+          unpack16(r[k], f);
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4)
+            *(float4*)(x + (size_t)v * VEC + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+        }
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < H; i += 256) x[i] = load_w<WT>(row + i);
+  }
+}
+
+template <typename WT>
+__global__ __launch_bounds__(256) void embed_kernel(const WT* table, int V, int H, const int* ids, float* x) {
+  const int m = blockIdx.x;
+  embed_row<WT>(table, V, H, ids[m], x + (size_t)m * H);
 }
 
 template <typename WT>
@@ -109,13 +137,41 @@ __global__ __launch_bounds__(256) void add_kernel(const float* x, const float* y
   for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) out[i] = x[i] + y[i];
 }
 
-__global__ void decode_prologue_kernel(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, int* d_epoch) {
-  const int i = threadIdx.x;
-  if (i < B) ids_dst[i] = ids_src[i];
-  if (i == 0) {
-    *d_pos = pos;
-    if (d_epoch) *d_epoch += 1;
+// One decode step's prologue: workgroup b embeds token ids_src[b] into x row b;
+// workgroup 0 also keeps the ids, sets the position and bumps the step's epoch.
+template <typename WT>
+__global__ __launch_bounds__(256) void decode_prologue_kernel(const int* ids_src, int* ids_dst, int B, int* d_pos,
+                                                              int pos, int* d_epoch, const WT* table, int V, int H,
+                                                              float* x) {
+  const int b = blockIdx.x;
+  if (b == 0) {
+    const int i = threadIdx.x;
+    if (i < B) ids_dst[i] = ids_src[i];
+    if (i == 0) {
+      *d_pos = pos;
+      if (d_epoch) *d_epoch += 1;
+    }
   }
+  embed_row<WT>(table, V, H, ids_src[b], x + (size_t)b * H);
+}
+
+// Streaming read of n 16-byte vectors, each workgroup a contiguous share: the measured
+// HBM read ceiling of the part.  The sum only keeps the loads alive.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n, int iters,
+                                                         float* sink) {
+  const size_t base = (size_t)blockIdx.x * iters * 1024;
+  float acc = 0.f;
+  for (int it = 0; it < iters; ++it) {
+    uint4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const size_t i = base + ((size_t)it * 4 + k) * 256 + threadIdx.x;
+      v[k] = i < n ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc += __uint_as_float(v[k].x ^ v[k].y ^ v[k].z ^ v[k].w);
+  }
+  if (acc == 1.0f) sink[blockIdx.x] = acc;            // practically never
 }
 
 __global__ void epoch_bump_kernel(int* d_epoch) {
@@ -171,9 +227,24 @@ hipError_t launch_add(const float* x, const float* y, float* out, size_t n, hipS
   return hipGetLastError();
 }
 
+hipError_t launch_read_probe(const void* buf, size_t bytes, int grid, float* sink, hipStream_t s) {
+  const size_t n = bytes / 16;
+  if (grid < 1 || n == 0) return hipErrorInvalidValue;
+  const size_t per = (n + grid - 1) / grid;
+  const int iters = (int)((per + 1023) / 1024);
+  hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, s, (const uint4*)buf, n, iters, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_prologue(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, int* d_epoch,
-                                  hipStream_t s) {
-  hipLaunchKernelGGL(decode_prologue_kernel, dim3(1), dim3(64), 0, s, ids_src, ids_dst, B, d_pos, pos, d_epoch);
+                                  int wdtype, const void* table, int V, int H, float* x, hipStream_t s) {
+  if (B < 1 || B > 256) return hipErrorInvalidValue;
+  if (wdtype == W_BF16)
+    hipLaunchKernelGGL(decode_prologue_kernel<uint16_t>, dim3(B), dim3(256), 0, s, ids_src, ids_dst, B, d_pos, pos,
+                       d_epoch, (const uint16_t*)table, V, H, x);
+  else
+    hipLaunchKernelGGL(decode_prologue_kernel<float>, dim3(B), dim3(256), 0, s, ids_src, ids_dst, B, d_pos, pos,
+                       d_epoch, (const float*)table, V, H, x);
   return hipGetLastError();
 }
 

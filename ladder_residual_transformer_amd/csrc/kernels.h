@@ -188,8 +188,12 @@ hipError_t launch_rope_kv(int wdtype, const float* qkv, int B, int T, int start_
 hipError_t launch_swiglu(const float* gu, int M, int F, float* a, hipStream_t s);
 hipError_t launch_add(const float* x, const float* y, float* out, size_t n, hipStream_t s);
 hipError_t launch_epoch_bump(int* d_epoch, hipStream_t s);   // ++*d_epoch
-// ids_dst = ids_src, *d_pos = pos, ++*d_epoch (the step counter of in-kernel signals; nullable)
+// plain streaming read of bytes of buf by grid workgroups (sink: >= grid floats, never
+// read in practice)
+hipError_t launch_read_probe(const void* buf, size_t bytes, int grid, float* sink, hipStream_t s);
+// ids_dst = ids_src, *d_pos = pos, ++*d_epoch (the step counter of in-kernel signals;
+// nullable), and x[b][:] = table[ids_src[b]][:] in fp32 for b < B (B <= 256)
 hipError_t launch_decode_prologue(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, int* d_epoch,
-                                  hipStream_t s);
+                                  int wdtype, const void* table, int V, int H, float* x, hipStream_t s);
 
 }  // namespace ladder

@@ -739,12 +739,12 @@ ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream
   return run_gemv(ctx, lmhead_params(ctx, x, ldx, B), s);
 }
 
-// One decode step reading ids_dev / pos_dev, leaving logits/next in the context and
-// x_{2L} in dx[(2L) % 2].  Enqueued on s0 (possibly under graph capture).
+// One decode step from the embeddings the prologue left in dx[0] and pos_dev, leaving
+// logits/next in the context and x_{2L} in dx[(2L) % 2].  Enqueued on s0 (possibly under
+// graph capture).
 ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
   const ladder_config& g = ctx->cfg;
   ctx->trace_n = 0;
-  HIPCHK(launch_embed(ctx->wdt, ctx->w.tok_embed, g.vocab, g.hidden, ctx->ids_dev, B, ctx->dx[0], ctx->s0));
   ladder_status st;
   if (ctx->sched == LADDER_SCHED_PERSISTENT && step_usable(ctx, B)) {
     TRACE(LADDER_KERNEL_LAYER_STACK, ctx->s0, false);
@@ -1000,6 +1000,42 @@ ladder_status ladder_trace_result(ladder_ctx* ctx, float* mean_us, int32_t* coun
   return LADDER_OK;
 }
 
+ladder_status ladder_read_probe(void* stream, size_t bytes, int32_t reps, float* gbs_out) {
+  if (!gbs_out || reps < 1 || bytes < (1u << 20)) return LADDER_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev))
+    return LADDER_ERR_HIP;
+  void* buf = nullptr;
+  float* sink = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  ladder_status st = LADDER_OK;
+  float best = 0.f;
+  if (hipMalloc(&buf, bytes) != hipSuccess) return LADDER_ERR_OOM;
+  if (hipMalloc((void**)&sink, sizeof(float) * 8 * (size_t)ncu) != hipSuccess || hipMemsetAsync(buf, 1, bytes, s) ||
+      hipEventCreate(&e0) || hipEventCreate(&e1)) {
+    st = LADDER_ERR_HIP;
+  } else {
+    for (int per_cu : {2, 4, 8}) {
+      const int grid = per_cu * ncu;
+      if (launch_read_probe(buf, bytes, grid, sink, s) != hipSuccess) { st = LADDER_ERR_HIP; break; }   // warm
+      bool ok = hipEventRecord(e0, s) == hipSuccess;
+      for (int r = 0; r < reps && ok; ++r) ok = launch_read_probe(buf, bytes, grid, sink, s) == hipSuccess;
+      ok = ok && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+      float ms = 0.f;
+      if (!ok || hipEventElapsedTime(&ms, e0, e1) != hipSuccess || ms <= 0.f) { st = LADDER_ERR_HIP; break; }
+      const float gbs = (float)((double)bytes * reps / (ms * 1e-3) / 1e9);
+      if (gbs > best) best = gbs;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (sink) (void)hipFree(sink);
+  (void)hipFree(buf);
+  if (st == LADDER_OK) *gbs_out = best;
+  return st;
+}
+
 ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, float* us_out) {
   if (!ctx || !us_out || reps < 1) return LADDER_ERR_ARG;
   if (ctx->broken) return LADDER_ERR_HIP;
@@ -1143,7 +1179,8 @@ ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t 
   if (pos > ctx->filled) return fail(ctx, LADDER_ERR_STATE, "decode position after unfilled positions%s");
   ladder_status st = begin_call(ctx);
   if (st) return st;
-  HIPCHK(launch_decode_prologue(d_ids, ctx->ids_dev, B, ctx->pos_dev, pos, ctx->epoch, ctx->s0));
+  HIPCHK(launch_decode_prologue(d_ids, ctx->ids_dev, B, ctx->pos_dev, pos, ctx->epoch, ctx->wdt, ctx->w.tok_embed,
+                                g.vocab, g.hidden, ctx->dx[0], ctx->s0));
   // occupancy queries of the persistent launch happen here, not under graph capture
   if (ctx->sched == LADDER_SCHED_PERSISTENT) (void)step_usable(ctx, B);
   // traced steps run eagerly: event records captured into a graph carry no timestamps

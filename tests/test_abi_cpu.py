@@ -114,6 +114,10 @@ def test_null_context_calls():
     assert lib.ladder_sync(None) == abi.LADDER_ERR_ARG
     assert lib.ladder_trace_kernel(None, 0) == abi.LADDER_ERR_ARG
     assert lib.ladder_trace_result(None, None, None) == abi.LADDER_ERR_ARG
+    g = ctypes.c_float()
+    assert lib.ladder_read_probe(None, 1 << 20, 1, None) == abi.LADDER_ERR_ARG      # no output
+    assert lib.ladder_read_probe(None, 1 << 20, 0, ctypes.byref(g)) == abi.LADDER_ERR_ARG   # no repetition
+    assert lib.ladder_read_probe(None, 4096, 1, ctypes.byref(g)) == abi.LADDER_ERR_ARG     # below 1 MiB
     lib.ladder_free(None)                                  # no-op
     assert lib.ladder_last_error(None) == b""
 

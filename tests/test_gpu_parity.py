@@ -243,3 +243,11 @@ def test_long_context_split_kv(edge, B, T, max_seq, n_dec):
     eh = step_rel_err(gh, ref.hidden[:, T - 1:])
     log(f"edge long context: rel err logits {el:.3g} hidden {eh:.3g}")
     assert el <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_read_probe_reports_a_plausible_ceiling():
+    """The streaming-read probe runs and reports a rate between 1 TB/s and the 8 TB/s peak."""
+    from ladder_residual_transformer_amd import abi
+    g = abi.ladder_read_probe(torch.cuda.current_stream().cuda_stream, 256 << 20, 2)
+    log(f"streaming-read ceiling over 256 MiB: {g:.0f} GB/s")
+    assert 1000.0 < g < 8000.0
