@@ -49,7 +49,8 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
     wt.flag = mp.wait_flag;
     wt.epoch = epoch;
     wt.err = mp.err;
-    rw_pass<WT, BT, VPL, RW_OUT_ADD2_LDS>(mp.prob[1], pr0, pr1, blk, u, dres, wt, sh, part);
+    uint4* wpre = mp.wpre_off ? reinterpret_cast<uint4*>(lds_raw + mp.wpre_off) : nullptr;
+    rw_pass<WT, BT, VPL, RW_OUT_ADD2_LDS>(mp.prob[1], pr0, pr1, blk, u, dres, wt, sh, part, nullptr, wpre);
   } else {
     const int pi = (NP > 1 && blk >= mp.blk_begin[1]) ? 1 : 0;
     const int lb = blk - mp.blk_begin[pi];
@@ -98,6 +99,7 @@ namespace {
 
 constexpr int kRwTargetBlocks = 1024;  // upper bound; the launch uses what fits on the device at once
 constexpr int kRwBlocksPerCu = 2;
+constexpr size_t kRwLdsTwoPerCu = 80 * 1024;   // LDS of a workgroup that keeps two per CU
 
 int rw_bt(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : 4; }
 
@@ -173,6 +175,25 @@ hipError_t rw_go(MultiGemvParams& mp, size_t gemv_lds, size_t attn_lds, hipStrea
   }
   mp.part_off = (int)((gemv_lds + 15) / 16 * 16);
   size_t total = (size_t)mp.part_off + part * sizeof(float);
+  // paired launch with attention: the second pass's weights, copied into LDS while its
+  // workgroups wait for the attention, when that keeps two workgroups per CU
+  mp.wpre_off = 0;
+  if (NP == 3 && HDA != 0) {
+    const int nb = mp.blk_begin[1];
+    const int P = (mp.prob[0].N + 1) / 2;
+    const int pairs = (P + nb - 1) / nb;
+    const int nvec = mp.prob[1].K / vec;
+    const int chunk = 64 * VPL;
+    const int nchunk = (nvec + chunk - 1) / chunk;
+    const int spu = nvec < chunk ? (nvec + 63) / 64 : VPL;
+    const size_t units_max = (size_t)((pairs * nchunk + 3) / 4) * 4;   // every wave's slots
+    const size_t wbytes = units_max * spu * 2 * 1024;
+    const size_t off = (total + 1023) / 1024 * 1024;
+    if (off + wbytes <= kRwLdsTwoPerCu) {
+      mp.wpre_off = (int)off;
+      total = off + wbytes;
+    }
+  }
   if (attn_lds > total) total = attn_lds;
   static size_t attr_lds = 65536;
   if (total > attr_lds) {

@@ -195,7 +195,8 @@ __host__ __device__ inline size_t rw_part_floats(int n_pairs, int K, int vec, in
 // producers' signal (a cached copy would be stale).
 template <typename WT, int BT, int VPL, int OUT, bool COH = false>
 __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, int lb, float* u, float* dres,
-                                        const RwWait& wt, RwShared& sh, float* part, float* res = nullptr) {
+                                        const RwWait& wt, RwShared& sh, float* part, float* res = nullptr,
+                                        uint4* wpre = nullptr) {
   constexpr int VEC = Vec<WT>::N;
   constexpr int CHUNK = 64 * VPL;                 // vectors of a row one wave covers per step
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -232,9 +233,29 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
   };
   const int ustride = K + VEC;                     // u rows carry a zero pad of VEC floats
 
+  // wpre (LDS, with a wait): before waiting, each wave copies all of its units into LDS by
+  // direct global-to-LDS loads (slot s of unit un, row r: 64 lanes x 16 B at
+  // wpre + ((un * spu + s) * 2 + r) * 64), and computes them from there afterwards
+  const int spu = nvec < 64 * VPL ? (nvec + 63) / 64 : VPL;
   const bool waits = wt.flag != nullptr || wt.prog != nullptr;
+  if (waits && wpre) {
+    for (int i = 0; i < n_units; ++i) {
+      const int un = wid + 4 * i;
+      const int pair = pr0 + un / nchunk, c = un % nchunk;
+      const WT* r0 = rw_row_ptr<WT>(p.rows, 2 * pair, K);
+      const WT* r1 = rw_row_ptr<WT>(p.rows, min(2 * pair + 1, p.N - 1), K);
+      for (int v = 0; v < spu; ++v) {
+        const int vi = min(c * CHUNK + lane + 64 * v, nvec - 1);
+        uint4* slot = wpre + ((size_t)(un * spu + v) * 2) * 64;
+        __builtin_amdgcn_global_load_lds((const void*)(r0 + (size_t)vi * VEC),
+                                         (__attribute__((address_space(3))) void*)slot, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(r1 + (size_t)vi * VEC),
+                                         (__attribute__((address_space(3))) void*)(slot + 64), 16, 0, 0);
+      }
+    }
+  }
   if (waits) {
-    if (n_units > 0) load_unit(wa, 0);
+    if (n_units > 0 && !wpre) load_unit(wa, 0);
     if (wt.prog) prog_wait(wt.prog, wt.nprog, wt.code, wt.err);
     else if constexpr (COH) wg_wait_coh(wt.flag, wt.epoch, wt.err);
     else wg_wait(wt.flag, wt.epoch, wt.err);
@@ -364,12 +385,32 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
         if (lane == 0) part[((size_t)un * 2 + r) * BT + b] = y;
       }
   };
-  for (int i = 0; i < n_units; i += 2) {
-    if (i + 1 < n_units) load_unit(wb, i + 1);
-    compute_unit(wa, i);
-    if (i + 1 < n_units) {
-      if (i + 2 < n_units) load_unit(wa, i + 2);
-      compute_unit(wb, i + 1);
+  if (waits && wpre) {
+    wave_stores_done_fwd();                        // this wave's copies have landed
+    for (int i = 0; i < n_units; ++i) {
+      const int un = wid + 4 * i;
+      uint4 w[2][VPL];
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        if (v < spu) {
+          const uint4* slot = wpre + ((size_t)(un * spu + v) * 2) * 64;
+          w[0][v] = slot[lane];
+          w[1][v] = slot[64 + lane];
+        } else {
+          w[0][v] = make_uint4(0u, 0u, 0u, 0u);    // past every row end (u reads the zero pad)
+          w[1][v] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+      compute_unit(w, i);
+    }
+  } else {
+    for (int i = 0; i < n_units; i += 2) {
+      if (i + 1 < n_units) load_unit(wb, i + 1);
+      compute_unit(wa, i);
+      if (i + 1 < n_units) {
+        if (i + 2 < n_units) load_unit(wa, i + 2);
+        compute_unit(wb, i + 1);
+      }
     }
   }
   __syncthreads();

@@ -91,6 +91,7 @@ struct MultiGemvParams {
   const int* d_epoch;
   int* err;               // set to 1 if a wait ever gives up (never expected)
   int part_off;           // LDS byte offset of the partial sums (set by the launcher)
+  int wpre_off;           // LDS byte offset of prob[1]'s weights copied during the wait (0: none)
 };
 bool gemv_rw_supported(int wdtype, int K, int B);
 bool gemv_rw_attn_fusable(int wdtype, int K);   // a launch of this K can carry attention workgroups
