@@ -43,10 +43,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeParams p) {
 
 // Chunks per (sequence, kv head): one 64-key tile each up to 32 tiles of context
 // (longer contexts get several tiles per chunk); the merge reads all chunks at once.
+// Key chunks per sequence and kv head: one 64-key tile each up to 16 chunks (beyond 16,
+// the merge's inputs cost more than the shorter chunks save on the 70B shard's decode).
 int attn_decode_splits(int max_seq) {
   int n = (max_seq + kAttnKeyTile - 1) / kAttnKeyTile;
   if (n < 1) n = 1;
-  if (n > kAttnMaxSplits) n = kAttnMaxSplits;
+  if (n > kAttnDefaultSplits) n = kAttnDefaultSplits;
   return n;
 }
 

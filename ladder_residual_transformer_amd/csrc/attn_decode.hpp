@@ -34,6 +34,7 @@ namespace ladder {
 constexpr int kAttnKeyTile = 64;
 constexpr int kAttnMaxGroup = 16;
 constexpr int kAttnMaxSplits = 32;
+constexpr int kAttnDefaultSplits = 16;   // chunks the decode path uses (at most kAttnMaxSplits)
 
 // fp32 caches
 template <typename WT, int HD>

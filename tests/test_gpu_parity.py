@@ -230,7 +230,7 @@ def test_kernel_tracing_keeps_results_and_counts_launches(edge):
 @pytest.mark.parametrize("B, T, max_seq, n_dec", [(2, 150, 256, 6), (1, 2100, 2200, 3)])
 def test_long_context_split_kv(edge, B, T, max_seq, n_dec):
     """Decode attention over several key chunks (150 keys in 64-key chunks, merged across
-    chunks) and over chunks of several tiles (2100 keys: 32 chunks of two tiles)."""
+    chunks) and over chunks of several tiles (2100 keys: 16 chunks of three tiles)."""
     cfg, w = edge
     prompt = synth.gen_ids(B, T, cfg.vocab, seed=13)
     cont = synth.gen_ids(B, n_dec, cfg.vocab, seed=13, stream=1)

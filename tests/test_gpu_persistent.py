@@ -65,7 +65,7 @@ def test_persistent_is_bitwise_the_per_layer_path(model_w, B, use_graph):
 
 
 def test_persistent_long_context(model_w):
-    """2100 cached keys: 32 key chunks of two tiles each, merged across chunks."""
+    """2100 cached keys: 16 key chunks of three tiles each, merged across chunks."""
     cfg, w = model_w
     prompt = synth.gen_ids(1, 2100, cfg.vocab, seed=23)
     cont = synth.gen_ids(1, 3, cfg.vocab, seed=23, stream=1)
