@@ -164,12 +164,22 @@ def module_input_index(m: int, ladder_mask) -> int:
     """Index j of the residual x_j that module m (0-based) reads.
 
     Modules are numbered m = 0..2L-1: m = 2l is layer l's attention, m = 2l+1
-    its MLP, and x_{m+1} = x_m + out_m.  A standard module reads x_m (the
-    residual right before it); a ladder module reads x_{m-1}, one step
-    earlier, with x_{-1} taken as x_0.
-    Pin: the hand-expanded two-layer formulas for all four masks.
+    its MLP, and x_{m+1} = x_m + out_m.  The layer's mask value picks the rule:
+
+    * 0, standard: every module reads x_m, the residual right before it;
+    * 1, ladder (Ladder Residual paper, section 3, the ladder recurrence): every
+      module reads x_{m-1}, one step earlier, with x_{-1} taken as x_0;
+    * 2, parallel block (the "Parallel" baseline the paper compares against,
+      which it does not define; read as the GPT-J style block): both modules
+      of the layer read the layer input x_{2l}, so the attention follows the
+      standard rule and the MLP the ladder one.
+
+    Pins: the hand-expanded two-layer formulas for every mask over {0, 1, 2};
+    the parallel block's closed form x_{2l+2} = x_{2l} + A(x_{2l}) + M(x_{2l});
+    a parallel first layer equals a ladder first layer.
     """
-    if ladder_mask[m // 2]:
+    mode = ladder_mask[m // 2]
+    if mode == 1 or (mode == 2 and m % 2 == 1):
         return max(m - 1, 0)
     return m
 
@@ -209,6 +219,8 @@ class LadderOracle:
         self.mask = tuple(int(v) for v in (cfg.ladder_mask if ladder_mask is None else ladder_mask))
         if len(self.mask) != cfg.n_layers:
             raise ValueError("one mask entry per layer")
+        if any(v not in (0, 1, 2) for v in self.mask):
+            raise ValueError("mask entries are 0 (standard), 1 (ladder) or 2 (parallel)")
         self.cache_weights = cache_weights
         self._cache: Dict[int, dict] = {}
         self._head: Optional[dict] = None

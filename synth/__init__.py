@@ -46,12 +46,14 @@ class ModelConfig:
     vocab: int
     rope_theta: float
     dtype: str                      # "f32" or "bf16": weights and KV cache
-    ladder_mask: tuple              # one entry per layer: 1 = ladder, 0 = standard
+    ladder_mask: tuple              # one entry per layer: 0 = standard, 1 = ladder, 2 = parallel
     norm_eps: float = 1e-5
 
     def __post_init__(self):
         if len(self.ladder_mask) != self.n_layers:
             raise ValueError("ladder_mask needs one entry per layer")
+        if any(int(m) not in (0, 1, 2) for m in self.ladder_mask):
+            raise ValueError("ladder_mask entries are 0, 1 or 2")
         if self.dtype not in ("f32", "bf16"):
             raise ValueError("dtype must be 'f32' or 'bf16'")
 

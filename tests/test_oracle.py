@@ -171,8 +171,11 @@ def test_silu_and_swiglu():
 # I1: no ladder layers -> the standard pre-norm Transformer (independent torch model)
 # ---------------------------------------------------------------------------
 
-def torch_standard_transformer(cfg, w, ids):
-    """Textbook pre-norm Llama-style decoder in torch fp64, written independently of oracle/."""
+def torch_standard_transformer(cfg, w, ids, parallel=False):
+    """Textbook pre-norm Llama-style decoder in torch fp64, written independently of oracle/.
+
+    parallel=True: GPT-J style parallel blocks, the MLP normalises the block input
+    instead of the residual after the attention."""
     def t(a):
         return torch.from_numpy(upcast(a))
     nq, nkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
@@ -187,6 +190,7 @@ def torch_standard_transformer(cfg, w, ids):
         return torch.view_as_real(zc * phase[None, :, None, :]).flatten(3)
 
     for lw in w.layers:
+        x_block = x
         h = F.rms_norm(x, (cfg.hidden,), t(lw.attn_norm), eps=cfg.norm_eps)
         q = rot(F.linear(h, t(lw.wq)).view(B, T, nq, hd)).transpose(1, 2)
         k = rot(F.linear(h, t(lw.wk)).view(B, T, nkv, hd)).transpose(1, 2)
@@ -195,7 +199,7 @@ def torch_standard_transformer(cfg, w, ids):
         v = v.repeat_interleave(nq // nkv, dim=1)
         o = F.scaled_dot_product_attention(q, k, v, is_causal=True).transpose(1, 2).reshape(B, T, nq * hd)
         x = x + F.linear(o, t(lw.wo))
-        h = F.rms_norm(x, (cfg.hidden,), t(lw.mlp_norm), eps=cfg.norm_eps)
+        h = F.rms_norm(x_block if parallel else x, (cfg.hidden,), t(lw.mlp_norm), eps=cfg.norm_eps)
         x = x + F.linear(F.silu(F.linear(h, t(lw.w_gate))) * F.linear(h, t(lw.w_up)), t(lw.w_down))
     logits = F.linear(F.rms_norm(x, (cfg.hidden,), t(w.final_norm), eps=cfg.norm_eps), t(w.lm_head))
     return x.numpy(), logits.numpy()
@@ -220,6 +224,20 @@ def test_zero_ladder_equals_standard_transformer_tiny_shape():
     hx, lg = torch_standard_transformer(cfg, w, ids)
     np.testing.assert_allclose(r.hidden, hx, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(r.logits, lg, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_parallel_equals_textbook_parallel_transformer(dtype):
+    cfg = small_cfg(mask=(2, 2, 2), dtype=dtype)
+    w = model(cfg, seed=17)
+    ids = synth.gen_ids(2, 9, cfg.vocab, seed=8)
+    r = LadderOracle(cfg, w, kv_store_dtype=False).forward(ids)
+    hx, lg = torch_standard_transformer(cfg, w, ids, parallel=True)
+    np.testing.assert_allclose(r.hidden, hx, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r.logits, lg, rtol=1e-10, atol=1e-12)
+    # and the textbook parallel model is not the sequential one on these weights
+    hs, _ = torch_standard_transformer(cfg, w, ids)
+    assert np.max(np.abs(hx - hs)) > 1e-6
 
 
 def test_ladder_differs_from_standard():
@@ -247,27 +265,68 @@ def _module_fns(cfg, w):
     return o, A, M
 
 
-@pytest.mark.parametrize("mask", [(1, 1), (0, 0), (0, 1), (1, 0)])
+@pytest.mark.parametrize("mask", [(a, b) for a in (0, 1, 2) for b in (0, 1, 2)])
 def test_two_layer_brute_force_all_masks(mask):
     cfg = small_cfg(mask=mask)
     w = model(cfg, seed=13)
     ids = synth.gen_ids(2, 6, cfg.vocab, seed=5)
     o, A, M = _module_fns(cfg, w)
     x0 = o.embed(ids)
-    # written out by hand from x_{i+1} = h_{i+1}(x_{i-1}) + x_i (ladder) and
-    # x_{i+1} = h_{i+1}(x_i) + x_i (standard), with x_{-1} = x_0
+    # written out by hand from x_{i+1} = h_{i+1}(x_{i-1}) + x_i (ladder, 1),
+    # x_{i+1} = h_{i+1}(x_i) + x_i (standard, 0), with x_{-1} = x_0, and the parallel
+    # block (2) x_{2l+2} = x_{2l} + A(x_{2l}) + M(x_{2l})
     x1 = x0 + A(0, x0)
-    x2 = x1 + (M(0, x0) if mask[0] else M(0, x1))
-    x3 = x2 + (A(1, x1) if mask[1] else A(1, x2))
-    x4 = x3 + (M(1, x2) if mask[1] else M(1, x3))
+    x2 = x1 + {0: M(0, x1), 1: M(0, x0), 2: M(0, x0)}[mask[0]]
+    x3 = x2 + {0: A(1, x2), 1: A(1, x1), 2: A(1, x2)}[mask[1]]
+    x4 = x3 + {0: M(1, x3), 1: M(1, x2), 2: M(1, x2)}[mask[1]]
     r = o.forward(ids, record=True)
     np.testing.assert_array_equal(r.hidden, x4)
     np.testing.assert_array_equal(r.residuals[2], x2)
-    assert [module_input_index(m, mask) for m in range(4)] == {
-        (1, 1): [0, 0, 1, 2], (0, 0): [0, 1, 2, 3], (0, 1): [0, 1, 1, 2], (1, 0): [0, 0, 2, 3]}[mask]
+    per_layer = {0: lambda l: [2 * l, 2 * l + 1], 1: lambda l: [max(2 * l - 1, 0), 2 * l],
+                 2: lambda l: [2 * l, 2 * l]}
+    assert [module_input_index(m, mask) for m in range(4)] == per_layer[mask[0]](0) + per_layer[mask[1]](1)
 
 
-@pytest.mark.parametrize("mask", [(1, 1, 1), (0, 1, 1), (1, 0, 1), (0, 0, 0)])
+@pytest.mark.parametrize("rest", [(0,), (1,), (2,), (2, 1)])
+def test_parallel_first_layer_equals_ladder_first_layer(rest):
+    """At layer 0 the ladder rule's x_{-1} = x_0 makes both modules read x_0, which is
+    exactly the parallel block."""
+    cfg = small_cfg(mask=(1,) + rest)
+    w = model(cfg, seed=18)
+    ids = synth.gen_ids(2, 5, cfg.vocab, seed=9)
+    a = LadderOracle(cfg, w).forward(ids)
+    b = LadderOracle(cfg, w, ladder_mask=(2,) + rest).forward(ids)
+    np.testing.assert_array_equal(a.hidden, b.hidden)
+    np.testing.assert_array_equal(a.logits, b.logits)
+
+
+def test_parallel_block_closed_form_in_mixed_stack():
+    """x_{2l+2} = x_{2l} + A_l(x_{2l}) + M_l(x_{2l}) for every parallel layer of a mixed
+    stack; the ladder and standard layers around it leave it whole."""
+    mask = (0, 2, 1, 2)
+    cfg = small_cfg(mask=mask)
+    w = model(cfg, seed=19)
+    ids = synth.gen_ids(1, 6, cfg.vocab, seed=10)
+    o, A, M = _module_fns(cfg, w)
+    r = o.forward(ids, record=True)
+    xs = r.residuals
+    for l in (1, 3):
+        xin = xs[2 * l]
+        np.testing.assert_allclose(xs[2 * l + 2], xin + A(l, xin) + M(l, xin), rtol=1e-13, atol=1e-14)
+    # the ladder layer 2 reads x_3 and x_4: not the parallel closed form
+    assert np.max(np.abs(xs[6] - (xs[4] + A(2, xs[4]) + M(2, xs[4])))) > 1e-8
+
+
+def test_mask_values_beyond_parallel_rejected():
+    cfg = small_cfg(mask=(1, 1))
+    w = model(cfg, seed=20)
+    with pytest.raises(ValueError):
+        LadderOracle(cfg, w, ladder_mask=(1, 3))
+    with pytest.raises(ValueError):
+        cfg.with_mask((0, 3))
+
+
+@pytest.mark.parametrize("mask", [(1, 1, 1), (0, 1, 1), (1, 0, 1), (0, 0, 0), (2, 2, 2), (0, 2, 1)])
 def test_sum_invariant(mask):
     """The stream accumulates every module output: x_{2L} = x_0 + sum_m out_m."""
     cfg = small_cfg(mask=mask)
