@@ -34,7 +34,10 @@ DOMINANT = {
     "persistent": ("layer_stack", "persistent decode launch of the whole layer stack (every projection, "
                    "attention and residual add of every layer)", "traffic_layer_stack_70b_b1.json",
                    ("decode_step.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
+    # module-by-module schedules and all-standard stacks: the MLP's gate/up launch
+    "module": ("gateup", "RMSNorm+gate/up+SwiGLU launch of each MLP module", None, ()),
 }
+LAYER_KINDS = {"standard": 0, "ladder": 1, "parallel": 2}
 
 
 def log(*a):
@@ -75,6 +78,14 @@ def qkv_gateup_bytes(cfg, B):
     q, kv = cfg.n_q_heads * hd, cfg.n_kv_heads * hd
     weights = (H * (q + 2 * kv) + 2 * F * H + 2 * H) * esz
     return weights + 2 * B * H * 4 + B * q * 4 + B * F * 4 + 2 * B * kv * esz
+
+
+def gateup_bytes(cfg, B):
+    """Algorithmic bytes of one gate/up launch: both weight blocks and the norm gain once,
+    the input residual row read and the SwiGLU output written."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    H, F = cfg.hidden, cfg.ffn
+    return (2 * F * H + H) * esz + B * H * 4 + B * F * 4
 
 
 def layer_stack_bytes(cfg, B, pos):
@@ -140,6 +151,9 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--schedule", choices=("serial", "side", "dual", "fused", "persistent"), default="fused")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--layers", choices=("workload",) + tuple(LAYER_KINDS), default="workload",
+                    help="layer kind of every layer: the workload's own mask (default; the 70B shard is "
+                         "all ladder), or all standard, all ladder, or all parallel blocks")
     ap.add_argument("--prefill-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-layers", type=int, default=16)
@@ -172,6 +186,10 @@ def main():
     load()
     wl = synth.WORKLOADS[args.workload]
     cfg = wl.model
+    if args.layers != "workload":
+        mask = (LAYER_KINDS[args.layers],) * cfg.n_layers
+        if mask != tuple(cfg.ladder_mask):
+            cfg = cfg.with_mask(mask, name=f"{cfg.name} ({args.layers} layers)")
     B, P = args.batch, wl.prompt_len
     if args.steps < 1 or args.warmup < 0 or max(args.steps, args.warmup) > wl.decode_len:
         sys.exit(f"steps and warmup must be within the {wl.decode_len} decode positions")
@@ -237,7 +255,13 @@ def main():
     # dispatch's own begin/end timestamps (traced steps are launched eagerly).  Fused
     # schedule: the [QKV | gate/up] launch of every layer (~80% of the step's bytes);
     # persistent schedule: the one launch of the whole layer stack.
-    kind, kdesc, tfile, ksrc = DOMINANT["persistent" if args.schedule == "persistent" else "fused"]
+    if args.schedule == "persistent" and all(v == 1 for v in cfg.ladder_mask) and B <= 4:
+        dom = "persistent"
+    elif args.schedule in ("fused", "persistent") and any(cfg.ladder_mask):
+        dom = "fused"
+    else:
+        dom = "module"
+    kind, kdesc, tfile, ksrc = DOMINANT[dom]
     model.trace_kernel(kind)
     bufs[0].copy_(first)
     model.decode_step(bufs[0], P, out=(None, bufs[1], None))
@@ -251,9 +275,13 @@ def main():
         us, n = model.trace_result()                # waits for the step
         tot_us += us * n
         n_launch += n
-        tot_bytes += n * (layer_stack_bytes(cfg, B, P + k) if kind == "layer_stack" else qkv_gateup_bytes(cfg, B))
+        tot_bytes += n * {"layer_stack": lambda: layer_stack_bytes(cfg, B, P + k),
+                          "qkv_gateup": lambda: qkv_gateup_bytes(cfg, B),
+                          "gateup": lambda: gateup_bytes(cfg, B)}[kind]()
     torch.cuda.synchronize()
     dt_traced = time.perf_counter() - t0
+    if n_launch == 0:
+        sys.exit(f"bench.py: no {kind} launch in the traced steps")
     us_launch = tot_us / n_launch
     bytes_launch = tot_bytes / n_launch
     model.trace_kernel(None)
@@ -261,8 +289,8 @@ def main():
     log(f"[bench] traced decode: {dt_traced * 1e3 / args.steps:.3f} ms/step (read out per step); {kind} "
         f"launch {us_launch:.2f} us mean over {n_launch} launches, {achieved:.0f} GB/s")
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", tfile)
-    if os.path.exists(tpath):
+    tpath = os.path.join(ROOT, "profiles", tfile) if tfile else None
+    if tpath and os.path.exists(tpath):
         with open(tpath) as f:
             tr = json.load(f)
         if tr.get("kernel_sha") == kernel_sha(ksrc) and tr.get("batch") == B and tr.get("workload") == cfg.name:
@@ -289,7 +317,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}, batch {B}, prompt {P}, decode positions {P}..{P + args.steps - 1}",
                    "batch": B, "prompt_len": P, "layers": cfg.n_layers, "hidden": cfg.hidden,
-                   "schedule": args.schedule, "hip_graph": not args.no_graph},
+                   "schedule": args.schedule, "hip_graph": not args.no_graph,
+                   "layer_kinds": {k: sum(1 for v in cfg.ladder_mask if v == c) for k, c in LAYER_KINDS.items()}},
         "decode_hbm_frac": round(hbm_frac, 4),
         "decode_bytes_per_step": total_bytes // args.steps,
         "prefill_tok_s": round(B * P / prefill_s, 1),

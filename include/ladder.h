@@ -13,13 +13,16 @@
  * previous module's result; the pages use this to overlap the tensor-parallel
  * all-reduce with compute (section "asynchronous AllReduce implementation").
  * Layers can be mixed: standard lower layers, ladder upper layers (section
- * "hybrid Ladder adaptation").
+ * "hybrid Ladder adaptation"), and parallel blocks (the "Parallel" baseline of the
+ * results tables, which the pages do not define; taken here as the block whose
+ * attention and MLP both read the layer input, x_{2l+2} = x_{2l} + A(x_{2l}) + M(x_{2l})).
  *
  * This library runs one tensor-parallel rank's shard of such a model with the
  * cross-GPU all-reduce replaced by identity.  Module numbering: m = 0..2L-1,
  * m = 2l is layer l's attention, m = 2l+1 its MLP; x_0 is the token embedding,
  * x_{m+1} = x_m + out_m; a ladder module reads x_{m-1} (x_{-1} taken as x_0), a
- * standard module reads x_m.  The final hidden state is x_{2L}; logits are
+ * standard module reads x_m, and a parallel block's attention reads x_m and its MLP
+ * x_{m-1}.  The final hidden state is x_{2L}; logits are
  * RMSNorm(x_{2L}) . W_lm^T and the next token is their argmax (lowest index on
  * exact ties).
  *
@@ -66,9 +69,10 @@ typedef int32_t ladder_status;
 #define LADDER_SCHED_DUAL 2      /* attention and MLP modules on two streams, residual add
                                     fused into each module's output projection; a ladder
                                     module overlaps the previous module */
-#define LADDER_SCHED_FUSED 3     /* one stream; a ladder layer's attention and MLP run side
-                                    by side: [QKV | gate/up] in one launch (they read
-                                    x_{2l-1} and x_{2l}), [attention | down projection] in
+#define LADDER_SCHED_FUSED 3     /* one stream; a ladder layer's (or parallel block's)
+                                    attention and MLP run side by side: [QKV | gate/up] in
+                                    one launch (they read x_{2l-1} and x_{2l}; a parallel
+                                    block x_{2l} twice), [attention | down projection] in
                                     one launch, then the O projection adds both residual
                                     updates (with bf16 weights and batch <= 4 in the same
                                     launch as the down projection) (default) */
@@ -91,7 +95,11 @@ typedef struct ladder_config {
   int32_t max_seq;         /* KV capacity per sequence */
   int32_t max_prefill_tokens; /* rows per prefill chunk (B * tokens); 0 = 8192 */
   int32_t kv_filled;       /* KV positions already valid at init (resume on an existing cache) */
-  const uint8_t* ladder_mask; /* host, n_layers bytes: 1 = ladder layer, 0 = standard; copied */
+  const uint8_t* ladder_mask; /* host, n_layers bytes, copied: 0 = standard layer (each module
+                                 reads the residual right before it), 1 = ladder layer (each
+                                 module reads the residual one module earlier), 2 = parallel
+                                 block (attention and MLP both read the layer input); other
+                                 values: LADDER_ERR_ARG */
 } ladder_config;
 
 typedef struct ladder_layer_weights {

@@ -174,7 +174,7 @@ ladder_status validate(const ladder_config* c, const ladder_weights* w, const la
       (c->hidden % 64 || c->ffn % 64 || (c->n_q_heads * c->head_dim) % 64))
     return LADDER_ERR_SHAPE;   // K of every prefill contraction is a whole number of 64-wide MFMA steps
   for (int l = 0; l < c->n_layers; ++l)
-    if (c->ladder_mask[l] > 1) return LADDER_ERR_ARG;
+    if (c->ladder_mask[l] > 2) return LADDER_ERR_ARG;
   if (!aligned16(w->tok_embed) || !aligned16(w->final_norm) || !aligned16(w->lm_head)) return LADDER_ERR_ARG;
   for (int l = 0; l < c->n_layers; ++l) {
     const ladder_layer_weights& L = w->layers[l];
@@ -278,8 +278,14 @@ ladder_status trace_mark(ladder_ctx* ctx, int kind, hipStream_t s, bool end) {
     if (t_) return t_;                                        \
   } while (0)
 
+// Index j of the residual x_j that module m (2l attention, 2l+1 MLP of layer l) reads:
+// standard layers (mask 0) read x_m; ladder layers (mask 1) x_{m-1}, with x_{-1} = x_0
+// (Ladder Residual paper, section 3); parallel blocks (mask 2) feed both modules the layer
+// input x_{2l}, i.e. the attention reads x_m and the MLP x_{m-1}.
 inline int module_src(const ladder_ctx* c, int m) {
-  return c->mask[m / 2] ? (m > 0 ? m - 1 : 0) : m;
+  const int mode = c->mask[m / 2];
+  const bool back = mode == 1 || (mode == 2 && (m & 1));
+  return back ? (m > 0 ? m - 1 : 0) : m;
 }
 
 void* layer_k(const ladder_ctx* c, int l) { return (char*)c->kv.k + (size_t)l * c->layer_kv_elems * c->esz; }
@@ -477,8 +483,9 @@ ladder_status decode_module(ladder_ctx* ctx, int m, int B, const float* xin, con
   return LADDER_OK;
 }
 
-// One ladder layer l of a decode step on one stream, in three launches:
-//   [QKV_l | gate/up_l]   the attention reads x_{2l-1}, the MLP x_{2l}: both exist;
+// One ladder layer l (or parallel block) of a decode step on one stream, in three launches:
+//   [QKV_l | gate/up_l]   the attention reads x_{2l-1} (parallel block: x_{2l}), the MLP
+//                         x_{2l}: both exist;
 //   [attention_l | down_l] the down projection needs only the SwiGLU output; stores d;
 //   [O_l]                 x_{2l+1} = x_{2l} + o, then x_{2l+2} = x_{2l+1} + d.
 // The values are those of the module-by-module order (same kernels per row, same adds).
@@ -751,7 +758,8 @@ ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
     HIPCHK(launch_decode_step(step_params(ctx, B), ctx->s0));
     TRACE(LADDER_KERNEL_LAYER_STACK, ctx->s0, true);
   } else if (ctx->sched >= LADDER_SCHED_FUSED) {
-    // ladder layers in three launches; standard layers module by module (fused adds)
+    // ladder and parallel layers (both modules' inputs exist before the layer starts) in
+    // two or three launches; standard layers module by module (fused adds)
     for (int l = 0; l < g.n_layers; ++l) {
       if (ctx->mask[l]) {
         if ((st = decode_layer_fused(ctx, l, B))) return st;
@@ -893,7 +901,7 @@ ladder_status ladder_init(const ladder_config* cfg, const ladder_weights* w, con
   INITCHK(hipEventCreateWithFlags(&ctx->ev_done, hipEventDisableTiming));
 
   ctx->all_ladder = true;
-  for (int l = 0; l < cfg->n_layers; ++l) ctx->all_ladder = ctx->all_ladder && ctx->mask[l];
+  for (int l = 0; l < cfg->n_layers; ++l) ctx->all_ladder = ctx->all_ladder && ctx->mask[l] == 1;
   Carver measure;
   carve(ctx, measure);
   ctx->ws_bytes = measure.off;

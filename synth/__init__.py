@@ -100,6 +100,9 @@ CONFIGS = {
     "1b": ModelConfig("1b", 16, 2048, 32, 8, 64, 8192, 32000, 1e4, "bf16", _all_ladder(16)),
     "8b_hybrid": ModelConfig("8b_hybrid", 32, 4096, 32, 8, 128, 14336, 128256, 5e5, "bf16",
                              tuple([0] * 16 + [1] * 16)),
+    # the hybrid with 20 converted layers: the upper 20 of 32 layers ladder
+    "8b_hybrid20": ModelConfig("8b_hybrid20", 32, 4096, 32, 8, 128, 14336, 128256, 5e5, "bf16",
+                               tuple([0] * 12 + [1] * 20)),
     "70b_tp8_shard": ModelConfig("70b_tp8_shard", 80, 8192, 8, 1, 128, 3584, 16032, 5e5,
                                  "bf16", _all_ladder(80)),
     "405b_tp16_shard": ModelConfig("405b_tp16_shard", 126, 16384, 8, 1, 128, 3328, 8016, 5e5,

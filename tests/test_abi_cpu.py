@@ -80,7 +80,7 @@ def init_status(cfg, w, kv):
     (dict(dtype=2), abi.LADDER_ERR_ARG),
     (dict(n_layers=0), abi.LADDER_ERR_ARG),
     (dict(max_seq=0), abi.LADDER_ERR_ARG),
-    (dict(mask=[1, 2]), abi.LADDER_ERR_ARG),
+    (dict(mask=[1, 3]), abi.LADDER_ERR_ARG),           # 0 standard, 1 ladder, 2 parallel only
     (dict(ptr=FAKE + 2), abi.LADDER_ERR_ARG),          # misaligned weight pointer
 ])
 def test_init_rejects_bad_arguments(change, status):
@@ -100,8 +100,9 @@ def test_init_null_pointers():
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
-def test_valid_config_without_device_reports_hip_error():
-    cfg, w, kv, keep = make_args()
+@pytest.mark.parametrize("mask", [None, [2, 0], [0, 2, 1]])
+def test_valid_config_without_device_reports_hip_error(mask):
+    cfg, w, kv, keep = make_args(n_layers=len(mask) if mask else 2, mask=mask)
     st, out = init_status(cfg, w, kv)
     assert st == abi.LADDER_ERR_HIP and out is None
 

@@ -14,7 +14,7 @@ from oracle import LadderOracle, teacher_forced
 
 pytestmark = pytest.mark.gpu
 
-SERIAL, SIDE, DUAL, FUSED = 0, 1, 2, 3
+SERIAL, SIDE, DUAL, FUSED, PERSISTENT = 0, 1, 2, 3, 4
 
 # bf16 model with ragged shapes: H = 2112 (264 vectors: two K slices at batch > 4, the
 # second one short), 6 query / 2 kv heads of 64, F = 1344, vocab 1001 (ragged row
@@ -43,7 +43,7 @@ def test_tiny_fp32_matches_oracle_and_greedy_is_identical(tiny):
     model.free()
 
 
-@pytest.mark.parametrize("mask", [(0, 0), (0, 1), (1, 0)])
+@pytest.mark.parametrize("mask", [(0, 0), (0, 1), (1, 0), (2, 2), (0, 2), (2, 1)])
 def test_tiny_every_mask(tiny, mask):
     cfg, w = tiny
     cfg = cfg.with_mask(mask)
@@ -103,6 +103,48 @@ def test_schedules_are_bitwise_identical(edge, use_graph, B):
         outs[sched] = gpu_teacher_forced(model, prompt, cont)
         model.free()
     for sched in (SIDE, DUAL, FUSED):
+        for a, b in zip(outs[SERIAL], outs[sched]):
+            assert np.array_equal(a, b), f"schedule {sched} differs from serial"
+
+
+# The edge shapes with four layers mixing every layer kind: standard, then parallel blocks
+# around a ladder layer (a parallel block after a standard or ladder layer and a ladder
+# layer after a parallel block).
+MIXED = synth.ModelConfig("mixed", 4, 2112, 6, 2, 64, 1344, 1001, 1e4, "bf16", (0, 2, 1, 2))
+
+
+@pytest.fixture(scope="module")
+def mixed():
+    return MIXED, synth.gen_weights(MIXED, seed=9)
+
+
+@pytest.mark.parametrize("B", [1, 5])
+def test_mixed_layer_kinds_match_oracle(mixed, B):
+    cfg, w = mixed
+    prompt = synth.gen_ids(B, 23, cfg.vocab, seed=13)
+    log(f"mixed mask {cfg.ladder_mask} bf16 B={B}")
+    ref = oracle_record(cfg, w, prompt, 5, dtype=np.float64)
+    model = make_model(cfg, w, B, 32)
+    gl, gh, gt = gpu_teacher_forced(model, prompt, ref["tokens"][:, :-1])
+    check_against_oracle(cfg, gl, gh, gt, ref, TOL["bf16"], f"mixed B={B}")
+    model.free()
+
+
+@pytest.mark.parametrize("B", [2, 5])
+@pytest.mark.parametrize("use_graph", [False, True])
+def test_mixed_layer_kinds_schedules_bitwise(mixed, use_graph, B):
+    """Every schedule, including the persistent one (which falls back to the fused layers
+    when not every layer is ladder), reproduces the serial result bit for bit."""
+    cfg, w = mixed
+    prompt = synth.gen_ids(B, 19, cfg.vocab, seed=14)
+    cont = synth.gen_ids(B, 4, cfg.vocab, seed=14, stream=1)
+    outs = {}
+    for sched in (SERIAL, SIDE, DUAL, FUSED, PERSISTENT):
+        model = make_model(cfg, w, B, 32)
+        model.set_schedule(sched, use_graph)
+        outs[sched] = gpu_teacher_forced(model, prompt, cont)
+        model.free()
+    for sched in (SIDE, DUAL, FUSED, PERSISTENT):
         for a, b in zip(outs[SERIAL], outs[sched]):
             assert np.array_equal(a, b), f"schedule {sched} differs from serial"
 
@@ -217,7 +259,7 @@ def test_kernel_tracing_keeps_results_and_counts_launches(edge):
     m.trace_kernel("qkv_gateup")
     traced = gpu_teacher_forced(m, prompt, cont)
     us, n = m.trace_result()
-    assert n == sum(cfg.ladder_mask) and us > 0.0
+    assert n == sum(1 for v in cfg.ladder_mask if v) and us > 0.0
     m.trace_kernel("lmhead")
     m.decode_step(torch.from_numpy(cont[:, 0].copy()).cuda(), 9)
     us2, n2 = m.trace_result()

@@ -55,4 +55,5 @@ def test_config_shapes():
     assert c.weight_bytes() == 2 * (80 * (8192 * 1280 + 1024 * 8192 + 3 * 8192 * 3584 + 2 * 8192)
                                     + 2 * 16032 * 8192 + 8192)
     assert synth.CONFIGS["8b_hybrid"].ladder_mask == tuple([0] * 16 + [1] * 16)
+    assert synth.CONFIGS["8b_hybrid20"].ladder_mask == tuple([0] * 12 + [1] * 20)
     assert synth.scaled_config(c, 4).n_layers == 4
