@@ -28,9 +28,15 @@ MFMA_BF16_PEAK = 2.5e15      # FLOP/s, dense bf16
 CSRC = "ladder_residual_transformer_amd/csrc/"
 # the kernel each schedule's roofline reports: (trace kind, description, traffic file, sources)
 DOMINANT = {
-    "fused": ("qkv_gateup", "fused ladder launch [RMSNorm+QKV+RoPE+KV | RMSNorm+gate/up+SwiGLU]",
-              "traffic_qkv_gateup_70b_b1.json",
+    "fused": ("qkv_attn_gateup", "fused ladder launch [RMSNorm+QKV+RoPE+KV, then RMSNorm+gate/up+SwiGLU, in "
+              "every workgroup | split-KV GQA attention once every QKV share is done]",
+              "traffic_qkv_attn_gateup_70b_b1.json",
               ("gemv_rw.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
+    # FUSED without the bf16 two-launch layers, and the schedule with the attention in the
+    # down projection's launch: the [QKV | gate/up] launch
+    "fused3": ("qkv_gateup", "fused ladder launch [RMSNorm+QKV+RoPE+KV | RMSNorm+gate/up+SwiGLU]",
+               "traffic_qkv_gateup_70b_b1.json",
+               ("gemv_rw.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
     "persistent": ("layer_stack", "persistent decode launch of the whole layer stack (every projection, "
                    "attention and residual add of every layer)", "traffic_layer_stack_70b_b1.json",
                    ("decode_step.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
@@ -78,6 +84,15 @@ def qkv_gateup_bytes(cfg, B):
     q, kv = cfg.n_q_heads * hd, cfg.n_kv_heads * hd
     weights = (H * (q + 2 * kv) + 2 * F * H + 2 * H) * esz
     return weights + 2 * B * H * 4 + B * q * 4 + B * F * 4 + 2 * B * kv * esz
+
+
+def qkv_attn_gateup_bytes(cfg, B, pos):
+    """Algorithmic bytes of one sequential [QKV, then gate/up | attention] launch at position
+    pos: those of [QKV | gate/up], plus the attention's reads of q and of the KV rows
+    0..pos (the newest one just written) and its output written."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    q, kv = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    return qkv_gateup_bytes(cfg, B) + 2 * B * q * 4 + 2 * B * kv * esz * (pos + 1)
 
 
 def gateup_bytes(cfg, B):
@@ -149,7 +164,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="70b_tp8_shard")
     ap.add_argument("--batch", type=int, default=1)
-    ap.add_argument("--schedule", choices=("serial", "side", "dual", "fused", "persistent"), default="fused")
+    ap.add_argument("--schedule", choices=("serial", "side", "dual", "fused", "persistent", "fused_late_attn"),
+                    default="fused")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--layers", choices=("workload",) + tuple(LAYER_KINDS), default="workload",
                     help="layer kind of every layer: the workload's own mask (default; the 70B shard is "
@@ -200,7 +216,7 @@ def main():
     t = time.time()
     dw = DeviceWeights(w)
     model = LadderModel(cfg, dw, B, wl.max_seq)
-    sched = {"serial": 0, "side": 1, "dual": 2, "fused": 3, "persistent": 4}[args.schedule]
+    sched = {"serial": 0, "side": 1, "dual": 2, "fused": 3, "persistent": 4, "fused_late_attn": 5}[args.schedule]
     model.set_schedule(sched, not args.no_graph)
     torch.cuda.synchronize()
     log(f"[bench] uploaded weights and built the context in {time.time() - t:.1f} s "
@@ -253,12 +269,17 @@ def main():
     # ---- the dominant kernel, measured live: the same K decode steps again, each launch
     # of that kernel with a pair of HIP events on the stream it runs on, taken from its
     # dispatch's own begin/end timestamps (traced steps are launched eagerly).  Fused
-    # schedule: the [QKV | gate/up] launch of every layer (~80% of the step's bytes);
-    # persistent schedule: the one launch of the whole layer stack.
-    if args.schedule == "persistent" and all(v == 1 for v in cfg.ladder_mask) and B <= 4:
+    # schedule: the [QKV, then gate/up | attention] launch of every layer (~80% of the
+    # step's bytes; [QKV | gate/up] where layers take three launches, and under the
+    # schedule with the attention in the down projection's launch); persistent schedule:
+    # the one launch of the whole layer stack.
+    two_launch = cfg.dtype == "bf16" and B <= 4
+    if args.schedule == "persistent" and all(v == 1 for v in cfg.ladder_mask) and B <= 4 and cfg.dtype == "bf16":
         dom = "persistent"
     elif args.schedule in ("fused", "persistent") and any(cfg.ladder_mask):
-        dom = "fused"
+        dom = "fused" if two_launch else "fused3"
+    elif args.schedule == "fused_late_attn" and any(cfg.ladder_mask):
+        dom = "fused3"
     else:
         dom = "module"
     kind, kdesc, tfile, ksrc = DOMINANT[dom]
@@ -277,6 +298,7 @@ def main():
         n_launch += n
         tot_bytes += n * {"layer_stack": lambda: layer_stack_bytes(cfg, B, P + k),
                           "qkv_gateup": lambda: qkv_gateup_bytes(cfg, B),
+                          "qkv_attn_gateup": lambda: qkv_attn_gateup_bytes(cfg, B, P + k),
                           "gateup": lambda: gateup_bytes(cfg, B)}[kind]()
     torch.cuda.synchronize()
     dt_traced = time.perf_counter() - t0

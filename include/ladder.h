@@ -70,15 +70,22 @@ typedef int32_t ladder_status;
                                     fused into each module's output projection; a ladder
                                     module overlaps the previous module */
 #define LADDER_SCHED_FUSED 3     /* one stream; a ladder layer's (or parallel block's)
-                                    attention and MLP run side by side: [QKV | gate/up] in
-                                    one launch (they read x_{2l-1} and x_{2l}; a parallel
-                                    block x_{2l} twice), [attention | down projection] in
-                                    one launch, then the O projection adds both residual
-                                    updates (with bf16 weights and batch <= 4 in the same
-                                    launch as the down projection) (default) */
+                                    attention and MLP run side by side (their inputs
+                                    x_{2l-1} and x_{2l} both exist when the layer starts; a
+                                    parallel block reads x_{2l} twice).  bf16, batch <= 4:
+                                    two launches per layer, [QKV, then gate/up, in every
+                                    workgroup | the attention's key chunks once every QKV
+                                    share is done] and [merge of the chunks | down rows,
+                                    then the O rows + both residual adds];
+                                    otherwise [QKV | gate/up], [attention | down], [O + both
+                                    adds] (default) */
 #define LADDER_SCHED_PERSISTENT 4 /* decode: the whole layer stack in one launch of resident
                                     workgroups that signal each other (every layer ladder,
                                     bf16, batch <= 4; otherwise as FUSED); prefill as FUSED */
+#define LADDER_SCHED_FUSED_LATE_ATTN 5 /* as FUSED, but with bf16 and batch <= 4 the attention
+                                    shares the down projection's launch and the O rows wait
+                                    for it there: [QKV | gate/up], [attention | down, then O +
+                                    both adds]; prefill as FUSED */
 
 typedef struct ladder_config {
   int32_t n_layers;
@@ -180,7 +187,14 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 #define LADDER_KERNEL_LAYER_STACK 9  /* persistent launch of a decode step's whole layer stack
                                         (LADDER_SCHED_PERSISTENT); ladder_time_kernels stores
                                         -1 where that launch is not available */
-#define LADDER_N_KERNELS 10
+#define LADDER_KERNEL_QKV_ATTN_GATEUP 10 /* fused ladder launch (FUSED, bf16, batch <= 4): QKV
+                                        (+RoPE/KV), then gate/up (+SwiGLU), in every workgroup |
+                                        the attention's key chunks once every QKV share is
+                                        done; -1 from ladder_time_kernels where not available */
+#define LADDER_KERNEL_DOWN_OPROJ 11  /* fused ladder launch (FUSED, bf16, batch <= 4): merge of
+                                        the attention's chunks | down rows, then the O rows +
+                                        both residual adds; -1 where not available */
+#define LADDER_N_KERNELS 12
 
 /* Profiling aid.  For each kernel kind, enqueue it on the context's stream exactly as
  * a decode step at batch B launches it (once per layer; the LM head once), reps times,

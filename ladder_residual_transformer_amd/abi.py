@@ -31,14 +31,18 @@ LADDER_SCHED_SIDE = 1
 LADDER_SCHED_DUAL = 2
 LADDER_SCHED_FUSED = 3
 LADDER_SCHED_PERSISTENT = 4
+LADDER_SCHED_FUSED_LATE_ATTN = 5
 
 EXPORTED = ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_filled",
             "ladder_workspace_bytes", "ladder_sync", "ladder_free", "ladder_status_string", "ladder_last_error",
             "ladder_time_kernels", "ladder_trace_kernel", "ladder_trace_result", "ladder_read_probe")
 
 LADDER_KERNEL_LAYER_STACK = 9
-LADDER_N_KERNELS = 10
-KERNEL_KINDS = ("qkv", "attn", "oproj", "gateup", "down", "lmhead", "qkv_gateup", "attn_down", "oproj_add2", "layer_stack")
+LADDER_KERNEL_QKV_ATTN_GATEUP = 10
+LADDER_KERNEL_DOWN_OPROJ = 11
+LADDER_N_KERNELS = 12
+KERNEL_KINDS = ("qkv", "attn", "oproj", "gateup", "down", "lmhead", "qkv_gateup", "attn_down", "oproj_add2", "layer_stack",
+                "qkv_attn_gateup", "down_oproj")
 
 
 class ladder_config(ctypes.Structure):

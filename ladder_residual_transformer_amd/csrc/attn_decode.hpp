@@ -81,25 +81,15 @@ __host__ __device__ constexpr int attn_hpw(int G) { return G <= 4 ? 1 : (G <= 8 
 // max), two unused, then the accumulator (16-byte aligned).
 template <int HD> constexpr size_t attn_rec() { return HD + 4; }
 
-// Ticket and merge, after this workgroup has written its records (G heads of one chunk).
-// COH: records, output and signal use coherent accesses (no cache write-back or
-// invalidate is needed).
+// Merge of the n_act chunk records of (sequence b, kv head kvh) into the attention
+// output, then (if p.done_flag) the completion signal.  COH: records, output and signal
+// use coherent accesses (no cache write-back or invalidate is needed).  The counter of
+// the chunks' tickets is reset for the next use.
 template <int HD, bool COH = false, typename Lds>
-__device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, int n_act, Lds& L) {
+__device__ void attn_merge(const AttnDecodeParams& p, int b, int kvh, int G, int n_act, Lds& L) {
   const int tid = threadIdx.x;
   const size_t stride = attn_rec<HD>();
-  // release this chunk's records, take a ticket; the last one acquires everybody's
-  wave_stores_done();
-  __syncthreads();
   int* counter = p.counters + (size_t)b * p.nkv + kvh;
-  if (tid == 0) {
-    if (!COH) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const bool last = __hip_atomic_fetch_add(gbl(counter), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_act - 1;
-    if (!COH && last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    L.is_last = last;
-  }
-  __syncthreads();
-  if (!L.is_last) return;
   // merge: per head M = max_s m_s, w_s = e^{m_s - M}, L = sum_s l_s w_s,
   // o[d] = sum_s acc_s[d] w_s / L, summed in chunk order.  Thread i owns (head, 4 dims)
   // item i (G*HD/4 <= 256 items for G*HD <= 1024; larger groups loop).
@@ -175,13 +165,38 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
   }
 }
 
+// Ticket and merge, after this workgroup has written its records (G heads of one chunk):
+// the last chunk's workgroup merges (attn_merge).
+template <int HD, bool COH = false, typename Lds>
+__device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, int n_act, Lds& L) {
+  const int tid = threadIdx.x;
+  // release this chunk's records, take a ticket; the last one acquires everybody's
+  wave_stores_done();
+  __syncthreads();
+  int* counter = p.counters + (size_t)b * p.nkv + kvh;
+  if (tid == 0) {
+    if (!COH) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const bool last = __hip_atomic_fetch_add(gbl(counter), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_act - 1;
+    if (!COH && last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    L.is_last = last;
+  }
+  __syncthreads();
+  if (!L.is_last) return;
+  attn_merge<HD, COH>(p, b, kvh, G, n_act, L);
+}
+
 // ----------------------------------------------------------------- bf16 (MFMA)
 //
 // MFMA 16x16x32 f16: lane l supplies A row l%16 and B column l%16 with k-slots
 // 8*(l/16) .. +8; 16x16x16 f16: the same rows/columns with k-slots 4*(l/16) .. +4.  The
 // result holds column l%16, rows 4*(l/16) + i, i = 0..3.
+// wprog (COH only, nullable): q and the newest K/V row are written by other workgroups of
+// the same launch, which publish wcode in wprog[0..wn) when done; the first tile's older
+// rows are loaded before the wait (they come from earlier steps), the rest after it.
 template <int HD, bool COH = false>
-__device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnLds<uint16_t, HD>& L) {
+__device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnLds<uint16_t, HD>& L,
+                                       const uint32_t* wprog = nullptr, int wn = 0, uint32_t wcode = 0,
+                                       int* werr = nullptr) {
   constexpr int T = kAttnKeyTile;
   constexpr int CPR = HD / 8;                  // 16-byte chunks per K/V row
   constexpr int KCH = T * CPR / 256;           // K chunks per thread per tile
@@ -202,6 +217,8 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
   if (s >= n_act) return;                                  // whole workgroup: nothing to do
   const int start = s * chunk;
   const int end = min(len, start + chunk);
+  const bool pre = COH && wprog != nullptr;
+  bool defer = pre;                            // the newest row is not loaded before the wait
   const size_t kv_base = ((size_t)b * p.nkv + kvh) * p.max_seq * HD;
   const uint16_t* kc = (const uint16_t*)p.k_cache + kv_base;
   const uint16_t* vc = (const uint16_t*)p.v_cache + kv_base;
@@ -213,6 +230,7 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
   auto ld_row = [&](const uint16_t* base, int r, int c) -> uint4 {
     const uint16_t* a = base + (size_t)r * HD + c;
     if (COH && r == len - 1) {
+      if (defer) return make_uint4(0u, 0u, 0u, 0u);      // not written yet: loaded after the wait
       const uint32_t* w = (const uint32_t*)a;
       return make_uint4(ld_coh(w), ld_coh(w + 1), ld_coh(w + 2), ld_coh(w + 3));
     }
@@ -233,6 +251,26 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
     }
   };
   load_tile(start);
+  if (pre) {
+    prog_wait(wprog, wn, wcode, werr);
+    defer = false;                             // later tiles load the newest row themselves
+    // the newest row of the first tile (if it holds it), coherently
+    auto ld_new = [&](const uint16_t* base, int c) -> uint4 {
+      const uint32_t* w = (const uint32_t*)(base + (size_t)(len - 1) * HD + c);
+      return make_uint4(ld_coh(w), ld_coh(w + 1), ld_coh(w + 2), ld_coh(w + 3));
+    };
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int e = tid + 256 * i, r = min(start + e / CPR, end - 1), c = (e % CPR) * 8;
+      if (r == len - 1) kr[i] = ld_new(kc, c);
+    }
+#pragma unroll
+    for (int i = 0; i < VPAIR; ++i) {
+      const int e = tid + 256 * i, j = e / CPR, c = (e % CPR) * 8;
+      if (min(start + 2 * j, end - 1) == len - 1) vr[i][0] = ld_new(vc, c);
+      if (min(start + 2 * j + 1, end - 1) == len - 1) vr[i][1] = ld_new(vc, c);
+    }
+  }
 
   // Q^T operand as fp16 pairs: column = head (zero past the group), step st holds dims
   // 32*st + 8*grp .. +8

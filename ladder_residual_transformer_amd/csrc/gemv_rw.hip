@@ -20,15 +20,70 @@
 
 namespace ladder {
 
-// NP: GEMV problems of the launch: 1, 2 (side by side), or 3 = the paired launch (rows
-// of prob[0], then after the signal the same rows of prob[1]).  With HDA != 0 the first
-// n_attn workgroups run decode attention.
+// Shares of workgroup g of NG in a sequential launch over P0 row pairs of the first
+// problem and P1 of the second.  The first NQ workgroups split the first problem evenly;
+// the second problem's pairs fill every workgroup up to an even split of the total, so
+// that a workgroup's shares add up to within one pair of the average.  The other
+// workgroups stream the second problem from the start, which keeps HBM busy while the
+// first group publishes its results and restages its input.  (With fewer pairs than
+// workgroups the ranges of the second problem may overlap: some pairs are then computed
+// twice, with the same values, and none is missed.)
+__host__ __device__ inline int seq_first_group(int NG) { return NG > 1 ? NG / 2 : 1; }
+__host__ __device__ inline void seq_shares(int P0, int P1, int g, int NG, int& a0, int& a1, int& b0, int& b1) {
+  const int NQ = seq_first_group(NG);
+  const long long Pt = (long long)P0 + P1;
+  auto first = [&](int h) { return (int)((long long)(h < NQ ? h : NQ) * P0 / NQ); };
+  a0 = first(g);
+  a1 = first(g + 1);
+  b0 = (int)((long long)g * Pt / NG) - a0;
+  b1 = (int)((long long)(g + 1) * Pt / NG) - a1;
+}
+
+// NP: GEMV problems of the launch: 1, 2 (side by side), 3 = the paired launch (rows of
+// prob[0], then after the signal the same rows of prob[1]), or 4 = the sequential launch
+// (a first group of workgroups: its share of prob[0], then of prob[1]; the others: prob[1]).
+// With HDA != 0 the first n_attn workgroups run decode attention (NP 4: once every share
+// of prob[0] is done).
 template <typename WT, int BT, int VPL, int HDA, int HPW, int NP>
 __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  if constexpr (NP == 4) {
+    static_assert(sizeof(WT) == 2 && HDA != 0, "sequential launches: bf16, with attention");
+    const int NG = (int)gridDim.x - mp.n_attn;
+    const uint32_t code = (uint32_t)*gbl(mp.d_epoch) * kSeqCodeStride + (uint32_t)mp.seq_tag;
+    if ((int)blockIdx.x < mp.n_attn) {
+      // q and the newest K/V row come from this launch: the first key tile's older rows
+      // are loaded, then the workgroup waits for every QKV share; the attention reads q
+      // with ordinary loads (nothing in this launch read it before) and the newest row,
+      // its records and its output coherently
+      attn_decode_block_mfma<HDA, true>(mp.attn, blockIdx.x, *reinterpret_cast<AttnLds<uint16_t, HDA>*>(lds_raw),
+                                        mp.prog, seq_first_group(NG), code, mp.err);
+      return;
+    }
+    __shared__ RwShared sh;
+    const int g = (int)blockIdx.x - mp.n_attn;
+    float* u = reinterpret_cast<float*>(lds_raw);
+    float* part = reinterpret_cast<float*>(lds_raw + mp.part_off);
+    int a0, a1, b0, b1;
+    seq_shares((mp.prob[0].N + 1) / 2, (mp.prob[1].N + 1) / 2, g, NG, a0, a1, b0, b1);
+    if (g < seq_first_group(NG)) {
+      if (a1 > a0) rw_pass<WT, BT, VPL, RW_OUT_EPI, true>(mp.prob[0], a0, a1, g, u, nullptr, RwWait{}, sh, part);
+      prog_publish(mp.prog + g, code);             // also the barrier before u is restaged
+    }
+    if (b1 > b0) rw_pass<WT, BT, VPL, RW_OUT_EPI>(mp.prob[1], b0, b1, g, u, nullptr, RwWait{}, sh, part);
+    return;
+  }
+  // paired launch with bf16 attention: the attention output and its signal are
+  // coherent stores and the second pass waits for the signal without an L2 invalidate
+  // (its input, the attention output, is read by nothing in this launch before the signal)
+  constexpr bool kCohPair = NP == 3 && HDA != 0 && sizeof(WT) == 2;
   if constexpr (HDA != 0) {
     if ((int)blockIdx.x < mp.n_attn) {
-      attn_decode_block<WT, HDA, HPW>(mp.attn, blockIdx.x, *reinterpret_cast<AttnLds<WT, HDA>*>(lds_raw));
+      if constexpr (kCohPair) {
+        attn_decode_block_mfma<HDA, true>(mp.attn, blockIdx.x, *reinterpret_cast<AttnLds<uint16_t, HDA>*>(lds_raw));
+      } else {
+        attn_decode_block<WT, HDA, HPW>(mp.attn, blockIdx.x, *reinterpret_cast<AttnLds<WT, HDA>*>(lds_raw));
+      }
       return;
     }
   }
@@ -50,7 +105,7 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
     wt.epoch = epoch;
     wt.err = mp.err;
     uint4* wpre = mp.wpre_off ? reinterpret_cast<uint4*>(lds_raw + mp.wpre_off) : nullptr;
-    rw_pass<WT, BT, VPL, RW_OUT_ADD2_LDS>(mp.prob[1], pr0, pr1, blk, u, dres, wt, sh, part, nullptr, wpre);
+    rw_pass<WT, BT, VPL, RW_OUT_ADD2_LDS, kCohPair>(mp.prob[1], pr0, pr1, blk, u, dres, wt, sh, part, nullptr, wpre);
   } else {
     const int pi = (NP > 1 && blk >= mp.blk_begin[1]) ? 1 : 0;
     const int lb = blk - mp.blk_begin[pi];
@@ -156,13 +211,29 @@ hipError_t rw_go(MultiGemvParams& mp, size_t gemv_lds, size_t attn_lds, hipStrea
     rw_split_blocks(mp, target);
     mp.np = 2;
     mp.blk_begin[2] = mp.blk_begin[1];
+  } else if (NP == 4) {               // sequential: every block has a share of both
+    if (target > kSeqProgWords) target = kSeqProgWords;
+    mp.blk_begin[0] = 0;
+    mp.blk_begin[1] = mp.blk_begin[2] = target;
   } else {
     rw_split_blocks(mp, target);
   }
   // partial sums: the most pairs any workgroup of a problem gets, times its chunks
   const int vec = sizeof(WT) == 2 ? 8 : 4;
   size_t part = 0;
-  for (int i = 0; i < (NP == 3 ? 1 : mp.np); ++i) {
+  if (NP == 4) {
+    const int NG = mp.blk_begin[1];
+    const int P0 = (mp.prob[0].N + 1) / 2, P1 = (mp.prob[1].N + 1) / 2;
+    for (int g = 0; g < NG; ++g) {
+      int a0, a1, b0, b1;
+      seq_shares(P0, P1, g, NG, a0, a1, b0, b1);
+      const size_t f0 = rw_part_floats(a1 - a0, mp.prob[0].K, vec, BT);
+      const size_t f1 = rw_part_floats(b1 - b0, mp.prob[1].K, vec, BT);
+      if (f0 > part) part = f0;
+      if (f1 > part) part = f1;
+    }
+  }
+  for (int i = 0; i < (NP == 3 ? 1 : NP == 4 ? 0 : mp.np); ++i) {
     const int nb = mp.blk_begin[i + 1] - mp.blk_begin[i];
     const int P = (mp.prob[i].N + 1) / 2;
     const int pairs = (P + nb - 1) / nb;
@@ -215,6 +286,14 @@ hipError_t rw_hda(MultiGemvParams& mp, int hda, size_t lds, size_t alds, hipStre
     // heads-per-wave instance, the bf16 (matrix core) path has one
     // attention rides with one problem, or (bf16) in front of a paired launch; the fp32
     // path needs the heads-per-wave instance, the bf16 (matrix core) path has one
+    if constexpr (sizeof(WT) == 2) {
+      if (mp.seq) {
+        if (hda == 128) return rw_go<WT, BT, VPL, 128, 1, 4>(mp, lds, alds, s);
+        if (hda == 64) return rw_go<WT, BT, VPL, 64, 1, 4>(mp, lds, alds, s);
+        return hipErrorInvalidValue;
+      }
+    }
+    if (mp.seq) return hipErrorInvalidValue;
     const int hpw = hda ? (sizeof(WT) == 2 ? 1 : attn_hpw(mp.attn.nq / mp.attn.nkv)) : 0;
     if (hda != 0 && mp.np != 1 && !(sizeof(WT) == 2 && mp.paired)) return hipErrorInvalidValue;
     if (hda == 128) {
@@ -230,7 +309,7 @@ hipError_t rw_hda(MultiGemvParams& mp, int hda, size_t lds, size_t alds, hipStre
       return rw_go<WT, BT, VPL, 64, 4, 1>(mp, lds, alds, s);
     }
   }
-  if (hda != 0) return hipErrorInvalidValue;
+  if (hda != 0 || mp.seq) return hipErrorInvalidValue;
   if (mp.paired) return sizeof(WT) == 2 ? rw_go<WT, BT, VPL, 0, 0, 3>(mp, lds, 0, s) : hipErrorInvalidValue;
   if (mp.np == 2) return rw_go<WT, BT, VPL, 0, 0, 2>(mp, lds, 0, s);
   return rw_go<WT, BT, VPL, 0, 0, 1>(mp, lds, 0, s);
@@ -291,6 +370,50 @@ hipError_t launch_gemv_paired(const GemvParams& first, const GemvParams& second,
   mp.d_epoch = attn.d_epoch;
   mp.err = err;
   const size_t lds = rw_pair_lds(wdt, first.K, second.K, first.N, B, &mp.dres_off);
+  const size_t al = attn.hd == 128 ? sizeof(AttnLds<uint16_t, 128>) : sizeof(AttnLds<uint16_t, 64>);
+  return rw_bt_go<uint16_t>(mp, rw_bt(B), attn.hd, lds, al, s);
+}
+
+hipError_t launch_gemv_paired_nowait(const GemvParams& first, const GemvParams& second, hipStream_t s) {
+  const int B = first.B, wdt = first.wdtype;
+  if (!gemv_rw_pair_supported(wdt, first.K, second.K, B) || second.B != B || second.wdtype != wdt ||
+      first.N != second.N || second.epi != EPI_ADD2)
+    return hipErrorInvalidValue;
+  MultiGemvParams mp{};
+  mp.np = 2;
+  mp.prob[0] = first;
+  mp.prob[1] = second;
+  mp.paired = 1;
+  const size_t lds = rw_pair_lds(wdt, first.K, second.K, first.N, B, &mp.dres_off);
+  return rw_bt_go<uint16_t>(mp, rw_bt(B), 0, lds, 0, s);
+}
+
+bool gemv_rw_seq_supported(int wdtype, int K, int B, int hd) {
+  return wdtype == W_BF16 && gemv_rw_supported(wdtype, K, B) && (hd == 64 || hd == 128);
+}
+
+hipError_t launch_gemv_seq(const GemvParams& first, const GemvParams& second, const AttnDecodeParams& attn,
+                           uint32_t* prog, int tag, int* err, hipStream_t s) {
+  const int B = first.B, wdt = first.wdtype, K = first.K;
+  if (!gemv_rw_seq_supported(wdt, K, B, attn.hd) || second.K != K || second.B != B || second.wdtype != wdt ||
+      first.epi != EPI_QKV_ROPE || first.N < 1 || second.N < 1 || !prog || !err || !attn.d_epoch ||
+      attn.done_flag || tag < 1 || tag >= (int)kSeqCodeStride)
+    return hipErrorInvalidValue;
+  if (attn.nkv < 1 || attn.nq % attn.nkv != 0 || attn.nq / attn.nkv > kAttnMaxGroup ||
+      attn.n_split > kAttnMaxSplits || attn.wdtype != wdt || attn.B != B || attn.q != first.out)
+    return hipErrorInvalidValue;
+  MultiGemvParams mp{};
+  mp.np = 2;
+  mp.prob[0] = first;
+  mp.prob[1] = second;
+  mp.seq = 1;
+  mp.prog = prog;
+  mp.seq_tag = tag;
+  mp.err = err;
+  mp.d_epoch = attn.d_epoch;
+  mp.attn = attn;
+  mp.n_attn = attn.n_split * attn.nkv * attn.B;
+  const size_t lds = (size_t)B * (K + 8) * 4;
   const size_t al = attn.hd == 128 ? sizeof(AttnLds<uint16_t, 128>) : sizeof(AttnLds<uint16_t, 64>);
   return rw_bt_go<uint16_t>(mp, rw_bt(B), attn.hd, lds, al, s);
 }

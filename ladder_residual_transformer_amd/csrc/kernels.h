@@ -92,7 +92,17 @@ struct MultiGemvParams {
   int* err;               // set to 1 if a wait ever gives up (never expected)
   int part_off;           // LDS byte offset of the partial sums (set by the launcher)
   int wpre_off;           // LDS byte offset of prob[1]'s weights copied during the wait (0: none)
+  // sequential launch: every GEMV workgroup computes its share of prob[0] (coherent
+  // stores), publishes code(*d_epoch, seq_tag) in prog[its index], then its share of
+  // prob[1]; the attention workgroups start once every word has reached that code
+  int seq;
+  uint32_t* prog;
+  int seq_tag;            // 1 <= seq_tag < kSeqCodeStride
 };
+// Progress code of a sequential launch: epoch * kSeqCodeStride + tag, so that the codes
+// of a decode step exceed those of every earlier step.
+constexpr uint32_t kSeqCodeStride = 1024;
+constexpr int kSeqProgWords = 1024;     // progress words of a sequential launch (>= its GEMV workgroups)
 bool gemv_rw_supported(int wdtype, int K, int B);
 bool gemv_rw_attn_fusable(int wdtype, int K);   // a launch of this K can carry attention workgroups
 int gemv_rw_blocks(int wdtype, int N, int K, int B);   // workgroups of a one-problem launch
@@ -107,6 +117,19 @@ hipError_t launch_gemv_multi(const GemvParams* probs, int np, const AttnDecodePa
 bool gemv_rw_pair_supported(int wdtype, int K_first, int K_second, int B);
 hipError_t launch_gemv_paired(const GemvParams& first, const GemvParams& second, const AttnDecodeParams& attn,
                               int* err, hipStream_t s);
+// Paired launch without attention: rows R of first (kept in LDS), then the same rows R of
+// second with EPI_ADD2 taking first's result as add2; nothing waits.
+hipError_t launch_gemv_paired_nowait(const GemvParams& first, const GemvParams& second, hipStream_t s);
+// Sequential launch [first, then second, in every GEMV workgroup | attention once every
+// workgroup has finished first]: first must be the QKV projection (EPI_QKV_ROPE) that
+// produces the attention's q and newest K/V row; the attention must not signal
+// (done_flag null).  prog: kSeqProgWords words, zero or holding codes of earlier launches
+// of this context; tag: distinguishes the launches of one decode step (1 <= tag <
+// kSeqCodeStride, increasing within the step); the code waited for is
+// *attn.d_epoch * kSeqCodeStride + tag.  err: set if the wait gives up.
+bool gemv_rw_seq_supported(int wdtype, int K, int B, int hd);
+hipError_t launch_gemv_seq(const GemvParams& first, const GemvParams& second, const AttnDecodeParams& attn,
+                           uint32_t* prog, int tag, int* err, hipStream_t s);
 // next[b] = first maximum of n per-workgroup candidates (best_val/best_idx [n][BT])
 hipError_t launch_argmax_finalize(const float* best_val, const int* best_idx, int n, int BT, int B, int* next,
                                   hipStream_t s);

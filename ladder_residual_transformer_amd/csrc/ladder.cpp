@@ -115,6 +115,7 @@ struct ladder_ctx {
   StepLayer* step_layers = nullptr;  // [L] per-layer pointers of the persistent decode step
   int* step_sync = nullptr;          // [L][8] its counters and flags
   uint32_t* step_prog = nullptr;     // [kStepProgWords] its progress words
+  uint32_t* seq_prog = nullptr;      // [kSeqProgWords] progress words of the sequential launches
   float* step_x = nullptr;           // x_1 .. x_{2L-1}
   float* step_q = nullptr;           // q per layer
   float* step_o = nullptr;           // attention output per layer
@@ -226,6 +227,7 @@ void carve(ladder_ctx* c, Carver& cv) {
   c->step_layers = cv.take<StepLayer>((size_t)g.n_layers);
   c->step_sync = cv.take<int>((size_t)8 * g.n_layers);
   c->step_prog = cv.take<uint32_t>(kStepProgWords);
+  c->seq_prog = cv.take<uint32_t>(kSeqProgWords);
   // vectors of the persistent decode step, each at an address of its own per step
   if (c->all_ladder && c->wdt == W_BF16) {
     const size_t sb = std::min(B, 4);
@@ -359,6 +361,7 @@ AttnDecodeParams attn_params(const ladder_ctx* ctx, int l, int B, const StreamSc
   a.part = sc.attn_part;
   a.counters = sc.attn_cnt;
   a.out = sc.o;
+  a.d_epoch = ctx->epoch;   // the step counter (codes of the sequential launch's waits)
   return a;
 }
 
@@ -375,6 +378,15 @@ AttnDecodeParams signalled(const ladder_ctx* ctx, AttnDecodeParams a, int l) {
 bool two_launch_layers(const ladder_ctx* ctx, int B) {
   const ladder_config& g = ctx->cfg;
   return gemv_rw_supported(ctx->wdt, g.hidden, B) && gemv_rw_pair_supported(ctx->wdt, g.ffn, ctx->qrows, B);
+}
+
+// The two launches of the FUSED schedule instead: [QKV, then gate/up, in every workgroup |
+// attention once every QKV share is done] and [down rows, then O + both residual adds].
+// Layer l's launch uses the progress tag l + 1.
+bool seq_layers(const ladder_ctx* ctx, int B) {
+  const ladder_config& g = ctx->cfg;
+  return two_launch_layers(ctx, B) && gemv_rw_seq_supported(ctx->wdt, g.hidden, B, g.head_dim) &&
+         g.n_layers < (int)kSeqCodeStride;
 }
 
 // RMSNorm + [Wgate,Wup] (row pairs) + SwiGLU of layer l
@@ -497,6 +509,24 @@ ladder_status decode_layer_fused(ladder_ctx* ctx, int l, int B) {
   ladder_status st;
   GemvParams pr[2] = {qkv_params(ctx, l, B, X[module_src(ctx, ma) % 2], sc),
                       gateup_params(ctx, l, B, X[module_src(ctx, mm) % 2], sc)};
+  if (ctx->sched != LADDER_SCHED_FUSED_LATE_ATTN && seq_layers(ctx, B)) {
+    // [QKV_l, then gate/up_l, in half of the workgroups, gate/up_l in the others |
+    // attention_l once all of QKV_l is done]: the QKV rows come first, so the attention
+    // runs while gate/up streams; then [down_l rows | the same O_l rows with x_{2l+1} =
+    // x_{2l} + o and x_{2l+2} = x_{2l+1} + d], which waits for nothing
+    TRACE(LADDER_KERNEL_QKV_ATTN_GATEUP, s, false);
+    HIPCHK(launch_gemv_seq(pr[0], pr[1], attn_params(ctx, l, B, sc), ctx->seq_prog, l + 1, ctx->err_word, s));
+    TRACE(LADDER_KERNEL_QKV_ATTN_GATEUP, s, true);
+    const GemvParams down = outproj_params(ctx, mm, B, sc, nullptr, nullptr, ctx->dout[0]);
+    GemvParams o = outproj_params(ctx, ma, B, sc, X[ma % 2], X[(ma + 1) % 2], nullptr);
+    o.epi = EPI_ADD2;
+    o.add2 = nullptr;
+    o.out2 = X[(ma + 2) % 2];
+    TRACE(LADDER_KERNEL_DOWN_OPROJ, s, false);
+    HIPCHK(launch_gemv_paired_nowait(down, o, s));
+    TRACE(LADDER_KERNEL_DOWN_OPROJ, s, true);
+    return LADDER_OK;
+  }
   if (two_launch_layers(ctx, B)) {
     TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
     HIPCHK(launch_gemv_multi(pr, 2, nullptr, s, nullptr));
@@ -945,7 +975,7 @@ ladder_status ladder_init(const ladder_config* cfg, const ladder_weights* w, con
 
 ladder_status ladder_set_schedule(ladder_ctx* ctx, int32_t schedule, int32_t use_graph) {
   if (!ctx) return LADDER_ERR_ARG;
-  if (schedule < LADDER_SCHED_SERIAL || schedule > LADDER_SCHED_PERSISTENT) return LADDER_ERR_ARG;
+  if (schedule < LADDER_SCHED_SERIAL || schedule > LADDER_SCHED_FUSED_LATE_ATTN) return LADDER_ERR_ARG;
   ctx->sched = schedule;
   ctx->use_graph = use_graph ? 1 : 0;
   return LADDER_OK;
@@ -972,7 +1002,7 @@ ladder_status ladder_sync(ladder_ctx* ctx) {
   HIPCHK(hipMemcpy(&err, ctx->err_word, sizeof(int), hipMemcpyDeviceToHost));
   if (err) {
     ctx->broken = true;
-    return fail(ctx, LADDER_ERR_HIP, "an in-kernel wait for the attention's signal gave up%s");
+    return fail(ctx, LADDER_ERR_HIP, "an in-kernel wait for another workgroup's signal gave up%s");
   }
   return LADDER_OK;
 }
@@ -1060,10 +1090,29 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
   const bool rw_h = gemv_rw_supported(ctx->wdt, g.hidden, B);
   const bool rw_f = gemv_rw_supported(ctx->wdt, g.ffn, B) && gemv_rw_attn_fusable(ctx->wdt, g.ffn);
   const bool two = two_launch_layers(ctx, B);
+  const bool seq = seq_layers(ctx, B);
   for (int kind = 0; kind < LADDER_N_KERNELS; ++kind) {
     int launches = 0;
     HIPCHK(hipEventRecord(e0, s));
     for (int r = 0; r < reps; ++r) {
+      if (kind == LADDER_KERNEL_QKV_ATTN_GATEUP || kind == LADDER_KERNEL_DOWN_OPROJ) {
+        if (!seq) break;
+        for (int l = 0; l < g.n_layers; ++l, ++launches) {
+          HIPCHK(launch_epoch_bump(ctx->epoch, s));   // a new epoch per launch, as per decode step
+          if (kind == LADDER_KERNEL_QKV_ATTN_GATEUP) {
+            GemvParams pr[2] = {qkv_params(ctx, l, B, ctx->dx[1], sc), gateup_params(ctx, l, B, ctx->dx[0], sc)};
+            HIPCHK(launch_gemv_seq(pr[0], pr[1], attn_params(ctx, l, B, sc), ctx->seq_prog, l + 1, ctx->err_word, s));
+          } else {
+            const GemvParams down = outproj_params(ctx, 2 * l + 1, B, sc, nullptr, nullptr, ctx->dout[0]);
+            GemvParams o = outproj_params(ctx, 2 * l, B, sc, ctx->dx[0], ctx->dx[1], nullptr);
+            o.epi = EPI_ADD2;
+            o.add2 = nullptr;
+            o.out2 = ctx->dx[0];
+            HIPCHK(launch_gemv_paired_nowait(down, o, s));
+          }
+        }
+        continue;
+      }
       if (kind == LADDER_KERNEL_LAYER_STACK) {
         if (!step_usable(ctx, B)) break;
         HIPCHK(launch_epoch_bump(ctx->epoch, s));

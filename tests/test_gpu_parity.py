@@ -14,7 +14,7 @@ from oracle import LadderOracle, teacher_forced
 
 pytestmark = pytest.mark.gpu
 
-SERIAL, SIDE, DUAL, FUSED, PERSISTENT = 0, 1, 2, 3, 4
+SERIAL, SIDE, DUAL, FUSED, PERSISTENT, LATE = 0, 1, 2, 3, 4, 5
 
 # bf16 model with ragged shapes: H = 2112 (264 vectors: two K slices at batch > 4, the
 # second one short), 6 query / 2 kv heads of 64, F = 1344, vocab 1001 (ragged row
@@ -97,12 +97,12 @@ def test_schedules_are_bitwise_identical(edge, use_graph, B):
     prompt = synth.gen_ids(B, 21, cfg.vocab, seed=7)
     cont = synth.gen_ids(B, 4, cfg.vocab, seed=7, stream=1)
     outs = {}
-    for sched in (SERIAL, SIDE, DUAL, FUSED):
+    for sched in (SERIAL, SIDE, DUAL, FUSED, LATE):
         model = make_model(cfg, w, B, 32)
         model.set_schedule(sched, use_graph)
         outs[sched] = gpu_teacher_forced(model, prompt, cont)
         model.free()
-    for sched in (SIDE, DUAL, FUSED):
+    for sched in (SIDE, DUAL, FUSED, LATE):
         for a, b in zip(outs[SERIAL], outs[sched]):
             assert np.array_equal(a, b), f"schedule {sched} differs from serial"
 
@@ -139,12 +139,12 @@ def test_mixed_layer_kinds_schedules_bitwise(mixed, use_graph, B):
     prompt = synth.gen_ids(B, 19, cfg.vocab, seed=14)
     cont = synth.gen_ids(B, 4, cfg.vocab, seed=14, stream=1)
     outs = {}
-    for sched in (SERIAL, SIDE, DUAL, FUSED, PERSISTENT):
+    for sched in (SERIAL, SIDE, DUAL, FUSED, PERSISTENT, LATE):
         model = make_model(cfg, w, B, 32)
         model.set_schedule(sched, use_graph)
         outs[sched] = gpu_teacher_forced(model, prompt, cont)
         model.free()
-    for sched in (SIDE, DUAL, FUSED, PERSISTENT):
+    for sched in (SIDE, DUAL, FUSED, PERSISTENT, LATE):
         for a, b in zip(outs[SERIAL], outs[sched]):
             assert np.array_equal(a, b), f"schedule {sched} differs from serial"
 
@@ -244,7 +244,8 @@ def test_batch_rows_match_single_sequence(edge):
 
 def test_kernel_tracing_keeps_results_and_counts_launches(edge):
     """Event-bracketed decode graphs give the same bits as plain ones and one timed
-    launch per ladder layer for a fused kind (the standard layer 0 has none)."""
+    launch per ladder layer for a fused kind (the standard layer 0 has none), under the
+    default schedule and the one with the attention in the down projection's launch."""
     from ladder_residual_transformer_amd import LadderError, abi
     cfg, w = edge
     prompt = synth.gen_ids(1, 9, cfg.vocab, seed=12)
@@ -256,7 +257,7 @@ def test_kernel_tracing_keeps_results_and_counts_launches(edge):
     with pytest.raises(LadderError) as e:
         m.trace_result()
     assert e.value.status == abi.LADDER_ERR_STATE
-    m.trace_kernel("qkv_gateup")
+    m.trace_kernel("qkv_attn_gateup")
     traced = gpu_teacher_forced(m, prompt, cont)
     us, n = m.trace_result()
     assert n == sum(1 for v in cfg.ladder_mask if v) and us > 0.0
@@ -267,24 +268,44 @@ def test_kernel_tracing_keeps_results_and_counts_launches(edge):
     m.free()
     for a, b in zip(plain, traced):
         assert np.array_equal(a, b)
+    m = make_model(cfg, w, 1, 16)
+    m.set_schedule(LATE, True)
+    m.trace_kernel("qkv_gateup")
+    late = gpu_teacher_forced(m, prompt, cont)
+    us3, n3 = m.trace_result()
+    assert n3 == sum(1 for v in cfg.ladder_mask if v) and us3 > 0.0
+    m.free()
+    for a, b in zip(plain, late):
+        assert np.array_equal(a, b)
 
 
 @pytest.mark.parametrize("B, T, max_seq, n_dec", [(2, 150, 256, 6), (1, 2100, 2200, 3)])
 def test_long_context_split_kv(edge, B, T, max_seq, n_dec):
     """Decode attention over several key chunks (150 keys in 64-key chunks, merged across
-    chunks) and over chunks of several tiles (2100 keys: 16 chunks of three tiles)."""
+    chunks) and over chunks of several tiles (2100 keys: 16 chunks of three tiles, the
+    newest key in a later tile of the last chunk), against the oracle; and the default
+    schedule (attention inside the fused launch) bit for bit against the serial one (the
+    stand-alone attention kernel), which the tolerance alone would not see if one key
+    were read wrongly."""
     cfg, w = edge
     prompt = synth.gen_ids(B, T, cfg.vocab, seed=13)
     cont = synth.gen_ids(B, n_dec, cfg.vocab, seed=13, stream=1)
     log(f"edge long context B={B} T={T} max_seq={max_seq}")
     ref = teacher_forced(LadderOracle(cfg, w), prompt, cont)
-    model = make_model(cfg, w, B, max_seq)
-    gl, gh, _ = gpu_teacher_forced(model, prompt, cont)
-    model.free()
+    outs = {}
+    for sched in (FUSED, SERIAL):
+        model = make_model(cfg, w, B, max_seq)
+        model.set_schedule(sched, True)
+        outs[sched] = gpu_teacher_forced(model, prompt, cont)
+        model.free()
+    gl, gh, _ = outs[FUSED]
     el = step_rel_err(gl, ref.logits[:, T - 1:])
     eh = step_rel_err(gh, ref.hidden[:, T - 1:])
     log(f"edge long context: rel err logits {el:.3g} hidden {eh:.3g}")
     assert el <= TOL["bf16"] and eh <= TOL["bf16"]
+    for a, b in zip(outs[SERIAL], outs[FUSED]):
+        assert np.array_equal(a, b), "fused schedule differs from serial"
+
 
 
 def test_read_probe_reports_a_plausible_ceiling():
