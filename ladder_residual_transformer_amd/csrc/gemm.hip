@@ -11,9 +11,11 @@
 //
 // Tiling: a workgroup of 4 waves owns a 128x128 tile of C (2x2 waves of 64x64, i.e.
 // 4x4 MFMA tiles each; 64x64 tiles when 128x128 ones would leave CUs idle) and walks K
-// in steps of 32 through double-buffered LDS with padded rows; the next step's global
-// loads are in flight during the current MFMAs.  Optional epilogues: a residual add,
-// or SwiGLU over interleaved gate/up columns.
+// in steps of 32 through double-buffered LDS with padded rows.  The global loads run
+// kStages steps ahead of the MFMAs in a ring of register buffers (a step's MFMA work,
+// ~0.2-0.4 us per workgroup, is well below the latency of a global load under a full
+// device's traffic, so one step of prefetch leaves the matrix cores waiting).
+// Optional epilogues: a residual add, or SwiGLU over interleaved gate/up columns.
 // Workgroups are dealt to the 8 XCDs round robin, so the tile list (M fastest) is cut
 // into 8 contiguous runs and run x goes to XCD x: workgroups that share a weight tile
 // run together on one XCD and read it once into that XCD's L2.
@@ -36,6 +38,7 @@ __device__ __forceinline__ const WT* gemm_row(const RowSrc& s, int r, int K) {
 
 constexpr int BK = 32, LDK = BK + 8;
 constexpr int kXcds = 8;
+constexpr int kStages = 4;   // K steps whose global loads are in flight (even: LDS buffers alternate)
 
 // TM x TN workgroup tile (128x128, or 64x64 when the big tiles would not fill the
 // device), 4 waves of (TM/2) x (TN/2), i.e. (TM/32) x (TN/32) MFMA tiles of 16x16 each.
@@ -76,25 +79,27 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
     const int n = n0 + br[i];
     brow[i] = n < p.N ? gemm_row<uint16_t>(p.rows, n, p.K) + bc[i] : nullptr;
   }
-  float4 ra[AV];
-  uint4 rb[BV];
-  auto gload = [&](int k0) {
+  // register ring: stage st holds the global loads of one K step
+  float4 ra[kStages][AV];
+  uint4 rb[kStages][BV];
+  auto gload = [&](int st, int k0) {
 #pragma unroll
-    for (int i = 0; i < AV; ++i) ra[i] = arow[i] ? *(const float4*)(arow[i] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < AV; ++i)
+      ra[st][i] = arow[i] ? *(const float4*)(arow[i] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int i = 0; i < BV; ++i) rb[i] = brow[i] ? *(const uint4*)(brow[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < BV; ++i) rb[st][i] = brow[i] ? *(const uint4*)(brow[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int st, int buf) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
       uint32_t h0, l0, h1, l1;
-      split_h2(ra[i].x, ra[i].y, h0, l0);
-      split_h2(ra[i].z, ra[i].w, h1, l1);
+      split_h2(ra[st][i].x, ra[st][i].y, h0, l0);
+      split_h2(ra[st][i].z, ra[st][i].w, h1, l1);
       *(uint2*)&Ah[buf][ar[i]][ac[i]] = make_uint2(h0, h1);
       *(uint2*)&Al[buf][ar[i]][ac[i]] = make_uint2(l0, l1);
     }
 #pragma unroll
-    for (int i = 0; i < BV; ++i) *(uint4*)&Bs[buf][br[i]][bc[i]] = bf16x8_to_f16x8(rb[i]);
+    for (int i = 0; i < BV; ++i) *(uint4*)&Bs[buf][br[i]][bc[i]] = bf16x8_to_f16x8(rb[st][i]);
   };
 
   f32x4 acc[FM][FN];
@@ -104,31 +109,48 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = p.K / BK;
-  gload(0);
-  sstore(0);
+  // prologue: steps 0 .. kStages-1 in flight, step 0 into LDS buffer 0, then stage 0
+  // refilled with step kStages
+#pragma unroll
+  for (int st = 0; st < kStages; ++st)
+    if (st < nk) gload(st, st * BK);
+  sstore(0, 0);
+  if (kStages < nk) gload(0, kStages * BK);
   __syncthreads();
   // 16x16x32 fragments: lane holds row (A) / column (W) lane%16, k = 8*(lane/16) .. +8
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    half8 ah[FM], al[FM], b[FN];
+  // step kt reads LDS buffer kt & 1 and register stage kt % kStages holds (in flight)
+  // step kt + kStages; after the MFMAs, step kt + 1 goes from its stage into the other
+  // LDS buffer and that stage is refilled with step kt + 1 + kStages
+  for (int k0 = 0; k0 < nk; k0 += kStages) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      ah[i] = *(const half8*)&Ah[cur][wm * (TM / 2) + i * 16 + fr][fk];
-      al[i] = *(const half8*)&Al[cur][wm * (TM / 2) + i * 16 + fr][fk];
-    }
+    for (int u = 0; u < kStages; ++u) {
+      const int kt = k0 + u;
+      if (kt < nk) {
+        const int cur = u & 1;
+        half8 ah[FM], al[FM], b[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) b[j] = *(const half8*)&Bs[cur][wn * (TN / 2) + j * 16 + fr][fk];
+        for (int i = 0; i < FM; ++i) {
+          ah[i] = *(const half8*)&Ah[cur][wm * (TM / 2) + i * 16 + fr][fk];
+          al[i] = *(const half8*)&Al[cur][wm * (TM / 2) + i * 16 + fr][fk];
+        }
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j) b[j] = *(const half8*)&Bs[cur][wn * (TN / 2) + j * 16 + fr][fk];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], b[j], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], b[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], b[j], acc[i][j], 0, 0, 0);
+          }
+        if (kt + 1 < nk) {
+          const int nxt = (u + 1) % kStages;       // a constant once the loop is unrolled
+          sstore(nxt, cur ^ 1);
+          if (kt + 1 + kStages < nk) gload(nxt, (kt + 1 + kStages) * BK);
+        }
+        __syncthreads();
       }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+    }
   }
 
   // C fragment: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile.
