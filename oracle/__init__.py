@@ -25,3 +25,12 @@ from .ladder import (  # noqa: F401
     greedy_generate,
     teacher_forced,
 )
+from .sampling import (  # noqa: F401
+    philox4x32,
+    sampling_uniforms,
+    topk_keep,
+    sampling_probs,
+    sample_scores,
+    sample_token,
+    sample_rows,
+)
