@@ -170,6 +170,9 @@ def main():
     ap.add_argument("--layers", choices=("workload",) + tuple(LAYER_KINDS), default="workload",
                     help="layer kind of every layer: the workload's own mask (default; the 70B shard is "
                          "all ladder), or all standard, all ladder, or all parallel blocks")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: next tokens drawn from softmax(logits / T) (Gumbel-max, seeded) instead of greedy")
+    ap.add_argument("--top-k", type=int, default=0, help="with --temperature: keep only the k largest logits")
     ap.add_argument("--prefill-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-layers", type=int, default=16)
@@ -218,6 +221,8 @@ def main():
     model = LadderModel(cfg, dw, B, wl.max_seq)
     sched = {"serial": 0, "side": 1, "dual": 2, "fused": 3, "persistent": 4, "fused_late_attn": 5}[args.schedule]
     model.set_schedule(sched, not args.no_graph)
+    if args.temperature > 0:
+        model.set_sampling(args.temperature, args.top_k, seed=0)
     torch.cuda.synchronize()
     log(f"[bench] uploaded weights and built the context in {time.time() - t:.1f} s "
         f"(workspace {model.workspace_bytes() / 1e6:.0f} MB)")
@@ -340,6 +345,8 @@ def main():
         "config": {"workload": f"{cfg.name}, batch {B}, prompt {P}, decode positions {P}..{P + args.steps - 1}",
                    "batch": B, "prompt_len": P, "layers": cfg.n_layers, "hidden": cfg.hidden,
                    "schedule": args.schedule, "hip_graph": not args.no_graph,
+                   "next_token": ({"rule": "sample", "temperature": args.temperature, "top_k": args.top_k, "seed": 0}
+                                  if args.temperature > 0 else {"rule": "greedy"}),
                    "layer_kinds": {k: sum(1 for v in cfg.ladder_mask if v == c) for k, c in LAYER_KINDS.items()}},
         "decode_hbm_frac": round(hbm_frac, 4),
         "decode_bytes_per_step": total_bytes // args.steps,

@@ -160,6 +160,28 @@ ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t 
 /* Select the schedule (LADDER_SCHED_*) and whether decode steps use HIP graphs. */
 ladder_status ladder_set_schedule(ladder_ctx* ctx, int32_t schedule, int32_t use_graph);
 
+/* Next-token rule of prefill and decode steps (the inference code's `logits_to_probs`,
+ * `multinomial_sample_one_no_sync` and `sample`, named on the codewithpapers record of the
+ * method's pages).  temperature <= 0: greedy argmax (the default; top_k and seed ignored).
+ * temperature > 0: d_next[b] is drawn from softmax(logits[b] / temperature) over the
+ * top_k largest logits (every logit >= the k-th largest; top_k 0 or >= vocab keeps all)
+ * by the Gumbel-max rule, argmax_i logits_i / temperature - log(-log U_i), with U_i from
+ * Philox4x32-10 (Salmon et al., SC 2011): counter (i / 4, b, pos, 0), key (seed low 32
+ * bits, seed high 32 bits), word i % 4, U = (2 (word >> 9) + 1) / 2^24.  pos is the
+ * position whose logits are drawn from (the decode step's pos; start_pos + T - 1 in a
+ * prefill), so a draw depends only on (seed, pos, b, i).  The logits output is unchanged.
+ * LADDER_ERR_ARG: temperature not finite, or top_k < 0.  Drops the cached decode graphs. */
+ladder_status ladder_set_sampling(ladder_ctx* ctx, float temperature, int32_t top_k, uint64_t seed);
+
+/* The same draw on caller logits, outside any context: d_next[b] (device, B int32) from
+ * d_logits (device, fp32 [B][ld], the first V of each row used) at position pos, with
+ * temperature > 0 (finite), top_k >= 0 and seed as in ladder_set_sampling.  Enqueued on
+ * `stream` (a hipStream_t, NULL = the null stream); nothing is allocated.  LADDER_ERR_ARG
+ * on null pointers, B < 1, V < 1, ld < V, pos < 0 or a bad temperature / top_k;
+ * LADDER_ERR_HIP if the launch fails. */
+ladder_status ladder_sample(const float* d_logits, int32_t B, int32_t V, int32_t ld, float temperature,
+                            int32_t top_k, uint64_t seed, int32_t pos, int32_t* d_next, void* stream);
+
 /* Number of KV positions the context regards as filled. */
 ladder_status ladder_filled(const ladder_ctx* ctx, int32_t* out);
 
@@ -194,7 +216,10 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 #define LADDER_KERNEL_DOWN_OPROJ 11  /* fused ladder launch (FUSED, bf16, batch <= 4): merge of
                                         the attention's chunks | down rows, then the O rows +
                                         both residual adds; -1 where not available */
-#define LADDER_N_KERNELS 12
+#define LADDER_KERNEL_SAMPLE 12   /* stochastic draw from the logits (ladder_set_sampling); timed
+                                        with the context's sampling settings, or temperature 1
+                                        and no top-k cut when sampling is off */
+#define LADDER_N_KERNELS 13
 
 /* Profiling aid.  For each kernel kind, enqueue it on the context's stream exactly as
  * a decode step at batch B launches it (once per layer; the LM head once), reps times,

@@ -33,16 +33,18 @@ LADDER_SCHED_FUSED = 3
 LADDER_SCHED_PERSISTENT = 4
 LADDER_SCHED_FUSED_LATE_ATTN = 5
 
-EXPORTED = ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_filled",
+EXPORTED = ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_set_sampling",
+            "ladder_filled",
             "ladder_workspace_bytes", "ladder_sync", "ladder_free", "ladder_status_string", "ladder_last_error",
-            "ladder_time_kernels", "ladder_trace_kernel", "ladder_trace_result", "ladder_read_probe")
+            "ladder_time_kernels", "ladder_trace_kernel", "ladder_trace_result", "ladder_read_probe", "ladder_sample")
 
 LADDER_KERNEL_LAYER_STACK = 9
 LADDER_KERNEL_QKV_ATTN_GATEUP = 10
 LADDER_KERNEL_DOWN_OPROJ = 11
-LADDER_N_KERNELS = 12
+LADDER_KERNEL_SAMPLE = 12
+LADDER_N_KERNELS = 13
 KERNEL_KINDS = ("qkv", "attn", "oproj", "gateup", "down", "lmhead", "qkv_gateup", "attn_down", "oproj_add2", "layer_stack",
-                "qkv_attn_gateup", "down_oproj")
+                "qkv_attn_gateup", "down_oproj", "sample")
 
 
 class ladder_config(ctypes.Structure):
@@ -89,6 +91,9 @@ def load(path: str = LIB_PATH):
     lib.ladder_prefill.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     lib.ladder_decode_step.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     lib.ladder_set_schedule.argtypes = [c_void_p, c_int32, c_int32]
+    lib.ladder_set_sampling.argtypes = [c_void_p, c_float, c_int32, ctypes.c_uint64]
+    lib.ladder_sample.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_float, c_int32, ctypes.c_uint64, c_int32,
+                                  c_void_p, c_void_p]
     lib.ladder_filled.argtypes = [c_void_p, POINTER(c_int32)]
     lib.ladder_workspace_bytes.argtypes = [c_void_p, POINTER(c_size_t)]
     lib.ladder_sync.argtypes = [c_void_p]
@@ -102,9 +107,10 @@ def load(path: str = LIB_PATH):
     lib.ladder_status_string.restype = ctypes.c_char_p
     lib.ladder_last_error.argtypes = [c_void_p]
     lib.ladder_last_error.restype = ctypes.c_char_p
-    for name in ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_filled",
+    for name in ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_set_sampling",
+                 "ladder_filled",
                  "ladder_workspace_bytes", "ladder_sync", "ladder_time_kernels", "ladder_trace_kernel",
-                 "ladder_trace_result", "ladder_read_probe"):
+                 "ladder_trace_result", "ladder_read_probe", "ladder_sample"):
         getattr(lib, name).restype = c_int32
     _lib = lib
     return lib
@@ -145,6 +151,16 @@ def ladder_decode_step(ctx: int, d_ids: int, B: int, pos: int, d_logits: int = 0
 
 def ladder_set_schedule(ctx: int, schedule: int, use_graph: bool = True) -> None:
     _check(ctx, load().ladder_set_schedule(c_void_p(ctx), schedule, 1 if use_graph else 0), "ladder_set_schedule")
+
+
+def ladder_set_sampling(ctx: int, temperature: float, top_k: int = 0, seed: int = 0) -> None:
+    _check(ctx, load().ladder_set_sampling(c_void_p(ctx), temperature, top_k, seed), "ladder_set_sampling")
+
+
+def ladder_sample(d_logits: int, B: int, V: int, ld: int, temperature: float, top_k: int, seed: int, pos: int,
+                  d_next: int, stream: int = 0) -> None:
+    _check(0, load().ladder_sample(c_void_p(d_logits), B, V, ld, temperature, top_k, seed, pos, c_void_p(d_next),
+                                   c_void_p(stream or None)), "ladder_sample")
 
 
 def ladder_filled(ctx: int) -> int:

@@ -168,6 +168,22 @@ bool step_supported(int wdtype, int H, int F, int qrows, int B, int hd, int G);
 bool step_fits(const StepParams& sp);
 hipError_t launch_decode_step(const StepParams& sp, hipStream_t s);
 
+// ------------------------------------------------------------ sampling
+// next[b] = a draw from softmax(logits[b] / temperature) over the top_k largest logits
+// (all when top_k is 0 or >= V; ties at the cut are kept), by the Gumbel-max rule with
+// Philox4x32-10 uniforms of counter (i / 4, b, pos, 0) and key (seed_lo, seed_hi).
+// pos = *d_pos when d_pos is set (read when the kernel runs), else pos.
+struct SampleParams {
+  const float* logits; int ldl;        // [B][ldl], V used
+  int V, B;
+  float temperature;                   // > 0, finite
+  int top_k;                           // >= 0
+  uint32_t seed_lo, seed_hi;
+  const int* d_pos; int pos;
+  int* next;                           // [B]
+};
+hipError_t launch_sample(const SampleParams& p, hipStream_t s);
+
 // ---------------------------------------------------------- prefill attention
 struct AttnPrefillParams {
   int wdtype;

@@ -126,6 +126,10 @@ struct ladder_ctx {
 
   int sched = LADDER_SCHED_FUSED;
   int use_graph = 1;
+  // next-token rule: greedy, or a draw (temperature > 0) with an optional top-k cut
+  float temperature = 0.f;
+  int top_k = 0;
+  uint64_t seed = 0;
   int trace_kind = -1;               // kernel kind timed with events during decode (-1: none)
   std::vector<hipEvent_t> trace_ev;  // start/end pairs, one pair per traced launch
   int trace_n = 0;                   // pairs recorded by the step being enqueued
@@ -772,8 +776,35 @@ StepParams step_params(const ladder_ctx* ctx, int B) {
   return sp;
 }
 
-ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream_t s) {
-  return run_gemv(ctx, lmhead_params(ctx, x, ldx, B), s);
+// The draw that replaces the greedy token when sampling is on: position *d_pos (decode,
+// read when the kernel runs) or pos (prefill).
+SampleParams sample_params(const ladder_ctx* ctx, int B, const int* d_pos, int pos) {
+  SampleParams sp{};
+  sp.logits = ctx->logits;
+  sp.ldl = ctx->cfg.vocab;
+  sp.V = ctx->cfg.vocab;
+  sp.B = B;
+  sp.temperature = ctx->temperature > 0.f ? ctx->temperature : 1.f;
+  sp.top_k = ctx->top_k;
+  sp.seed_lo = (uint32_t)(ctx->seed & 0xffffffffu);
+  sp.seed_hi = (uint32_t)(ctx->seed >> 32);
+  sp.d_pos = d_pos;
+  sp.pos = pos;
+  sp.next = ctx->next;
+  return sp;
+}
+
+// Final RMSNorm + LM head + greedy token; with sampling on, the draw then overwrites the
+// token (the logits are the same either way).
+ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream_t s, const int* d_pos, int pos) {
+  ladder_status st = run_gemv(ctx, lmhead_params(ctx, x, ldx, B), s);
+  if (st) return st;
+  if (ctx->temperature > 0.f) {
+    TRACE(LADDER_KERNEL_SAMPLE, s, false);
+    HIPCHK(launch_sample(sample_params(ctx, B, d_pos, pos), s));
+    TRACE(LADDER_KERNEL_SAMPLE, s, true);
+  }
+  return LADDER_OK;
 }
 
 // One decode step from the embeddings the prologue left in dx[0] and pos_dev, leaving
@@ -808,7 +839,7 @@ ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
     if (st) return st;
   }
   TRACE(LADDER_KERNEL_LMHEAD, ctx->s0, false);
-  if ((st = lm_head(ctx, ctx->dx[(2 * g.n_layers) % 2], g.hidden, B, ctx->s0))) return st;
+  if ((st = lm_head(ctx, ctx->dx[(2 * g.n_layers) % 2], g.hidden, B, ctx->s0, ctx->pos_dev, 0))) return st;
   TRACE(LADDER_KERNEL_LMHEAD, ctx->s0, true);
   ctx->trace_count = ctx->trace_n;
   return LADDER_OK;
@@ -981,6 +1012,38 @@ ladder_status ladder_set_schedule(ladder_ctx* ctx, int32_t schedule, int32_t use
   return LADDER_OK;
 }
 
+ladder_status ladder_set_sampling(ladder_ctx* ctx, float temperature, int32_t top_k, uint64_t seed) {
+  if (!ctx) return LADDER_ERR_ARG;
+  if (!std::isfinite(temperature) || top_k < 0) return fail(ctx, LADDER_ERR_ARG, "bad temperature or top_k%s");
+  // the decode graphs hold the draw's parameters by value
+  for (auto& kv : ctx->graphs) (void)hipGraphExecDestroy(kv.second);
+  ctx->graphs.clear();
+  ctx->temperature = temperature > 0.f ? temperature : 0.f;
+  ctx->top_k = top_k;
+  ctx->seed = seed;
+  return LADDER_OK;
+}
+
+ladder_status ladder_sample(const float* d_logits, int32_t B, int32_t V, int32_t ld, float temperature,
+                            int32_t top_k, uint64_t seed, int32_t pos, int32_t* d_next, void* stream) {
+  if (!d_logits || !d_next || B < 1 || V < 1 || ld < V || pos < 0 || !std::isfinite(temperature) ||
+      !(temperature > 0.f) || top_k < 0)
+    return LADDER_ERR_ARG;
+  SampleParams sp{};
+  sp.logits = d_logits;
+  sp.ldl = ld;
+  sp.V = V;
+  sp.B = B;
+  sp.temperature = temperature;
+  sp.top_k = top_k;
+  sp.seed_lo = (uint32_t)(seed & 0xffffffffu);
+  sp.seed_hi = (uint32_t)(seed >> 32);
+  sp.pos = pos;
+  sp.next = d_next;
+  if (launch_sample(sp, (hipStream_t)stream) != hipSuccess) return LADDER_ERR_HIP;
+  return LADDER_OK;
+}
+
 ladder_status ladder_filled(const ladder_ctx* ctx, int32_t* out) {
   if (!ctx || !out) return LADDER_ERR_ARG;
   *out = ctx->filled;
@@ -1120,6 +1183,13 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
         ++launches;
         continue;
       }
+      if (kind == LADDER_KERNEL_SAMPLE) {
+        SampleParams sp = sample_params(ctx, B, ctx->pos_dev, 0);
+        if (!(ctx->temperature > 0.f)) sp.top_k = 0;
+        HIPCHK(launch_sample(sp, s));
+        ++launches;
+        continue;
+      }
       if (kind == LADDER_KERNEL_LMHEAD) {
         if ((st = run_gemv(ctx, lmhead_params(ctx, ctx->dx[0], g.hidden, B), s))) return st;
         ++launches;
@@ -1216,7 +1286,7 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
     if (st) return st;
     if (t0 + Tc == T) {
       const float* xl = ctx->px[NM % 2] + (size_t)(Tc - 1) * g.hidden;
-      st = lm_head(ctx, xl, Tc * g.hidden, B, ctx->s0);
+      st = lm_head(ctx, xl, Tc * g.hidden, B, ctx->s0, nullptr, start_pos + T - 1);
       if (st) return st;
       st = copy_outputs(ctx, B, xl, (size_t)Tc * g.hidden * 4, d_logits, d_next, d_hidden);
       if (st) return st;
@@ -1242,7 +1312,7 @@ ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t 
   if (ctx->sched == LADDER_SCHED_PERSISTENT) (void)step_usable(ctx, B);
   // traced steps run eagerly: event records captured into a graph carry no timestamps
   if (ctx->use_graph && ctx->trace_kind < 0) {
-    const int key = B * 8 + ctx->sched;
+    const int key = (B * 8 + ctx->sched) * 2 + (ctx->temperature > 0.f ? 1 : 0);
     auto it = ctx->graphs.find(key);
     if (it == ctx->graphs.end()) {
       hipGraph_t graph = nullptr;

@@ -84,6 +84,10 @@ class LadderModel:
     def set_schedule(self, schedule: int, use_graph: bool = True):
         abi.ladder_set_schedule(self.ctx, schedule, use_graph)
 
+    def set_sampling(self, temperature: float, top_k: int = 0, seed: int = 0):
+        """temperature <= 0: greedy next tokens; else a seeded draw (see ladder_set_sampling)."""
+        abi.ladder_set_sampling(self.ctx, temperature, top_k, seed)
+
     def _outs(self, B, logits, hidden):
         lg = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=self.device) if logits else None
         nx = torch.empty((B,), dtype=torch.int32, device=self.device)

@@ -33,7 +33,9 @@ def test_header_constants_match_binding():
     for name in ("LADDER_OK", "LADDER_ERR_ARG", "LADDER_ERR_SHAPE", "LADDER_ERR_CAPACITY", "LADDER_ERR_STATE",
                  "LADDER_ERR_HIP", "LADDER_ERR_OOM", "LADDER_F32", "LADDER_BF16", "LADDER_SCHED_SERIAL",
                  "LADDER_SCHED_SIDE", "LADDER_SCHED_DUAL", "LADDER_SCHED_FUSED",
-                 "LADDER_SCHED_PERSISTENT", "LADDER_KERNEL_LAYER_STACK", "LADDER_N_KERNELS"):
+                 "LADDER_SCHED_PERSISTENT", "LADDER_SCHED_FUSED_LATE_ATTN", "LADDER_KERNEL_LAYER_STACK",
+                 "LADDER_KERNEL_QKV_ATTN_GATEUP", "LADDER_KERNEL_DOWN_OPROJ", "LADDER_KERNEL_SAMPLE",
+                 "LADDER_N_KERNELS"):
         m = re.search(r"#define\s+%s\s+\(?(-?\d+)\)?" % name, text)
         assert m, name
         assert int(m.group(1)) == getattr(abi, name), name
@@ -112,6 +114,17 @@ def test_null_context_calls():
     assert lib.ladder_prefill(None, None, 1, 1, 0, None, None, None) == abi.LADDER_ERR_ARG
     assert lib.ladder_decode_step(None, None, 1, 0, None, None, None) == abi.LADDER_ERR_ARG
     assert lib.ladder_set_schedule(None, 0, 0) == abi.LADDER_ERR_ARG
+    assert lib.ladder_set_sampling(None, 1.0, 0, 0) == abi.LADDER_ERR_ARG
+    # argument errors of the context-free draw are found before anything is launched
+    fake = ctypes.c_void_p(FAKE)
+    assert lib.ladder_sample(None, 1, 8, 8, 1.0, 0, 0, 0, fake, None) == abi.LADDER_ERR_ARG      # no logits
+    assert lib.ladder_sample(fake, 1, 8, 8, 1.0, 0, 0, 0, None, None) == abi.LADDER_ERR_ARG      # no output
+    assert lib.ladder_sample(fake, 0, 8, 8, 1.0, 0, 0, 0, fake, None) == abi.LADDER_ERR_ARG      # B < 1
+    assert lib.ladder_sample(fake, 1, 8, 7, 1.0, 0, 0, 0, fake, None) == abi.LADDER_ERR_ARG      # ld < V
+    assert lib.ladder_sample(fake, 1, 8, 8, 0.0, 0, 0, 0, fake, None) == abi.LADDER_ERR_ARG      # T = 0
+    assert lib.ladder_sample(fake, 1, 8, 8, float("inf"), 0, 0, 0, fake, None) == abi.LADDER_ERR_ARG
+    assert lib.ladder_sample(fake, 1, 8, 8, 1.0, -1, 0, 0, fake, None) == abi.LADDER_ERR_ARG     # top_k < 0
+    assert lib.ladder_sample(fake, 1, 8, 8, 1.0, 0, 0, -1, fake, None) == abi.LADDER_ERR_ARG     # pos < 0
     assert lib.ladder_sync(None) == abi.LADDER_ERR_ARG
     assert lib.ladder_trace_kernel(None, 0) == abi.LADDER_ERR_ARG
     assert lib.ladder_trace_result(None, None, None) == abi.LADDER_ERR_ARG
