@@ -15,10 +15,12 @@
 // float in (0, 1).  A draw is a function of (seed, position, sequence, vocabulary entry)
 // only, so a replayed graph draws the same tokens for the same positions.
 //
-// One workgroup per sequence.  The top-k threshold is found by a radix select over the
-// order-preserving 32-bit keys of the logits, 8 bits per pass (4 passes over the row,
-// histograms in LDS); the draw is one more pass computing the Gumbel scores of the kept
-// entries and a workgroup argmax (lowest index on equal scores).
+// One workgroup per sequence.  Rows of up to kSampleLdsFloats logits are first copied
+// into LDS with independent loads (every later pass reads LDS); longer rows are read
+// from global memory in each pass.  The top-k threshold is found by a radix select over
+// the order-preserving 32-bit keys of the logits, 8 bits per pass (4 passes over the
+// row, histograms in LDS); the draw is one more pass computing the Gumbel scores of the
+// kept entries and a workgroup argmax (lowest index on equal scores).
 #include <climits>
 
 #include "common.hpp"
@@ -51,14 +53,24 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int kSampleLdsFloats = 32768;   // 128 KB of LDS: rows up to this many logits are staged
+
+template <bool STAGED>
 __global__ __launch_bounds__(256) void sample_kernel(SampleParams p) {
+  extern __shared__ float zs[];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sel_digit, sel_rank;
   __shared__ float rv[256];
   __shared__ int ri[256];
   const int tid = threadIdx.x, b = blockIdx.x;
-  const float* z = p.logits + (size_t)b * p.ldl;
   const int V = p.V;
+  const float* zg = p.logits + (size_t)b * p.ldl;
+  if constexpr (STAGED) {
+#pragma unroll 8
+    for (int i = tid; i < V; i += 256) zs[i] = zg[i];
+    __syncthreads();
+  }
+  const float* z = STAGED ? zs : zg;
 
   // ---- top-k threshold: key of the k-th largest logit (0 keeps everything)
   uint32_t thr = 0;
@@ -138,7 +150,20 @@ hipError_t launch_sample(const SampleParams& p, hipStream_t s) {
   if (!p.logits || !p.next || p.B < 1 || p.V < 1 || p.ldl < p.V || !(p.temperature > 0.f) ||
       !(p.temperature < INFINITY) || p.top_k < 0)
     return hipErrorInvalidValue;
-  launch_timed(sample_kernel, dim3(p.B), dim3(256), 0, s, p);
+  if (p.V <= kSampleLdsFloats) {
+    const size_t lds = (size_t)p.V * sizeof(float);
+    static bool attr = false;
+    if (!attr) {
+      const hipError_t e = hipFuncSetAttribute((const void*)sample_kernel<true>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               kSampleLdsFloats * (int)sizeof(float));
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    launch_timed(sample_kernel<true>, dim3(p.B), dim3(256), (uint32_t)lds, s, p);
+  } else {
+    launch_timed(sample_kernel<false>, dim3(p.B), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
