@@ -19,6 +19,10 @@
 // Workgroups are dealt to the 8 XCDs round robin, so the tile list (M fastest) is cut
 // into 8 contiguous runs and run x goes to XCD x: workgroups that share a weight tile
 // run together on one XCD and read it once into that XCD's L2.
+// Split K: when a projection has too few 128x128 tiles to fill the device (the QKV
+// projection of a narrow shard: 80 tiles at M 1024), S workgroups share each tile, each
+// over K/S, and store fp32 partial tiles; a reduction kernel sums them in slice order
+// (deterministic) and applies the epilogue.
 //
 // fp32 models (small correctness-only models): a plain LDS-tiled VALU GEMM.
 #include "common.hpp"
@@ -42,8 +46,11 @@ constexpr int kStages = 4;   // K steps whose global loads are in flight (even: 
 
 // TM x TN workgroup tile (128x128, or 64x64 when the big tiles would not fill the
 // device), 4 waves of (TM/2) x (TN/2), i.e. (TM/32) x (TN/32) MFMA tiles of 16x16 each.
+// Slice blockIdx.y covers K range [blockIdx.y * kchunk, + kchunk); with more than one
+// slice the raw partial tile goes to p.ws[slice][M][N].
 template <int TM, int TN>
-__global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd) {
+__global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd,
+                                                         int kchunk) {
   constexpr int FM = TM / 32, FN = TN / 32;       // MFMA tiles per wave
   constexpr int AV = TM * BK / 4 / 256;           // float4 of A per thread per K step
   constexpr int BV = TN * BK / 8 / 256;           // 16-byte W chunks per thread per K step
@@ -56,7 +63,8 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int m0 = (tile % n_tiles_m) * TM, n0 = (tile / n_tiles_m) * TN;
-  const float* A = (const float*)p.A;
+  const int kbase = (int)blockIdx.y * kchunk;
+  const float* A = (const float*)p.A + kbase;
 
   // per K step a thread moves AV float4 of A (rows c/8, columns 4*(c%8)) and BV 16-byte
   // chunks of W (rows c/4, columns 8*(c%4))
@@ -77,7 +85,7 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
     br[i] = c >> 2;
     bc[i] = (c & 3) * 8;
     const int n = n0 + br[i];
-    brow[i] = n < p.N ? gemm_row<uint16_t>(p.rows, n, p.K) + bc[i] : nullptr;
+    brow[i] = n < p.N ? gemm_row<uint16_t>(p.rows, n, p.K) + kbase + bc[i] : nullptr;
   }
   // register ring: stage st holds the global loads of one K step
   float4 ra[kStages][AV];
@@ -108,7 +116,7 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = p.K / BK;
+  const int nk = kchunk / BK;
   // prologue: steps 0 .. kStages-1 in flight, step 0 into LDS buffer 0, then stage 0
   // refilled with step kStages
 #pragma unroll
@@ -165,7 +173,9 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + wm * (TM / 2) + i * 16 + (lane >> 4) * 4 + r;
         float v = acc[i][j][r];
-        if (p.swiglu) {
+        if (gridDim.y > 1) {
+          if (row < p.M && col < p.N) p.ws[((size_t)blockIdx.y * p.M + row) * p.N + col] = v;
+        } else if (p.swiglu) {
           const float up = __shfl_xor(v, 1, 64);
           if (!(col & 1) && row < p.M && col < p.N) p.C[(size_t)row * p.ldc + (col >> 1)] = silu(v) * up;
         } else if (row < p.M && col < p.N) {
@@ -174,6 +184,31 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
         }
       }
     }
+}
+
+// C = (res +) sum over the S slices of ws[s] in slice order, or with swiglu
+// C[m][n] = silu(g) * u of the summed columns 2n, 2n+1.  One thread per output element.
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmParams p, int S) {
+  const int NO = p.swiglu ? p.N / 2 : p.N;
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (size_t)p.M * NO) return;
+  const int m = (int)(e / NO), n = (int)(e % NO);
+  const size_t plane = (size_t)p.M * p.N;
+  if (p.swiglu) {
+    const float* w = p.ws + (size_t)m * p.N + 2 * n;
+    float g = 0.f, u = 0.f;
+    for (int s = 0; s < S; ++s) {
+      g += w[s * plane];
+      u += w[s * plane + 1];
+    }
+    p.C[(size_t)m * p.ldc + n] = silu(g) * u;
+  } else {
+    const float* w = p.ws + (size_t)m * p.N + n;
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += w[s * plane];
+    if (p.res) v = p.res[(size_t)m * p.ldr + n] + v;
+    p.C[(size_t)m * p.ldc + n] = v;
+  }
 }
 
 constexpr int FT = 64, FK = 16;
@@ -229,14 +264,28 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.M < 1 || p.N < 1 || p.K < 1) return hipErrorInvalidValue;
   if (p.wdtype == W_BF16) {
     if (p.K % BK != 0 || p.lda % 4 != 0 || (p.swiglu && (p.N % 2 != 0 || p.res))) return hipErrorInvalidValue;
-    // 128x128 tiles when they give the device at least one round of work, else 64x64
+    // 128x128 tiles when they give the device at least one round of work; else 128x128
+    // tiles with K split over the fewest slices that reach a round (each slice at least
+    // kStages steps long, partials within the workspace); else 64x64
     const int big = ((p.M + 127) / 128) * ((p.N + 127) / 128);
-    if (big >= 256) {
+    int S = 1;
+    if (big < 256 && p.ws) {
+      for (int c = 2; c <= 8 && S == 1; c *= 2)
+        if ((long long)big * c >= 256 && p.K % (c * BK) == 0 && p.K / c >= kStages * BK &&
+            (size_t)c * p.M * p.N <= p.ws_floats)
+          S = c;
+    }
+    if (big >= 256 || S > 1) {
       const int tm = (p.M + 127) / 128, tiles = big, per = (tiles + kXcds - 1) / kXcds;
-      hipLaunchKernelGGL((gemm_f16x2_kernel<128, 128>), dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per);
+      hipLaunchKernelGGL((gemm_f16x2_kernel<128, 128>), dim3(per * kXcds, S), dim3(256), 0, s, p, tm, tiles, per,
+                         p.K / S);
+      if (S > 1) {
+        const size_t n_out = (size_t)p.M * (p.swiglu ? p.N / 2 : p.N);
+        hipLaunchKernelGGL(gemm_splitk_reduce_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, p, S);
+      }
     } else {
       const int tm = (p.M + 63) / 64, tiles = tm * ((p.N + 63) / 64), per = (tiles + kXcds - 1) / kXcds;
-      hipLaunchKernelGGL((gemm_f16x2_kernel<64, 64>), dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per);
+      hipLaunchKernelGGL((gemm_f16x2_kernel<64, 64>), dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per, p.K);
     }
   } else if (p.swiglu) {
     return hipErrorInvalidValue;

@@ -206,7 +206,11 @@ struct GemmParams {
   float* C; int ldc;
   const float* res; int ldr;
   int swiglu;
+  // split-K partials (nullable: no split); kGemmSplitWsFloats floats cover any split the
+  // launcher chooses
+  float* ws; size_t ws_floats;
 };
+constexpr size_t kGemmSplitWsFloats = (size_t)512 * 128 * 128;
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
 // ------------------------------------------------------------ launch timing

@@ -54,6 +54,7 @@ struct StreamScratch {
   float* ob = nullptr;
   float* gu = nullptr;
   float* ab = nullptr;
+  float* gk = nullptr;   // split-K partials of the prefill GEMMs (bf16 models)
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -258,6 +259,7 @@ void carve(ladder_ctx* c, Carver& cv) {
     sc.qr = cv.take<float>((size_t)c->mmax * c->qrows);
     sc.ob = cv.take<float>((size_t)c->mmax * c->qrows);
     sc.gu = cv.take<float>((size_t)c->mmax * 2 * F);
+    if (c->wdt == W_BF16) sc.gk = cv.take<float>(kGemmSplitWsFloats);
     sc.ab = cv.take<float>((size_t)c->mmax * F);
   }
 }
@@ -588,6 +590,8 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
   GemmParams gp{};
   gp.wdtype = ctx->wdt;
   gp.M = M;
+  gp.ws = sc.gk;
+  gp.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
   const void* proj_in;
   int proj_k;
   const void* proj_w;
@@ -645,6 +649,8 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
   }
   GemmParams op{};
   op.wdtype = ctx->wdt;
+  op.ws = sc.gk;
+  op.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
   op.A = proj_in;
   op.lda = proj_k;
   op.rows = RowSrc{{proj_w, nullptr, nullptr}, g.hidden, g.hidden, 0};
