@@ -277,16 +277,25 @@ def main():
     # schedule: the [QKV, then gate/up | attention] launch of every layer (~80% of the
     # step's bytes; [QKV | gate/up] where layers take three launches, and under the
     # schedule with the attention in the down projection's launch); persistent schedule:
-    # the one launch of the whole layer stack.
-    two_launch = cfg.dtype == "bf16" and B <= 4
-    if args.schedule == "persistent" and all(v == 1 for v in cfg.ladder_mask) and B <= 4 and cfg.dtype == "bf16":
-        dom = "persistent"
-    elif args.schedule in ("fused", "persistent") and any(cfg.ladder_mask):
-        dom = "fused" if two_launch else "fused3"
-    elif args.schedule == "fused_late_attn" and any(cfg.ladder_mask):
-        dom = "fused3"
-    else:
-        dom = "module"
+    # the one launch of the whole layer stack.  Which of them a step launches depends on
+    # the shape (the two-launch layers need the staged input rows to fit in LDS), so the
+    # candidates are probed in order with one traced step.
+    from ladder_residual_transformer_amd import LadderError
+    cands = {"persistent": ("persistent", "fused", "fused3", "module"), "fused": ("fused", "fused3", "module"),
+             "fused_late_attn": ("fused3", "module")}.get(args.schedule, ("module",))
+    dom = None
+    for c in cands:
+        model.trace_kernel(DOMINANT[c][0])
+        bufs[0].copy_(first)
+        model.decode_step(bufs[0], P, out=(None, bufs[1], None))
+        try:
+            if model.trace_result()[1] > 0:
+                dom = c
+                break
+        except LadderError:
+            pass
+    if dom is None:
+        sys.exit("bench.py: no launch of a dominant kernel kind in a traced step")
     kind, kdesc, tfile, ksrc = DOMINANT[dom]
     model.trace_kernel(kind)
     bufs[0].copy_(first)

@@ -222,7 +222,8 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 #define LADDER_N_KERNELS 13
 
 /* Profiling aid.  For each kernel kind, enqueue it on the context's stream exactly as
- * a decode step at batch B launches it (once per layer; the LM head once), reps times,
+ * a decode step at batch B launches it (once per layer; the LM head once), once untimed
+ * and then reps times,
  * (the fused kinds use each layer as if it were a ladder layer),
  * between two HIP events, and store the mean duration of one launch in microseconds
  * in us_out[kind] (host array of LADDER_N_KERNELS floats).  Works on the context's

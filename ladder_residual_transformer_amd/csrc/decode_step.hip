@@ -302,8 +302,11 @@ int step_plan(StepParams& sp, size_t* lds_out, hipError_t* err) {
 }  // namespace
 
 bool step_supported(int wdtype, int H, int F, int qrows, int B, int hd, int G) {
+  // every projection's staged input within ~65 KB of LDS (two resident workgroups per CU)
+  int kmax = H > F ? H : F;
+  if (qrows > kmax) kmax = qrows;
   return wdtype == W_BF16 && (hd == 64 || hd == 128) && G >= 1 && G <= kAttnMaxGroup &&
-         gemv_rw_supported(wdtype, H, B) && gemv_rw_supported(wdtype, F, B) && gemv_rw_supported(wdtype, qrows, B);
+         gemv_rw_supported(wdtype, kmax, B) && (size_t)B * (kmax + 8) * 4 <= 66560;
 }
 
 bool step_fits(const StepParams& sp_in) {

@@ -418,8 +418,17 @@ hipError_t launch_gemv_seq(const GemvParams& first, const GemvParams& second, co
   return rw_bt_go<uint16_t>(mp, rw_bt(B), attn.hd, lds, al, s);
 }
 
+// The staged input rows (fp32, B x (K + pad)) must fit in LDS next to the partial sums:
+// up to ~65 KB two workgroups share a CU, beyond that (batch 2-4 at hidden 8192, say) one
+// workgroup per CU streams (the launcher sizes the grid from the occupancy it gets).
+constexpr size_t kRwMaxInputLds = 150 * 1024;
+
 bool gemv_rw_supported(int wdtype, int K, int B) {
-  return B >= 1 && B <= 4 && (size_t)B * (K + (wdtype == W_BF16 ? 8 : 4)) * 4 <= 66560;
+  return B >= 1 && B <= 4 && (size_t)B * (K + (wdtype == W_BF16 ? 8 : 4)) * 4 <= kRwMaxInputLds;
+}
+
+bool gemv_rw_two_per_cu(int wdtype, int K, int B) {
+  return gemv_rw_supported(wdtype, K, B) && (size_t)B * (K + (wdtype == W_BF16 ? 8 : 4)) * 4 <= 66560;
 }
 
 int gemv_rw_blocks(int wdtype, int N, int K, int B) {

@@ -104,6 +104,7 @@ struct MultiGemvParams {
 constexpr uint32_t kSeqCodeStride = 1024;
 constexpr int kSeqProgWords = 1024;     // progress words of a sequential launch (>= its GEMV workgroups)
 bool gemv_rw_supported(int wdtype, int K, int B);
+bool gemv_rw_two_per_cu(int wdtype, int K, int B);   // ... with two workgroups per CU
 bool gemv_rw_attn_fusable(int wdtype, int K);   // a launch of this K can carry attention workgroups
 int gemv_rw_blocks(int wdtype, int N, int K, int B);   // workgroups of a one-problem launch
 int gemv_rw_bt(int B);

@@ -84,6 +84,27 @@ def test_8b_hybrid_widths(B, T, n_dec):
     _free(model)
 
 
+@pytest.mark.parametrize("B", [2, 4])
+def test_70b_tp8_shard_widths_small_batch(B):
+    """70B TP=8 shard widths (hidden 8192), four ladder layers, batch 2 and 4: the staged
+    input rows exceed the two-workgroups-per-CU budget, so the row-wave launches run one
+    workgroup per CU (and at batch 4 the fused launch carries 64 attention workgroups)."""
+    base = synth.CONFIGS["70b_tp8_shard"]
+    cfg = synth.scaled_config(base, 4)
+    w = synth.gen_weights(cfg, seed=8)
+    T, n_dec = 40, 3
+    prompt = synth.gen_ids(B, T, cfg.vocab, seed=9)
+    cont = synth.gen_ids(B, n_dec, cfg.vocab, seed=9, stream=1)
+    ref = teacher_forced(LadderOracle(cfg, w, dtype=np.float32), prompt, cont)
+    model = make_model(cfg, w, B, T + n_dec + 4)
+    gl, gh, _ = gpu_teacher_forced(model, prompt, cont)
+    el = step_rel_err(gl, ref.logits[:, T - 1:])
+    eh = step_rel_err(gh, ref.hidden[:, T - 1:])
+    log(f"70b widths B={B}: rel err logits {el:.3g} hidden {eh:.3g}")
+    assert el <= TOL["bf16"] and eh <= TOL["bf16"]
+    _free(model)
+
+
 @pytest.mark.timeout(900)
 def test_70b_tp8_shard_full_depth_bench_configuration():
     """The benchmark's workload: 70B-shape TP=8 one-rank shard, all 80 ladder layers,
