@@ -1,4 +1,6 @@
 // Small memory-bound kernels of the prefill path and the decode step prologue.
+#include <climits>
+
 #include "common.hpp"
 #include "kernels.h"
 
@@ -96,11 +98,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int ldx, c
 
 // Row m = b*T + t of qkv holds token t of sequence b at position start_pos + t.
 template <typename WT>
-__global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int T, int start_pos, int nq, int nkv, int hd,
-                                                      const float* rope_cos, const float* rope_sin, float* q_out,
-                                                      WT* k_cache, WT* v_cache, int max_seq) {
+__global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int T, int start_pos, const int* d_pos, int nq,
+                                                      int nkv, int hd, const float* rope_cos, const float* rope_sin,
+                                                      float* q_out, WT* k_cache, WT* v_cache, int max_seq) {
   const int m = blockIdx.x;
-  const int b = m / T, t = m % T, pos = start_pos + t;
+  const int b = m / T, t = m % T, pos = (d_pos ? *d_pos : start_pos) + t;
   const int qr = nq * hd, kr = nkv * hd, half = hd / 2;
   const float* row = qkv + (size_t)m * (qr + 2 * kr);
   for (int i = threadIdx.x; i < (qr + kr) / 2; i += 256) {
@@ -199,14 +201,14 @@ hipError_t launch_rmsnorm(int wdtype, const float* x, int ldx, const void* gain,
   return hipGetLastError();
 }
 
-hipError_t launch_rope_kv(int wdtype, const float* qkv, int B, int T, int start_pos, int nq, int nkv, int hd,
+hipError_t launch_rope_kv(int wdtype, const float* qkv, int B, int T, int start_pos, const int* d_pos, int nq, int nkv, int hd,
                           const float* rope_cos, const float* rope_sin, float* q_out,
                           void* k_cache, void* v_cache, int max_seq, hipStream_t s) {
   if (wdtype == W_BF16)
-    hipLaunchKernelGGL(rope_kv_kernel<uint16_t>, dim3(B * T), dim3(256), 0, s, qkv, T, start_pos, nq, nkv, hd,
+    hipLaunchKernelGGL(rope_kv_kernel<uint16_t>, dim3(B * T), dim3(256), 0, s, qkv, T, start_pos, d_pos, nq, nkv, hd,
                        rope_cos, rope_sin, q_out, (uint16_t*)k_cache, (uint16_t*)v_cache, max_seq);
   else
-    hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(B * T), dim3(256), 0, s, qkv, T, start_pos, nq, nkv, hd,
+    hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(B * T), dim3(256), 0, s, qkv, T, start_pos, d_pos, nq, nkv, hd,
                        rope_cos, rope_sin, q_out, (float*)k_cache, (float*)v_cache, max_seq);
   return hipGetLastError();
 }
@@ -245,6 +247,38 @@ hipError_t launch_decode_prologue(const int* ids_src, int* ids_dst, int B, int* 
   else
     hipLaunchKernelGGL(decode_prologue_kernel<float>, dim3(B), dim3(256), 0, s, ids_src, ids_dst, B, d_pos, pos,
                        d_epoch, (const float*)table, V, H, x);
+  return hipGetLastError();
+}
+
+// next[b] = index of the first maximum of x[b][0..V) (one workgroup per row).
+__global__ __launch_bounds__(256) void argmax_rows_kernel(const float* x, int V, int ld, int* next) {
+  __shared__ float rv[256];
+  __shared__ int ri[256];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const float* row = x + (size_t)b * ld;
+  float best = -INFINITY;
+  int idx = INT_MAX;
+  for (int i = tid; i < V; i += 256) {
+    const float v = row[i];
+    if (v > best) { best = v; idx = i; }        // i grows: the first maximum of this thread's entries
+  }
+  rv[tid] = best;
+  ri[tid] = idx;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) {
+      const float v = rv[tid + o];
+      const int i = ri[tid + o];
+      if (v > rv[tid] || (v == rv[tid] && i < ri[tid])) { rv[tid] = v; ri[tid] = i; }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) next[b] = ri[0] == INT_MAX ? 0 : ri[0];
+}
+
+hipError_t launch_argmax_rows(const float* x, int B, int V, int ld, int* next, hipStream_t s) {
+  if (!x || !next || B < 1 || V < 1 || ld < V) return hipErrorInvalidValue;
+  launch_timed(argmax_rows_kernel, dim3(B), dim3(256), 0, s, x, V, ld, next);
   return hipGetLastError();
 }
 

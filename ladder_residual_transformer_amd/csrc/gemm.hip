@@ -270,22 +270,21 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     const int big = ((p.M + 127) / 128) * ((p.N + 127) / 128);
     int S = 1;
     if (big < 256 && p.ws) {
-      for (int c = 2; c <= 8 && S == 1; c *= 2)
+      for (int c = 2; c <= 32 && S == 1; c *= 2)
         if ((long long)big * c >= 256 && p.K % (c * BK) == 0 && p.K / c >= kStages * BK &&
             (size_t)c * p.M * p.N <= p.ws_floats)
           S = c;
     }
     if (big >= 256 || S > 1) {
       const int tm = (p.M + 127) / 128, tiles = big, per = (tiles + kXcds - 1) / kXcds;
-      hipLaunchKernelGGL((gemm_f16x2_kernel<128, 128>), dim3(per * kXcds, S), dim3(256), 0, s, p, tm, tiles, per,
-                         p.K / S);
+      launch_timed(gemm_f16x2_kernel<128, 128>, dim3(per * kXcds, S), dim3(256), 0, s, p, tm, tiles, per, p.K / S);
       if (S > 1) {
         const size_t n_out = (size_t)p.M * (p.swiglu ? p.N / 2 : p.N);
-        hipLaunchKernelGGL(gemm_splitk_reduce_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, p, S);
+        launch_timed(gemm_splitk_reduce_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, p, S);
       }
     } else {
       const int tm = (p.M + 63) / 64, tiles = tm * ((p.N + 63) / 64), per = (tiles + kXcds - 1) / kXcds;
-      hipLaunchKernelGGL((gemm_f16x2_kernel<64, 64>), dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per, p.K);
+      launch_timed(gemm_f16x2_kernel<64, 64>, dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per, p.K);
     }
   } else if (p.swiglu) {
     return hipErrorInvalidValue;

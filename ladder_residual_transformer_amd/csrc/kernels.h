@@ -225,13 +225,16 @@ hipError_t launch_embed(int wdtype, const void* table, int V, int H, const int* 
 // out[m][:] = RMSNorm(x[m*ldx + :]) * gain (fp32)
 hipError_t launch_rmsnorm(int wdtype, const float* x, int ldx, const void* gain, float eps, int M, int H,
                           float* out, hipStream_t s);
-// qkv [B*T][q_rows + 2 kv_rows] -> q (rotated, fp32) and KV cache rows start_pos..start_pos+T-1
-hipError_t launch_rope_kv(int wdtype, const float* qkv, int B, int T, int start_pos, int nq, int nkv, int hd,
+// qkv [B*T][q_rows + 2 kv_rows] -> q (rotated, fp32) and KV cache rows p0..p0+T-1, with
+// p0 = *d_pos when d_pos is set (read when the kernel runs), else start_pos
+hipError_t launch_rope_kv(int wdtype, const float* qkv, int B, int T, int start_pos, const int* d_pos, int nq, int nkv, int hd,
                           const float* rope_cos, const float* rope_sin, float* q_out,
                           void* k_cache, void* v_cache, int max_seq, hipStream_t s);
 // gu [M][2F] interleaved (gate, up) -> a [M][F] (fp32)
 hipError_t launch_swiglu(const float* gu, int M, int F, float* a, hipStream_t s);
 hipError_t launch_add(const float* x, const float* y, float* out, size_t n, hipStream_t s);
+// next[b] = index of the first maximum of x[b][0..V) (row pitch ld)
+hipError_t launch_argmax_rows(const float* x, int B, int V, int ld, int* next, hipStream_t s);
 hipError_t launch_epoch_bump(int* d_epoch, hipStream_t s);   // ++*d_epoch
 // plain streaming read of bytes of buf by grid workgroups (sink: >= grid floats, never
 // read in practice)

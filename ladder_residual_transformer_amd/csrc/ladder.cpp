@@ -127,6 +127,7 @@ struct ladder_ctx {
 
   int sched = LADDER_SCHED_FUSED;
   int use_graph = 1;
+  bool gemm_step = false;            // a decode step is running through the prefill modules
   // next-token rule: greedy, or a draw (temperature > 0) with an optional top-k cut
   float temperature = 0.f;
   int top_k = 0;
@@ -610,22 +611,30 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
     gp.C = sc.qkv;
     gp.ldc = nqkv;
     HIPCHK(launch_gemm(gp, s));
-    HIPCHK(launch_rope_kv(ctx->wdt, sc.qkv, B, T, start_pos, g.n_q_heads, g.n_kv_heads, g.head_dim, ctx->rope_cos,
+    HIPCHK(launch_rope_kv(ctx->wdt, sc.qkv, B, T, start_pos, ctx->gemm_step ? ctx->pos_dev : nullptr, g.n_q_heads, g.n_kv_heads, g.head_dim, ctx->rope_cos,
                           ctx->rope_sin, sc.qr, layer_k(ctx, l), layer_v(ctx, l), g.max_seq, s));
-    AttnPrefillParams ap{};
-    ap.wdtype = ctx->wdt;
-    ap.q = sc.qr;
-    ap.k_cache = layer_k(ctx, l);
-    ap.v_cache = layer_v(ctx, l);
-    ap.max_seq = g.max_seq;
-    ap.nq = g.n_q_heads;
-    ap.nkv = g.n_kv_heads;
-    ap.hd = g.head_dim;
-    ap.B = B;
-    ap.T = T;
-    ap.start_pos = start_pos;
-    ap.out = sc.ob;
-    HIPCHK(launch_attn_prefill(ap, s));
+    if (ctx->gemm_step) {
+      // a decode step (one query per sequence at *pos_dev): the split-KV decode attention
+      AttnDecodeParams a = attn_params(ctx, l, B, sc);
+      a.q = sc.qr;
+      a.out = sc.ob;
+      HIPCHK(launch_attn_decode(a, s));
+    } else {
+      AttnPrefillParams ap{};
+      ap.wdtype = ctx->wdt;
+      ap.q = sc.qr;
+      ap.k_cache = layer_k(ctx, l);
+      ap.v_cache = layer_v(ctx, l);
+      ap.max_seq = g.max_seq;
+      ap.nq = g.n_q_heads;
+      ap.nkv = g.n_kv_heads;
+      ap.hd = g.head_dim;
+      ap.B = B;
+      ap.T = T;
+      ap.start_pos = start_pos;
+      ap.out = sc.ob;
+      HIPCHK(launch_attn_prefill(ap, s));
+    }
     proj_in = sc.ob;
     proj_k = ctx->qrows;
     proj_w = L.wo;
@@ -640,7 +649,9 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
       gp.swiglu = 1;
       gp.C = sc.ab;
       gp.ldc = g.ffn;
+      if (T == 1) TRACE(LADDER_KERNEL_GATEUP, s, false);   // a decode step on the matrix cores
       HIPCHK(launch_gemm(gp, s));
+      if (T == 1) TRACE(LADDER_KERNEL_GATEUP, s, true);
     } else {
       gp.C = sc.gu;
       gp.ldc = 2 * g.ffn;
@@ -820,7 +831,11 @@ ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream
 // One decode step from the embeddings the prologue left in dx[0] and pos_dev, leaving
 // logits/next in the context and x_{2L} in dx[(2L) % 2].  Enqueued on s0 (possibly under
 // graph capture).
+bool gemm_decode(const ladder_ctx* ctx, int B);
+ladder_status enqueue_decode_gemm(ladder_ctx* ctx, int B);
+
 ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
+  if (gemm_decode(ctx, B)) return enqueue_decode_gemm(ctx, B);
   const ladder_config& g = ctx->cfg;
   ctx->trace_n = 0;
   ladder_status st;
@@ -851,6 +866,58 @@ ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
   TRACE(LADDER_KERNEL_LMHEAD, ctx->s0, false);
   if ((st = lm_head(ctx, ctx->dx[(2 * g.n_layers) % 2], g.hidden, B, ctx->s0, ctx->pos_dev, 0))) return st;
   TRACE(LADDER_KERNEL_LMHEAD, ctx->s0, true);
+  ctx->trace_count = ctx->trace_n;
+  return LADDER_OK;
+}
+
+// Decode steps that the row-wave projections cannot take (bf16 weights, batch beyond
+// their LDS budget, batch > 4): one token per sequence through the prefill modules, whose
+// projections run on the matrix cores (the K-sliced GEMV kernels leave most of the HBM
+// bandwidth unused at those batches), with the split-KV decode attention, then the final
+// RMSNorm, the LM head as a GEMM and a row argmax.  Every kernel of the route takes the
+// position from the device (the prologue's pos_dev), so it is replayed as a graph too.
+bool gemm_decode(const ladder_ctx* ctx, int B) {
+  return ctx->wdt == W_BF16 && !gemv_rw_supported(ctx->wdt, ctx->cfg.hidden, B);
+}
+
+ladder_status enqueue_decode_gemm(ladder_ctx* ctx, int B) {
+  const int pos = 0;   // unused: every kernel reads the position from pos_dev
+  const ladder_config& g = ctx->cfg;
+  ctx->trace_n = 0;
+  const int saved = ctx->sched;
+  const bool fused = saved >= LADDER_SCHED_FUSED;
+  if (fused) ctx->sched = LADDER_SCHED_SERIAL;   // module order, adds in the GEMM epilogues
+  auto mod = [&](int m, const float* xin, const float* xm, float* xn, float* store, hipStream_t s, bool wait,
+                 hipEvent_t ev) { return prefill_module(ctx, m, B, 1, pos, xin, xm, xn, store, s, wait, ev); };
+  ctx->gemm_step = true;
+  ladder_status st = run_modules(ctx, ctx->dx, ctx->dout, (size_t)B * g.hidden, mod, fused);
+  ctx->gemm_step = false;
+  ctx->sched = saved;
+  if (st) return st;
+  StreamScratch& sc = ctx->sc[0];
+  HIPCHK(launch_rmsnorm(ctx->wdt, ctx->dx[(2 * g.n_layers) % 2], g.hidden, ctx->w.final_norm, g.norm_eps, B, g.hidden,
+                        sc.u, ctx->s0));
+  GemmParams hp{};
+  hp.wdtype = ctx->wdt;
+  hp.A = sc.u;
+  hp.lda = g.hidden;
+  hp.rows = RowSrc{{ctx->w.lm_head, nullptr, nullptr}, g.vocab, g.vocab, 0};
+  hp.M = B;
+  hp.N = g.vocab;
+  hp.K = g.hidden;
+  hp.C = ctx->logits;
+  hp.ldc = g.vocab;
+  hp.ws = sc.gk;
+  hp.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
+  TRACE(LADDER_KERNEL_LMHEAD, ctx->s0, false);
+  HIPCHK(launch_gemm(hp, ctx->s0));
+  HIPCHK(launch_argmax_rows(ctx->logits, B, g.vocab, g.vocab, ctx->next, ctx->s0));
+  TRACE(LADDER_KERNEL_LMHEAD, ctx->s0, true);
+  if (ctx->temperature > 0.f) {
+    TRACE(LADDER_KERNEL_SAMPLE, ctx->s0, false);
+    HIPCHK(launch_sample(sample_params(ctx, B, ctx->pos_dev, 0), ctx->s0));
+    TRACE(LADDER_KERNEL_SAMPLE, ctx->s0, true);
+  }
   ctx->trace_count = ctx->trace_n;
   return LADDER_OK;
 }
