@@ -98,7 +98,7 @@ typedef struct ladder_config {
   double rope_theta;       /* pair j of a head rotates by p * theta^(-2j/head_dim) */
   float norm_eps;          /* RMSNorm epsilon (1e-5) */
   int32_t dtype;           /* LADDER_F32 or LADDER_BF16 */
-  int32_t max_batch;       /* 1..16 */
+  int32_t max_batch;       /* 1..256 with bf16 weights, 1..16 with fp32 */
   int32_t max_seq;         /* KV capacity per sequence */
   int32_t max_prefill_tokens; /* rows per prefill chunk (B * tokens); 0 = 8192 */
   int32_t kv_filled;       /* KV positions already valid at init (resume on an existing cache) */
@@ -223,7 +223,7 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 
 /* Profiling aid.  For each kernel kind, enqueue it on the context's stream exactly as
  * a decode step at batch B launches it (once per layer; the LM head once), once untimed
- * and then reps times,
+ * and then reps times (the GEMV kinds at B <= 16 only; -1 beyond),
  * (the fused kinds use each layer as if it were a ladder layer),
  * between two HIP events, and store the mean duration of one launch in microseconds
  * in us_out[kind] (host array of LADDER_N_KERNELS floats).  Works on the context's

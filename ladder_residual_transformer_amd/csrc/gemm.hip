@@ -10,9 +10,9 @@
 // modules carries into the final residual.
 //
 // Tiling: a workgroup of 4 waves owns a 128x128 tile of C (2x2 waves of 64x64, i.e.
-// 4x4 MFMA tiles each; 32x128 tiles for at most 32 rows, as in a decode step of a large
-// batch, where 128-row tiles would be mostly padding; 64x64 tiles when 128x128 ones
-// would leave CUs idle) and walks K
+// 4x4 MFMA tiles each; 32x128 or 64x128 tiles for at most 32 or 64 rows, as in a decode
+// step of a large batch, where 128-row tiles would be mostly padding; 64x64 tiles when
+// 128x128 ones would leave CUs idle) and walks K
 // in steps of 32 through double-buffered LDS with padded rows.  The global loads run
 // kStages steps ahead of the MFMAs in a ring of register buffers (a step's MFMA work,
 // ~0.2-0.4 us per workgroup, is well below the latency of a global load under a full
@@ -266,12 +266,11 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.M < 1 || p.N < 1 || p.K < 1) return hipErrorInvalidValue;
   if (p.wdtype == W_BF16) {
     if (p.K % BK != 0 || p.lda % 4 != 0 || (p.swiglu && (p.N % 2 != 0 || p.res))) return hipErrorInvalidValue;
-    // 128x128 tiles (32x128 for at most 32 rows) when they give the device at least one
+    // 128x128 tiles (32x128 / 64x128 for at most 32 / 64 rows) when they give the device at least one
     // round of work; else the same tiles with K split over the fewest slices that reach a
     // round (each slice at least kStages steps long, partials within the workspace); else
     // 64x64
-    const bool skinny = p.M <= 32;
-    const int tmr = skinny ? 32 : 128;
+    const int tmr = p.M <= 32 ? 32 : p.M <= 64 ? 64 : 128;
     const int big = ((p.M + tmr - 1) / tmr) * ((p.N + 127) / 128);
     int S = 1;
     if (big < 256 && p.ws) {
@@ -282,8 +281,10 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     }
     if (big >= 256 || S > 1) {
       const int tm = (p.M + tmr - 1) / tmr, tiles = big, per = (tiles + kXcds - 1) / kXcds;
-      if (skinny)
+      if (tmr == 32)
         launch_timed(gemm_f16x2_kernel<32, 128>, dim3(per * kXcds, S), dim3(256), 0, s, p, tm, tiles, per, p.K / S);
+      else if (tmr == 64)
+        launch_timed(gemm_f16x2_kernel<64, 128>, dim3(per * kXcds, S), dim3(256), 0, s, p, tm, tiles, per, p.K / S);
       else
         launch_timed(gemm_f16x2_kernel<128, 128>, dim3(per * kXcds, S), dim3(256), 0, s, p, tm, tiles, per, p.K / S);
       if (S > 1) {

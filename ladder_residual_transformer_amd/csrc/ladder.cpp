@@ -172,7 +172,9 @@ ladder_status validate(const ladder_config* c, const ladder_weights* w, const la
   if (c->dtype != LADDER_F32 && c->dtype != LADDER_BF16) return LADDER_ERR_ARG;
   if (!(c->rope_theta > 0.0) || !(c->norm_eps >= 0.0f)) return LADDER_ERR_ARG;
   if (c->kv_filled < 0 || c->kv_filled > c->max_seq) return LADDER_ERR_ARG;
-  if (c->max_batch > 16) return LADDER_ERR_SHAPE;
+  // fp32 models decode beyond batch 4 with the K-sliced GEMV (at most 16 rows); bf16
+  // models on the matrix cores (the decode prologue takes at most 256 sequences)
+  if (c->max_batch > (c->dtype == LADDER_BF16 ? 256 : 16)) return LADDER_ERR_SHAPE;
   if (c->n_q_heads % c->n_kv_heads != 0 || c->n_q_heads / c->n_kv_heads > 16) return LADDER_ERR_SHAPE;
   if (c->head_dim != 64 && c->head_dim != 128) return LADDER_ERR_SHAPE;
   const int vec = c->dtype == LADDER_BF16 ? 8 : 4;
@@ -815,11 +817,34 @@ SampleParams sample_params(const ladder_ctx* ctx, int B, const int* d_pos, int p
   return sp;
 }
 
+bool gemm_decode(const ladder_ctx* ctx, int B);
+
 // Final RMSNorm + LM head + greedy token; with sampling on, the draw then overwrites the
-// token (the logits are the same either way).
+// token (the logits are the same either way).  Batches the row-wave GEMV cannot take (bf16)
+// run the LM head on the matrix cores: RMSNorm, GEMM, row argmax.
 ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream_t s, const int* d_pos, int pos) {
-  ladder_status st = run_gemv(ctx, lmhead_params(ctx, x, ldx, B), s);
-  if (st) return st;
+  const ladder_config& g = ctx->cfg;
+  if (gemm_decode(ctx, B)) {
+    StreamScratch& sc = ctx->sc[0];
+    HIPCHK(launch_rmsnorm(ctx->wdt, x, ldx, ctx->w.final_norm, g.norm_eps, B, g.hidden, sc.u, s));
+    GemmParams hp{};
+    hp.wdtype = ctx->wdt;
+    hp.A = sc.u;
+    hp.lda = g.hidden;
+    hp.rows = RowSrc{{ctx->w.lm_head, nullptr, nullptr}, g.vocab, g.vocab, 0};
+    hp.M = B;
+    hp.N = g.vocab;
+    hp.K = g.hidden;
+    hp.C = ctx->logits;
+    hp.ldc = g.vocab;
+    hp.ws = sc.gk;
+    hp.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
+    HIPCHK(launch_gemm(hp, s));
+    HIPCHK(launch_argmax_rows(ctx->logits, B, g.vocab, g.vocab, ctx->next, s));
+  } else {
+    ladder_status st = run_gemv(ctx, lmhead_params(ctx, x, ldx, B), s);
+    if (st) return st;
+  }
   if (ctx->temperature > 0.f) {
     TRACE(LADDER_KERNEL_SAMPLE, s, false);
     HIPCHK(launch_sample(sample_params(ctx, B, d_pos, pos), s));
@@ -894,30 +919,9 @@ ladder_status enqueue_decode_gemm(ladder_ctx* ctx, int B) {
   ctx->gemm_step = false;
   ctx->sched = saved;
   if (st) return st;
-  StreamScratch& sc = ctx->sc[0];
-  HIPCHK(launch_rmsnorm(ctx->wdt, ctx->dx[(2 * g.n_layers) % 2], g.hidden, ctx->w.final_norm, g.norm_eps, B, g.hidden,
-                        sc.u, ctx->s0));
-  GemmParams hp{};
-  hp.wdtype = ctx->wdt;
-  hp.A = sc.u;
-  hp.lda = g.hidden;
-  hp.rows = RowSrc{{ctx->w.lm_head, nullptr, nullptr}, g.vocab, g.vocab, 0};
-  hp.M = B;
-  hp.N = g.vocab;
-  hp.K = g.hidden;
-  hp.C = ctx->logits;
-  hp.ldc = g.vocab;
-  hp.ws = sc.gk;
-  hp.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
   TRACE(LADDER_KERNEL_LMHEAD, ctx->s0, false);
-  HIPCHK(launch_gemm(hp, ctx->s0));
-  HIPCHK(launch_argmax_rows(ctx->logits, B, g.vocab, g.vocab, ctx->next, ctx->s0));
+  if ((st = lm_head(ctx, ctx->dx[(2 * g.n_layers) % 2], g.hidden, B, ctx->s0, ctx->pos_dev, 0))) return st;
   TRACE(LADDER_KERNEL_LMHEAD, ctx->s0, true);
-  if (ctx->temperature > 0.f) {
-    TRACE(LADDER_KERNEL_SAMPLE, ctx->s0, false);
-    HIPCHK(launch_sample(sample_params(ctx, B, ctx->pos_dev, 0), ctx->s0));
-    TRACE(LADDER_KERNEL_SAMPLE, ctx->s0, true);
-  }
   ctx->trace_count = ctx->trace_n;
   return LADDER_OK;
 }
@@ -1231,12 +1235,14 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
   const bool rw_f = gemv_rw_supported(ctx->wdt, g.ffn, B) && gemv_rw_attn_fusable(ctx->wdt, g.ffn);
   const bool two = two_launch_layers(ctx, B);
   const bool seq = seq_layers(ctx, B);
+  const bool gemv_ok = B <= 16;        // the per-kind GEMV launches take at most 16 rows
   for (int kind = 0; kind < LADDER_N_KERNELS; ++kind) {
     int launches = 0;
     HIPCHK(hipEventRecord(e0, s));   // (re-recorded after the warm-up; kept for kinds that are unavailable)
     // repetition -1 is an untimed warm-up (a kernel's first launch in a process also loads
     // its code)
     for (int r = -1; r < reps; ++r) {
+      if (!gemv_ok && kind != LADDER_KERNEL_SAMPLE) break;
       if (r == 0) {
         launches = 0;
         HIPCHK(hipEventRecord(e0, s));

@@ -74,7 +74,8 @@ def init_status(cfg, w, kv):
 
 @pytest.mark.parametrize("change, status", [
     (dict(hd=96), abi.LADDER_ERR_SHAPE),
-    (dict(max_batch=17), abi.LADDER_ERR_SHAPE),
+    (dict(max_batch=17), abi.LADDER_ERR_SHAPE),         # fp32: the K-sliced GEMV takes at most 16 rows
+    (dict(dtype=1, ffn=704, max_batch=257), abi.LADDER_ERR_SHAPE),   # bf16: at most 256 sequences
     (dict(nq=6, nkv=4), abi.LADDER_ERR_SHAPE),
     (dict(nq=34, nkv=2), abi.LADDER_ERR_SHAPE),        # more than 16 query heads per kv head
     (dict(hidden=258), abi.LADDER_ERR_SHAPE),          # not a whole number of 16-byte vectors

@@ -149,6 +149,27 @@ def test_mixed_layer_kinds_schedules_bitwise(mixed, use_graph, B):
             assert np.array_equal(a, b), f"schedule {sched} differs from serial"
 
 
+def test_large_batch_matches_oracle_and_rows(edge):
+    """Batch 24 (beyond the K-sliced GEMV's 16 rows, so only the matrix-core decode route
+    can take it): against the oracle, and the graph replays bit for bit equal to eager
+    launches."""
+    cfg, w = edge
+    B = 24
+    prompt = synth.gen_ids(B, 9, cfg.vocab, seed=21)
+    cont = synth.gen_ids(B, 3, cfg.vocab, seed=21, stream=1)
+    ref = oracle_record(cfg, w, prompt, 4, dtype=np.float64)
+    res = []
+    for g in (False, True):
+        model = make_model(cfg, w, B, 16)
+        model.set_schedule(FUSED, g)
+        gl, gh, gt = gpu_teacher_forced(model, prompt, ref["tokens"][:, :-1])
+        model.free()
+        check_against_oracle(cfg, gl, gh, gt, ref, TOL["bf16"], f"edge B={B} graph={g}")
+        res.append((gl, gh, gt))
+    for a, b in zip(*res):
+        assert np.array_equal(a, b), "graph replay differs from eager launches"
+
+
 def test_graph_replay_matches_eager(edge):
     cfg, w = edge
     prompt = synth.gen_ids(2, 11, cfg.vocab, seed=8)
