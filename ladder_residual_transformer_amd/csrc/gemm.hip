@@ -199,6 +199,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmParams p, i
   if (p.swiglu) {
     const float* w = p.ws + (size_t)m * p.N + 2 * n;
     float g = 0.f, u = 0.f;
+#pragma unroll 8
     for (int s = 0; s < S; ++s) {
       g += w[s * plane];
       u += w[s * plane + 1];
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmParams p, i
   } else {
     const float* w = p.ws + (size_t)m * p.N + n;
     float v = 0.f;
+#pragma unroll 8
     for (int s = 0; s < S; ++s) v += w[s * plane];
     if (p.res) v = p.res[(size_t)m * p.ldr + n] + v;
     p.C[(size_t)m * p.ldc + n] = v;
