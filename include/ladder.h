@@ -72,13 +72,14 @@ typedef int32_t ladder_status;
 #define LADDER_SCHED_FUSED 3     /* one stream; a ladder layer's (or parallel block's)
                                     attention and MLP run side by side (their inputs
                                     x_{2l-1} and x_{2l} both exist when the layer starts; a
-                                    parallel block reads x_{2l} twice).  bf16, batch <= 4:
-                                    two launches per layer, [QKV, then gate/up, in every
-                                    workgroup | the attention's key chunks once every QKV
-                                    share is done] and [merge of the chunks | down rows,
-                                    then the O rows + both residual adds];
-                                    otherwise [QKV | gate/up], [attention | down], [O + both
-                                    adds] (default) */
+                                    parallel block reads x_{2l} twice).  bf16, row-wave
+                                    batches: two launches per layer, [QKV (half of the
+                                    workgroups first), then gate/up | the attention once
+                                    every QKV share is done] and [down rows, then the O rows
+                                    + both residual adds] while the first launch keeps two
+                                    workgroups per CU, else as FUSED_LATE_ATTN; fp32:
+                                    [QKV | gate/up], [attention | down], [O + both adds]
+                                    (default) */
 #define LADDER_SCHED_PERSISTENT 4 /* decode: the whole layer stack in one launch of resident
                                     workgroups that signal each other (every layer ladder,
                                     bf16, batch <= 4; otherwise as FUSED); prefill as FUSED */
@@ -153,7 +154,11 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
 /* One decode step: d_ids [B] int32 at position pos (pos <= positions filled,
  * pos < max_seq).  Same outputs as ladder_prefill.  d_ids may alias d_next of the
  * previous step, so a generation loop needs no host synchronisation.  Replays a
- * captured HIP graph per (B, schedule) when graphs are enabled. */
+ * captured HIP graph per (B, schedule, next-token rule) when graphs are enabled.
+ * Batches whose staged projection inputs fit the row-wave GEMV (B <= 4 and
+ * B * (hidden + 8) * 4 bytes <= 150 KB) run the schedule's GEMV launches; larger bf16
+ * batches run one token per sequence through the prefill modules on the matrix cores
+ * (with the split-KV decode attention), under every schedule. */
 ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t pos,
                                  float* d_logits, int32_t* d_next, float* d_hidden);
 
