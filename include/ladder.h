@@ -214,13 +214,14 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 #define LADDER_KERNEL_LAYER_STACK 9  /* persistent launch of a decode step's whole layer stack
                                         (LADDER_SCHED_PERSISTENT); ladder_time_kernels stores
                                         -1 where that launch is not available */
-#define LADDER_KERNEL_QKV_ATTN_GATEUP 10 /* fused ladder launch (FUSED, bf16, batch <= 4): QKV
-                                        (+RoPE/KV), then gate/up (+SwiGLU), in every workgroup |
-                                        the attention's key chunks once every QKV share is
-                                        done; -1 from ladder_time_kernels where not available */
-#define LADDER_KERNEL_DOWN_OPROJ 11  /* fused ladder launch (FUSED, bf16, batch <= 4): merge of
-                                        the attention's chunks | down rows, then the O rows +
-                                        both residual adds; -1 where not available */
+#define LADDER_KERNEL_QKV_ATTN_GATEUP 10 /* fused ladder launch (FUSED, bf16, row-wave batches
+                                        with two workgroups per CU): QKV (+RoPE/KV) in half of
+                                        the workgroups, then gate/up (+SwiGLU) in all | the
+                                        split-KV attention once every QKV share is done; -1
+                                        from ladder_time_kernels where not available */
+#define LADDER_KERNEL_DOWN_OPROJ 11  /* fused ladder launch (the same layers): down rows, then
+                                        the O rows + both residual adds; -1 where not
+                                        available */
 #define LADDER_KERNEL_SAMPLE 12   /* stochastic draw from the logits (ladder_set_sampling); timed
                                         with the context's sampling settings, or temperature 1
                                         and no top-k cut when sampling is off */
