@@ -188,7 +188,9 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillParam
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int n_qt = (p.T + kPqTile - 1) / kPqTile;
-  const int qt = n_qt - 1 - (int)blockIdx.x;   // longest causal ranges first
+  const int NC = p.nchunk;                     // key chunks per query tile (1: no split)
+  const int qt = n_qt - 1 - (int)blockIdx.x / NC;   // longest causal ranges first
+  const int chunk = (int)blockIdx.x % NC;
   const int h = blockIdx.y, b = blockIdx.z;
   const int G = p.nq / p.nkv, kvh = h / G;
   const size_t kv_base = ((size_t)b * p.nkv + kvh) * p.max_seq * HD;
@@ -202,8 +204,13 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillParam
   const int t_q = t_raw < p.T ? t_raw : p.T - 1;
   const int qpos = p.start_pos + t_q;
   const int wave_last = p.start_pos + min(p.T - 1, qt * kPqTile + w * kPqWave + kPqWave - 1);
-  const int n_keys = p.start_pos + min(p.T, (qt + 1) * kPqTile);   // keys of the workgroup
-  const int n_kt = (n_keys + kPkTile - 1) / kPkTile;
+  const int n_keys = p.start_pos + min(p.T, (qt + 1) * kPqTile);   // keys of the query tile
+  // this workgroup's keys [k_lo, k_hi): all of them, or one chunk of them
+  const int k_lo = NC > 1 ? chunk * p.kchunk : 0;
+  if (k_lo >= n_keys) return;                  // whole workgroup: the tile has fewer chunks
+  const int k_hi = NC > 1 ? min(n_keys, k_lo + p.kchunk) : n_keys;
+  const int tile_chunks = NC > 1 ? (n_keys + p.kchunk - 1) / p.kchunk : 1;
+  const int n_kt = (k_hi - k_lo + kPkTile - 1) / kPkTile;
 
   // Q^T operand as fp16 pairs: step s holds dims 16s + 8*half .. +8 of this lane's query
   half8 qh[NST], ql[NST];
@@ -232,14 +239,14 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillParam
     for (int i = 0; i < KCH; ++i) {
       const int e = tid + 256 * i, r = e / CPR, c = e % CPR;
       const int kp = k0 + r;
-      kr[i] = kp < n_keys ? *(const uint4*)(kc + (size_t)kp * HD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+      kr[i] = kp < k_hi ? *(const uint4*)(kc + (size_t)kp * HD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int i = 0; i < VPAIR; ++i) {
       const int e = tid + 256 * i, j = e / CPR, c = e % CPR;
       const int kp = k0 + 2 * j;
-      vr[i][0] = kp < n_keys ? *(const uint4*)(vc + (size_t)kp * HD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
-      vr[i][1] = kp + 1 < n_keys ? *(const uint4*)(vc + (size_t)(kp + 1) * HD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+      vr[i][0] = kp < k_hi ? *(const uint4*)(vc + (size_t)kp * HD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+      vr[i][1] = kp + 1 < k_hi ? *(const uint4*)(vc + (size_t)(kp + 1) * HD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
     }
   };
   auto store_tile = [&]() {
@@ -269,9 +276,9 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillParam
   const float c2 = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(hd)
   float m_run = -INFINITY, l_run = 0.f;
 
-  load_tile(0);
+  load_tile(k_lo);
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = kt * kPkTile;
+    const int k0 = k_lo + kt * kPkTile;
     __syncthreads();                 // previous tile fully consumed
     store_tile();
     __syncthreads();
@@ -301,10 +308,12 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillParam
         mx = fmaxf(mx, s[kb][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);   // finite from tile 0 on: key 0 is visible to every query
-    const float alpha = exp2f((m_run - m_new) * c2);
+    // finite from the first tile on without a split (key 0 is visible to every query); a
+    // later key chunk may hold no visible key yet for this lane's query
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f((m_run - m_new) * c2);
     m_run = m_new;
-    const float mc = m_new * c2;
+    const float mc = m_new == -INFINITY ? 0.f : m_new * c2;
     float ls = 0.f;
     uint32_t ph[2][8], pl[2][8];
 #pragma unroll
@@ -344,6 +353,22 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillParam
   }
   l_run += __shfl_xor(l_run, 32, 64);
   if (t_raw >= p.T) return;
+  if (tile_chunks > 1) {
+    // chunk record: max (raw score units), sum, two unused, unnormalized accumulator
+    float* rec = p.part + ((((size_t)b * p.nq + h) * p.T + t_raw) * NC + chunk) * (HD + 4);
+    if (half == 0) {
+      rec[0] = m_run;
+      rec[1] = l_run;
+    }
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = d * 32 + 8 * g + 4 * half;
+        *(float4*)(rec + 4 + dim) = make_float4(o[d][4 * g], o[d][4 * g + 1], o[d][4 * g + 2], o[d][4 * g + 3]);
+      }
+    return;
+  }
   const float inv = 1.0f / l_run;
   float* dst = p.out + ((size_t)b * p.T + t_raw) * qld + (size_t)h * HD;
 #pragma unroll
@@ -356,13 +381,70 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillParam
     }
 }
 
-hipError_t launch_attn_prefill(const AttnPrefillParams& p, hipStream_t s) {
+// Combines the chunk records of the query tiles that were split: per (sequence, head,
+// query) M = max_c m_c, w_c = 2^((m_c - M) log2(e)/sqrt(hd)), out = sum_c w_c acc_c /
+// sum_c w_c l_c, in chunk order.  One thread per 4 output dimensions.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_prefill_merge_kernel(AttnPrefillParams p) {
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int e = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  const int t = e / (HD / 4), d4 = (e % (HD / 4)) * 4;
+  if (t >= p.T) return;
+  const int qt = t / kPqTile;
+  const int n_keys = p.start_pos + min(p.T, (qt + 1) * kPqTile);
+  const int nc = (n_keys + p.kchunk - 1) / p.kchunk;
+  if (nc <= 1) return;                         // written by its only workgroup
+  const float c2 = 1.4426950408889634f / sqrtf((float)HD);
+  const float* rec = p.part + (((size_t)b * p.nq + h) * p.T + t) * p.nchunk * (HD + 4);
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, rec[(size_t)c * (HD + 4)]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = 0; c < nc; ++c) {
+    const float* r = rec + (size_t)c * (HD + 4);
+    const float w = r[0] == -INFINITY ? 0.f : exp2f((r[0] - M) * c2);
+    L = fmaf(r[1], w, L);
+    const float4 a = *(const float4*)(r + 4 + d4);
+    acc.x = fmaf(a.x, w, acc.x);
+    acc.y = fmaf(a.y, w, acc.y);
+    acc.z = fmaf(a.z, w, acc.z);
+    acc.w = fmaf(a.w, w, acc.w);
+  }
+  const float inv = 1.0f / L;
+  float* dst = p.out + ((size_t)b * p.T + t) * ((size_t)p.nq * HD) + (size_t)h * HD + d4;
+  *(float4*)dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
+hipError_t launch_attn_prefill(const AttnPrefillParams& p_in, hipStream_t s) {
+  AttnPrefillParams p = p_in;
   if (p.nkv < 1 || p.nq % p.nkv != 0 || p.T < 1) return hipErrorInvalidValue;
   if (p.wdtype == W_BF16) {
-    dim3 grid((p.T + kPqTile - 1) / kPqTile, p.nq, p.B);
+    if (p.hd != 128 && p.hd != 64) return hipErrorInvalidValue;
+    // few query tiles (one prompt of ~1k tokens: 8 tiles per head): cut each tile's keys
+    // into at most kAttnPrefillMaxChunks chunks of >= 256 keys, so that the longest causal
+    // range no longer sets the launch's duration alone
+    const int n_qt = (p.T + kPqTile - 1) / kPqTile;
+    p.nchunk = 1;
+    p.kchunk = 0;
+    if (p.part && (long long)n_qt * p.nq * p.B < 256) {
+      const int n_keys_max = p.start_pos + p.T;
+      int ck = (n_keys_max + kAttnPrefillMaxChunks - 1) / kAttnPrefillMaxChunks;
+      ck = (ck + kPkTile - 1) / kPkTile * kPkTile;
+      if (ck < 256) ck = 256;
+      const int nc = (n_keys_max + ck - 1) / ck;
+      if (nc > 1 && (size_t)p.B * p.nq * p.T * nc * (p.hd + 4) <= p.part_floats) {
+        p.nchunk = nc;
+        p.kchunk = ck;
+      }
+    }
+    dim3 grid(n_qt * p.nchunk, p.nq, p.B);
     if (p.hd == 128) hipLaunchKernelGGL(attn_prefill_mfma_kernel<128>, grid, dim3(256), 0, s, p);
-    else if (p.hd == 64) hipLaunchKernelGGL(attn_prefill_mfma_kernel<64>, grid, dim3(256), 0, s, p);
-    else return hipErrorInvalidValue;
+    else hipLaunchKernelGGL(attn_prefill_mfma_kernel<64>, grid, dim3(256), 0, s, p);
+    if (p.nchunk > 1) {
+      dim3 mg((p.T * (p.hd / 4) + 255) / 256, p.nq, p.B);
+      if (p.hd == 128) hipLaunchKernelGGL(attn_prefill_merge_kernel<128>, mg, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL(attn_prefill_merge_kernel<64>, mg, dim3(256), 0, s, p);
+    }
     return hipGetLastError();
   }
   dim3 grid((p.T + kQTile - 1) / kQTile, p.nq, p.B);

@@ -192,7 +192,16 @@ struct AttnPrefillParams {
   const void* k_cache; const void* v_cache;
   int max_seq, nq, nkv, hd, B, T, start_pos;
   float* out;                          // [B*T][nq*hd]
+  // key split (bf16, nullable): when the query tiles give the device few workgroups, each
+  // tile's keys are cut into at most kAttnPrefillMaxChunks chunks whose records
+  // [B][nq][T][chunks][hd+4] a merge kernel combines; part_floats >= attn_prefill_part_floats(hd)
+  float* part; size_t part_floats;
+  int kchunk, nchunk;                  // set by the launcher
 };
+constexpr int kAttnPrefillMaxChunks = 4;
+constexpr size_t attn_prefill_part_floats(int hd) {
+  return (size_t)256 * 128 * kAttnPrefillMaxChunks * (hd + 4);   // B*T*nq < 256 query tiles of 128
+}
 hipError_t launch_attn_prefill(const AttnPrefillParams& p, hipStream_t s);
 
 // ----------------------------------------------------------------- GEMM (prefill)

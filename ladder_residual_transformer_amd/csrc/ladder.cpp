@@ -55,6 +55,7 @@ struct StreamScratch {
   float* gu = nullptr;
   float* ab = nullptr;
   float* gk = nullptr;   // split-K partials of the prefill GEMMs (bf16 models)
+  float* apart = nullptr;  // key-chunk records of the prefill attention (bf16 models)
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -262,7 +263,10 @@ void carve(ladder_ctx* c, Carver& cv) {
     sc.qr = cv.take<float>((size_t)c->mmax * c->qrows);
     sc.ob = cv.take<float>((size_t)c->mmax * c->qrows);
     sc.gu = cv.take<float>((size_t)c->mmax * 2 * F);
-    if (c->wdt == W_BF16) sc.gk = cv.take<float>(kGemmSplitWsFloats);
+    if (c->wdt == W_BF16) {
+      sc.gk = cv.take<float>(kGemmSplitWsFloats);
+      sc.apart = cv.take<float>(attn_prefill_part_floats(g.head_dim));
+    }
     sc.ab = cv.take<float>((size_t)c->mmax * F);
   }
 }
@@ -635,6 +639,8 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
       ap.T = T;
       ap.start_pos = start_pos;
       ap.out = sc.ob;
+      ap.part = sc.apart;
+      ap.part_floats = sc.apart ? attn_prefill_part_floats(g.head_dim) : 0;
       HIPCHK(launch_attn_prefill(ap, s));
     }
     proj_in = sc.ob;

@@ -201,6 +201,31 @@ def test_chunked_prefill_equals_prefill_then_decode(edge):
     model.free()
 
 
+def test_split_key_prefill_continuing_a_cache(edge):
+    """A long prefill that continues an existing cache (start_pos 300, 1000 more tokens:
+    its query tiles' keys are cut into chunks and merged) against the oracle at every
+    position of the second chunk."""
+    cfg, w = edge
+    ids = synth.gen_ids(1, 1300, cfg.vocab, seed=17)
+    ref = LadderOracle(cfg, w).forward(ids, logits="all")
+    model = make_model(cfg, w, 1, 1310)
+    t = torch.from_numpy(ids).cuda()
+    model.prefill(t[:, :300].contiguous())
+    lg, nx, hd = model.prefill(t[:, 300:].contiguous(), start_pos=300)
+    torch.cuda.synchronize()
+    log(f"split-key prefill: rel err logits {rel_err(lg.cpu().numpy(), ref.logits[:, 1299]):.3g}")
+    assert rel_err(lg.cpu().numpy(), ref.logits[:, 1299]) <= TOL["bf16"]
+    assert rel_err(hd.cpu().numpy(), ref.hidden[:, 1299]) <= TOL["bf16"]
+    # the next decode step reads every cached key written by both prefills
+    step = torch.from_numpy(synth.gen_ids(1, 1, cfg.vocab, seed=18)[:, 0].copy()).cuda()
+    lg2, _, _ = model.decode_step(step, 1300)
+    torch.cuda.synchronize()
+    ids2 = np.concatenate([ids, step.cpu().numpy()[:, None].astype(ids.dtype)], axis=1)
+    ref2 = LadderOracle(cfg, w).forward(ids2, logits="last")
+    assert rel_err(lg2.cpu().numpy(), ref2.logits[:, -1]) <= TOL["bf16"]
+    model.free()
+
+
 def test_resume_on_existing_cache_is_bitwise(edge):
     """Prefill and two decode steps in one context, then a fresh context on the same KV
     cache (kv_filled) continues exactly like the uninterrupted one."""
