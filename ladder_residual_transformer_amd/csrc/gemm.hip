@@ -274,12 +274,16 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     // 64x64
     const int tmr = p.M <= 32 ? 32 : p.M <= 64 ? 64 : 128;
     const int big = ((p.M + tmr - 1) / tmr) * ((p.N + 127) / 128);
+    // the fewest slices that give one round of workgroups (two rounds, two per CU, for
+    // skinny tiles, which stream weights with little work per byte: more of them in flight)
+    const int want = tmr < 128 ? 512 : 256;
     int S = 1;
     if (big < 256 && p.ws) {
-      for (int c = 2; c <= 32 && S == 1; c *= 2)
-        if ((long long)big * c >= 256 && p.K % (c * BK) == 0 && p.K / c >= kStages * BK &&
-            (size_t)c * p.M * p.N <= p.ws_floats)
-          S = c;
+      for (int c = 2; c <= 64; c *= 2) {
+        if (p.K % (c * BK) != 0 || p.K / c < kStages * BK || (size_t)c * p.M * p.N > p.ws_floats) break;
+        if ((long long)big * c >= 256) S = c;          // a valid split that fills one round
+        if ((long long)big * c >= want) break;
+      }
     }
     if (big >= 256 || S > 1) {
       const int tm = (p.M + tmr - 1) / tmr, tiles = big, per = (tiles + kXcds - 1) / kXcds;
