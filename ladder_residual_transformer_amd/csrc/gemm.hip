@@ -18,6 +18,10 @@
 // ~0.2-0.4 us per workgroup, is well below the latency of a global load under a full
 // device's traffic, so one step of prefetch leaves the matrix cores waiting).
 // Optional epilogues: a residual add, or SwiGLU over interleaved gate/up columns.
+// Optional RMSNorm (split launches of a decode step): RMSNorm(x) W^T = (x * g) W^T / rms(x)
+// row by row, so A is the raw residual row, it is multiplied by the gain on its way into
+// LDS, the workgroups of the first column tile add up each row's squares over their K
+// slice, and the reduction divides each row's sums by its rms.
 // Workgroups are dealt to the 8 XCDs round robin, so the tile list (M fastest) is cut
 // into 8 contiguous runs and run x goes to XCD x: workgroups that share a weight tile
 // run together on one XCD and read it once into that XCD's L2.
@@ -50,7 +54,7 @@ constexpr int kStages = 4;   // K steps whose global loads are in flight (even: 
 // device), 4 waves of (TM/2) x (TN/2), i.e. (TM/32) x (TN/32) MFMA tiles of 16x16 each.
 // Slice blockIdx.y covers K range [blockIdx.y * kchunk, + kchunk); with more than one
 // slice the raw partial tile goes to p.ws[slice][M][N].
-template <int TM, int TN>
+template <int TM, int TN, bool NORM = false>
 __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd,
                                                          int kchunk) {
   constexpr int FM = TM / 32, FN = TN / 32;       // MFMA tiles per wave
@@ -92,16 +96,38 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
   // register ring: stage st holds the global loads of one K step
   float4 ra[kStages][AV];
   uint4 rb[kStages][BV];
+  uint2 rg[kStages][AV];                          // NORM: the gain of each A float4 (4 x bf16)
+  const uint16_t* gain = NORM ? (const uint16_t*)p.gain + kbase : nullptr;
+  const bool sum_sq = NORM && tile < n_tiles_m;   // the first column tile adds up the squares
+  float sq[AV];
+#pragma unroll
+  for (int i = 0; i < AV; ++i) sq[i] = 0.f;
   auto gload = [&](int st, int k0) {
 #pragma unroll
-    for (int i = 0; i < AV; ++i)
+    for (int i = 0; i < AV; ++i) {
       ra[st][i] = arow[i] ? *(const float4*)(arow[i] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (NORM) rg[st][i] = *(const uint2*)(gain + k0 + ac[i]);
+    }
 #pragma unroll
     for (int i = 0; i < BV; ++i) rb[st][i] = brow[i] ? *(const uint4*)(brow[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
   };
   auto sstore = [&](int st, int buf) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
+      if constexpr (NORM) {
+        float4& a = ra[st][i];
+        if (sum_sq) {
+          sq[i] = fmaf(a.x, a.x, sq[i]);
+          sq[i] = fmaf(a.y, a.y, sq[i]);
+          sq[i] = fmaf(a.z, a.z, sq[i]);
+          sq[i] = fmaf(a.w, a.w, sq[i]);
+        }
+        const uint2 g = rg[st][i];
+        a.x *= __uint_as_float(g.x << 16);
+        a.y *= __uint_as_float(g.x & 0xffff0000u);
+        a.z *= __uint_as_float(g.y << 16);
+        a.w *= __uint_as_float(g.y & 0xffff0000u);
+      }
       uint32_t h0, l0, h1, l1;
       split_h2(ra[st][i].x, ra[st][i].y, h0, l0);
       split_h2(ra[st][i].z, ra[st][i].w, h1, l1);
@@ -163,6 +189,21 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
     }
   }
 
+  if (sum_sq) {
+    // the 8 threads of a row (consecutive lanes) hold its squares over 4 columns of each
+    // K step; slice blockIdx.y's sum of row m goes to ws[S*M*N + blockIdx.y*M + m]
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      float v = sq[i];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      const int row = m0 + ar[i];
+      if ((tid & 7) == 0 && row < p.M)
+        p.ws[(size_t)gridDim.y * p.M * p.N + (size_t)blockIdx.y * p.M + row] = v;
+    }
+  }
+
   // C fragment: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile.
   // SwiGLU: columns 2n (gate) and 2n+1 (up) sit in neighbouring lanes; the even lane
   // writes a[row][n] = silu(gate) * up.
@@ -196,6 +237,14 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmParams p, i
   if (e >= (size_t)p.M * NO) return;
   const int m = (int)(e / NO), n = (int)(e % NO);
   const size_t plane = (size_t)p.M * p.N;
+  float inv = 1.f;                                 // fused RMSNorm: 1 / rms of row m
+  if (p.gain) {
+    const float* q = p.ws + (size_t)S * plane + m;
+    float t = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) t += q[(size_t)s * p.M];
+    inv = 1.0f / sqrtf(t / (float)p.K + p.eps);
+  }
   if (p.swiglu) {
     const float* w = p.ws + (size_t)m * p.N + 2 * n;
     float g = 0.f, u = 0.f;
@@ -204,12 +253,17 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmParams p, i
       g += w[s * plane];
       u += w[s * plane + 1];
     }
+    if (p.gain) {
+      g *= inv;
+      u *= inv;
+    }
     p.C[(size_t)m * p.ldc + n] = silu(g) * u;
   } else {
     const float* w = p.ws + (size_t)m * p.N + n;
     float v = 0.f;
 #pragma unroll 8
     for (int s = 0; s < S; ++s) v += w[s * plane];
+    if (p.gain) v *= inv;
     if (p.res) v = p.res[(size_t)m * p.ldr + n] + v;
     p.C[(size_t)m * p.ldc + n] = v;
   }
@@ -264,35 +318,56 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     }
 }
 
+// Row tile height of a bf16 launch: 32 / 64 rows for at most 32 / 64 rows, else 128.
+static int gemm_tile_rows(const GemmParams& p) { return p.M <= 32 ? 32 : p.M <= 64 ? 64 : 128; }
+
+int gemm_splits(const GemmParams& p) {
+  if (p.wdtype != W_BF16 || !p.ws || p.M < 1 || p.N < 1 || p.K < 1) return 1;
+  // the fewest slices that give one round of workgroups (two rounds, two per CU, for
+  // skinny tiles, which stream weights with little work per byte: more of them in flight);
+  // each slice at least kStages steps long, partials (and the fused norm's row sums)
+  // within the workspace
+  const int tmr = gemm_tile_rows(p);
+  const int big = ((p.M + tmr - 1) / tmr) * ((p.N + 127) / 128);
+  const int want = tmr < 128 ? 512 : 256;
+  int S = 1;
+  if (big < 256) {
+    for (int c = 2; c <= 64; c *= 2) {
+      const size_t ws = (size_t)c * p.M * p.N + (p.gain ? (size_t)c * p.M : 0);
+      if (p.K % (c * BK) != 0 || p.K / c < kStages * BK || ws > p.ws_floats) break;
+      if ((long long)big * c >= 256) S = c;            // a valid split that fills one round
+      if ((long long)big * c >= want) break;
+    }
+  }
+  return S;
+}
+
+// The fused RMSNorm: split launches of the 32-row tiles (the larger tiles' registers do
+// not leave room for the gain without halving their occupancy).
+bool gemm_norm_fusable(const GemmParams& p) {
+  return p.wdtype == W_BF16 && p.M <= 32 && p.lda % 4 == 0 && p.K % BK == 0 && gemm_splits(p) > 1;
+}
+
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.M < 1 || p.N < 1 || p.K < 1) return hipErrorInvalidValue;
   if (p.wdtype == W_BF16) {
     if (p.K % BK != 0 || p.lda % 4 != 0 || (p.swiglu && (p.N % 2 != 0 || p.res))) return hipErrorInvalidValue;
-    // 128x128 tiles (32x128 / 64x128 for at most 32 / 64 rows) when they give the device at least one
-    // round of work; else the same tiles with K split over the fewest slices that reach a
-    // round (each slice at least kStages steps long, partials within the workspace); else
-    // 64x64
-    const int tmr = p.M <= 32 ? 32 : p.M <= 64 ? 64 : 128;
+    // 128x128 tiles (32x128 / 64x128 for at most 32 / 64 rows) when they give the device at
+    // least one round of work; else the same tiles with K split (gemm_splits); else 64x64
+    const int tmr = gemm_tile_rows(p);
     const int big = ((p.M + tmr - 1) / tmr) * ((p.N + 127) / 128);
-    // the fewest slices that give one round of workgroups (two rounds, two per CU, for
-    // skinny tiles, which stream weights with little work per byte: more of them in flight)
-    const int want = tmr < 128 ? 512 : 256;
-    int S = 1;
-    if (big < 256 && p.ws) {
-      for (int c = 2; c <= 64; c *= 2) {
-        if (p.K % (c * BK) != 0 || p.K / c < kStages * BK || (size_t)c * p.M * p.N > p.ws_floats) break;
-        if ((long long)big * c >= 256) S = c;          // a valid split that fills one round
-        if ((long long)big * c >= want) break;
-      }
-    }
+    const int S = gemm_splits(p);
+    if (p.gain && (S < 2 || tmr != 32)) return hipErrorInvalidValue;   // see gemm_norm_fusable
     if (big >= 256 || S > 1) {
       const int tm = (p.M + tmr - 1) / tmr, tiles = big, per = (tiles + kXcds - 1) / kXcds;
+      const dim3 grid(per * kXcds, S);
       if (tmr == 32)
-        launch_timed(gemm_f16x2_kernel<32, 128>, dim3(per * kXcds, S), dim3(256), 0, s, p, tm, tiles, per, p.K / S);
+        launch_timed(p.gain ? gemm_f16x2_kernel<32, 128, true> : gemm_f16x2_kernel<32, 128>, grid, dim3(256), 0, s, p,
+                     tm, tiles, per, p.K / S);
       else if (tmr == 64)
-        launch_timed(gemm_f16x2_kernel<64, 128>, dim3(per * kXcds, S), dim3(256), 0, s, p, tm, tiles, per, p.K / S);
+        launch_timed(gemm_f16x2_kernel<64, 128>, grid, dim3(256), 0, s, p, tm, tiles, per, p.K / S);
       else
-        launch_timed(gemm_f16x2_kernel<128, 128>, dim3(per * kXcds, S), dim3(256), 0, s, p, tm, tiles, per, p.K / S);
+        launch_timed(gemm_f16x2_kernel<128, 128>, grid, dim3(256), 0, s, p, tm, tiles, per, p.K / S);
       if (S > 1) {
         const size_t n_out = (size_t)p.M * (p.swiglu ? p.N / 2 : p.N);
         launch_timed(gemm_splitk_reduce_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, p, S);
@@ -301,7 +376,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
       const int tm = (p.M + 63) / 64, tiles = tm * ((p.N + 63) / 64), per = (tiles + kXcds - 1) / kXcds;
       launch_timed(gemm_f16x2_kernel<64, 64>, dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per, p.K);
     }
-  } else if (p.swiglu) {
+  } else if (p.swiglu || p.gain) {
     return hipErrorInvalidValue;
   } else {
     dim3 grid((p.N + FT - 1) / FT, (p.M + FT - 1) / FT);

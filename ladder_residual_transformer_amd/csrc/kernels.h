@@ -219,9 +219,18 @@ struct GemmParams {
   // split-K partials (nullable: no split); kGemmSplitWsFloats floats cover any split the
   // launcher chooses
   float* ws; size_t ws_floats;
+  // gain (nullable, bf16 [K]): RMSNorm fused into a split-K launch, A being the raw rows:
+  // the workgroups multiply A by the gain on its way into LDS, those of the first column
+  // tile also store each slice's per-row sum of squares after the partials in ws, and the
+  // reduction scales each row's sums by 1 / sqrt(mean square + eps).  Only valid where
+  // gemm_norm_fusable() holds for p with the gain set (the launch is refused otherwise).
+  const void* gain; float eps;
 };
 constexpr size_t kGemmSplitWsFloats = (size_t)512 * 128 * 128;
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+// K slices launch_gemm uses for p (1: no split).
+int gemm_splits(const GemmParams& p);
+bool gemm_norm_fusable(const GemmParams& p);
 
 // ------------------------------------------------------------ launch timing
 // Arm: the decode-path kernels launched until disarm record `start` (first dispatch

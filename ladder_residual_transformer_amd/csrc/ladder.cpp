@@ -606,16 +606,34 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
   const void* proj_in;
   int proj_k;
   const void* proj_w;
-  if (m % 2 == 0) {
-    HIPCHK(launch_rmsnorm(ctx->wdt, xin, g.hidden, L.attn_norm, g.norm_eps, M, g.hidden, sc.u, s));
-    const int nqkv = ctx->qrows + 2 * ctx->kvrows;
-    gp.A = sc.u;
+  // the module's RMSNorm: folded into the projection when it is a split-K launch of a
+  // decode step on the matrix cores (A = the raw rows, the reduction divides by the rms),
+  // else its own kernel into sc.u
+  auto norm_input = [&](const void* gain) -> ladder_status {
     gp.lda = g.hidden;
+    if (ctx->gemm_step && ctx->wdt == W_BF16) {
+      GemmParams t = gp;
+      t.A = xin;
+      t.gain = gain;
+      t.eps = g.norm_eps;
+      if (gemm_norm_fusable(t)) {
+        gp = t;
+        return LADDER_OK;
+      }
+    }
+    HIPCHK(launch_rmsnorm(ctx->wdt, xin, g.hidden, gain, g.norm_eps, M, g.hidden, sc.u, s));
+    gp.A = sc.u;
+    return LADDER_OK;
+  };
+  ladder_status nst;
+  if (m % 2 == 0) {
+    const int nqkv = ctx->qrows + 2 * ctx->kvrows;
     gp.rows = RowSrc{{L.wq, L.wk, L.wv}, ctx->qrows, ctx->qrows + ctx->kvrows, 0};
     gp.N = nqkv;
     gp.K = g.hidden;
     gp.C = sc.qkv;
     gp.ldc = nqkv;
+    if ((nst = norm_input(L.attn_norm))) return nst;
     HIPCHK(launch_gemm(gp, s));
     HIPCHK(launch_rope_kv(ctx->wdt, sc.qkv, B, T, start_pos, ctx->gemm_step ? ctx->pos_dev : nullptr, g.n_q_heads, g.n_kv_heads, g.head_dim, ctx->rope_cos,
                           ctx->rope_sin, sc.qr, layer_k(ctx, l), layer_v(ctx, l), g.max_seq, s));
@@ -647,12 +665,11 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
     proj_k = ctx->qrows;
     proj_w = L.wo;
   } else {
-    HIPCHK(launch_rmsnorm(ctx->wdt, xin, g.hidden, L.mlp_norm, g.norm_eps, M, g.hidden, sc.u, s));
-    gp.A = sc.u;
-    gp.lda = g.hidden;
     gp.rows = RowSrc{{L.w_gate, L.w_up, nullptr}, 0, 0, 1};
     gp.N = 2 * g.ffn;
     gp.K = g.hidden;
+    if (ctx->wdt == W_BF16) gp.swiglu = 1;
+    if ((nst = norm_input(L.mlp_norm))) return nst;
     if (ctx->wdt == W_BF16) {               // SwiGLU in the GEMM epilogue
       gp.swiglu = 1;
       gp.C = sc.ab;
