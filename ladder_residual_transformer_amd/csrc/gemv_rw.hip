@@ -105,7 +105,14 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
     wt.epoch = epoch;
     wt.err = mp.err;
     uint4* wpre = mp.wpre_off ? reinterpret_cast<uint4*>(lds_raw + mp.wpre_off) : nullptr;
-    rw_pass<WT, BT, VPL, RW_OUT_ADD2_LDS, kCohPair>(mp.prob[1], pr0, pr1, blk, u, dres, wt, sh, part, nullptr, wpre);
+    // a second problem of at most 128 vectors per row (the O projection, K 1024) fills
+    // every lane with half-length units: the same per-lane sums as the longer units,
+    // whose upper halves would only read the zero pad
+    if (VPL == 4 && !wpre && mp.prob[1].K <= 128 * Vec<WT>::N)
+      rw_pass<WT, BT, 2, RW_OUT_ADD2_LDS, kCohPair>(mp.prob[1], pr0, pr1, blk, u, dres, wt, sh, part);
+    else
+      rw_pass<WT, BT, VPL, RW_OUT_ADD2_LDS, kCohPair>(mp.prob[1], pr0, pr1, blk, u, dres, wt, sh, part, nullptr,
+                                                      wpre);
   } else {
     const int pi = (NP > 1 && blk >= mp.blk_begin[1]) ? 1 : 0;
     const int lb = blk - mp.blk_begin[pi];
@@ -114,8 +121,11 @@ __global__ __launch_bounds__(256) void gemv_rw_kernel(MultiGemvParams mp) {
     const int P = (p.N + 1) / 2;
     const int pr0 = (int)((long long)lb * P / nb);
     const int pr1 = (int)((long long)(lb + 1) * P / nb);
-    rw_pass<WT, BT, VPL, RW_OUT_EPI>(p, pr0, pr1, lb, u, nullptr, RwWait{}, sh,
-                                     reinterpret_cast<float*>(lds_raw + mp.part_off));
+    float* part = reinterpret_cast<float*>(lds_raw + mp.part_off);
+    if (VPL == 4 && p.K <= 128 * Vec<WT>::N)      // half-length units, as in the paired launch
+      rw_pass<WT, BT, 2, RW_OUT_EPI>(p, pr0, pr1, lb, u, nullptr, RwWait{}, sh, part);
+    else
+      rw_pass<WT, BT, VPL, RW_OUT_EPI>(p, pr0, pr1, lb, u, nullptr, RwWait{}, sh, part);
   }
 }
 
