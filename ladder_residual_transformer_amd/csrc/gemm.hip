@@ -325,14 +325,15 @@ int gemm_splits(const GemmParams& p) {
   if (p.wdtype != W_BF16 || !p.ws || p.M < 1 || p.N < 1 || p.K < 1) return 1;
   // the fewest slices that give one round of workgroups (two rounds, two per CU, for
   // skinny tiles, which stream weights with little work per byte: more of them in flight);
-  // each slice at least kStages steps long, partials (and the fused norm's row sums)
-  // within the workspace
+  // at most 32 slices (64 made the 10-tile QKV projection of a 70B shard's decode step
+  // slower: slices of 4 K steps and 64 partials per output); each slice at least kStages
+  // steps long, partials (and the fused norm's row sums) within the workspace
   const int tmr = gemm_tile_rows(p);
   const int big = ((p.M + tmr - 1) / tmr) * ((p.N + 127) / 128);
   const int want = tmr < 128 ? 512 : 256;
   int S = 1;
   if (big < 256) {
-    for (int c = 2; c <= 64; c *= 2) {
+    for (int c = 2; c <= 32; c *= 2) {
       const size_t ws = (size_t)c * p.M * p.N + (p.gain ? (size_t)c * p.M : 0);
       if (p.K % (c * BK) != 0 || p.K / c < kStages * BK || ws > p.ws_floats) break;
       if ((long long)big * c >= 256) S = c;            // a valid split that fills one round

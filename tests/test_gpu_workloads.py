@@ -90,7 +90,7 @@ def test_70b_tp8_shard_widths_batches(B):
     input rows exceed the two-workgroups-per-CU budget, so the row-wave launches run one
     workgroup per CU (and at batch 4 the fused launch carries 64 attention workgroups).
     Batch 6, 8 and 16: the decode steps run on the matrix cores, whose 32-row GEMMs split
-    K over up to 64 slices at these widths (the QKV projection: 10 tiles, 64 slices) with
+    K over up to 32 slices at these widths (the QKV projection: 10 tiles, 32 slices) with
     the RMSNorm folded in (batch 6: 26 of the 32 tile rows are padding)."""
     base = synth.CONFIGS["70b_tp8_shard"]
     cfg = synth.scaled_config(base, 4)
