@@ -922,14 +922,17 @@ ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
   return LADDER_OK;
 }
 
-// Decode steps that the row-wave projections cannot take (bf16 weights, batch beyond
-// their LDS budget, batch > 4): one token per sequence through the prefill modules, whose
+// Decode steps that the row-wave projections cannot take (bf16 weights, batch > 4, or the
+// staged input rows of any projection, the widest of hidden, ffn and the attention rows,
+// beyond their LDS budget): one token per sequence through the prefill modules, whose
 // projections run on the matrix cores (the K-sliced GEMV kernels leave most of the HBM
-// bandwidth unused at those batches), with the split-KV decode attention, then the final
-// RMSNorm, the LM head as a GEMM and a row argmax.  Every kernel of the route takes the
-// position from the device (the prologue's pos_dev), so it is replayed as a graph too.
+// bandwidth unused at those batches: the 8B model's down projection, K 14336, at batch 3
+// and 4 took them and halved the step rate), with the split-KV decode attention, then the
+// final RMSNorm, the LM head as a GEMM and a row argmax.  Every kernel of the route takes
+// the position from the device (the prologue's pos_dev), so it is replayed as a graph too.
 bool gemm_decode(const ladder_ctx* ctx, int B) {
-  return ctx->wdt == W_BF16 && !gemv_rw_supported(ctx->wdt, ctx->cfg.hidden, B);
+  const int kmax = std::max(ctx->cfg.hidden, std::max(ctx->cfg.ffn, ctx->qrows));
+  return ctx->wdt == W_BF16 && !gemv_rw_supported(ctx->wdt, kmax, B);
 }
 
 ladder_status enqueue_decode_gemm(ladder_ctx* ctx, int B) {
