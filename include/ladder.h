@@ -82,8 +82,9 @@ typedef int32_t ladder_status;
                                     (default) */
 #define LADDER_SCHED_PERSISTENT 4 /* decode: the whole layer stack in one launch of resident
                                     workgroups that signal each other (every layer ladder,
-                                    bf16, batch <= 4; otherwise as FUSED); prefill as FUSED */
-#define LADDER_SCHED_FUSED_LATE_ATTN 5 /* as FUSED, but with bf16 and batch <= 4 the attention
+                                    bf16, a batch the row-wave GEMV takes, see
+                                    ladder_decode_step; otherwise as FUSED); prefill as FUSED */
+#define LADDER_SCHED_FUSED_LATE_ATTN 5 /* as FUSED, but with bf16 and a row-wave batch the attention
                                     shares the down projection's launch and the O rows wait
                                     for it there: [QKV | gate/up], [attention | down, then O +
                                     both adds]; prefill as FUSED */
@@ -208,7 +209,7 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 #define LADDER_KERNEL_LMHEAD 5   /* final RMSNorm + LM head GEMV + greedy argmax */
 #define LADDER_KERNEL_QKV_GATEUP 6  /* fused ladder launch: QKV (+RoPE/KV) | gate/up (+SwiGLU) */
 #define LADDER_KERNEL_ATTN_DOWN 7   /* fused ladder launch: decode attention | down projection; with
-                                       bf16 weights and batch <= 4 followed, in the same launch, by
+                                       bf16 weights and a row-wave batch followed, in the same launch, by
                                        the O projection + both residual adds */
 #define LADDER_KERNEL_OPROJ_ADD2 8  /* fused ladder launch: O projection + both residual adds (three-
                                        launch layers only) */
