@@ -930,9 +930,13 @@ ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
 // and 4 took them and halved the step rate), with the split-KV decode attention, then the
 // final RMSNorm, the LM head as a GEMM and a row argmax.  Every kernel of the route takes
 // the position from the device (the prologue's pos_dev), so it is replayed as a graph too.
+// Batch 4 also takes it where the row-wave launches would hold one workgroup per CU (the
+// 70B shard: 455.5 against 427.8 tok/s; at batch 3 the two routes measured equal there,
+// and the row-wave launches 11% faster on the 1B model).
 bool gemm_decode(const ladder_ctx* ctx, int B) {
   const int kmax = std::max(ctx->cfg.hidden, std::max(ctx->cfg.ffn, ctx->qrows));
-  return ctx->wdt == W_BF16 && !gemv_rw_supported(ctx->wdt, kmax, B);
+  if (ctx->wdt != W_BF16) return false;
+  return !gemv_rw_supported(ctx->wdt, kmax, B) || (B >= 4 && !gemv_rw_two_per_cu(ctx->wdt, kmax, B));
 }
 
 ladder_status enqueue_decode_gemm(ladder_ctx* ctx, int B) {

@@ -84,12 +84,12 @@ def test_8b_hybrid_widths(B, T, n_dec):
     _free(model)
 
 
-@pytest.mark.parametrize("B", [2, 4, 6, 8, 16])
+@pytest.mark.parametrize("B", [2, 3, 4, 6, 8, 16])
 def test_70b_tp8_shard_widths_batches(B):
-    """70B TP=8 shard widths (hidden 8192), four ladder layers.  Batch 2 and 4: the staged
-    input rows exceed the two-workgroups-per-CU budget, so the row-wave launches run one
-    workgroup per CU (and at batch 4 the fused launch carries 64 attention workgroups).
-    Batch 6, 8 and 16: the decode steps run on the matrix cores, whose 32-row GEMMs split
+    """70B TP=8 shard widths (hidden 8192), four ladder layers.  Batch 2: the staged input
+    rows (65.6 KB) just keep two row-wave workgroups per CU.  Batch 3: one workgroup per CU,
+    and the attention (48 workgroups) runs in the down projection's launch.
+    Batch 4, 6, 8 and 16: the decode steps run on the matrix cores, whose 32-row GEMMs split
     K over up to 32 slices at these widths (the QKV projection: 10 tiles, 32 slices) with
     the RMSNorm folded in (batch 6: 26 of the 32 tile rows are padding)."""
     base = synth.CONFIGS["70b_tp8_shard"]
