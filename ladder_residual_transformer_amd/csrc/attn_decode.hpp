@@ -193,10 +193,55 @@ __device__ void attn_finish(const AttnDecodeParams& p, int b, int kvh, int G, in
 // wprog (COH only, nullable): q and the newest K/V row are written by other workgroups of
 // the same launch, which publish wcode in wprog[0..wn) when done; the first tile's older
 // rows are loaded before the wait (they come from earlier steps), the rest after it.
-template <int HD, bool COH = false>
+// Poll of the tagged QKV outputs of one kv group (batch 1): entry e of the group (its G
+// query heads' rows, then its K row, then its V row) is the 64-bit word (tag << 32 |
+// value bits) at tagged[row]; once every entry of the group carries `code`, the values are
+// in stage[(G + 2) * HD].  Bounded: a poll that gives up sets *err.
+template <int HD>
+__device__ __forceinline__ void tagged_poll(const unsigned long long* tagged, int qrows, int kvrows, int kvh, int G,
+                                            uint32_t code, float* stage, int* err) {
+  const int n = (G + 2) * HD;
+  constexpr int PER = 18 * HD / 256 + 1;       // entries per thread for G <= 16
+  int pending = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    if ((int)threadIdx.x + 256 * k < n) pending |= 1 << k;
+  for (unsigned rounds = 0;; ++rounds) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if (pending & (1 << k)) {
+        const int e = (int)threadIdx.x + 256 * k;
+        const int row = e < G * HD ? kvh * G * HD + e
+                        : e < (G + 1) * HD ? qrows + kvh * HD + (e - G * HD)
+                                           : qrows + kvrows + kvh * HD + (e - (G + 1) * HD);
+        const unsigned long long w =
+            __hip_atomic_load(gbl(tagged) + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(w >> 32) == code) {
+          stage[e] = __uint_as_float((uint32_t)w);
+          pending &= ~(1 << k);
+        }
+      }
+    }
+    if (__syncthreads_and(pending == 0)) return;
+    if (rounds == (1u << 16)) {
+      if (threadIdx.x == 0) __hip_atomic_fetch_or(gbl(err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// MERGE false: the workgroup only writes its chunk's records (no ticket, no merge); a
+// later launch merges them with attn_merge.  TAGGED (batch 1, COH): q and the newest K/V
+// row come from the tagged QKV outputs of this launch (tagged_poll with code wcode, staged
+// in tstage) instead of a progress-word wait and loads.
+template <int HD, bool COH = false, bool MERGE = true, bool TAGGED = false>
 __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnLds<uint16_t, HD>& L,
                                        const uint32_t* wprog = nullptr, int wn = 0, uint32_t wcode = 0,
-                                       int* werr = nullptr) {
+                                       int* werr = nullptr, const unsigned long long* tagged = nullptr,
+                                       float* tstage = nullptr) {
+  static_assert(!TAGGED || COH, "the tagged hand-over reads rows written in the same launch");
   constexpr int T = kAttnKeyTile;
   constexpr int CPR = HD / 8;                  // 16-byte chunks per K/V row
   constexpr int KCH = T * CPR / 256;           // K chunks per thread per tile
@@ -217,7 +262,7 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
   if (s >= n_act) return;                                  // whole workgroup: nothing to do
   const int start = s * chunk;
   const int end = min(len, start + chunk);
-  const bool pre = COH && wprog != nullptr;
+  const bool pre = COH && (wprog != nullptr || TAGGED);
   bool defer = pre;                            // the newest row is not loaded before the wait
   const size_t kv_base = ((size_t)b * p.nkv + kvh) * p.max_seq * HD;
   const uint16_t* kc = (const uint16_t*)p.k_cache + kv_base;
@@ -227,10 +272,18 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
   // newest row (position len-1) was written in this kernel and is read coherently (q is
   // read with ordinary loads: its producer gives it an address of its own per layer).
   uint4 kr[KCH], vr[VPAIR][2];
+  // TAGGED: the newest row's 8 values at dimension c from the staged K (which 0) or V (1)
+  // row, rounded to bf16 as the cache holds them
+  auto tagged_row = [&](int which, int c) -> uint4 {
+    const float* v = tstage + (G + which) * HD + c;
+    auto pk = [&](int e) { return (uint32_t)f32_to_bf16(v[e]) | ((uint32_t)f32_to_bf16(v[e + 1]) << 16); };
+    return make_uint4(pk(0), pk(2), pk(4), pk(6));
+  };
   auto ld_row = [&](const uint16_t* base, int r, int c) -> uint4 {
     const uint16_t* a = base + (size_t)r * HD + c;
     if (COH && r == len - 1) {
       if (defer) return make_uint4(0u, 0u, 0u, 0u);      // not written yet: loaded after the wait
+      if constexpr (TAGGED) return tagged_row(base == kc ? 0 : 1, c);
       const uint32_t* w = (const uint32_t*)a;
       return make_uint4(ld_coh(w), ld_coh(w + 1), ld_coh(w + 2), ld_coh(w + 3));
     }
@@ -251,7 +304,21 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
     }
   };
   load_tile(start);
-  if (pre) {
+  if (TAGGED) {
+    tagged_poll<HD>(tagged, p.nq * HD, p.nkv * HD, kvh, G, wcode, tstage, werr);
+    defer = false;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int e = tid + 256 * i, r = min(start + e / CPR, end - 1), c = (e % CPR) * 8;
+      if (r == len - 1) kr[i] = tagged_row(0, c);
+    }
+#pragma unroll
+    for (int i = 0; i < VPAIR; ++i) {
+      const int e = tid + 256 * i, j = e / CPR, c = (e % CPR) * 8;
+      if (min(start + 2 * j, end - 1) == len - 1) vr[i][0] = tagged_row(1, c);
+      if (min(start + 2 * j + 1, end - 1) == len - 1) vr[i][1] = tagged_row(1, c);
+    }
+  } else if (pre) {
     prog_wait(wprog, wn, wcode, werr);
     defer = false;                             // later tiles load the newest row themselves
     // the newest row of the first tile (if it holds it), coherently
@@ -278,10 +345,11 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
   {
     const float* qrow = p.q + (size_t)b * p.nq * HD + (size_t)(kvh * G + min(col, G - 1)) * HD;
     const float qz = col < G ? 1.f : 0.f;
+    const float* qst = tstage + (size_t)min(col, G - 1) * HD;
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      const float4 x = ldg4(qrow + 32 * st + 8 * grp);
-      const float4 y = ldg4(qrow + 32 * st + 8 * grp + 4);
+      const float4 x = TAGGED ? *(const float4*)(qst + 32 * st + 8 * grp) : ldg4(qrow + 32 * st + 8 * grp);
+      const float4 y = TAGGED ? *(const float4*)(qst + 32 * st + 8 * grp + 4) : ldg4(qrow + 32 * st + 8 * grp + 4);
       uint4 hi, lo;
       split_h2(x.x * qz, x.y * qz, hi.x, lo.x);
       split_h2(x.z * qz, x.w * qz, hi.y, lo.y);
@@ -389,7 +457,15 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
       else { gbl(dst)[0] = mr; gbl(dst)[1] = l_run; }
     }
   }
-  attn_finish<HD, COH>(p, b, kvh, G, n_act, L);
+  if constexpr (MERGE) attn_finish<HD, COH>(p, b, kvh, G, n_act, L);
+}
+
+// Chunks holding keys of a decode attention at the current position (the workgroups of
+// chunks past them leave at once).
+__device__ __forceinline__ int attn_active_chunks(const AttnDecodeParams& p) {
+  const int len = *gbl(p.d_pos) + 1;
+  const int chunk = attn_chunk(len, p.n_split);
+  return (len + chunk - 1) / chunk;
 }
 
 // ----------------------------------------------------------------- fp32 (VALU)

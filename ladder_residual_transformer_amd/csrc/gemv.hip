@@ -89,10 +89,7 @@ __device__ void gemv_epilogue(const GemvParams& p, int row0, const float* fin, c
           const int d = (n < p.q_rows ? n : n - p.q_rows) % p.head_dim;
           const float c = p.rope_cos[(size_t)pos * half + (d >> 1)];
           const float s = p.rope_sin[(size_t)pos * half + (d >> 1)];
-          const float r0 = y0 * c - y1 * s;
-          const float r1 = y0 * s + y1 * c;
-          y0 = r0;
-          y1 = r1;
+          rope_rot(y0, y1, c, s);
         }
         if (n < p.q_rows) {
           p.out[(size_t)b * p.ldo + n] = y0;

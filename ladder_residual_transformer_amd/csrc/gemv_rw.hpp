@@ -80,10 +80,7 @@ __device__ __forceinline__ void rw_epilogue(const GemvParams& p, int pair, int b
         const int half = p.head_dim >> 1;
         const float c = gbl(p.rope_cos)[(size_t)pos * half + (d >> 1)];
         const float s = gbl(p.rope_sin)[(size_t)pos * half + (d >> 1)];
-        const float r0 = y0 * c - y1 * s;
-        const float r1 = y0 * s + y1 * c;
-        y0 = r0;
-        y1 = r1;
+        rope_rot(y0, y1, c, s);
       }
       if (n0 < p.q_rows) {
         p.out[(size_t)b * p.ldo + n0] = y0;
@@ -122,10 +119,7 @@ __device__ __forceinline__ void rw_epilogue_coh(const GemvParams& p, int pair, i
         const int half = p.head_dim >> 1;
         const float c = gbl(p.rope_cos)[(size_t)pos * half + (d >> 1)];
         const float s = gbl(p.rope_sin)[(size_t)pos * half + (d >> 1)];
-        const float r0 = y0 * c - y1 * s;
-        const float r1 = y0 * s + y1 * c;
-        y0 = r0;
-        y1 = r1;
+        rope_rot(y0, y1, c, s);
       }
       if (n0 < p.q_rows) {
         st_coh(p.out + (size_t)b * p.ldo + n0, y0);
@@ -218,17 +212,24 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
   const int total_units = n_pairs * nchunk;
   const int n_units = total_units > wid ? (total_units - wid + 3) / 4 : 0;
   uint4 wa[2][VPL], wb[2][VPL];
+  // Every load is issued unconditionally: a unit index past the wave's last unit loads
+  // one vector of a valid row for all lanes (a dummy, never used), so that no branch
+  // separates a load from its use and the compiler keeps both buffers in flight (with a
+  // conditional load it waits for every outstanding load before issuing the next unit).
+  const int pclamp = min(pr0, (p.N + 1) / 2 - 1);
   auto load_unit = [&](uint4 (&w)[2][VPL], int i) {
-    const int un = wid + 4 * i;
-    const int pair = pr0 + un / nchunk, c = un % nchunk;
+    const bool real = i < n_units;
+    const int un = real ? wid + 4 * i : 0;
+    const int pair = real ? pr0 + un / nchunk : pclamp, c = un % nchunk;
     const int n0 = 2 * pair;
     const WT* r0 = rw_row_ptr<WT>(p.rows, n0, K);
     const WT* r1 = rw_row_ptr<WT>(p.rows, min(n0 + 1, p.N - 1), K);
+    const int li = real ? lane : 0, vs = real ? 64 : 0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      const int vi = min(c * CHUNK + lane + 64 * v, nvec - 1);
-      w[0][v] = ldg4u(r0 + (size_t)vi * VEC);
-      w[1][v] = ldg4u(r1 + (size_t)vi * VEC);
+      const int vi = min(c * CHUNK + li + vs * v, nvec - 1);
+      w[0][v] = ldg4u_nt(r0 + (size_t)vi * VEC);
+      w[1][v] = ldg4u_nt(r1 + (size_t)vi * VEC);
     }
   };
   const int ustride = K + VEC;                     // u rows carry a zero pad of VEC floats
@@ -248,14 +249,17 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
         const int vi = min(c * CHUNK + lane + 64 * v, nvec - 1);
         uint4* slot = wpre + ((size_t)(un * spu + v) * 2) * 64;
         __builtin_amdgcn_global_load_lds((const void*)(r0 + (size_t)vi * VEC),
-                                         (__attribute__((address_space(3))) void*)slot, 16, 0, 0);
+                                         (__attribute__((address_space(3))) void*)slot, 16, 0, 2);
         __builtin_amdgcn_global_load_lds((const void*)(r1 + (size_t)vi * VEC),
-                                         (__attribute__((address_space(3))) void*)(slot + 64), 16, 0, 0);
+                                         (__attribute__((address_space(3))) void*)(slot + 64), 16, 0, 2);
       }
     }
   }
   if (waits) {
-    if (n_units > 0 && !wpre) load_unit(wa, 0);
+    if (!wpre) {
+      load_unit(wa, 0);
+      load_unit(wb, 1);
+    }
     if (wt.prog) prog_wait(wt.prog, wt.nprog, wt.code, wt.err);
     else if constexpr (COH) wg_wait_coh(wt.flag, wt.epoch, wt.err);
     else wg_wait(wt.flag, wt.epoch, wt.err);
@@ -276,7 +280,10 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
         xr[i][e] = ldg4(p.x + (size_t)v * VEC + 4 * e);
       gr[i] = norm ? ldg4u((const WT*)p.gain + (size_t)v * VEC) : make_uint4(0u, 0u, 0u, 0u);
     }
-    if (!waits && n_units > 0) load_unit(wa, 0);
+    if (!waits) {
+      load_unit(wa, 0);
+      load_unit(wb, 1);
+    }
     float sq = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -303,7 +310,10 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
     sq = wave_sum(sq);
     if (lane == 0) sh.sqw[wid][0] = sq;
   } else {
-    if (!waits && n_units > 0) load_unit(wa, 0);
+    if (!waits) {
+      load_unit(wa, 0);
+      load_unit(wb, 1);
+    }
     for (int b = 0; b < BT; ++b) {
       float sq = 0.f;
       if (b < B) {
@@ -382,7 +392,7 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
 #pragma unroll
       for (int b = 0; b < BT; ++b) {
         const float y = wave_sum(acc[r][b]);
-        if (lane == 0) part[((size_t)un * 2 + r) * BT + b] = y;
+        if (lane == 0 && i < n_units) part[((size_t)un * 2 + r) * BT + b] = y;
       }
   };
   if (waits && wpre) {
@@ -404,13 +414,13 @@ __device__ __forceinline__ void rw_pass(const GemvParams& p, int pr0, int pr1, i
       compute_unit(w, i);
     }
   } else {
+    // units i and i + 1 are in flight at the top of each iteration; a past-the-end unit
+    // is computed on its dummy load and its sums are dropped
     for (int i = 0; i < n_units; i += 2) {
-      if (i + 1 < n_units) load_unit(wb, i + 1);
       compute_unit(wa, i);
-      if (i + 1 < n_units) {
-        if (i + 2 < n_units) load_unit(wa, i + 2);
-        compute_unit(wb, i + 1);
-      }
+      load_unit(wa, i + 2);
+      compute_unit(wb, i + 1);
+      load_unit(wb, i + 3);
     }
   }
   __syncthreads();

@@ -98,6 +98,9 @@ struct MultiGemvParams {
   int seq;
   uint32_t* prog;
   int seq_tag;            // 1 <= seq_tag < kSeqCodeStride
+  // batch-1 streaming front launch: the QKV outputs as (code << 32 | value bits) words,
+  // one per QKV row, polled by the attention workgroups of the same launch
+  unsigned long long* tagged;
 };
 // Progress code of a sequential launch: epoch * kSeqCodeStride + tag, so that the codes
 // of a decode step exceed those of every earlier step.
@@ -131,6 +134,23 @@ hipError_t launch_gemv_paired_nowait(const GemvParams& first, const GemvParams& 
 bool gemv_rw_seq_supported(int wdtype, int K, int B, int hd);
 hipError_t launch_gemv_seq(const GemvParams& first, const GemvParams& second, const AttnDecodeParams& attn,
                            uint32_t* prog, int tag, int* err, hipStream_t s);
+// Batch-1 streaming launches of one ladder layer (stream.hip), always used as a pair:
+//   front: [QKV then gate/up in every workgroup | attention chunk records once every QKV
+//          output of the kv group is there]; the QKV outputs reach the attention as tagged
+//          words (no progress words);
+//   back:  [attention merge of those records (attn.done_cnt/done_flag signal, epoch
+//          *attn.d_epoch) | down, then (after the signal) O + both residual adds]; same
+//          projections as launch_gemv_paired_nowait.
+// Each workgroup streams its weight units with the next pass's units in flight across
+// the pass boundary; the results equal the row-wave launches' bit for bit.
+bool stream_front_supported(int wdtype, int K, int B, int hd);
+bool stream_back_supported(int wdtype, int Kd, int Ko, int B);
+// tagged: one 64-bit word per QKV row (zero or holding codes of earlier launches of this
+// context); tag as for launch_gemv_seq.
+hipError_t launch_stream_front(const GemvParams& first, const GemvParams& second, const AttnDecodeParams& attn,
+                               unsigned long long* tagged, int tag, int* err, hipStream_t s);
+hipError_t launch_stream_back(const GemvParams& down, const GemvParams& o, const AttnDecodeParams& attn, int* err,
+                              hipStream_t s);
 // next[b] = first maximum of n per-workgroup candidates (best_val/best_idx [n][BT])
 hipError_t launch_argmax_finalize(const float* best_val, const int* best_idx, int n, int BT, int B, int* next,
                                   hipStream_t s);

@@ -118,6 +118,7 @@ struct ladder_ctx {
   int* step_sync = nullptr;          // [L][8] its counters and flags
   uint32_t* step_prog = nullptr;     // [kStepProgWords] its progress words
   uint32_t* seq_prog = nullptr;      // [kSeqProgWords] progress words of the sequential launches
+  unsigned long long* qkv_tagged = nullptr;  // [qkv rows] tagged QKV outputs of the batch-1 streaming launch
   float* step_x = nullptr;           // x_1 .. x_{2L-1}
   float* step_q = nullptr;           // q per layer
   float* step_o = nullptr;           // attention output per layer
@@ -237,6 +238,7 @@ void carve(ladder_ctx* c, Carver& cv) {
   c->step_sync = cv.take<int>((size_t)8 * g.n_layers);
   c->step_prog = cv.take<uint32_t>(kStepProgWords);
   c->seq_prog = cv.take<uint32_t>(kSeqProgWords);
+  c->qkv_tagged = cv.take<unsigned long long>((size_t)qkv);
   // vectors of the persistent decode step, each at an address of its own per step
   if (c->all_ladder && c->wdt == W_BF16) {
     const size_t sb = std::min(B, 4);
@@ -406,6 +408,14 @@ bool seq_layers(const ladder_ctx* ctx, int B) {
          gemv_rw_two_per_cu(ctx->wdt, g.hidden, B) && g.n_layers < (int)kSeqCodeStride;
 }
 
+// Batch 1 with both decode launches of a layer streaming (stream.hip): the front launch
+// leaves the attention as chunk records, the back launch merges them.
+bool stream_layers(const ladder_ctx* ctx, int B) {
+  const ladder_config& g = ctx->cfg;
+  return B == 1 && seq_layers(ctx, B) && stream_front_supported(ctx->wdt, g.hidden, B, g.head_dim) &&
+         stream_back_supported(ctx->wdt, g.ffn, ctx->qrows, B);
+}
+
 // RMSNorm + [Wgate,Wup] (row pairs) + SwiGLU of layer l
 GemvParams gateup_params(const ladder_ctx* ctx, int l, int B, const float* xin, const StreamScratch& sc) {
   const ladder_config& g = ctx->cfg;
@@ -512,6 +522,28 @@ ladder_status decode_module(ladder_ctx* ctx, int m, int B, const float* xin, con
   return LADDER_OK;
 }
 
+// The two launches of a ladder layer under FUSED at row-wave batches: [QKV, then gate/up |
+// attention] and [down, then O + both residual adds]; at batch 1 the streaming pair, whose
+// back launch also merges the attention's chunk records.  Traced as the kernel kinds
+// QKV_ATTN_GATEUP and DOWN_OPROJ.
+ladder_status launch_layer_pair(ladder_ctx* ctx, int l, int B, const GemvParams* pr, const GemvParams& down,
+                                const GemvParams& o, StreamScratch& sc, hipStream_t s) {
+  const bool stream = stream_layers(ctx, B);
+  TRACE(LADDER_KERNEL_QKV_ATTN_GATEUP, s, false);
+  if (stream)
+    HIPCHK(launch_stream_front(pr[0], pr[1], attn_params(ctx, l, B, sc), ctx->qkv_tagged, l + 1, ctx->err_word, s));
+  else
+    HIPCHK(launch_gemv_seq(pr[0], pr[1], attn_params(ctx, l, B, sc), ctx->seq_prog, l + 1, ctx->err_word, s));
+  TRACE(LADDER_KERNEL_QKV_ATTN_GATEUP, s, true);
+  TRACE(LADDER_KERNEL_DOWN_OPROJ, s, false);
+  if (stream)
+    HIPCHK(launch_stream_back(down, o, signalled(ctx, attn_params(ctx, l, B, sc), l), ctx->err_word, s));
+  else
+    HIPCHK(launch_gemv_paired_nowait(down, o, s));
+  TRACE(LADDER_KERNEL_DOWN_OPROJ, s, true);
+  return LADDER_OK;
+}
+
 // One ladder layer l (or parallel block) of a decode step on one stream, in three launches:
 //   [QKV_l | gate/up_l]   the attention reads x_{2l-1} (parallel block: x_{2l}), the MLP
 //                         x_{2l}: both exist;
@@ -531,18 +563,12 @@ ladder_status decode_layer_fused(ladder_ctx* ctx, int l, int B) {
     // attention_l once all of QKV_l is done]: the QKV rows come first, so the attention
     // runs while gate/up streams; then [down_l rows | the same O_l rows with x_{2l+1} =
     // x_{2l} + o and x_{2l+2} = x_{2l+1} + d], which waits for nothing
-    TRACE(LADDER_KERNEL_QKV_ATTN_GATEUP, s, false);
-    HIPCHK(launch_gemv_seq(pr[0], pr[1], attn_params(ctx, l, B, sc), ctx->seq_prog, l + 1, ctx->err_word, s));
-    TRACE(LADDER_KERNEL_QKV_ATTN_GATEUP, s, true);
     const GemvParams down = outproj_params(ctx, mm, B, sc, nullptr, nullptr, ctx->dout[0]);
     GemvParams o = outproj_params(ctx, ma, B, sc, X[ma % 2], X[(ma + 1) % 2], nullptr);
     o.epi = EPI_ADD2;
     o.add2 = nullptr;
     o.out2 = X[(ma + 2) % 2];
-    TRACE(LADDER_KERNEL_DOWN_OPROJ, s, false);
-    HIPCHK(launch_gemv_paired_nowait(down, o, s));
-    TRACE(LADDER_KERNEL_DOWN_OPROJ, s, true);
-    return LADDER_OK;
+    return launch_layer_pair(ctx, l, B, pr, down, o, sc, s);
   }
   if (two_launch_layers(ctx, B)) {
     TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
@@ -1285,16 +1311,24 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
         if (!seq) break;
         for (int l = 0; l < g.n_layers; ++l, ++launches) {
           HIPCHK(launch_epoch_bump(ctx->epoch, s));   // a new epoch per launch, as per decode step
+          const bool stream = stream_layers(ctx, B);
           if (kind == LADDER_KERNEL_QKV_ATTN_GATEUP) {
             GemvParams pr[2] = {qkv_params(ctx, l, B, ctx->dx[1], sc), gateup_params(ctx, l, B, ctx->dx[0], sc)};
-            HIPCHK(launch_gemv_seq(pr[0], pr[1], attn_params(ctx, l, B, sc), ctx->seq_prog, l + 1, ctx->err_word, s));
+            if (stream)
+              HIPCHK(launch_stream_front(pr[0], pr[1], attn_params(ctx, l, B, sc), ctx->qkv_tagged, l + 1,
+                                         ctx->err_word, s));
+            else
+              HIPCHK(launch_gemv_seq(pr[0], pr[1], attn_params(ctx, l, B, sc), ctx->seq_prog, l + 1, ctx->err_word, s));
           } else {
             const GemvParams down = outproj_params(ctx, 2 * l + 1, B, sc, nullptr, nullptr, ctx->dout[0]);
             GemvParams o = outproj_params(ctx, 2 * l, B, sc, ctx->dx[0], ctx->dx[1], nullptr);
             o.epi = EPI_ADD2;
             o.add2 = nullptr;
             o.out2 = ctx->dx[0];
-            HIPCHK(launch_gemv_paired_nowait(down, o, s));
+            if (stream)
+              HIPCHK(launch_stream_back(down, o, signalled(ctx, attn_params(ctx, l, B, sc), l), ctx->err_word, s));
+            else
+              HIPCHK(launch_gemv_paired_nowait(down, o, s));
           }
         }
         continue;
