@@ -36,7 +36,13 @@ def test_1b_full_depth_greedy():
     ref = greedy_generate(LadderOracle(cfg, w, dtype=np.float32, cache_weights=True), prompt, n_dec)
     model = make_model(cfg, w, 1, 256)
     gl, gh, gt = gpu_teacher_forced(model, prompt, ref["tokens"][:, :-1])
-    el, _ = check_against_oracle(cfg, gl, gh, gt, ref, TOL["bf16"], "1b teacher-forced")
+    el, eh = check_against_oracle(cfg, gl, gh, gt, ref, TOL["bf16"], "1b teacher-forced")
+    # the same tokens through the oracle that keeps every cached K/V row unrounded: what
+    # the reading "the cache holds the model's storage type" accounts for (logged only)
+    un = teacher_forced(LadderOracle(cfg, w, dtype=np.float32, cache_weights=True, kv_store_dtype=False), prompt,
+                        ref["tokens"][:, :-1])
+    log(f"1b full depth: rel err vs the bf16-cache oracle logits {el:.3g} hidden {eh:.3g}; vs the unrounded-cache "
+        f"oracle logits {step_rel_err(gl, un.logits[:, 127:]):.3g} hidden {step_rel_err(gh, un.hidden[:, 127:]):.3g}")
     free = gpu_free_running(model, prompt, n_dec)
     abs_err = np.max(np.abs(gl - ref["logits"]))
     for k in range(n_dec + 1):
@@ -48,7 +54,9 @@ def test_1b_full_depth_greedy():
 
 
 def test_1b_batch8_split_k():
-    """Batch 8 takes the K-sliced GEMV with the 8192-wide down projection split over K."""
+    """Batch 8 takes the matrix-core decode route: 32-row GEMM tiles with K split over
+    slices (the 8192-wide down projection too) and the RMSNorm folded into the QKV and
+    gate/up GEMMs."""
     cfg = synth.CONFIGS["1b"]
     cfg4 = synth.scaled_config(cfg, 4)
     w = synth.gen_weights(cfg4, seed=2)
@@ -67,7 +75,8 @@ def test_1b_batch8_split_k():
 @pytest.mark.parametrize("B, T, n_dec", [(1, 64, 8), (16, 16, 3)])
 def test_8b_hybrid_widths(B, T, n_dec):
     """Llama-3.1-8B widths with the hybrid mask across the standard->ladder boundary
-    (layers 0-1 standard, 2-3 ladder); batch 16 uses the K-sliced kernels."""
+    (layers 0-1 standard, 2-3 ladder); batch 1 takes the streaming launches for the
+    ladder layers, batch 16 the matrix-core decode route."""
     base = synth.CONFIGS["8b_hybrid"]
     cfg = synth.ModelConfig("8b_hybrid_4l", 4, base.hidden, base.n_q_heads, base.n_kv_heads, base.head_dim,
                             base.ffn, base.vocab, base.rope_theta, "bf16", (0, 0, 1, 1))
@@ -84,18 +93,21 @@ def test_8b_hybrid_widths(B, T, n_dec):
     _free(model)
 
 
-@pytest.mark.parametrize("B", [2, 3, 4, 6, 8, 16])
-def test_70b_tp8_shard_widths_batches(B):
-    """70B TP=8 shard widths (hidden 8192), four ladder layers.  Batch 2: the staged input
-    rows (65.6 KB) just keep two row-wave workgroups per CU.  Batch 3: one workgroup per CU,
-    and the attention (48 workgroups) runs in the down projection's launch.
-    Batch 4, 6, 8 and 16: the decode steps run on the matrix cores, whose 32-row GEMMs split
-    K over up to 32 slices at these widths (the QKV projection: 10 tiles, 32 slices) with
-    the RMSNorm folded in (batch 6: 26 of the 32 tile rows are padding)."""
+@pytest.mark.parametrize("B, T", [(1, 40), (2, 40), (3, 40), (4, 40), (6, 40), (8, 40), (16, 40), (32, 16),
+                                  (33, 16)])
+def test_70b_tp8_shard_widths_batches(B, T):
+    """70B TP=8 shard widths (hidden 8192), four ladder layers.  Batch 1: the two streaming
+    launches per layer.  Batch 2: the staged input rows (65.6 KB) just keep two row-wave
+    workgroups per CU.  Batch 3: one workgroup per CU, and the attention (48 workgroups)
+    runs in the down projection's launch.  Batch 4, 6, 8, 16 and 32: the decode steps run
+    on the matrix cores, whose 32-row GEMMs split K over up to 32 slices at these widths
+    (the QKV projection: 10 tiles, 32 slices) with the RMSNorm folded in (batch 6: 26 of
+    the 32 tile rows are padding; batch 32: the last batch the fold takes).  Batch 33: the
+    64-row tiles with the RMSNorm kernel ahead of them (31 rows of padding)."""
     base = synth.CONFIGS["70b_tp8_shard"]
     cfg = synth.scaled_config(base, 4)
     w = synth.gen_weights(cfg, seed=8)
-    T, n_dec = 40, 3
+    n_dec = 3
     prompt = synth.gen_ids(B, T, cfg.vocab, seed=9)
     cont = synth.gen_ids(B, n_dec, cfg.vocab, seed=9, stream=1)
     ref = teacher_forced(LadderOracle(cfg, w, dtype=np.float32), prompt, cont)
@@ -130,6 +142,11 @@ def test_70b_tp8_shard_full_depth_bench_configuration():
     el, eh = step_rel_err(gl, rl), step_rel_err(gh, rh)
     log(f"70b shard full depth: rel err logits {el:.3g} hidden {eh:.3g}")
     assert el <= TOL["bf16"] and eh <= TOL["bf16"]
+    # against the oracle that keeps every cached K/V row unrounded (logged only)
+    un = teacher_forced(LadderOracle(cfg, w, dtype=np.float32, kv_store_dtype=False), prompt, cont, logits="all")
+    log(f"70b shard full depth vs the unrounded-cache oracle: rel err logits "
+        f"{step_rel_err(gl, un.logits[:, wl.prompt_len - 1:]):.3g} hidden "
+        f"{step_rel_err(gh, un.hidden[:, wl.prompt_len - 1:]):.3g}")
     abs_err = np.max(np.abs(gl - rl))
     srt = np.sort(rl, axis=-1)
     margins = srt[..., -1] - srt[..., -2]
@@ -141,11 +158,13 @@ def test_70b_tp8_shard_full_depth_bench_configuration():
 
 def test_405b_tp16_shard_widths():
     """405B-shape TP=16 shard widths (hidden 16384: the staged input exceeds 64 KB of
-    LDS), four ladder layers; batch 1 and 16."""
+    LDS), four ladder layers; batch 1, 16 and 64 (the workload's batches).  Batch 64 runs
+    the 64-row GEMM tiles with the RMSNorm kernel ahead of them, the split-KV attention
+    over 4 key chunks per sequence and the row argmax over 64 rows."""
     base = synth.CONFIGS["405b_tp16_shard"]
     cfg = synth.scaled_config(base, 4)
     w = synth.gen_weights(cfg, seed=6)
-    for B, T, n_dec in ((1, 48, 4), (16, 12, 2)):
+    for B, T, n_dec in ((1, 48, 4), (16, 12, 2), (64, 16, 2)):
         prompt = synth.gen_ids(B, T, cfg.vocab, seed=7)
         cont = synth.gen_ids(B, n_dec, cfg.vocab, seed=7, stream=1)
         ref = teacher_forced(LadderOracle(cfg, w, dtype=np.float32), prompt, cont)
