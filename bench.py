@@ -28,10 +28,11 @@ MFMA_BF16_PEAK = 2.5e15      # FLOP/s, dense bf16
 CSRC = "ladder_residual_transformer_amd/csrc/"
 # the kernel each schedule's roofline reports: (trace kind, description, traffic file, sources)
 DOMINANT = {
-    "fused": ("qkv_attn_gateup", "fused ladder launch [RMSNorm+QKV+RoPE+KV, then RMSNorm+gate/up+SwiGLU, in "
-              "every workgroup | split-KV GQA attention once every QKV share is done]",
+    "fused": ("qkv_attn_gateup", "front launch of a ladder layer [RMSNorm+QKV+RoPE+KV, then RMSNorm+gate/up+"
+              "SwiGLU, in every workgroup | split-KV GQA attention chunks once their kv group's QKV outputs "
+              "arrive]; at batch 1 the streaming launch (stream.hip), else the row-wave one",
               "traffic_qkv_attn_gateup_70b_b1.json",
-              ("gemv_rw.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
+              ("stream.hip", "gemv_rw.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
     # FUSED without the bf16 two-launch layers, and the schedule with the attention in the
     # down projection's launch: the [QKV | gate/up] launch
     "fused3": ("qkv_gateup", "fused ladder launch [RMSNorm+QKV+RoPE+KV | RMSNorm+gate/up+SwiGLU]",
@@ -59,11 +60,12 @@ def kernel_sha(sources) -> str:
 
 
 def decode_bytes(cfg, B, pos):
-    """Algorithmic HBM bytes of one decode step at position pos: every weight once, the
-    KV rows 0..pos read and row pos written."""
+    """Algorithmic HBM bytes of one decode step at position pos: every layer weight, the
+    final norm and the LM head once, one embedding row per sequence, the KV rows 0..pos
+    read and row pos written."""
     esz = 2 if cfg.dtype == "bf16" else 4
     kv_row = B * cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * esz
-    return cfg.weight_bytes() + kv_row * (pos + 1) + kv_row
+    return cfg.decode_weight_bytes(B) + kv_row * (pos + 1) + kv_row
 
 
 def prefill_flops(cfg, B, T):
@@ -87,9 +89,11 @@ def qkv_gateup_bytes(cfg, B):
 
 
 def qkv_attn_gateup_bytes(cfg, B, pos):
-    """Algorithmic bytes of one sequential [QKV, then gate/up | attention] launch at position
+    """Algorithmic bytes of one front launch [QKV, then gate/up | attention] at position
     pos: those of [QKV | gate/up], plus the attention's reads of q and of the KV rows
-    0..pos (the newest one just written) and its output written."""
+    0..pos (the newest one just written) and its output written (at batch 1 the launch
+    leaves per-chunk records that the back launch merges into that output; the count is
+    the method's, B * nq * hd * 4 bytes, 0.003% of the launch)."""
     esz = 2 if cfg.dtype == "bf16" else 4
     q, kv = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
     return qkv_gateup_bytes(cfg, B) + 2 * B * q * 4 + 2 * B * kv * esz * (pos + 1)
@@ -150,6 +154,8 @@ def cpu_baseline(cfg, w, prompt, sample_layers, steps):
     t_head = (time.perf_counter() - t0) / steps
     per_token = t_layers * cfg.n_layers / sample_layers + t_head
     return {"value": B / per_token, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "extrapolated": sample_layers < cfg.n_layers, "layers_timed": sample_layers,
+            "layers_total": cfg.n_layers,
             "sample": (f"numpy float32 oracle, {sample_layers} of {cfg.n_layers} layers at full width plus the LM "
                        f"head, {steps} decode steps at KV length {T + 1}, per-token time scaled by "
                        f"{cfg.n_layers}/{sample_layers} for the layer stack; prefill of the {T}-token prompt "

@@ -66,12 +66,19 @@ class ModelConfig:
                                    name=name or self.name)
 
     def weight_bytes(self) -> int:
-        """Bytes of every weight tensor as stored (what one decode step streams)."""
+        """Bytes of every weight tensor as stored, the whole token-embedding table included."""
         e = 4 if self.dtype == "f32" else 2
         H, F, hd = self.hidden, self.ffn, self.head_dim
         per_layer = (H * (self.n_q_heads + 2 * self.n_kv_heads) * hd
                      + self.n_q_heads * hd * H + 3 * H * F + 2 * H)
         return e * (self.n_layers * per_layer + 2 * self.vocab * H + H)
+
+    def decode_weight_bytes(self, batch: int) -> int:
+        """Weight bytes one decode step of `batch` sequences reads: every layer's matrices
+        and norm gains, the final norm and the LM head once, and one embedding row per
+        sequence (not the whole table)."""
+        e = 4 if self.dtype == "f32" else 2
+        return self.weight_bytes() - e * (self.vocab - batch) * self.hidden
 
 
 @dataclasses.dataclass(frozen=True)

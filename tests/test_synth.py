@@ -54,6 +54,8 @@ def test_config_shapes():
     c = synth.CONFIGS["70b_tp8_shard"]
     assert c.weight_bytes() == 2 * (80 * (8192 * 1280 + 1024 * 8192 + 3 * 8192 * 3584 + 2 * 8192)
                                     + 2 * 16032 * 8192 + 8192)
+    # a decode step reads one embedding row per sequence, not the table
+    assert c.decode_weight_bytes(1) == c.weight_bytes() - 2 * 16031 * 8192
     assert synth.CONFIGS["8b_hybrid"].ladder_mask == tuple([0] * 16 + [1] * 16)
     assert synth.CONFIGS["8b_hybrid20"].ladder_mask == tuple([0] * 12 + [1] * 20)
     assert synth.scaled_config(c, 4).n_layers == 4
