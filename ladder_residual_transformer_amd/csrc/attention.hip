@@ -41,8 +41,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeParams p) {
   attn_decode_block<WT, HD, HPW>(p, blockIdx.x, L);
 }
 
-// Chunks per (sequence, kv head): one 64-key tile each up to 32 tiles of context
-// (longer contexts get several tiles per chunk); the merge reads all chunks at once.
 // Key chunks per sequence and kv head: one 64-key tile each up to 16 chunks (beyond 16,
 // the merge's inputs cost more than the shorter chunks save on the 70B shard's decode).
 int attn_decode_splits(int max_seq) {

@@ -21,7 +21,10 @@
 // Optional RMSNorm (split launches of a decode step): RMSNorm(x) W^T = (x * g) W^T / rms(x)
 // row by row, so A is the raw residual row, it is multiplied by the gain on its way into
 // LDS, the workgroups of the first column tile add up each row's squares over their K
-// slice, and the reduction divides each row's sums by its rms.
+// slice, and the reduction divides each row's sums by its rms.  The raw rows pass through
+// the fp16 pairs unnormalized, so the fold needs |x_k g_k| below fp16's largest finite value
+// (65504; beyond it the pair is infinite) and holds fp32-grade precision from about 2^-3
+// up (smaller magnitudes lose low bits of the lo half to fp16 subnormals).
 // Workgroups are dealt to the 8 XCDs round robin, so the tile list (M fastest) is cut
 // into 8 contiguous runs and run x goes to XCD x: workgroups that share a weight tile
 // run together on one XCD and read it once into that XCD's L2.

@@ -297,8 +297,9 @@ ladder_status trace_mark(ladder_ctx* ctx, int kind, hipStream_t s, bool end) {
 
 // Index j of the residual x_j that module m (2l attention, 2l+1 MLP of layer l) reads:
 // standard layers (mask 0) read x_m; ladder layers (mask 1) x_{m-1}, with x_{-1} = x_0
-// (Ladder Residual paper, section 3); parallel blocks (mask 2) feed both modules the layer
-// input x_{2l}, i.e. the attention reads x_m and the MLP x_{m-1}.
+// (Paper-Notes page, "method details / key design: staggered residual connection");
+// parallel blocks (mask 2) feed both modules the layer input x_{2l}, i.e. the attention
+// reads x_m and the MLP x_{m-1}.
 inline int module_src(const ladder_ctx* c, int m) {
   const int mode = c->mask[m / 2];
   const bool back = mode == 1 || (mode == 2 && (m & 1));

@@ -167,8 +167,9 @@ def module_input_index(m: int, ladder_mask) -> int:
     its MLP, and x_{m+1} = x_m + out_m.  The layer's mask value picks the rule:
 
     * 0, standard: every module reads x_m, the residual right before it;
-    * 1, ladder (Ladder Residual paper, section 3, the ladder recurrence): every
-      module reads x_{m-1}, one step earlier, with x_{-1} taken as x_0;
+    * 1, ladder (Paper-Notes page, "method details / key design: staggered residual
+      connection"): every module reads x_{m-1}, one step earlier, with x_{-1}
+      taken as x_0;
     * 2, parallel block (the "Parallel" baseline the paper compares against,
       which it does not define; read as the GPT-J style block): both modules
       of the layer read the layer input x_{2l}, so the attention follows the
