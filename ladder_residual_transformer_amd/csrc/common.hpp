@@ -89,6 +89,19 @@ __device__ __forceinline__ void split_h2(float a, float b, uint32_t& hi, uint32_
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
+// bf16 operands of the matrix cores: a pair hi = bf16(a), lo = bf16(a - hi) carries about
+// 16 significant bits of an fp32 value over fp32's exponent range.  Both conversions are
+// gfx950's packed v_cvt_pk_bf16_f32 (round to nearest even).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void split_bf2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 h = {(__bf16)a, (__bf16)b};
+  const bf2 l = {(__bf16)(a - (float)h[0]), (__bf16)(b - (float)h[1])};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 // 8 bf16 (one 16-byte chunk) -> 8 fp16
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& v) {
   return make_uint4(pack_h2(bf16_lo(v.x), bf16_hi(v.x)), pack_h2(bf16_lo(v.y), bf16_hi(v.y)),

@@ -1,13 +1,15 @@
 // Prefill projections C[M][N] = (R) + A[M][K] . W^T with M = batch x tokens.
 //
 // bf16 models: a dense contraction, so it runs on the CDNA4 matrix cores
-// (v_mfma_f32_16x16x32_f16, fp32 accumulation).  A arrives in fp32 and is split on
-// its way into LDS into a pair of fp16 values, hi = fp16(a) and lo = fp16(a - hi),
-// which together carry about 22 significant bits; the stored bf16 weights convert to
-// fp16 exactly (for |w| in [2^-17, 65504]).  Each product is then two MFMAs, hi.W and
-// lo.W, into one fp32 accumulator: a single fp16 or bf16 rounding of the activations
-// would perturb every module input by up to 2^-12 relative, which a deep stack of
-// modules carries into the final residual.
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  A arrives in fp32 and is split on
+// its way into LDS into a pair of bf16 values, hi = bf16(a) and lo = bf16(a - hi),
+// which together carry about 16 significant bits over fp32's range; the stored bf16
+// weights feed the matrix cores as they are.  Each product is then two MFMAs, hi.W and
+// lo.W, into one fp32 accumulator: a single 16-bit rounding of the activations perturbs
+// every module input by up to 2^-9 (bf16) or 2^-12 (fp16) relative, and a CPU emulation
+// of the 70B-shape shard (80 ladder layers) carries one rounding to 5.3e-2 (bf16) or
+// 1.25e-2 (fp16) in the logits, above the 1e-2 bar, while a bf16 or fp16 pair stays at
+// the ~5e-3 that any 2^-22 perturbation reaches at that depth.
 //
 // Tiling: a workgroup of 4 waves owns a 128x128 tile of C (2x2 waves of 64x64, i.e.
 // 4x4 MFMA tiles each; 32x128 or 64x128 tiles for at most 32 or 64 rows, as in a decode
@@ -22,9 +24,7 @@
 // row by row, so A is the raw residual row, it is multiplied by the gain on its way into
 // LDS, the workgroups of the first column tile add up each row's squares over their K
 // slice, and the reduction divides each row's sums by its rms.  The raw rows pass through
-// the fp16 pairs unnormalized, so the fold needs |x_k g_k| below fp16's largest finite value
-// (65504; beyond it the pair is infinite) and holds fp32-grade precision from about 2^-3
-// up (smaller magnitudes lose low bits of the lo half to fp16 subnormals).
+// the bf16 pairs unnormalized, which hold fp32's exponent range.
 // Workgroups are dealt to the 8 XCDs round robin, so the tile list (M fastest) is cut
 // into 8 contiguous runs and run x goes to XCD x: workgroups that share a weight tile
 // run together on one XCD and read it once into that XCD's L2.
@@ -58,7 +58,7 @@ constexpr int kStages = 4;   // K steps whose global loads are in flight (even: 
 // Slice blockIdx.y covers K range [blockIdx.y * kchunk, + kchunk); with more than one
 // slice the raw partial tile goes to p.ws[slice][M][N].
 template <int TM, int TN, bool NORM = false>
-__global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd,
+__global__ __launch_bounds__(256) void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd,
                                                          int kchunk) {
   constexpr int FM = TM / 32, FN = TN / 32;       // MFMA tiles per wave
   constexpr int AV = TM * BK / 4 / 256;           // float4 of A per thread per K step
@@ -132,13 +132,13 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
         a.w *= __uint_as_float(g.y & 0xffff0000u);
       }
       uint32_t h0, l0, h1, l1;
-      split_h2(ra[st][i].x, ra[st][i].y, h0, l0);
-      split_h2(ra[st][i].z, ra[st][i].w, h1, l1);
+      split_bf2(ra[st][i].x, ra[st][i].y, h0, l0);
+      split_bf2(ra[st][i].z, ra[st][i].w, h1, l1);
       *(uint2*)&Ah[buf][ar[i]][ac[i]] = make_uint2(h0, h1);
       *(uint2*)&Al[buf][ar[i]][ac[i]] = make_uint2(l0, l1);
     }
 #pragma unroll
-    for (int i = 0; i < BV; ++i) *(uint4*)&Bs[buf][br[i]][bc[i]] = bf16x8_to_f16x8(rb[st][i]);
+    for (int i = 0; i < BV; ++i) *(uint4*)&Bs[buf][br[i]][bc[i]] = rb[st][i];
   };
 
   f32x4 acc[FM][FN];
@@ -167,20 +167,20 @@ __global__ __launch_bounds__(256) void gemm_f16x2_kernel(GemmParams p, int n_til
       const int kt = k0 + u;
       if (kt < nk) {
         const int cur = u & 1;
-        half8 ah[FM], al[FM], b[FN];
+        bf16x8 ah[FM], al[FM], b[FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          ah[i] = *(const half8*)&Ah[cur][wm * (TM / 2) + i * 16 + fr][fk];
-          al[i] = *(const half8*)&Al[cur][wm * (TM / 2) + i * 16 + fr][fk];
+          ah[i] = *(const bf16x8*)&Ah[cur][wm * (TM / 2) + i * 16 + fr][fk];
+          al[i] = *(const bf16x8*)&Al[cur][wm * (TM / 2) + i * 16 + fr][fk];
         }
 #pragma unroll
-        for (int j = 0; j < FN; ++j) b[j] = *(const half8*)&Bs[cur][wn * (TN / 2) + j * 16 + fr][fk];
+        for (int j = 0; j < FN; ++j) b[j] = *(const bf16x8*)&Bs[cur][wn * (TN / 2) + j * 16 + fr][fk];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], b[j], acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], b[j], acc[i][j], 0, 0, 0);
           }
         if (kt + 1 < nk) {
           const int nxt = (u + 1) % kStages;       // a constant once the loop is unrolled
@@ -366,19 +366,19 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
       const int tm = (p.M + tmr - 1) / tmr, tiles = big, per = (tiles + kXcds - 1) / kXcds;
       const dim3 grid(per * kXcds, S);
       if (tmr == 32)
-        launch_timed(p.gain ? gemm_f16x2_kernel<32, 128, true> : gemm_f16x2_kernel<32, 128>, grid, dim3(256), 0, s, p,
+        launch_timed(p.gain ? gemm_bf16x2_kernel<32, 128, true> : gemm_bf16x2_kernel<32, 128>, grid, dim3(256), 0, s, p,
                      tm, tiles, per, p.K / S);
       else if (tmr == 64)
-        launch_timed(gemm_f16x2_kernel<64, 128>, grid, dim3(256), 0, s, p, tm, tiles, per, p.K / S);
+        launch_timed(gemm_bf16x2_kernel<64, 128>, grid, dim3(256), 0, s, p, tm, tiles, per, p.K / S);
       else
-        launch_timed(gemm_f16x2_kernel<128, 128>, grid, dim3(256), 0, s, p, tm, tiles, per, p.K / S);
+        launch_timed(gemm_bf16x2_kernel<128, 128>, grid, dim3(256), 0, s, p, tm, tiles, per, p.K / S);
       if (S > 1) {
         const size_t n_out = (size_t)p.M * (p.swiglu ? p.N / 2 : p.N);
         launch_timed(gemm_splitk_reduce_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, p, S);
       }
     } else {
       const int tm = (p.M + 63) / 64, tiles = tm * ((p.N + 63) / 64), per = (tiles + kXcds - 1) / kXcds;
-      launch_timed(gemm_f16x2_kernel<64, 64>, dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per, p.K);
+      launch_timed(gemm_bf16x2_kernel<64, 64>, dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per, p.K);
     }
   } else if (p.swiglu || p.gain) {
     return hipErrorInvalidValue;

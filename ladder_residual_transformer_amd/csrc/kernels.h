@@ -228,7 +228,7 @@ hipError_t launch_attn_prefill(const AttnPrefillParams& p, hipStream_t s);
 // C[M][N] (fp32, ldc) = (res ? res[M][N] : 0) + A[M][K] . B^T, B rows from RowSrc; with
 // swiglu (bf16 models, N even, rows interleaved gate/up): C[M][N/2] = silu(c[2n]) * c[2n+1].
 struct GemmParams {
-  int wdtype;                          // W_BF16: MFMA on fp16 pairs of A, W bf16 -> fp16; W_F32: VALU
+  int wdtype;                          // W_BF16: MFMA on bf16 pairs of A and the bf16 weights; W_F32: VALU
   // A: fp32 [M][lda] (lda a multiple of 4 for bf16 models)
   const void* A; int lda;
   RowSrc rows;
