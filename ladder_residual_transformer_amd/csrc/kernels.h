@@ -144,7 +144,7 @@ hipError_t launch_gemv_seq(const GemvParams& first, const GemvParams& second, co
 // Each workgroup streams its weight units with the next pass's units in flight across
 // the pass boundary; the results equal the row-wave launches' bit for bit.
 bool stream_front_supported(int wdtype, int K, int B, int hd);
-bool stream_back_supported(int wdtype, int Kd, int Ko, int B);
+bool stream_back_supported(int wdtype, int Kd, int Ko, int B, int N, int nq, int n_split);
 // tagged: one 64-bit word per QKV row (zero or holding codes of earlier launches of this
 // context); tag as for launch_gemv_seq.
 hipError_t launch_stream_front(const GemvParams& first, const GemvParams& second, const AttnDecodeParams& attn,

@@ -414,7 +414,7 @@ bool seq_layers(const ladder_ctx* ctx, int B) {
 bool stream_layers(const ladder_ctx* ctx, int B) {
   const ladder_config& g = ctx->cfg;
   return B == 1 && seq_layers(ctx, B) && stream_front_supported(ctx->wdt, g.hidden, B, g.head_dim) &&
-         stream_back_supported(ctx->wdt, g.ffn, ctx->qrows, B);
+         stream_back_supported(ctx->wdt, g.ffn, ctx->qrows, B, g.hidden, g.n_q_heads, ctx->n_split);
 }
 
 // RMSNorm + [Wgate,Wup] (row pairs) + SwiGLU of layer l

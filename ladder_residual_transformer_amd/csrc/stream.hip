@@ -600,9 +600,9 @@ bool stream_front_supported(int wdtype, int K, int B, int hd) {
   return wdtype == W_BF16 && B == 1 && (hd == 64 || hd == 128) && K % kSVec == 0 && K <= 1024 * kSVec;
 }
 
-bool stream_back_supported(int wdtype, int Kd, int Ko, int B) {
+bool stream_back_supported(int wdtype, int Kd, int Ko, int B, int N, int nq, int n_split) {
   return wdtype == W_BF16 && B == 1 && Kd % kSVec == 0 && Ko % kSVec == 0 && Kd <= 1024 * kSVec &&
-         Ko <= 1024 * kSVec;
+         Ko <= 1024 * kSVec && N >= 128 && nq <= kMergeHeads && n_split <= kMergeChunks;
 }
 
 namespace {
@@ -694,11 +694,12 @@ hipError_t back_go(MultiGemvParams& mp, hipStream_t s) {
 
 hipError_t launch_stream_back(const GemvParams& down, const GemvParams& o, const AttnDecodeParams& attn, int* err,
                               hipStream_t s) {
-  if (!stream_back_supported(down.wdtype, down.K, o.K, down.B) || o.B != 1 || o.wdtype != down.wdtype ||
-      down.N != o.N || o.epi != EPI_ADD2 || down.gain || o.gain || down.N < 128 || !o.xres || !o.out || !o.out2)
+  if (!stream_back_supported(down.wdtype, down.K, o.K, down.B, down.N, attn.nq, attn.n_split) || o.B != 1 ||
+      o.wdtype != down.wdtype || down.N != o.N || o.epi != EPI_ADD2 || down.gain || o.gain || !o.xres || !o.out ||
+      !o.out2)
     return hipErrorInvalidValue;
-  if (attn.B != 1 || attn.nkv < 1 || attn.nq % attn.nkv != 0 || attn.nq > kMergeHeads ||
-      attn.n_split > kMergeChunks || (attn.hd != 64 && attn.hd != 128) || attn.wdtype != down.wdtype ||
+  if (attn.B != 1 || attn.nkv < 1 || attn.nq % attn.nkv != 0 || (attn.hd != 64 && attn.hd != 128) ||
+      attn.wdtype != down.wdtype ||
       attn.nq * attn.hd != o.K || !attn.part || !attn.d_pos)
     return hipErrorInvalidValue;
   (void)err;

@@ -89,6 +89,22 @@ def test_single_key_prompt(tiny):
     model.free()
 
 
+@pytest.mark.parametrize("B", [1, 2])
+def test_narrow_bf16_model(B):
+    """hidden 64, one query head: too narrow for the batch-1 streaming launches (their back
+    launch needs at least 128 output rows), so batch 1 takes the row-wave launches of the
+    FUSED schedule instead, as batch 2 does."""
+    cfg = synth.ModelConfig("narrow", 2, 64, 1, 1, 64, 128, 777, 1e4, "bf16", (1, 1))
+    w = synth.gen_weights(cfg, seed=8)
+    prompt = synth.gen_ids(B, 7, cfg.vocab, seed=9)
+    log(f"narrow bf16 B={B}: prompt 7, decode 5")
+    ref = oracle_record(cfg, w, prompt, 5)
+    model = make_model(cfg, w, B, 16)
+    gl, gh, gt = gpu_teacher_forced(model, prompt, ref["tokens"][:, :-1])
+    check_against_oracle(cfg, gl, gh, gt, ref, TOL["bf16"], f"narrow B={B}")
+    model.free()
+
+
 @pytest.fixture(scope="module")
 def edge():
     return EDGE, synth.gen_weights(EDGE, seed=5)
