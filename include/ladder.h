@@ -165,6 +165,24 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
 ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t pos,
                                  float* d_logits, int32_t* d_next, float* d_hidden);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): ladder_decode_step with the same
+ * arguments, checks and outputs (bitwise the same values), enqueued eagerly on the
+ * context's stream with the FUSED schedule whatever schedule is selected, whose per-step
+ * buffers (residual ring, GEMV split-K partials and counters, attention chunk records,
+ * handoff words, logits and argmax partials) live in the library's static scratch: one
+ * 64 MiB device array per GPU (LADDER_STATIC_SCRATCH_BYTES), held from the library's
+ * load until the process ends, its address looked up by ladder_init.  The call allocates
+ * nothing (no hipMalloc or hipFree, no graph, no event) and clears the scratch's counters
+ * and flags itself with a kernel.  Every call on one GPU shares that GPU's array, and it
+ * keeps the last call's contents: calls that overlap on one GPU (other streams, other
+ * contexts) race and give wrong results; calls ordered on one stream are safe.
+ * LADDER_ERR_CAPACITY (with the bytes needed in ladder_last_error) when the step at batch
+ * B needs more than the array holds; LADDER_ERR_HIP if the address lookup failed. */
+#define LADDER_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+ladder_status ladder_decode_step_static(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t pos,
+                                        float* d_logits, int32_t* d_next, float* d_hidden);
+
 /* Select the schedule (LADDER_SCHED_*) and whether decode steps use HIP graphs. */
 ladder_status ladder_set_schedule(ladder_ctx* ctx, int32_t schedule, int32_t use_graph);
 

@@ -8,7 +8,7 @@ raises.
 """
 from .abi import (  # noqa: F401
     LADDER_BF16, LADDER_F32, LADDER_SCHED_DUAL, LADDER_SCHED_FUSED, LADDER_SCHED_FUSED_LATE_ATTN, LADDER_SCHED_PERSISTENT, LADDER_SCHED_SERIAL, LADDER_SCHED_SIDE, LadderError, load,
-    ladder_decode_step, ladder_filled, ladder_free, ladder_init, ladder_prefill, ladder_sample, ladder_set_sampling,
+    ladder_decode_step, ladder_decode_step_static, ladder_filled, ladder_free, ladder_init, ladder_prefill, ladder_sample, ladder_set_sampling,
     ladder_set_schedule,
     ladder_sync, ladder_time_kernels, ladder_workspace_bytes, status_string,
 )

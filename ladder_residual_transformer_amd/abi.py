@@ -16,6 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libladder.so")
 
 LADDER_OK = 0
+LADDER_STATIC_SCRATCH_BYTES = 64 << 20   # device bytes of the library's static scratch, per GPU
 LADDER_ERR_ARG = -1
 LADDER_ERR_SHAPE = -2
 LADDER_ERR_CAPACITY = -3
@@ -33,7 +34,7 @@ LADDER_SCHED_FUSED = 3
 LADDER_SCHED_PERSISTENT = 4
 LADDER_SCHED_FUSED_LATE_ATTN = 5
 
-EXPORTED = ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_set_sampling",
+EXPORTED = ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_decode_step_static", "ladder_set_schedule", "ladder_set_sampling",
             "ladder_filled",
             "ladder_workspace_bytes", "ladder_sync", "ladder_free", "ladder_status_string", "ladder_last_error",
             "ladder_time_kernels", "ladder_trace_kernel", "ladder_trace_result", "ladder_read_probe", "ladder_sample")
@@ -90,6 +91,7 @@ def load(path: str = LIB_PATH):
                                 POINTER(c_void_p)]
     lib.ladder_prefill.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     lib.ladder_decode_step.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
+    lib.ladder_decode_step_static.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     lib.ladder_set_schedule.argtypes = [c_void_p, c_int32, c_int32]
     lib.ladder_set_sampling.argtypes = [c_void_p, c_float, c_int32, ctypes.c_uint64]
     lib.ladder_sample.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_float, c_int32, ctypes.c_uint64, c_int32,
@@ -107,7 +109,7 @@ def load(path: str = LIB_PATH):
     lib.ladder_status_string.restype = ctypes.c_char_p
     lib.ladder_last_error.argtypes = [c_void_p]
     lib.ladder_last_error.restype = ctypes.c_char_p
-    for name in ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_set_schedule", "ladder_set_sampling",
+    for name in ("ladder_init", "ladder_prefill", "ladder_decode_step", "ladder_decode_step_static", "ladder_set_schedule", "ladder_set_sampling",
                  "ladder_filled",
                  "ladder_workspace_bytes", "ladder_sync", "ladder_time_kernels", "ladder_trace_kernel",
                  "ladder_trace_result", "ladder_read_probe", "ladder_sample"):
@@ -147,6 +149,13 @@ def ladder_decode_step(ctx: int, d_ids: int, B: int, pos: int, d_logits: int = 0
     _check(ctx, load().ladder_decode_step(c_void_p(ctx), c_void_p(d_ids), B, pos, c_void_p(d_logits or None),
                                           c_void_p(d_next or None), c_void_p(d_hidden or None)),
            "ladder_decode_step")
+
+
+def ladder_decode_step_static(ctx: int, d_ids: int, B: int, pos: int, d_logits: int = 0, d_next: int = 0,
+                              d_hidden: int = 0) -> None:
+    _check(ctx, load().ladder_decode_step_static(c_void_p(ctx), c_void_p(d_ids), B, pos, c_void_p(d_logits or None),
+                                                 c_void_p(d_next or None), c_void_p(d_hidden or None)),
+           "ladder_decode_step_static")
 
 
 def ladder_set_schedule(ctx: int, schedule: int, use_graph: bool = True) -> None:

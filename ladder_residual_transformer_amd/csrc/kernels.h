@@ -282,4 +282,16 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, int grid, float* sin
 hipError_t launch_decode_prologue(const int* ids_src, int* ids_dst, int B, int* d_pos, int pos, int* d_epoch,
                                   int wdtype, const void* table, int V, int H, float* x, hipStream_t s);
 
+// ------------------------------------------------------------------ static scratch
+// Device bytes of the library's static scratch array (one copy per GPU, held until the
+// process ends).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+// Look up the device address of device dev's copy (dev must be current); once per
+// device, later calls return the first result.
+hipError_t static_scratch_setup(int dev);
+// The address static_scratch_setup found (hipErrorNotInitialized before it ran).
+hipError_t static_scratch(int dev, void** ptr);
+// Zero bytes (a multiple of 16) at p (16-byte aligned) with a kernel.
+hipError_t launch_zero_bytes(void* p, size_t bytes, hipStream_t s);
+
 }  // namespace ladder

@@ -96,6 +96,8 @@ struct ladder_ctx {
 
   char* ws = nullptr;
   size_t ws_bytes = 0;
+  size_t step_off = 0;       // offset of the per-step part in ws
+  size_t step_zero_bytes = 0;   // leading bytes of the per-step part a step needs at zero
   float* rope_cos = nullptr;
   float* rope_sin = nullptr;
   float* dx[2] = {nullptr, nullptr};     // decode residual ring [max_batch][H]
@@ -197,48 +199,36 @@ ladder_status validate(const ladder_config* c, const ladder_weights* w, const la
   return LADDER_OK;
 }
 
-// Lay the workspace out (base == nullptr: only measure).
-void carve(ladder_ctx* c, Carver& cv) {
+// Shape of the per-step part of the workspace: buffers for batches up to B, prefill-route
+// rows up to `rows`, `nsc` stream scratch sets, the GEMMs' split-K partials and the prefill
+// attention's chunk records.
+struct StepShape {
+  int B, rows, nsc;
+  bool gk, apart;
+};
+
+StepShape ws_step_shape(const ladder_ctx* c) {
+  const bool bf = c->wdt == W_BF16;
+  return StepShape{c->cfg.max_batch, c->mmax, 2, bf, bf};
+}
+
+// The part of the workspace that lasts across calls: RoPE table, prefill residual rings,
+// step counter, error word and the persistent decode step's buffers.
+void carve_fixed(ladder_ctx* c, Carver& cv) {
   const ladder_config& g = c->cfg;
-  const int H = g.hidden, F = g.ffn, V = g.vocab, B = g.max_batch;
-  const int qkv = c->qrows + 2 * c->kvrows;
+  const int H = g.hidden, F = g.ffn, B = g.max_batch;
   c->rope_cos = cv.take<float>((size_t)g.max_seq * g.head_dim / 2);
   c->rope_sin = cv.take<float>((size_t)g.max_seq * g.head_dim / 2);
   for (int i = 0; i < 2; ++i) {
-    c->dx[i] = cv.take<float>((size_t)B * H);
-    c->dout[i] = cv.take<float>((size_t)B * H);
     c->px[i] = cv.take<float>((size_t)c->mmax * H);
     c->pout[i] = cv.take<float>((size_t)c->mmax * H);
   }
-  c->ids_dev = cv.take<int>(B);
-  c->pos_dev = cv.take<int>(1);
   c->ids_chunk = cv.take<int>(c->mmax);
-  c->logits = cv.take<float>((size_t)B * V);
-  c->next = cv.take<int>(B);
-  // GEMV split-K / argmax scratch: the largest need over every decode GEMV shape and batch
-  GemvWorkspaceReq need{};
-  const int shapes[5][2] = {{qkv, H}, {H, c->qrows}, {2 * F, H}, {H, F}, {V, H}};
-  for (int b = 1; b <= B; ++b)
-    for (auto& sh : shapes) {
-      GemvWorkspaceReq r = gemv_workspace(c->wdt, sh[0], sh[1], b);
-      need.part_floats = std::max(need.part_floats, r.part_floats);
-      need.part_sq_floats = std::max(need.part_sq_floats, r.part_sq_floats);
-      need.counters = std::max(need.counters, r.counters);
-      need.best = std::max(need.best, r.best);
-    }
-  const size_t nbest = std::max<size_t>(need.best, 1024 * 16);
-  c->best_val = cv.take<float>(nbest);
-  c->best_idx = cv.take<int>(nbest);
-  c->arg_cnt = cv.take<int>(1);
   c->epoch = cv.take<int>(1);
-  c->attn_done_cnt = cv.take<int>((size_t)g.n_layers);
-  c->attn_done_flag = cv.take<int>((size_t)g.n_layers);
   c->err_word = cv.take<int>(1);
   c->step_layers = cv.take<StepLayer>((size_t)g.n_layers);
   c->step_sync = cv.take<int>((size_t)8 * g.n_layers);
   c->step_prog = cv.take<uint32_t>(kStepProgWords);
-  c->seq_prog = cv.take<uint32_t>(kSeqProgWords);
-  c->qkv_tagged = cv.take<unsigned long long>((size_t)qkv);
   // vectors of the persistent decode step, each at an address of its own per step
   if (c->all_ladder && c->wdt == W_BF16) {
     const size_t sb = std::min(B, 4);
@@ -250,27 +240,81 @@ void carve(ladder_ctx* c, Carver& cv) {
     c->step_o = cv.take<float>((size_t)g.n_layers * c->step_qstride);
     c->step_a = cv.take<float>((size_t)g.n_layers * c->step_astride);
   }
-  for (int s = 0; s < 2; ++s) {
+}
+
+// The part a decode step (and a prefill chunk) uses only while it runs.  The counters,
+// flags and handoff words come first and end at c->step_zero_bytes from the part's start:
+// the kernels need them at zero, or holding earlier codes of this context, when a step
+// starts (each counter returns to zero after its last use in a step).
+void carve_step(ladder_ctx* c, Carver& cv, const StepShape& sh) {
+  const ladder_config& g = c->cfg;
+  const int H = g.hidden, F = g.ffn, V = g.vocab, B = sh.B;
+  const int qkv = c->qrows + 2 * c->kvrows;
+  // GEMV split-K / argmax scratch: the largest need over every decode GEMV shape and batch
+  GemvWorkspaceReq need{};
+  const int shapes[5][2] = {{qkv, H}, {H, c->qrows}, {2 * F, H}, {H, F}, {V, H}};
+  for (int b = 1; b <= B; ++b)
+    for (auto& shp : shapes) {
+      GemvWorkspaceReq r = gemv_workspace(c->wdt, shp[0], shp[1], b);
+      need.part_floats = std::max(need.part_floats, r.part_floats);
+      need.part_sq_floats = std::max(need.part_sq_floats, r.part_sq_floats);
+      need.counters = std::max(need.counters, r.counters);
+      need.best = std::max(need.best, r.best);
+    }
+  const size_t start = cv.off;
+  c->arg_cnt = cv.take<int>(1);
+  c->attn_done_cnt = cv.take<int>((size_t)g.n_layers);
+  c->attn_done_flag = cv.take<int>((size_t)g.n_layers);
+  c->seq_prog = cv.take<uint32_t>(kSeqProgWords);
+  c->qkv_tagged = cv.take<unsigned long long>((size_t)qkv);
+  for (int s = 0; s < sh.nsc; ++s) {
+    c->sc[s].attn_cnt = cv.take<int>((size_t)B * g.n_kv_heads);
+    c->sc[s].gcnt = cv.take<int>(need.counters);
+  }
+  c->step_zero_bytes = cv.off - start;
+  for (int i = 0; i < 2; ++i) {
+    c->dx[i] = cv.take<float>((size_t)B * H);
+    c->dout[i] = cv.take<float>((size_t)B * H);
+  }
+  c->ids_dev = cv.take<int>(B);
+  c->pos_dev = cv.take<int>(1);
+  c->logits = cv.take<float>((size_t)B * V);
+  c->next = cv.take<int>(B);
+  const size_t nbest = std::max<size_t>(need.best, 1024 * 16);
+  c->best_val = cv.take<float>(nbest);
+  c->best_idx = cv.take<int>(nbest);
+  for (int s = 0; s < sh.nsc; ++s) {
     StreamScratch& sc = c->sc[s];
     sc.q = cv.take<float>((size_t)B * c->qrows);
     sc.attn_part = cv.take<float>((size_t)B * g.n_q_heads * c->n_split * (g.head_dim + 4));
-    sc.attn_cnt = cv.take<int>((size_t)B * g.n_kv_heads);
     sc.o = cv.take<float>((size_t)B * c->qrows);
     sc.a = cv.take<float>((size_t)B * F);
     sc.gpart = cv.take<float>(need.part_floats);
     sc.gpart_sq = cv.take<float>(need.part_sq_floats);
-    sc.gcnt = cv.take<int>(need.counters);
-    sc.u = cv.take<float>((size_t)c->mmax * H);
-    sc.qkv = cv.take<float>((size_t)c->mmax * qkv);
-    sc.qr = cv.take<float>((size_t)c->mmax * c->qrows);
-    sc.ob = cv.take<float>((size_t)c->mmax * c->qrows);
-    sc.gu = cv.take<float>((size_t)c->mmax * 2 * F);
-    if (c->wdt == W_BF16) {
-      sc.gk = cv.take<float>(kGemmSplitWsFloats);
-      sc.apart = cv.take<float>(attn_prefill_part_floats(g.head_dim));
-    }
-    sc.ab = cv.take<float>((size_t)c->mmax * F);
+    sc.u = cv.take<float>((size_t)sh.rows * H);
+    sc.qkv = cv.take<float>((size_t)sh.rows * qkv);
+    sc.qr = cv.take<float>((size_t)sh.rows * c->qrows);
+    sc.ob = cv.take<float>((size_t)sh.rows * c->qrows);
+    sc.gu = cv.take<float>((size_t)sh.rows * 2 * F);
+    sc.gk = sh.gk ? cv.take<float>(kGemmSplitWsFloats) : nullptr;
+    sc.apart = sh.apart ? cv.take<float>(attn_prefill_part_floats(g.head_dim)) : nullptr;
+    sc.ab = cv.take<float>((size_t)sh.rows * F);
   }
+}
+
+// Lay the whole workspace out (base == nullptr: only measure).
+void carve(ladder_ctx* c, Carver& cv) {
+  carve_fixed(c, cv);
+  c->step_off = cv.off;
+  carve_step(c, cv, ws_step_shape(c));
+}
+
+// Point the per-step buffers back at the context's own workspace.
+void carve_ws_step(ladder_ctx* c) {
+  Carver cv;
+  cv.off = c->step_off;
+  cv.base = c->ws;
+  carve_step(c, cv, ws_step_shape(c));
 }
 
 // Event pair spanning the dispatches of the launches of kernel kind `kind` (traced
@@ -1091,6 +1135,9 @@ ladder_status ladder_init(const ladder_config* cfg, const ladder_weights* w, con
     hipError_t e_ = (call);                                                      \
     if (e_ != hipSuccess) return bail(e_ == hipErrorOutOfMemory ? LADDER_ERR_OOM : LADDER_ERR_HIP); \
   } while (0)
+  // the device address of this GPU's static scratch (ladder_decode_step_static); a failed
+  // lookup is kept and reported by that entry point, the context itself does not need it
+  (void)static_scratch_setup(ctx->dev);
   INITCHK(hipStreamCreateWithFlags(&ctx->s0, hipStreamNonBlocking));
   INITCHK(hipStreamCreateWithFlags(&ctx->sb, hipStreamNonBlocking));
   INITCHK(hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking));
@@ -1493,6 +1540,54 @@ ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t 
     st = enqueue_decode(ctx, B);
     if (st) return st;
   }
+  st = copy_outputs(ctx, B, ctx->dx[(2 * g.n_layers) % 2], (size_t)g.hidden * 4, d_logits, d_next, d_hidden);
+  if (st) return st;
+  ctx->filled = std::max(ctx->filled, pos + 1);
+  return end_call(ctx);
+}
+
+ladder_status ladder_decode_step_static(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t pos,
+                                        float* d_logits, int32_t* d_next, float* d_hidden) {
+  if (!ctx || !d_ids) return LADDER_ERR_ARG;
+  if (ctx->broken) return LADDER_ERR_HIP;
+  const ladder_config& g = ctx->cfg;
+  if (B < 1 || pos < 0) return fail(ctx, LADDER_ERR_ARG, "bad B/pos%s");
+  if (B > g.max_batch || pos >= g.max_seq) return fail(ctx, LADDER_ERR_CAPACITY, "batch or position beyond capacity%s");
+  if (pos > ctx->filled) return fail(ctx, LADDER_ERR_STATE, "decode position after unfilled positions%s");
+  void* base = nullptr;
+  const hipError_t se = static_scratch(ctx->dev, &base);
+  if (se != hipSuccess || !base)
+    return fail(ctx, LADDER_ERR_HIP, "the static scratch has no device address: %s", hipGetErrorString(se));
+  // every schedule gives the same bits; FUSED runs on the context's stream alone with one
+  // set of stream scratch
+  const StepShape sh{B, B, 1, gemm_decode(ctx, B), false};
+  // the per-step pointers go back to the workspace however this call ends
+  struct Restore {
+    ladder_ctx* c;
+    int sched;
+    ~Restore() {
+      c->sched = sched;
+      carve_ws_step(c);
+    }
+  } restore{ctx, ctx->sched};
+  Carver measure;
+  carve_step(ctx, measure, sh);
+  if (measure.off > kStaticScratchBytes) {
+    char what[160];
+    snprintf(what, sizeof what, "%zu bytes at batch %d, above the %zu bytes it holds", measure.off, (int)B,
+             kStaticScratchBytes);
+    return fail(ctx, LADDER_ERR_CAPACITY, "the static scratch is too small for this step: %s", what);
+  }
+  Carver cv;
+  cv.base = (char*)base;
+  carve_step(ctx, cv, sh);
+  ctx->sched = LADDER_SCHED_FUSED;
+  ladder_status st = begin_call(ctx);
+  if (st) return st;
+  HIPCHK(launch_zero_bytes(base, ctx->step_zero_bytes, ctx->s0));
+  HIPCHK(launch_decode_prologue(d_ids, ctx->ids_dev, B, ctx->pos_dev, pos, ctx->epoch, ctx->wdt, ctx->w.tok_embed,
+                                g.vocab, g.hidden, ctx->dx[0], ctx->s0));
+  if ((st = enqueue_decode(ctx, B))) return st;
   st = copy_outputs(ctx, B, ctx->dx[(2 * g.n_layers) % 2], (size_t)g.hidden * 4, d_logits, d_next, d_hidden);
   if (st) return st;
   ctx->filled = std::max(ctx->filled, pos + 1);

@@ -114,6 +114,16 @@ class LadderModel:
         abi.ladder_decode_step(self.ctx, ids.data_ptr(), B, pos, self._ptr(lg), self._ptr(nx), self._ptr(hd))
         return lg, nx, hd
 
+    def decode_step_static(self, ids: torch.Tensor, pos: int, out):
+        """decode_step through ladder_decode_step_static: out = (logits, next, hidden)
+        tensors allocated beforehand (entries may be None), since the call allocates
+        nothing."""
+        assert ids.dtype == torch.int32 and ids.is_contiguous() and ids.dim() == 1
+        lg, nx, hd = out
+        abi.ladder_decode_step_static(self.ctx, ids.data_ptr(), ids.shape[0], pos, self._ptr(lg), self._ptr(nx),
+                                      self._ptr(hd))
+        return lg, nx, hd
+
     def time_kernels(self, B: int, reps: int = 3) -> dict:
         return abi.ladder_time_kernels(self.ctx, B, reps)
 
