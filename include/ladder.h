@@ -109,6 +109,20 @@ typedef struct ladder_config {
                                  module reads the residual one module earlier), 2 = parallel
                                  block (attention and MLP both read the layer input); other
                                  values: LADDER_ERR_ARG */
+  /* Rotary frequency scaling of Llama-3.1 checkpoints (the inference code's
+   * `apply_rope_scaling`, named on the codewithpapers record of the method's pages, which
+   * give no constants; the rule is Llama-3.1's published one, constants 8 / 1 / 4 / 8192).
+   * rope_scale_factor 0: off (pair j turns by p * theta^(-2j/head_dim)).  Otherwise, with
+   * f = theta^(-2j/head_dim), its wavelength w = 2 pi / f and N = rope_orig_max_pos, pair j
+   * turns by p * f' where f' = f for w < N / rope_high_freq_factor, f' = f /
+   * rope_scale_factor for w > N / rope_low_freq_factor, and in between f' = (1 - s) f /
+   * rope_scale_factor + s f with s = (N / w - rope_low_freq_factor) /
+   * (rope_high_freq_factor - rope_low_freq_factor).  Computed in fp64 at init.
+   * LADDER_ERR_ARG unless factor >= 1, 0 < low < high (finite) and N > 0. */
+  double rope_scale_factor;
+  double rope_low_freq_factor;
+  double rope_high_freq_factor;
+  int32_t rope_orig_max_pos;
 } ladder_config;
 
 typedef struct ladder_layer_weights {

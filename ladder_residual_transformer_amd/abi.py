@@ -52,7 +52,9 @@ class ladder_config(ctypes.Structure):
     _fields_ = [("n_layers", c_int32), ("hidden", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32),
                 ("head_dim", c_int32), ("ffn", c_int32), ("vocab", c_int32), ("rope_theta", c_double),
                 ("norm_eps", c_float), ("dtype", c_int32), ("max_batch", c_int32), ("max_seq", c_int32),
-                ("max_prefill_tokens", c_int32), ("kv_filled", c_int32), ("ladder_mask", POINTER(c_uint8))]
+                ("max_prefill_tokens", c_int32), ("kv_filled", c_int32), ("ladder_mask", POINTER(c_uint8)),
+                ("rope_scale_factor", c_double), ("rope_low_freq_factor", c_double),
+                ("rope_high_freq_factor", c_double), ("rope_orig_max_pos", c_int32)]
 
 
 class ladder_layer_weights(ctypes.Structure):

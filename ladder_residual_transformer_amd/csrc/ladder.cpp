@@ -176,6 +176,11 @@ ladder_status validate(const ladder_config* c, const ladder_weights* w, const la
   if (c->dtype != LADDER_F32 && c->dtype != LADDER_BF16) return LADDER_ERR_ARG;
   if (!(c->rope_theta > 0.0) || !(c->norm_eps >= 0.0f)) return LADDER_ERR_ARG;
   if (c->kv_filled < 0 || c->kv_filled > c->max_seq) return LADDER_ERR_ARG;
+  if (c->rope_scale_factor != 0.0 &&
+      !(c->rope_scale_factor >= 1.0 && std::isfinite(c->rope_scale_factor) && c->rope_low_freq_factor > 0.0 &&
+        c->rope_high_freq_factor > c->rope_low_freq_factor && std::isfinite(c->rope_high_freq_factor) &&
+        c->rope_orig_max_pos > 0))
+    return LADDER_ERR_ARG;
   // fp32 models decode beyond batch 4 with the K-sliced GEMV (at most 16 rows); bf16
   // models on the matrix cores (the decode prologue takes at most 256 sequences)
   if (c->max_batch > (c->dtype == LADDER_BF16 ? 256 : 16)) return LADDER_ERR_SHAPE;
@@ -197,6 +202,20 @@ ladder_status validate(const ladder_config* c, const ladder_weights* w, const la
   }
   if (!aligned16(kv->k) || !aligned16(kv->v)) return LADDER_ERR_ARG;
   return LADDER_OK;
+}
+
+// Rotation frequency of pair j: theta^(-2j/head_dim), then, with scaling on, Llama-3.1's
+// bands by wavelength w = 2 pi / f against the original context N: short waves (w < N /
+// high) keep f, long ones (w > N / low) take f / factor, and the waves between blend the
+// two linearly in N / w, so f' is continuous at both band edges.
+double rope_frequency(const ladder_config& c, int j) {
+  const double f = std::pow(c.rope_theta, -2.0 * j / c.head_dim);
+  if (c.rope_scale_factor == 0.0) return f;
+  const double N = c.rope_orig_max_pos, w = 2.0 * M_PI / f;
+  if (w < N / c.rope_high_freq_factor) return f;
+  if (w > N / c.rope_low_freq_factor) return f / c.rope_scale_factor;
+  const double s = (N / w - c.rope_low_freq_factor) / (c.rope_high_freq_factor - c.rope_low_freq_factor);
+  return (1.0 - s) * f / c.rope_scale_factor + s * f;
 }
 
 // Shape of the per-step part of the workspace: buffers for batches up to B, prefill-route
@@ -1172,12 +1191,12 @@ ladder_status ladder_init(const ladder_config* cfg, const ladder_weights* w, con
     INITCHK(hipStreamSynchronize(ctx->s0));
   }
 
-  // RoPE table: pair j at position p rotates by p * theta^(-2j/hd), computed in fp64
+  // RoPE table: pair j at position p rotates by p * rope_frequency(j), computed in fp64
   {
     const int half = cfg->head_dim / 2;
     std::vector<float> cs((size_t)cfg->max_seq * half), sn((size_t)cfg->max_seq * half);
     for (int j = 0; j < half; ++j) {
-      const double inv_freq = std::pow(cfg->rope_theta, -2.0 * j / cfg->head_dim);
+      const double inv_freq = rope_frequency(*cfg, j);
       for (int p = 0; p < cfg->max_seq; ++p) {
         const double a = (double)p * inv_freq;
         cs[(size_t)p * half + j] = (float)std::cos(a);

@@ -44,7 +44,8 @@ class LadderModel:
     """A libladder context over ``DeviceWeights``.
 
     ``cfg`` needs n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab,
-    rope_theta, norm_eps, dtype ("f32"/"bf16") and ladder_mask.  The KV cache
+    rope_theta, norm_eps, dtype ("f32"/"bf16") and ladder_mask (and may carry rope_scaling,
+    (factor, low_freq_factor, high_freq_factor, original context)).  The KV cache
     [n_layers][max_batch][n_kv][max_seq][head_dim] is allocated here unless given.
     """
 
@@ -69,6 +70,10 @@ class LadderModel:
         c.dtype = abi.LADDER_BF16 if cfg.dtype == "bf16" else abi.LADDER_F32
         c.max_batch, c.max_seq, c.max_prefill_tokens, c.kv_filled = max_batch, max_seq, max_prefill_tokens, kv_filled
         c.ladder_mask = ctypes.cast(self._mask, ctypes.POINTER(ctypes.c_uint8))
+        scaling = getattr(cfg, "rope_scaling", None)
+        if scaling is not None:
+            (c.rope_scale_factor, c.rope_low_freq_factor, c.rope_high_freq_factor,
+             c.rope_orig_max_pos) = float(scaling[0]), float(scaling[1]), float(scaling[2]), int(scaling[3])
         self._cfg = c
         self._layers = (abi.ladder_layer_weights * cfg.n_layers)()
         for i, lw in enumerate(weights.layers):

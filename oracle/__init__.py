@@ -17,6 +17,8 @@ from .ladder import (  # noqa: F401
     round_to_storage,
     rms_norm,
     rope_angles,
+    rope_inv_freq,
+    llama3_scale_inv_freq,
     apply_rope,
     gqa_attention,
     silu,

@@ -29,6 +29,10 @@ design notes of the repository):
     so at a standard->ladder boundary the first ladder module reads x_{m-1};
   * pre-norm RMSNorm with eps 1e-5, gains stored with the weights;
   * rotary pairs are adjacent elements (2j, 2j+1), angle p * theta^(-2j/hd);
+  * where a model config carries ``rope_scaling`` (Llama-3.1 shapes: factor 8,
+    low_freq_factor 1, high_freq_factor 4, original context 8192), the frequencies
+    theta^(-2j/hd) first go through Llama-3.1's published band rule
+    (llama3_scale_inv_freq); the pages only name the function;
   * no biases, untied LM head, greedy argmax takes the lowest index on ties;
   * the KV cache is model state kept in the model's storage type, like the
     weights it is computed from: each K and V value is rounded to that type
@@ -95,14 +99,48 @@ def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
     return x / np.sqrt(ms + eps) * gain
 
 
-def rope_angles(positions: np.ndarray, head_dim: int, theta: float) -> np.ndarray:
-    """Rotation angle of pair j at position p: p * theta^(-2j/head_dim), shape [P, head_dim/2]."""
+def llama3_scale_inv_freq(inv_freq: np.ndarray, factor: float, low_freq_factor: float,
+                          high_freq_factor: float, original_max_pos: int) -> np.ndarray:
+    """Llama-3.1 rotary frequency scaling (the function the method's inference code calls
+    ``apply_rope_scaling``, named on the codewithpapers record; the pages give no
+    constants, so the rule and its constants are those Llama-3.1 publishes, see the
+    readings in the module docstring).
+
+    With the wavelength w = 2 pi / f of a pair's frequency f and the original context
+    length N: a pair with w < N / high_freq_factor keeps f; a pair with
+    w > N / low_freq_factor gets f / factor; in between, with
+    s = (N / w - low_freq_factor) / (high_freq_factor - low_freq_factor) in [0, 1],
+    f becomes (1 - s) f / factor + s f, which meets both sides at the band edges.
+    Pins: the closed forms at chosen wavelengths (f, f, 5f/12 at w = N/2 for the
+    Llama-3.1 constants, f / factor), continuity at both edges, monotonicity in w and
+    the identity for factor 1.
+    """
+    f = np.asarray(inv_freq, dtype=np.float64)
+    wavelen = 2.0 * np.pi / f
+    low_wavelen = original_max_pos / low_freq_factor      # longer: fully scaled
+    high_wavelen = original_max_pos / high_freq_factor    # shorter: unchanged
+    s = (original_max_pos / wavelen - low_freq_factor) / (high_freq_factor - low_freq_factor)
+    mid = (1.0 - s) * f / factor + s * f
+    return np.where(wavelen < high_wavelen, f, np.where(wavelen > low_wavelen, f / factor, mid))
+
+
+def rope_inv_freq(head_dim: int, theta: float, scaling=None) -> np.ndarray:
+    """Frequency of pair j: theta^(-2j/head_dim), j < head_dim/2; with ``scaling`` =
+    (factor, low_freq_factor, high_freq_factor, original_max_pos) passed through
+    llama3_scale_inv_freq."""
     j = np.arange(head_dim // 2, dtype=np.float64)
     inv_freq = np.power(float(theta), -2.0 * j / head_dim)
-    return np.outer(np.asarray(positions, dtype=np.float64), inv_freq)
+    if scaling is not None:
+        inv_freq = llama3_scale_inv_freq(inv_freq, *scaling)
+    return inv_freq
 
 
-def apply_rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+def rope_angles(positions: np.ndarray, head_dim: int, theta: float, scaling=None) -> np.ndarray:
+    """Rotation angle of pair j at position p: p * f_j (rope_inv_freq), shape [P, head_dim/2]."""
+    return np.outer(np.asarray(positions, dtype=np.float64), rope_inv_freq(head_dim, theta, scaling))
+
+
+def apply_rope(x: np.ndarray, positions: np.ndarray, theta: float, scaling=None) -> np.ndarray:
     """Rotate adjacent pairs (x[2j], x[2j+1]) of the last axis by their angle.
 
     ``x`` has shape [..., P, head_dim] with positions along axis -2.
@@ -110,7 +148,7 @@ def apply_rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray
     identity at p = 0; preserves norms; q_p . k_s depends only on p - s.
     """
     hd = x.shape[-1]
-    ang = rope_angles(positions, hd, theta)
+    ang = rope_angles(positions, hd, theta, scaling)
     c = np.cos(ang).astype(x.dtype)
     s = np.sin(ang).astype(x.dtype)
     x0 = x[..., 0::2]
@@ -265,8 +303,9 @@ class LadderOracle:
         k = np.matmul(u, W["wk"].T).reshape(B, T, nkv, hd).transpose(0, 2, 1, 3)
         v = np.matmul(u, W["wv"].T).reshape(B, T, nkv, hd).transpose(0, 2, 1, 3)
         pos = start_pos + np.arange(T)
-        q = apply_rope(q, pos, cfg.rope_theta)
-        k = apply_rope(k, pos, cfg.rope_theta)
+        scaling = getattr(cfg, "rope_scaling", None)
+        q = apply_rope(q, pos, cfg.rope_theta, scaling)
+        k = apply_rope(k, pos, cfg.rope_theta, scaling)
         if self.kv_store_dtype:
             k = round_to_storage(k, cfg.dtype)
             v = round_to_storage(v, cfg.dtype)

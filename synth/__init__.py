@@ -24,7 +24,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "ModelConfig", "Workload", "CONFIGS", "WORKLOADS", "LayerWeights", "ModelWeights",
+    "ModelConfig", "Workload", "CONFIGS", "LLAMA31_ROPE_SCALING", "WORKLOADS", "LayerWeights", "ModelWeights",
     "gen_weights", "gen_ids", "f32_to_bf16_bits", "scaled_config",
 ]
 
@@ -48,6 +48,9 @@ class ModelConfig:
     dtype: str                      # "f32" or "bf16": weights and KV cache
     ladder_mask: tuple              # one entry per layer: 0 = standard, 1 = ladder, 2 = parallel
     norm_eps: float = 1e-5
+    # rotary frequency scaling (factor, low_freq_factor, high_freq_factor, original context
+    # length) of Llama-3.1 checkpoints, or None
+    rope_scaling: Optional[tuple] = None
 
     def __post_init__(self):
         if len(self.ladder_mask) != self.n_layers:
@@ -99,6 +102,9 @@ def _all_ladder(n):
     return tuple([1] * n)
 
 
+# Llama-3.1's published rotary scaling constants (its checkpoints' "llama3" rope_scaling).
+LLAMA31_ROPE_SCALING = (8.0, 1.0, 4.0, 8192)
+
 # The five workloads.  The 70B and 405B rows are one tensor-parallel rank's
 # shard: per-rank heads and ffn slice, vocabulary split over the ranks
 # (128256 / 8 = 16032 and 128256 / 16 = 8016 rows of embedding and LM head).
@@ -106,14 +112,14 @@ CONFIGS = {
     "tiny": ModelConfig("tiny", 2, 256, 4, 2, 64, 688, 1024, 1e4, "f32", _all_ladder(2)),
     "1b": ModelConfig("1b", 16, 2048, 32, 8, 64, 8192, 32000, 1e4, "bf16", _all_ladder(16)),
     "8b_hybrid": ModelConfig("8b_hybrid", 32, 4096, 32, 8, 128, 14336, 128256, 5e5, "bf16",
-                             tuple([0] * 16 + [1] * 16)),
+                             tuple([0] * 16 + [1] * 16), rope_scaling=LLAMA31_ROPE_SCALING),
     # the hybrid with 20 converted layers: the upper 20 of 32 layers ladder
     "8b_hybrid20": ModelConfig("8b_hybrid20", 32, 4096, 32, 8, 128, 14336, 128256, 5e5, "bf16",
-                               tuple([0] * 12 + [1] * 20)),
+                               tuple([0] * 12 + [1] * 20), rope_scaling=LLAMA31_ROPE_SCALING),
     "70b_tp8_shard": ModelConfig("70b_tp8_shard", 80, 8192, 8, 1, 128, 3584, 16032, 5e5,
-                                 "bf16", _all_ladder(80)),
+                                 "bf16", _all_ladder(80), rope_scaling=LLAMA31_ROPE_SCALING),
     "405b_tp16_shard": ModelConfig("405b_tp16_shard", 126, 16384, 8, 1, 128, 3328, 8016, 5e5,
-                                   "bf16", _all_ladder(126)),
+                                   "bf16", _all_ladder(126), rope_scaling=LLAMA31_ROPE_SCALING),
 }
 
 WORKLOADS = {

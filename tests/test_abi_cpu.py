@@ -42,21 +42,38 @@ def test_header_constants_match_binding():
 
 
 def test_struct_layout():
-    assert ctypes.sizeof(abi.ladder_config) == 72
-    assert abi.ladder_config.rope_theta.offset == 32
-    assert abi.ladder_config.ladder_mask.offset == 64
-    assert ctypes.sizeof(abi.ladder_layer_weights) == 9 * 8
-    assert ctypes.sizeof(abi.ladder_weights) == 32
+    """The ctypes structs lay out like the C header, as gcc compiles it."""
+    import shutil
+    import subprocess
+    import tempfile
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not found")
+    fields = [f[0] for f in abi.ladder_config._fields_]
+    src = "#include <stddef.h>\n#include <stdio.h>\n#include \"ladder.h\"\nint main(void) {\n"
+    src += '  printf("%zu\\n", sizeof(ladder_config));\n'
+    src += "".join('  printf("%%zu\\n", offsetof(ladder_config, %s));\n' % f for f in fields)
+    src += '  printf("%zu %zu\\n", sizeof(ladder_layer_weights), sizeof(ladder_weights));\n  return 0;\n}\n'
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "layout.c"), os.path.join(d, "layout")
+        with open(c, "w") as fh:
+            fh.write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()
+    assert int(out[0]) == ctypes.sizeof(abi.ladder_config)
+    for f, off in zip(fields, out[1:1 + len(fields)]):
+        assert int(off) == getattr(abi.ladder_config, f).offset, f
+    assert int(out[-2]) == ctypes.sizeof(abi.ladder_layer_weights) == 9 * 8
+    assert int(out[-1]) == ctypes.sizeof(abi.ladder_weights) == 32
 
 
 FAKE = 0x100000
 
 
 def make_args(n_layers=2, hidden=256, nq=4, nkv=2, hd=64, ffn=688, vocab=1024, dtype=0, max_batch=1, max_seq=32,
-              mask=None, ptr=FAKE):
+              mask=None, ptr=FAKE, rope=(0.0, 0.0, 0.0, 0)):
     m = (ctypes.c_uint8 * n_layers)(*(mask or [1] * n_layers))
     cfg = abi.ladder_config(n_layers, hidden, nq, nkv, hd, ffn, vocab, 1e4, 1e-5, dtype, max_batch, max_seq, 0, 0,
-                            ctypes.cast(m, ctypes.POINTER(ctypes.c_uint8)))
+                            ctypes.cast(m, ctypes.POINTER(ctypes.c_uint8)), *rope)
     layers = (abi.ladder_layer_weights * n_layers)()
     for i in range(n_layers):
         for f, _ in abi.ladder_layer_weights._fields_:
@@ -85,6 +102,11 @@ def init_status(cfg, w, kv):
     (dict(max_seq=0), abi.LADDER_ERR_ARG),
     (dict(mask=[1, 3]), abi.LADDER_ERR_ARG),           # 0 standard, 1 ladder, 2 parallel only
     (dict(ptr=FAKE + 2), abi.LADDER_ERR_ARG),          # misaligned weight pointer
+    (dict(rope=(0.5, 1.0, 4.0, 8192)), abi.LADDER_ERR_ARG),   # RoPE scaling factor below 1
+    (dict(rope=(8.0, 4.0, 1.0, 8192)), abi.LADDER_ERR_ARG),   # low_freq_factor >= high_freq_factor
+    (dict(rope=(8.0, 0.0, 4.0, 8192)), abi.LADDER_ERR_ARG),   # low_freq_factor not positive
+    (dict(rope=(8.0, 1.0, 4.0, 0)), abi.LADDER_ERR_ARG),      # no original context length
+    (dict(rope=(float("nan"), 1.0, 4.0, 8192)), abi.LADDER_ERR_ARG),
 ])
 def test_init_rejects_bad_arguments(change, status):
     cfg, w, kv, keep = make_args(**change)
@@ -103,9 +125,11 @@ def test_init_null_pointers():
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
-@pytest.mark.parametrize("mask", [None, [2, 0], [0, 2, 1]])
-def test_valid_config_without_device_reports_hip_error(mask):
-    cfg, w, kv, keep = make_args(n_layers=len(mask) if mask else 2, mask=mask)
+@pytest.mark.parametrize("mask, rope", [(None, (0.0, 0.0, 0.0, 0)), ([2, 0], (0.0, 0.0, 0.0, 0)),
+                                        ([0, 2, 1], (0.0, 0.0, 0.0, 0)), (None, (8.0, 1.0, 4.0, 8192)),
+                                        (None, (1.0, 1.0, 4.0, 8192))])
+def test_valid_config_without_device_reports_hip_error(mask, rope):
+    cfg, w, kv, keep = make_args(n_layers=len(mask) if mask else 2, mask=mask, rope=rope)
     st, out = init_status(cfg, w, kv)
     assert st == abi.LADDER_ERR_HIP and out is None
 
@@ -114,6 +138,7 @@ def test_null_context_calls():
     lib = L.load()
     assert lib.ladder_prefill(None, None, 1, 1, 0, None, None, None) == abi.LADDER_ERR_ARG
     assert lib.ladder_decode_step(None, None, 1, 0, None, None, None) == abi.LADDER_ERR_ARG
+    assert lib.ladder_decode_step_static(None, None, 1, 0, None, None, None) == abi.LADDER_ERR_ARG
     assert lib.ladder_set_schedule(None, 0, 0) == abi.LADDER_ERR_ARG
     assert lib.ladder_set_sampling(None, 1.0, 0, 0) == abi.LADDER_ERR_ARG
     # argument errors of the context-free draw are found before anything is launched

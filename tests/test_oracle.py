@@ -14,7 +14,8 @@ import torch
 import torch.nn.functional as F
 
 import synth
-from oracle import (LadderOracle, apply_rope, gqa_attention, greedy_generate, module_input_index,
+from oracle import (LadderOracle, apply_rope, gqa_attention, greedy_generate, llama3_scale_inv_freq,
+                    module_input_index, rope_inv_freq,
                     rms_norm, rope_angles, round_to_storage, silu, swiglu_mlp, teacher_forced, upcast)
 
 torch.set_default_dtype(torch.float64)
@@ -126,6 +127,67 @@ def test_rope_properties():
         return qp @ ks
     assert dot(9, 4) == pytest.approx(dot(105, 100), rel=1e-10)             # depends on p - s only
     assert dot(9, 4) != pytest.approx(dot(9, 5), rel=1e-3)
+
+
+LLAMA31 = (8.0, 1.0, 4.0, 8192)   # factor, low_freq_factor, high_freq_factor, original context
+
+
+def test_llama3_scaling_closed_forms():
+    """At wavelengths below N/4 = 2048 a frequency is kept, above N = 8192 divided by 8;
+    at w = N/2 = 4096 the blend weight is s = (2 - 1) / (4 - 1) = 1/3, so the frequency
+    becomes (2/3) f / 8 + f / 3 = 5 f / 12.  A dropped 1/factor, swapped band limits or an
+    inverted ratio w / N each break one of these."""
+    w = np.array([100.0, 1000.0, 2047.0, 4096.0, 8193.0, 20000.0, 1e6])
+    f = 2 * np.pi / w
+    got = llama3_scale_inv_freq(f, *LLAMA31)
+    want = np.array([f[0], f[1], f[2], 5 * f[3] / 12, f[4] / 8, f[5] / 8, f[6] / 8])
+    np.testing.assert_allclose(got, want, rtol=1e-14)
+
+
+def test_llama3_scaling_is_continuous_and_monotone():
+    """The blend meets the kept band at w = N/4 and the divided band at w = N (relative
+    jumps of order the step in w), and the scaled frequency falls monotonically with the
+    wavelength while its ratio to f falls from 1 to 1/8."""
+    for edge in (2048.0, 8192.0):
+        w = np.array([edge * (1 - 1e-9), edge, edge * (1 + 1e-9)])
+        g = llama3_scale_inv_freq(2 * np.pi / w, *LLAMA31)
+        assert np.all(np.abs(np.diff(g)) <= 1e-8 * g[1])
+    w = np.geomspace(10.0, 1e6, 20001)
+    f = 2 * np.pi / w
+    g = llama3_scale_inv_freq(f, *LLAMA31)
+    assert np.all(np.diff(g) < 0)
+    r = g / f
+    assert np.all(np.diff(r) <= 1e-15) and r[0] == 1.0 and r[-1] == pytest.approx(1 / 8, rel=1e-15)
+
+
+def test_llama3_scaling_on_a_llama31_head_and_identity_at_factor_1():
+    """theta 5e5, head_dim 128 (wavelength of pair j: 2 pi 5e5^(j/64)): pairs 0..28 (up to
+    1956.5) keep theta^(-2j/128), pairs 35..63 (from 8218.7) are divided by 8, pairs
+    29..34 (2401.7 .. 6695.1) are blended; with
+    factor 1 every pair keeps its frequency.  RoPE with scaled frequencies still
+    preserves norms and depends only on p - s."""
+    base = rope_inv_freq(128, 5e5)
+    scaled = rope_inv_freq(128, 5e5, LLAMA31)
+    wl = 2 * np.pi / base
+    keep, div = wl < 2048, wl > 8192
+    assert np.array_equal(np.flatnonzero(keep), np.arange(29))
+    assert np.array_equal(np.flatnonzero(div), np.arange(35, 64))
+    np.testing.assert_array_equal(scaled[keep], base[keep])
+    np.testing.assert_allclose(scaled[div], base[div] / 8, rtol=1e-15)
+    mid = ~keep & ~div
+    assert np.all(scaled[mid] < base[mid]) and np.all(scaled[mid] > base[mid] / 8)
+    np.testing.assert_allclose(rope_inv_freq(128, 5e5, (1.0, 1.0, 4.0, 8192)), base, rtol=1e-15)
+    rng = np.random.default_rng(9)
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+
+    def dot(p, s):
+        qp = apply_rope(q[None, None, None, :], np.array([p]), 5e5, LLAMA31)[0, 0, 0]
+        ks = apply_rope(k[None, None, None, :], np.array([s]), 5e5, LLAMA31)[0, 0, 0]
+        return qp @ ks
+    assert dot(30, 7) == pytest.approx(dot(1030, 1007), rel=1e-10)
+    y = apply_rope(q[None, None, None, :], np.array([777]), 5e5, LLAMA31)
+    assert np.linalg.norm(y) == pytest.approx(np.linalg.norm(q), rel=1e-12)
+    assert not np.allclose(y, apply_rope(q[None, None, None, :], np.array([777]), 5e5), atol=1e-3)
 
 
 def test_attention_matches_sdpa_with_repeated_kv():
