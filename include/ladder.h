@@ -172,10 +172,12 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
  * captured HIP graph per (B, schedule, next-token rule) when graphs are enabled.
  * Batches whose staged projection inputs fit the row-wave GEMV (B <= 4 and
  * B * (K + 8) * 4 bytes <= 150 KB for K the widest of hidden, ffn and
- * n_q_heads * head_dim; at B = 4 only up to 65 KB, two workgroups per CU) run the
- * schedule's GEMV launches; other bf16
- * batches run one token per sequence through the prefill modules on the matrix cores
- * (with the split-KV decode attention), under every schedule. */
+ * n_q_heads * head_dim; at B = 3 and 4 only up to 65 KB, two workgroups per CU) run the
+ * schedule's GEMV launches; other bf16 batches run one token per sequence on the matrix
+ * cores (with the split-KV decode attention), under every schedule: up to 32 sequences
+ * through skinny weight-streaming launches (a ladder layer in four launches under the
+ * FUSED schedules, module by module otherwise, with the same bits), beyond that through
+ * tiled GEMMs. */
 ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t pos,
                                  float* d_logits, int32_t* d_next, float* d_hidden);
 

@@ -349,11 +349,14 @@ int gemm_splits(const GemmParams& p) {
 // The fused RMSNorm: split launches of the 32-row tiles (the larger tiles' registers do
 // not leave room for the gain without halving their occupancy).
 bool gemm_norm_fusable(const GemmParams& p) {
+  if (skinny_supported(p)) return true;
   return p.wdtype == W_BF16 && p.M <= 32 && p.lda % 4 == 0 && p.K % BK == 0 && gemm_splits(p) > 1;
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.M < 1 || p.N < 1 || p.K < 1) return hipErrorInvalidValue;
+  if (skinny_supported(p)) return launch_skinny(p, s);
+  if (p.A2) return hipErrorInvalidValue;   // a second K part: skinny launches only
   if (p.wdtype == W_BF16) {
     if (p.K % BK != 0 || p.lda % 4 != 0 || (p.swiglu && (p.N % 2 != 0 || p.res))) return hipErrorInvalidValue;
     // 128x128 tiles (32x128 / 64x128 for at most 32 / 64 rows) when they give the device at

@@ -245,9 +245,30 @@ struct GemmParams {
   // reduction scales each row's sums by 1 / sqrt(mean square + eps).  Only valid where
   // gemm_norm_fusable() holds for p with the gain set (the launch is refused otherwise).
   const void* gain; float eps;
+  // tickets of the skinny launch (M <= 32): kSkinnyMaxTiles ints, zero between launches
+  // (each launch returns them to zero); nullable: no skinny launch
+  int* cnt;
+  // second K part (skinny launches only; A2 nullable): C = res + A . W^T and
+  // C2 = C + A2 . W2^T, with W2 rows from rows2 (the same N rows), K2 columns, fp32 A2 [M][lda2]
+  const void* A2; int lda2;
+  RowSrc rows2;
+  int K2;
+  float* C2;
 };
 constexpr size_t kGemmSplitWsFloats = (size_t)512 * 128 * 128;
+constexpr int kSkinnyMaxTiles = 2048;
+// C = (R) + A . W^T: for bf16 weights and M <= 64 rows a skinny launch (weights streamed
+// into the matrix cores, K slices reduced in the same launch) where skinny_supported(p),
+// else the tiled GEMM with a separate split-K reduction.
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+bool skinny_supported(const GemmParams& p);
+hipError_t launch_skinny(const GemmParams& p, hipStream_t s);
+// Two skinny problems in one launch (same M, both with or both without the RMSNorm fold,
+// workspaces and tickets of their own); each gives the bits of its own launch_skinny.
+bool skinny_pair_supported(const GemmParams& a, const GemmParams& b);
+hipError_t launch_skinny_pair(const GemmParams& a, const GemmParams& b, hipStream_t s);
+// Workspace floats the skinny launch of p takes (partials and sums of squares).
+size_t skinny_ws_floats(const GemmParams& p);
 // K slices launch_gemm uses for p (1: no split).
 int gemm_splits(const GemmParams& p);
 bool gemm_norm_fusable(const GemmParams& p);

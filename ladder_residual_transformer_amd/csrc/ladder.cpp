@@ -56,6 +56,7 @@ struct StreamScratch {
   float* ab = nullptr;
   float* gk = nullptr;   // split-K partials of the prefill GEMMs (bf16 models)
   float* apart = nullptr;  // key-chunk records of the prefill attention (bf16 models)
+  int* skcnt = nullptr;    // tickets of the skinny GEMM launches (bf16 models)
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -289,6 +290,7 @@ void carve_step(ladder_ctx* c, Carver& cv, const StepShape& sh) {
   for (int s = 0; s < sh.nsc; ++s) {
     c->sc[s].attn_cnt = cv.take<int>((size_t)B * g.n_kv_heads);
     c->sc[s].gcnt = cv.take<int>(need.counters);
+    c->sc[s].skcnt = sh.gk ? cv.take<int>(kSkinnyMaxTiles) : nullptr;
   }
   c->step_zero_bytes = cv.off - start;
   for (int i = 0; i < 2; ++i) {
@@ -693,6 +695,7 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
   gp.M = M;
   gp.ws = sc.gk;
   gp.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
+  gp.cnt = sc.skcnt;
   const void* proj_in;
   int proj_k;
   const void* proj_w;
@@ -785,6 +788,7 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
   op.wdtype = ctx->wdt;
   op.ws = sc.gk;
   op.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
+  op.cnt = sc.skcnt;
   op.A = proj_in;
   op.lda = proj_k;
   op.rows = RowSrc{{proj_w, nullptr, nullptr}, g.hidden, g.hidden, 0};
@@ -943,11 +947,12 @@ ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream
   const ladder_config& g = ctx->cfg;
   if (gemm_decode(ctx, B)) {
     StreamScratch& sc = ctx->sc[0];
-    HIPCHK(launch_rmsnorm(ctx->wdt, x, ldx, ctx->w.final_norm, g.norm_eps, B, g.hidden, sc.u, s));
     GemmParams hp{};
     hp.wdtype = ctx->wdt;
-    hp.A = sc.u;
-    hp.lda = g.hidden;
+    // the final RMSNorm folded into the skinny launch where it takes the LM head (A = the
+    // raw rows), else its own kernel
+    hp.A = x;
+    hp.lda = ldx;
     hp.rows = RowSrc{{ctx->w.lm_head, nullptr, nullptr}, g.vocab, g.vocab, 0};
     hp.M = B;
     hp.N = g.vocab;
@@ -956,6 +961,15 @@ ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream
     hp.ldc = g.vocab;
     hp.ws = sc.gk;
     hp.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
+    hp.cnt = sc.skcnt;
+    hp.gain = ctx->w.final_norm;
+    hp.eps = g.norm_eps;
+    if (!skinny_supported(hp)) {
+      HIPCHK(launch_rmsnorm(ctx->wdt, x, ldx, ctx->w.final_norm, g.norm_eps, B, g.hidden, sc.u, s));
+      hp.A = sc.u;
+      hp.lda = g.hidden;
+      hp.gain = nullptr;
+    }
     HIPCHK(launch_gemm(hp, s));
     HIPCHK(launch_argmax_rows(ctx->logits, B, g.vocab, g.vocab, ctx->next, s));
   } else {
@@ -1014,19 +1028,119 @@ ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
 
 // Decode steps that the row-wave projections cannot take (bf16 weights, batch > 4, or the
 // staged input rows of any projection, the widest of hidden, ffn and the attention rows,
-// beyond their LDS budget): one token per sequence through the prefill modules, whose
-// projections run on the matrix cores (the K-sliced GEMV kernels leave most of the HBM
-// bandwidth unused at those batches: the 8B model's down projection, K 14336, at batch 3
-// and 4 took them and halved the step rate), with the split-KV decode attention, then the
-// final RMSNorm, the LM head as a GEMM and a row argmax.  Every kernel of the route takes
-// the position from the device (the prologue's pos_dev), so it is replayed as a graph too.
-// Batch 4 also takes it where the row-wave launches would hold one workgroup per CU (the
-// 70B shard: 455.5 against 427.8 tok/s; at batch 3 the two routes measured equal there,
-// and the row-wave launches 11% faster on the 1B model).
+// beyond their LDS budget): one token per sequence on the matrix cores (the K-sliced GEMV
+// kernels leave most of the HBM bandwidth unused at those batches), through the skinny
+// projections up to 32 sequences (a ladder layer in four launches, decode_layer_skinny;
+// standard layers module by module) and the tiled GEMMs beyond, with the split-KV decode
+// attention, then the LM head with the final RMSNorm folded in and a row argmax.  Every
+// kernel of the route takes the position from the device (the prologue's pos_dev), so it
+// is replayed as a graph too.  Batches 3 and 4 also take it where the row-wave launches
+// would hold one workgroup per CU (the 70B shard at batch 3: 498 against 335 tok/s; the 1B
+// model at batch 3: 2290 against 2065).
 bool gemm_decode(const ladder_ctx* ctx, int B) {
   const int kmax = std::max(ctx->cfg.hidden, std::max(ctx->cfg.ffn, ctx->qrows));
   if (ctx->wdt != W_BF16) return false;
-  return !gemv_rw_supported(ctx->wdt, kmax, B) || (B >= 4 && !gemv_rw_two_per_cu(ctx->wdt, kmax, B));
+  return !gemv_rw_supported(ctx->wdt, kmax, B) || (B >= 3 && !gemv_rw_two_per_cu(ctx->wdt, kmax, B));
+}
+
+// The skinny parameters of a decode step's projections on the matrix cores, as the
+// module path (prefill_module with the RMSNorm folded in) builds them.
+GemmParams skinny_base(const ladder_ctx* ctx, int B, const StreamScratch& sc) {
+  GemmParams p{};
+  p.wdtype = ctx->wdt;
+  p.M = B;
+  p.ws = sc.gk;
+  p.ws_floats = kGemmSplitWsFloats;
+  p.cnt = sc.skcnt;
+  return p;
+}
+
+// A ladder layer (or parallel block) of a decode step on the matrix cores in four launches:
+// [QKV | gate/up] (both RMSNorms folded in; by the ladder rule both inputs exist when the
+// layer starts), RoPE + KV append, the split-KV attention, and [O + down] with both
+// residual adds, x_{2l+1} = x_{2l} + o and x_{2l+2} = x_{2l+1} + d.  Each projection is
+// sliced as in its own launch, so the layer gives the module path's bits.  qg: the
+// [QKV | gate/up] pair (the second with the workspace and tickets after the first's);
+// od: [O + down] over the attention and SwiGLU outputs.
+void skinny_layer_params(const ladder_ctx* ctx, int l, int B, GemmParams qg[2], GemmParams* od) {
+  const ladder_config& g = ctx->cfg;
+  const ladder_layer_weights& L = ctx->layers[l];
+  const StreamScratch& sc = ctx->sc[0];
+  float* const* X = ctx->dx;
+  const int nqkv = ctx->qrows + 2 * ctx->kvrows;
+  GemmParams& a = qg[0];
+  GemmParams& b = qg[1];
+  a = skinny_base(ctx, B, sc);
+  b = a;
+  *od = a;
+  a.A = X[module_src(ctx, 2 * l) % 2];
+  a.lda = g.hidden;
+  a.gain = L.attn_norm;
+  a.eps = g.norm_eps;
+  a.rows = RowSrc{{L.wq, L.wk, L.wv}, ctx->qrows, ctx->qrows + ctx->kvrows, 0};
+  a.N = nqkv;
+  a.K = g.hidden;
+  a.C = sc.qkv;
+  a.ldc = nqkv;
+  b.A = X[module_src(ctx, 2 * l + 1) % 2];
+  b.lda = g.hidden;
+  b.gain = L.mlp_norm;
+  b.eps = g.norm_eps;
+  b.rows = RowSrc{{L.w_gate, L.w_up, nullptr}, 0, 0, 1};
+  b.N = 2 * g.ffn;
+  b.K = g.hidden;
+  b.swiglu = 1;
+  b.C = sc.ab;
+  b.ldc = g.ffn;
+  const size_t na = align_up(skinny_ws_floats(a), 64);
+  b.ws = sc.gk + std::min(na, kGemmSplitWsFloats);
+  b.ws_floats = kGemmSplitWsFloats - std::min(na, kGemmSplitWsFloats);
+  b.cnt = sc.skcnt + (nqkv + 127) / 128;
+  GemmParams& o = *od;
+  o.A = sc.ob;
+  o.lda = ctx->qrows;
+  o.rows = RowSrc{{L.wo, nullptr, nullptr}, g.hidden, g.hidden, 0};
+  o.N = g.hidden;
+  o.K = ctx->qrows;
+  o.res = X[(2 * l) % 2];
+  o.ldr = g.hidden;
+  o.C = X[(2 * l + 1) % 2];
+  o.ldc = g.hidden;
+  o.A2 = sc.ab;
+  o.lda2 = g.ffn;
+  o.rows2 = RowSrc{{L.w_down, nullptr, nullptr}, g.hidden, g.hidden, 0};
+  o.K2 = g.ffn;
+  o.C2 = X[(2 * l + 2) % 2];
+}
+
+bool skinny_layer_ok(const ladder_ctx* ctx, int B) {
+  const StreamScratch& sc = ctx->sc[0];
+  if (ctx->wdt != W_BF16 || !sc.gk || !sc.skcnt) return false;
+  GemmParams qg[2], od;
+  skinny_layer_params(ctx, 0, B, qg, &od);
+  const int tiles = (qg[0].N + 127) / 128 + (qg[1].N + 127) / 128;
+  return tiles <= kSkinnyMaxTiles && skinny_pair_supported(qg[0], qg[1]) && skinny_supported(od);
+}
+
+ladder_status decode_layer_skinny(ladder_ctx* ctx, int l, int B, hipStream_t s) {
+  const ladder_config& g = ctx->cfg;
+  StreamScratch& sc = ctx->sc[0];
+  GemmParams qg[2], od;
+  skinny_layer_params(ctx, l, B, qg, &od);
+  TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
+  HIPCHK(launch_skinny_pair(qg[0], qg[1], s));
+  TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
+  HIPCHK(launch_rope_kv(ctx->wdt, sc.qkv, B, 1, 0, ctx->pos_dev, g.n_q_heads, g.n_kv_heads, g.head_dim, ctx->rope_cos,
+                        ctx->rope_sin, sc.qr, layer_k(ctx, l), layer_v(ctx, l), g.max_seq, s));
+  AttnDecodeParams at = attn_params(ctx, l, B, sc);
+  at.n_split = std::max(1, std::min(at.n_split, 256 / (B * g.n_kv_heads)));
+  at.q = sc.qr;
+  at.out = sc.ob;
+  HIPCHK(launch_attn_decode(at, s));
+  TRACE(LADDER_KERNEL_DOWN_OPROJ, s, false);
+  HIPCHK(launch_skinny(od, s));
+  TRACE(LADDER_KERNEL_DOWN_OPROJ, s, true);
+  return LADDER_OK;
 }
 
 ladder_status enqueue_decode_gemm(ladder_ctx* ctx, int B) {
@@ -1039,7 +1153,21 @@ ladder_status enqueue_decode_gemm(ladder_ctx* ctx, int B) {
   auto mod = [&](int m, const float* xin, const float* xm, float* xn, float* store, hipStream_t s, bool wait,
                  hipEvent_t ev) { return prefill_module(ctx, m, B, 1, pos, xin, xm, xn, store, s, wait, ev); };
   ctx->gemm_step = true;
-  ladder_status st = run_modules(ctx, ctx->dx, ctx->dout, (size_t)B * g.hidden, mod, fused);
+  ladder_status st = LADDER_OK;
+  if (fused && skinny_layer_ok(ctx, B)) {
+    // ladder and parallel layers in four launches each, standard layers module by module
+    float* const* X = ctx->dx;
+    for (int l = 0; l < g.n_layers && !st; ++l) {
+      if (ctx->mask[l]) {
+        st = decode_layer_skinny(ctx, l, B, ctx->s0);
+      } else {
+        for (int m = 2 * l; m < 2 * l + 2 && !st; ++m)
+          st = mod(m, X[module_src(ctx, m) % 2], X[m % 2], X[(m + 1) % 2], nullptr, ctx->s0, false, nullptr);
+      }
+    }
+  } else {
+    st = run_modules(ctx, ctx->dx, ctx->dout, (size_t)B * g.hidden, mod, fused);
+  }
   ctx->gemm_step = false;
   ctx->sched = saved;
   if (st) return st;
