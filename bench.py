@@ -35,7 +35,9 @@ DOMINANT = {
               ("stream.hip", "gemv_rw.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
     # FUSED without the bf16 two-launch layers, and the schedule with the attention in the
     # down projection's launch: the [QKV | gate/up] launch
-    "fused3": ("qkv_gateup", "fused ladder launch [RMSNorm+QKV+RoPE+KV | RMSNorm+gate/up+SwiGLU]",
+    "fused3": ("qkv_gateup", "fused ladder launch [RMSNorm+QKV | RMSNorm+gate/up+SwiGLU]: the row-wave launch "
+               "(RoPE+KV in its epilogue) or, at batches on the matrix cores, the skinny weight-streaming "
+               "launch (skinny.hip)",
                "traffic_qkv_gateup_70b_b1.json",
                ("gemv_rw.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
     "persistent": ("layer_stack", "persistent decode launch of the whole layer stack (every projection, "
@@ -80,7 +82,8 @@ def prefill_flops(cfg, B, T):
 def qkv_gateup_bytes(cfg, B):
     """Algorithmic bytes of one fused [QKV | gate/up] launch: both weight blocks and norm
     gains once, the two input residual rows, q and the SwiGLU output written, one K and
-    one V row appended per kv head."""
+    one V row appended per kv head (the skinny launch writes the K and V rows in fp32 for
+    the RoPE kernel instead; the weights are 99.9% of either count)."""
     esz = 2 if cfg.dtype == "bf16" else 4
     H, F, hd = cfg.hidden, cfg.ffn, cfg.head_dim
     q, kv = cfg.n_q_heads * hd, cfg.n_kv_heads * hd

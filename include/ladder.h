@@ -266,7 +266,9 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 
 /* Profiling aid.  For each kernel kind, enqueue it on the context's stream exactly as
  * a decode step at batch B launches it (once per layer; the LM head once), once untimed
- * and then reps times (the GEMV kinds at B <= 16 only; -1 beyond),
+ * and then reps times (the GEMV kinds at B <= 16 only; -1 beyond; at a batch that runs on
+ * the matrix cores only the kinds such a step launches: QKV_GATEUP and DOWN_OPROJ as its
+ * [QKV | gate/up] and [O + down] launches, ATTN, LMHEAD and SAMPLE, -1 for the others),
  * (the fused kinds use each layer as if it were a ladder layer),
  * between two HIP events, and store the mean duration of one launch in microseconds
  * in us_out[kind] (host array of LADDER_N_KERNELS floats).  Works on the context's

@@ -940,38 +940,15 @@ SampleParams sample_params(const ladder_ctx* ctx, int B, const int* d_pos, int p
 
 bool gemm_decode(const ladder_ctx* ctx, int B);
 
+ladder_status lm_head_mc(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream_t s);
+
 // Final RMSNorm + LM head + greedy token; with sampling on, the draw then overwrites the
 // token (the logits are the same either way).  Batches the row-wave GEMV cannot take (bf16)
-// run the LM head on the matrix cores: RMSNorm, GEMM, row argmax.
+// run the LM head on the matrix cores (lm_head_mc).
 ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream_t s, const int* d_pos, int pos) {
-  const ladder_config& g = ctx->cfg;
   if (gemm_decode(ctx, B)) {
-    StreamScratch& sc = ctx->sc[0];
-    GemmParams hp{};
-    hp.wdtype = ctx->wdt;
-    // the final RMSNorm folded into the skinny launch where it takes the LM head (A = the
-    // raw rows), else its own kernel
-    hp.A = x;
-    hp.lda = ldx;
-    hp.rows = RowSrc{{ctx->w.lm_head, nullptr, nullptr}, g.vocab, g.vocab, 0};
-    hp.M = B;
-    hp.N = g.vocab;
-    hp.K = g.hidden;
-    hp.C = ctx->logits;
-    hp.ldc = g.vocab;
-    hp.ws = sc.gk;
-    hp.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
-    hp.cnt = sc.skcnt;
-    hp.gain = ctx->w.final_norm;
-    hp.eps = g.norm_eps;
-    if (!skinny_supported(hp)) {
-      HIPCHK(launch_rmsnorm(ctx->wdt, x, ldx, ctx->w.final_norm, g.norm_eps, B, g.hidden, sc.u, s));
-      hp.A = sc.u;
-      hp.lda = g.hidden;
-      hp.gain = nullptr;
-    }
-    HIPCHK(launch_gemm(hp, s));
-    HIPCHK(launch_argmax_rows(ctx->logits, B, g.vocab, g.vocab, ctx->next, s));
+    ladder_status st = lm_head_mc(ctx, x, ldx, B, s);
+    if (st) return st;
   } else {
     ladder_status st = run_gemv(ctx, lmhead_params(ctx, x, ldx, B), s);
     if (st) return st;
@@ -981,6 +958,39 @@ ladder_status lm_head(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream
     HIPCHK(launch_sample(sample_params(ctx, B, d_pos, pos), s));
     TRACE(LADDER_KERNEL_SAMPLE, s, true);
   }
+  return LADDER_OK;
+}
+
+// The LM head of the matrix-core route: the GEMM (the final RMSNorm folded into the skinny
+// launch where it takes the LM head, A = the raw rows, else its own kernel) and a row argmax.
+ladder_status lm_head_mc(ladder_ctx* ctx, const float* x, int ldx, int B, hipStream_t s) {
+  const ladder_config& g = ctx->cfg;
+  StreamScratch& sc = ctx->sc[0];
+  GemmParams hp{};
+  hp.wdtype = ctx->wdt;
+  // the final RMSNorm folded into the skinny launch where it takes the LM head (A = the
+  // raw rows), else its own kernel
+  hp.A = x;
+  hp.lda = ldx;
+  hp.rows = RowSrc{{ctx->w.lm_head, nullptr, nullptr}, g.vocab, g.vocab, 0};
+  hp.M = B;
+  hp.N = g.vocab;
+  hp.K = g.hidden;
+  hp.C = ctx->logits;
+  hp.ldc = g.vocab;
+  hp.ws = sc.gk;
+  hp.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
+  hp.cnt = sc.skcnt;
+  hp.gain = ctx->w.final_norm;
+  hp.eps = g.norm_eps;
+  if (!skinny_supported(hp)) {
+    HIPCHK(launch_rmsnorm(ctx->wdt, x, ldx, ctx->w.final_norm, g.norm_eps, B, g.hidden, sc.u, s));
+    hp.A = sc.u;
+    hp.lda = g.hidden;
+    hp.gain = nullptr;
+  }
+  HIPCHK(launch_gemm(hp, s));
+  HIPCHK(launch_argmax_rows(ctx->logits, B, g.vocab, g.vocab, ctx->next, s));
   return LADDER_OK;
 }
 
@@ -1491,16 +1501,45 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
   const bool two = two_launch_layers(ctx, B);
   const bool seq = seq_layers(ctx, B);
   const bool gemv_ok = B <= 16;        // the per-kind GEMV launches take at most 16 rows
+  // a batch on the matrix cores: the kinds its step launches (the skinny [QKV | gate/up]
+  // and [O + down] launches of a ladder layer, the attention, the LM head, the draw)
+  const bool mc = gemm_decode(ctx, B);
+  const bool mc_layers = mc && skinny_layer_ok(ctx, B);
   for (int kind = 0; kind < LADDER_N_KERNELS; ++kind) {
     int launches = 0;
     HIPCHK(hipEventRecord(e0, s));   // (re-recorded after the warm-up; kept for kinds that are unavailable)
     // repetition -1 is an untimed warm-up (a kernel's first launch in a process also loads
     // its code)
     for (int r = -1; r < reps; ++r) {
-      if (!gemv_ok && kind != LADDER_KERNEL_SAMPLE) break;
+      if (!gemv_ok && !mc && kind != LADDER_KERNEL_SAMPLE) break;
       if (r == 0) {
         launches = 0;
         HIPCHK(hipEventRecord(e0, s));
+      }
+      if (mc && kind != LADDER_KERNEL_SAMPLE) {
+        if (kind == LADDER_KERNEL_LMHEAD) {
+          if ((st = lm_head_mc(ctx, ctx->dx[0], g.hidden, B, s))) return st;
+          ++launches;
+          continue;
+        }
+        const bool ok = kind == LADDER_KERNEL_ATTN ||
+                        (mc_layers && (kind == LADDER_KERNEL_QKV_GATEUP || kind == LADDER_KERNEL_DOWN_OPROJ));
+        if (!ok) break;
+        for (int l = 0; l < g.n_layers; ++l, ++launches) {
+          if (kind == LADDER_KERNEL_ATTN) {
+            AttnDecodeParams at = attn_params(ctx, l, B, sc);
+            at.n_split = std::max(1, std::min(at.n_split, 256 / (B * g.n_kv_heads)));
+            at.q = sc.qr;
+            at.out = sc.ob;
+            HIPCHK(launch_attn_decode(at, s));
+            continue;
+          }
+          GemmParams qg[2], od;
+          skinny_layer_params(ctx, l, B, qg, &od);
+          if (kind == LADDER_KERNEL_QKV_GATEUP) HIPCHK(launch_skinny_pair(qg[0], qg[1], s));
+          else HIPCHK(launch_skinny(od, s));
+        }
+        continue;
       }
       if (kind == LADDER_KERNEL_QKV_ATTN_GATEUP || kind == LADDER_KERNEL_DOWN_OPROJ) {
         if (!seq) break;
