@@ -49,7 +49,13 @@ __device__ __forceinline__ const WT* gemm_row(const RowSrc& s, int r, int K) {
   return (const WT*)s.m[2] + (size_t)(r - s.n1) * K;
 }
 
-constexpr int BK = 32, LDK = BK + 8;
+constexpr int BK = 32;
+// LDS operand tiles hold rows of BK = 32 bf16 (four 16-byte chunks) without padding; chunk c
+// of row r sits at position c ^ ((r / 4) % 4).  Then a pass of 16-byte or 8-byte staging
+// writes (4 rows of 64 bytes) and a pass of 16-byte MFMA operand reads (16 rows, one chunk
+// each) both cover every bank once; with rows padded to 40 bf16 the writes conflicted
+// 2-way (half of the LDS cycles of the prefill GEMMs were bank conflicts).
+__device__ __forceinline__ int gsw(int r, int chunk) { return 8 * (chunk ^ ((r >> 2) & 3)); }
 constexpr int kXcds = 8;
 constexpr int kStages = 4;   // K steps whose global loads are in flight (even: LDS buffers alternate)
 
@@ -64,9 +70,9 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(GemmParams p, int n_ti
   constexpr int AV = TM * BK / 4 / 256;           // float4 of A per thread per K step
   constexpr int BV = TN * BK / 8 / 256;           // 16-byte W chunks per thread per K step
   static_assert(AV >= 1 && BV >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t Ah[2][TM][LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Al[2][TM][LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TN][LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Ah[2][TM][BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Al[2][TM][BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TN][BK];
   const int tile = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (tile >= n_tiles) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -134,11 +140,12 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(GemmParams p, int n_ti
       uint32_t h0, l0, h1, l1;
       split_bf2(ra[st][i].x, ra[st][i].y, h0, l0);
       split_bf2(ra[st][i].z, ra[st][i].w, h1, l1);
-      *(uint2*)&Ah[buf][ar[i]][ac[i]] = make_uint2(h0, h1);
-      *(uint2*)&Al[buf][ar[i]][ac[i]] = make_uint2(l0, l1);
+      const int ak = gsw(ar[i], ac[i] >> 3) + (ac[i] & 7);
+      *(uint2*)&Ah[buf][ar[i]][ak] = make_uint2(h0, h1);
+      *(uint2*)&Al[buf][ar[i]][ak] = make_uint2(l0, l1);
     }
 #pragma unroll
-    for (int i = 0; i < BV; ++i) *(uint4*)&Bs[buf][br[i]][bc[i]] = rb[st][i];
+    for (int i = 0; i < BV; ++i) *(uint4*)&Bs[buf][br[i]][gsw(br[i], bc[i] >> 3)] = rb[st][i];
   };
 
   f32x4 acc[FM][FN];
@@ -170,11 +177,15 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(GemmParams p, int n_ti
         bf16x8 ah[FM], al[FM], b[FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          ah[i] = *(const bf16x8*)&Ah[cur][wm * (TM / 2) + i * 16 + fr][fk];
-          al[i] = *(const bf16x8*)&Al[cur][wm * (TM / 2) + i * 16 + fr][fk];
+          const int r = wm * (TM / 2) + i * 16 + fr;
+          ah[i] = *(const bf16x8*)&Ah[cur][r][gsw(r, fk >> 3)];
+          al[i] = *(const bf16x8*)&Al[cur][r][gsw(r, fk >> 3)];
         }
 #pragma unroll
-        for (int j = 0; j < FN; ++j) b[j] = *(const bf16x8*)&Bs[cur][wn * (TN / 2) + j * 16 + fr][fk];
+        for (int j = 0; j < FN; ++j) {
+          const int r = wn * (TN / 2) + j * 16 + fr;
+          b[j] = *(const bf16x8*)&Bs[cur][r][gsw(r, fk >> 3)];
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
