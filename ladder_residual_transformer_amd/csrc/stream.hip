@@ -383,8 +383,12 @@ __global__ __launch_bounds__(256) void stream_front_kernel(MultiGemvParams mp) {
       rs = gbl(pq.rope_sin)[(size_t)pos * half + (d >> 1)];
     }
   }
+  // The inputs go out before any weight load: issued behind the first weight units of
+  // every workgroup they would wait in the same memory queues for most of their drain.
   SStageRegs st;
   sstage_issue(pq.x, pq.gain, K, st);
+  sstage_finish(st, pq.gain, K, lds_raw, 0, sh.sqw[0]);
+  sstage_issue(pg.x, pg.gain, K, st);             // the gate/up input, ahead of the first units
   SRing<NB> R;
   if (wid == 0) {
 #pragma unroll
@@ -393,8 +397,6 @@ __global__ __launch_bounds__(256) void stream_front_kernel(MultiGemvParams mp) {
 #pragma unroll
     for (int d = 0; d < NB; ++d) sload_pos<UI3, UI4>(A, nua, Bp, nub, true, d, wid, lane, R.w[d]);
   }
-  sstage_finish(st, pq.gain, K, lds_raw, 0, sh.sqw[0]);
-  sstage_issue(pg.x, pg.gain, K, st);             // the gate/up input, behind the first units
   __syncthreads();
   const float inv_a = sinv(sh.sqw[0], K, pq.eps, pq.gain != nullptr);
 
@@ -441,43 +443,71 @@ __global__ __launch_bounds__(256) void stream_front_kernel(MultiGemvParams mp) {
 // Merge of the attention's chunk records (written by the front launch, B = 1) into the
 // attention output rows [nq * HD] at LDS offset uoff (zero pad of 8), with the arithmetic
 // of attn_merge: per head the chunk maxima, weights e^(m_s - M) and the sum of l_s w_s in
-// chunk order, then o = sum_s acc_s w_s in chunk order, times 1 / sum.  Every thread's
-// record loads are issued before any of them is used.
+// chunk order, then o = sum_s acc_s w_s in chunk order, times 1 / sum.  In two parts: the
+// record loads of the first 256 output quads (every output of up to 8 heads of 128 or 16
+// of 64) are issued with the launch's input, before any weight load, and used after the
+// first weight units are in flight; further quads load their records where they merge.
+constexpr int kMergeMl = kMergeHeads * kMergeChunks / 256;   // (m, l) pairs per thread
+
+struct MergeRegs {
+  float m[kMergeMl], l[kMergeMl];
+  float4 a[kMergeChunks];
+};
+
 template <int HD>
-__device__ __forceinline__ void merge_into_lds(const AttnDecodeParams& at, int n_act, char* lds, int uoff,
-                                               float* wsc /* [nq][kMergeChunks] */, float* lsc, float* linv) {
+__device__ __forceinline__ void merge_issue(const AttnDecodeParams& at, int n_act, MergeRegs& r) {
+  const int tid = threadIdx.x;
+  const size_t stride = attn_rec<HD>();
+  const int nrec = at.nq * n_act;
+#pragma unroll
+  for (int j = 0; j < kMergeMl; ++j) {
+    const int i = min(tid + 256 * j, nrec - 1), h = i / n_act, q = i % n_act;
+    const float* rec = at.part + ((size_t)h * at.n_split + q) * stride;
+    r.m[j] = gbl(rec)[0];
+    r.l[j] = gbl(rec)[1];
+  }
+  const int i = min(tid, at.nq * (HD / 4) - 1), h = i / (HD / 4), d4 = (i % (HD / 4)) * 4;
+  const float* src = at.part + (size_t)h * at.n_split * stride + 4 + d4;
+#pragma unroll
+  for (int q = 0; q < kMergeChunks; ++q) r.a[q] = ldg4(src + (size_t)min(q, n_act - 1) * stride);
+}
+
+template <int HD>
+__device__ __forceinline__ void merge_finish(const AttnDecodeParams& at, int n_act, MergeRegs& r, char* lds, int uoff,
+                                             float* wsc /* [nq][kMergeChunks] */, float* lsc, float* linv) {
   constexpr int QG = kMergeChunks;
   const int tid = threadIdx.x;
   const size_t stride = attn_rec<HD>();
-  const int n_items = at.nq * (HD / 4);
+  const int n_items = at.nq * (HD / 4), nrec = at.nq * n_act;
   float* u = reinterpret_cast<float*>(lds + uoff);
   if (tid < kSVec) u[at.nq * HD + tid] = 0.f;
-  for (int i = tid; i < at.nq * n_act; i += 256) {
-    const int h = i / n_act, q = i % n_act;
-    const float* rec = at.part + ((size_t)h * at.n_split + q) * stride;
-    wsc[h * QG + q] = gbl(rec)[0];
-    lsc[h * QG + q] = gbl(rec)[1];
+#pragma unroll
+  for (int j = 0; j < kMergeMl; ++j) {
+    const int i = tid + 256 * j;
+    if (i < nrec) {
+      wsc[(i / n_act) * QG + i % n_act] = r.m[j];
+      lsc[(i / n_act) * QG + i % n_act] = r.l[j];
+    }
   }
+  __syncthreads();
+  if (tid < at.nq) {
+    float M = -INFINITY;
+    for (int q = 0; q < n_act; ++q) M = fmaxf(M, wsc[tid * QG + q]);
+    float Ls = 0.f;
+    for (int q = 0; q < n_act; ++q) {
+      const float w = expf(wsc[tid * QG + q] - M);
+      wsc[tid * QG + q] = w;
+      Ls = fmaf(lsc[tid * QG + q], w, Ls);
+    }
+    linv[tid] = 1.0f / Ls;
+  }
+  __syncthreads();
   for (int i0 = 0; i0 < n_items; i0 += 256) {
     const int i = min(i0 + tid, n_items - 1), h = i / (HD / 4), d4 = (i % (HD / 4)) * 4;
-    const float* src = at.part + (size_t)h * at.n_split * stride + 4 + d4;
-    float4 a[QG];
+    if (i0 > 0) {
+      const float* src = at.part + (size_t)h * at.n_split * stride + 4 + d4;
 #pragma unroll
-    for (int q = 0; q < QG; ++q) a[q] = ldg4(src + (size_t)min(q, n_act - 1) * stride);
-    if (i0 == 0) {
-      __syncthreads();
-      if (tid < at.nq) {
-        float M = -INFINITY;
-        for (int q = 0; q < n_act; ++q) M = fmaxf(M, wsc[tid * QG + q]);
-        float Ls = 0.f;
-        for (int q = 0; q < n_act; ++q) {
-          const float w = expf(wsc[tid * QG + q] - M);
-          wsc[tid * QG + q] = w;
-          Ls = fmaf(lsc[tid * QG + q], w, Ls);
-        }
-        linv[tid] = 1.0f / Ls;
-      }
-      __syncthreads();
+      for (int q = 0; q < QG; ++q) r.a[q] = ldg4(src + (size_t)min(q, n_act - 1) * stride);
     }
     if (i0 + tid < n_items) {
       float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -485,10 +515,10 @@ __device__ __forceinline__ void merge_into_lds(const AttnDecodeParams& at, int n
       for (int q = 0; q < QG; ++q) {
         if (q < n_act) {
           const float w = wsc[h * QG + q];
-          o.x = fmaf(a[q].x, w, o.x);
-          o.y = fmaf(a[q].y, w, o.y);
-          o.z = fmaf(a[q].z, w, o.z);
-          o.w = fmaf(a[q].w, w, o.w);
+          o.x = fmaf(r.a[q].x, w, o.x);
+          o.y = fmaf(r.a[q].y, w, o.y);
+          o.z = fmaf(r.a[q].z, w, o.z);
+          o.w = fmaf(r.a[q].w, w, o.w);
         }
       }
       const float li = linv[h];
@@ -498,9 +528,10 @@ __device__ __forceinline__ void merge_into_lds(const AttnDecodeParams& at, int n
 }
 
 // prob[0] = down (no norm), prob[1] = O (no norm, EPI_ADD2: out = xres + o, out2 = out + d)
-// over the same row pairs.  Every workgroup streams its down units with its first O units
-// behind them, then merges the attention's chunk records (front launch) into its O input
-// and streams the O units; one epilogue for both.
+// over the same row pairs.  Every workgroup loads its input and the attention's chunk
+// records (front launch) first, issues its first down units, merges the records into its
+// O input while those loads are in flight, then streams its down units with its O units
+// behind them in the same ring; one epilogue for both.
 template <int HD, int NB>
 __global__ __launch_bounds__(256) void stream_back_kernel(MultiGemvParams mp) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
@@ -519,16 +550,18 @@ __global__ __launch_bounds__(256) void stream_back_kernel(MultiGemvParams mp) {
   const int nud = UI4::count(D.nunits, wid), nuo = UI4::count(O.nunits, wid);
   const int n_act = attn_active_chunks(mp.attn);
 
+  // the input and the records before the weights (front launch)
   SStageRegs st;
   sstage_issue(pd.x, nullptr, pd.K, st);
+  MergeRegs mr;
+  merge_issue<HD>(mp.attn, n_act, mr);
+  sstage_finish(st, nullptr, pd.K, lds_raw, D.uoff, sh.sqw[0]);
   SRing<NB> R;
 #pragma unroll
   for (int d = 0; d < NB; ++d) sload_pos<UI4, UI4>(D, nud, O, nuo, true, d, wid, lane, R.w[d]);
-  sstage_finish(st, nullptr, pd.K, lds_raw, D.uoff, sh.sqw[0]);
+  merge_finish<HD>(mp.attn, n_act, mr, lds_raw, O.uoff, m_wsc, m_lsc, m_linv);
   __syncthreads();
   sstream<NB, UI4, UI4>(D, nud, O, nuo, true, R, wid, lane, lds_raw);
-  merge_into_lds<HD>(mp.attn, n_act, lds_raw, O.uoff, m_wsc, m_lsc, m_linv);
-  __syncthreads();
   srotate<NB>(R, nud % NB);
   sstream<NB, UI4, UI4>(O, nuo, O, 0, false, R, wid, lane, lds_raw);
   __syncthreads();
