@@ -254,6 +254,14 @@ struct GemmParams {
   RowSrc rows2;
   int K2;
   float* C2;
+  // RoPE + KV append in the epilogue of a decode step's QKV projection (skinny launches
+  // only; rope_q nullable: none).  Row m is sequence m at position *d_pos; output columns
+  // [0, nq*hd) are q, then nkv*hd of k, then nkv*hd of v.  q is rotated into rope_q
+  // [M][nq*hd], k rotated and v as they are go to the bf16 caches [M][nkv][max_seq][hd] at
+  // that position (rope_kv's arithmetic and rounding); C is not written.
+  float* rope_q; void* k_cache; void* v_cache;
+  const float* rope_cos; const float* rope_sin; const int* d_pos;
+  int nq, nkv, hd, max_seq;
 };
 constexpr size_t kGemmSplitWsFloats = (size_t)512 * 128 * 128;
 constexpr int kSkinnyMaxTiles = 2048;

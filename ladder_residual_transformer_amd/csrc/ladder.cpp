@@ -1065,13 +1065,14 @@ GemmParams skinny_base(const ladder_ctx* ctx, int B, const StreamScratch& sc) {
   return p;
 }
 
-// A ladder layer (or parallel block) of a decode step on the matrix cores in four launches:
-// [QKV | gate/up] (both RMSNorms folded in; by the ladder rule both inputs exist when the
-// layer starts), RoPE + KV append, the split-KV attention, and [O + down] with both
-// residual adds, x_{2l+1} = x_{2l} + o and x_{2l+2} = x_{2l+1} + d.  Each projection is
-// sliced as in its own launch, so the layer gives the module path's bits.  qg: the
-// [QKV | gate/up] pair (the second with the workspace and tickets after the first's);
-// od: [O + down] over the attention and SwiGLU outputs.
+// A ladder layer (or parallel block) of a decode step on the matrix cores in three launches:
+// [QKV with RoPE + KV append in its epilogue | gate/up] (both RMSNorms folded in; by the
+// ladder rule both inputs exist when the layer starts), the split-KV attention, and
+// [O + down] with both residual adds, x_{2l+1} = x_{2l} + o and x_{2l+2} = x_{2l+1} + d.
+// Each projection is sliced as in its own launch and the epilogue repeats rope_kv's
+// arithmetic, so the layer gives the module path's bits.  qg: the [QKV | gate/up] pair (the
+// second with the workspace and tickets after the first's); od: [O + down] over the
+// attention and SwiGLU outputs.
 void skinny_layer_params(const ladder_ctx* ctx, int l, int B, GemmParams qg[2], GemmParams* od) {
   const ladder_config& g = ctx->cfg;
   const ladder_layer_weights& L = ctx->layers[l];
@@ -1092,6 +1093,17 @@ void skinny_layer_params(const ladder_ctx* ctx, int l, int B, GemmParams qg[2], 
   a.K = g.hidden;
   a.C = sc.qkv;
   a.ldc = nqkv;
+  // RoPE + KV append in the QKV epilogue (rope_kv's arithmetic): q into sc.qr
+  a.rope_q = sc.qr;
+  a.k_cache = layer_k(ctx, l);
+  a.v_cache = layer_v(ctx, l);
+  a.rope_cos = ctx->rope_cos;
+  a.rope_sin = ctx->rope_sin;
+  a.d_pos = ctx->pos_dev;
+  a.nq = g.n_q_heads;
+  a.nkv = g.n_kv_heads;
+  a.hd = g.head_dim;
+  a.max_seq = g.max_seq;
   b.A = X[module_src(ctx, 2 * l + 1) % 2];
   b.lda = g.hidden;
   b.gain = L.mlp_norm;
@@ -1140,8 +1152,6 @@ ladder_status decode_layer_skinny(ladder_ctx* ctx, int l, int B, hipStream_t s) 
   TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
   HIPCHK(launch_skinny_pair(qg[0], qg[1], s));
   TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
-  HIPCHK(launch_rope_kv(ctx->wdt, sc.qkv, B, 1, 0, ctx->pos_dev, g.n_q_heads, g.n_kv_heads, g.head_dim, ctx->rope_cos,
-                        ctx->rope_sin, sc.qr, layer_k(ctx, l), layer_v(ctx, l), g.max_seq, s));
   AttnDecodeParams at = attn_params(ctx, l, B, sc);
   at.n_split = std::max(1, std::min(at.n_split, 256 / (B * g.n_kv_heads)));
   at.q = sc.qr;

@@ -119,6 +119,7 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(SkArgs args) {
   const int kbeg = (part1 ? slice - S0 : slice) * ks, kend = min(K, kbeg + ks);
   const int nch = (kend - kbeg + C::KC - 1) / C::KC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rpos = p.rope_q ? *gbl(p.d_pos) : 0;   // RoPE epilogue: the position (used at the end)
 
   __shared__ __align__(16) uint16_t xs[2][2][C::ROWS * C::LDX];   // [buffer][hi, lo][row][k]
   __shared__ __align__(16) uint16_t wt[4][16 * C::KC];            // per wave: one 16-row unit
@@ -290,6 +291,8 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(SkArgs args) {
   const int n_base = tile * kSkRows;
   const int n_items = p.M * (kSkRows / 4);
   float4 t[IPT][SM];
+  float4 rcs[IPT];   // RoPE epilogue: cos and sin of the item's two pairs (c0, s0, c1, s1)
+  const int rq = p.nq * p.hd, rk = p.nkv * p.hd;
 #pragma unroll
   for (int jj = 0; jj < IPT; ++jj) {
     const int it = tid + 256 * jj;
@@ -298,6 +301,13 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(SkArgs args) {
 #pragma unroll
     for (int q = 0; q < SM; ++q)
       if (ok && q < S) t[jj][q] = ld_coh16(p.ws + q * plane + (size_t)m * p.N + n);
+    rcs[jj] = make_float4(1.f, 0.f, 1.f, 0.f);
+    if (p.rope_q && ok && n < rq + rk) {
+      const int d = (n < rq ? n : n - rq) % p.hd;
+      const size_t at = (size_t)rpos * (p.hd / 2) + d / 2;
+      const float2 c = *(const float2*)(p.rope_cos + at), sn = *(const float2*)(p.rope_sin + at);
+      rcs[jj] = make_float4(c.x, sn.x, c.y, sn.y);
+    }
   }
   float* red = (float*)&xs[0][0][0];   // the staging buffers are free now
   if constexpr (NORM) {
@@ -335,7 +345,24 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(SkArgs args) {
     }
     const float inv = inv_s[m];
     float4 o = make_float4(v0.x * inv, v0.y * inv, v0.z * inv, v0.w * inv);
-    if (p.swiglu) {
+    if (p.rope_q) {
+      // rope_kv's arithmetic on the same fp32 values: rotate the q and k pairs (d, d + 1),
+      // q to rope_q, k and v rounded to bf16 into the caches
+      if (n < rq + rk) {
+        rope_rot(o.x, o.y, rcs[jj].x, rcs[jj].y);
+        rope_rot(o.z, o.w, rcs[jj].z, rcs[jj].w);
+      }
+      if (n < rq) {
+        *(float4*)(p.rope_q + (size_t)m * rq + n) = o;
+      } else {
+        const bool isk = n < rq + rk;
+        const int r = isk ? n - rq : n - rq - rk, kvh = r / p.hd, d = r % p.hd;
+        uint16_t* cache = (uint16_t*)(isk ? p.k_cache : p.v_cache);
+        *(uint2*)(cache + (((size_t)m * p.nkv + kvh) * p.max_seq + rpos) * p.hd + d) =
+            make_uint2((uint32_t)f32_to_bf16(o.x) | ((uint32_t)f32_to_bf16(o.y) << 16),
+                       (uint32_t)f32_to_bf16(o.z) | ((uint32_t)f32_to_bf16(o.w) << 16));
+      }
+    } else if (p.swiglu) {
       *(float2*)(p.C + (size_t)m * p.ldc + n / 2) = make_float2(silu(o.x) * o.y, silu(o.z) * o.w);
     } else {
       if (p.res) {
@@ -386,6 +413,10 @@ bool sk_ok(const GemmParams& p) {
       (p.res && p.ldr % 4) || (!p.swiglu && p.ldc % 4) || (p.swiglu && (p.ldc % 2 || p.res)))
     return false;
   if (p.A2 && (p.gain || p.swiglu || !p.res || !p.C2 || p.K2 < 64 || p.K2 % 64 || p.lda2 % 4)) return false;
+  if (p.rope_q && (p.swiglu || p.res || p.A2 || !p.k_cache || !p.v_cache || !p.rope_cos || !p.rope_sin || !p.d_pos ||
+                   p.hd < 4 || p.hd % 4 || p.nq < 1 || p.nkv < 1 || p.max_seq < 1 ||
+                   p.N != (p.nq + 2 * p.nkv) * p.hd))
+    return false;
   const SkProb q = sk_prob(p);
   return q.S0 + q.S1 <= sk_max_slices(p.M) && q.nt <= kSkinnyMaxTiles && sk_need(q) <= p.ws_floats;
 }
