@@ -275,6 +275,16 @@ hipError_t launch_skinny(const GemmParams& p, hipStream_t s);
 // workspaces and tickets of their own); each gives the bits of its own launch_skinny.
 bool skinny_pair_supported(const GemmParams& a, const GemmParams& b);
 hipError_t launch_skinny_pair(const GemmParams& a, const GemmParams& b, hipStream_t s);
+// The pair [QKV | gate/up] of a decode step with its split-KV attention in the same launch:
+// a (the QKV projection) carries the RoPE + KV epilogue (rope_q set) and the RMSNorm fold;
+// the attention's q, caches, position and shape are a's; its workgroups wait (bounded; a
+// wait that gives up sets *err) until every QKV tile has published *at.d_epoch *
+// kSeqCodeStride + tag in prog[tile] (prog: one word per QKV tile, holding codes of earlier
+// launches only), then write their records and merge them (tickets at.counters, output
+// at.out); the attention gives the bits of launch_attn_decode with the same n_split.
+bool skinny_pair_attn_supported(const GemmParams& a, const GemmParams& b, const AttnDecodeParams& at);
+hipError_t launch_skinny_pair_attn(const GemmParams& a, const GemmParams& b, const AttnDecodeParams& at,
+                                   uint32_t* prog, int tag, int* err, hipStream_t s);
 // Workspace floats the skinny launch of p takes (partials and sums of squares).
 size_t skinny_ws_floats(const GemmParams& p);
 // K slices launch_gemm uses for p (1: no split).

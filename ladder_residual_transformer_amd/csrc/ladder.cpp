@@ -1065,10 +1065,11 @@ GemmParams skinny_base(const ladder_ctx* ctx, int B, const StreamScratch& sc) {
   return p;
 }
 
-// A ladder layer (or parallel block) of a decode step on the matrix cores in three launches:
-// [QKV with RoPE + KV append in its epilogue | gate/up] (both RMSNorms folded in; by the
-// ladder rule both inputs exist when the layer starts), the split-KV attention, and
-// [O + down] with both residual adds, x_{2l+1} = x_{2l} + o and x_{2l+2} = x_{2l+1} + d.
+// A ladder layer (or parallel block) of a decode step on the matrix cores in two launches:
+// [QKV with RoPE + KV append in its epilogue | split-KV attention once the QKV tiles are
+// done | gate/up] (both RMSNorms folded in; by the ladder rule both inputs exist when the
+// layer starts; a separate attention launch where the shapes do not allow the fused one),
+// and [O + down] with both residual adds, x_{2l+1} = x_{2l} + o and x_{2l+2} = x_{2l+1} + d.
 // Each projection is sliced as in its own launch and the epilogue repeats rope_kv's
 // arithmetic, so the layer gives the module path's bits.  qg: the [QKV | gate/up] pair (the
 // second with the workspace and tickets after the first's); od: [O + down] over the
@@ -1149,14 +1150,20 @@ ladder_status decode_layer_skinny(ladder_ctx* ctx, int l, int B, hipStream_t s) 
   StreamScratch& sc = ctx->sc[0];
   GemmParams qg[2], od;
   skinny_layer_params(ctx, l, B, qg, &od);
-  TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
-  HIPCHK(launch_skinny_pair(qg[0], qg[1], s));
-  TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
   AttnDecodeParams at = attn_params(ctx, l, B, sc);
   at.n_split = std::max(1, std::min(at.n_split, 256 / (B * g.n_kv_heads)));
   at.q = sc.qr;
   at.out = sc.ob;
-  HIPCHK(launch_attn_decode(at, s));
+  TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
+  if (skinny_pair_attn_supported(qg[0], qg[1], at)) {
+    // the attention waits for the QKV tiles inside the same launch, beside the gate/up rows
+    HIPCHK(launch_skinny_pair_attn(qg[0], qg[1], at, ctx->seq_prog, l + 1, ctx->err_word, s));
+    TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
+  } else {
+    HIPCHK(launch_skinny_pair(qg[0], qg[1], s));
+    TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
+    HIPCHK(launch_attn_decode(at, s));
+  }
   TRACE(LADDER_KERNEL_DOWN_OPROJ, s, false);
   HIPCHK(launch_skinny(od, s));
   TRACE(LADDER_KERNEL_DOWN_OPROJ, s, true);
@@ -1546,8 +1553,21 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
           }
           GemmParams qg[2], od;
           skinny_layer_params(ctx, l, B, qg, &od);
-          if (kind == LADDER_KERNEL_QKV_GATEUP) HIPCHK(launch_skinny_pair(qg[0], qg[1], s));
-          else HIPCHK(launch_skinny(od, s));
+          if (kind == LADDER_KERNEL_QKV_GATEUP) {
+            AttnDecodeParams at = attn_params(ctx, l, B, sc);
+            at.n_split = std::max(1, std::min(at.n_split, 256 / (B * g.n_kv_heads)));
+            at.q = sc.qr;
+            at.out = sc.ob;
+            if (skinny_pair_attn_supported(qg[0], qg[1], at)) {
+              // codes as in a decode step: a new epoch per pass over the layers, tag l + 1
+              if (l == 0) HIPCHK(launch_epoch_bump(ctx->epoch, s));
+              HIPCHK(launch_skinny_pair_attn(qg[0], qg[1], at, ctx->seq_prog, l + 1, ctx->err_word, s));
+            } else {
+              HIPCHK(launch_skinny_pair(qg[0], qg[1], s));
+            }
+          } else {
+            HIPCHK(launch_skinny(od, s));
+          }
         }
         continue;
       }

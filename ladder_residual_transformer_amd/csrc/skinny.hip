@@ -27,6 +27,7 @@
 // launch, and the result does not depend on the arrival order.
 #include <type_traits>
 
+#include "attn_decode.hpp"
 #include "common.hpp"
 #include "kernels.h"
 
@@ -92,14 +93,48 @@ struct SkProb {
 struct SkArgs {
   SkProb p[2];
   int items0, items, per_xcd;   // work items of problem 0, of the launch
+  // The decode attention in the launch (HDA != 0): blocks [0, items0) are the QKV items,
+  // blocks [items0, items0 + n_attn) run split-KV attention workgroups, which wait until
+  // every QKV tile's last workgroup has published `code` (epoch * kSeqCodeStride + tag) in
+  // prog[tile] after its coherent q and K/V stores, and the remaining blocks are the
+  // second problem's items, per1 per XCD.
+  AttnDecodeParams at;
+  int n_attn, per1, tag;
+  uint32_t* prog;
+  int* err;
 };
 
 // NORM: RMSNorm folded in (A the raw rows, multiplied by the gain on the way into LDS).
-template <int MT, bool NORM>
+// HDA: head dimension of the attention in the launch (0: none).
+template <int MT, bool NORM, int HDA = 0>
 __global__ __launch_bounds__(256, 2) void skinny_kernel(SkArgs args) {
   using C = Sk<MT>;
-  const int item0 = (int)(blockIdx.x % kSkXcds) * args.per_xcd + (int)(blockIdx.x / kSkXcds);
-  if (item0 >= args.items) return;
+  struct SkL {
+    uint16_t xs[2][2][C::ROWS * C::LDX];   // [buffer][hi, lo][row][k]
+    uint16_t wt[4][16 * C::KC];            // per wave: one 16-row unit
+  };
+  constexpr size_t kAttB = HDA ? sizeof(AttnLds<uint16_t, HDA ? HDA : 64>) : 0;
+  __shared__ __align__(16) char lds_u[sizeof(SkL) > kAttB ? sizeof(SkL) : kAttB];
+  int item0;
+  if constexpr (HDA != 0) {
+    const int bi = (int)blockIdx.x;
+    if (bi < args.items0) {
+      item0 = bi;
+    } else if (bi < args.items0 + args.n_attn) {
+      const uint32_t code = (uint32_t)*gbl(args.at.d_epoch) * kSeqCodeStride + (uint32_t)args.tag;
+      attn_decode_block_mfma<HDA, true>(args.at, bi - args.items0, *reinterpret_cast<AttnLds<uint16_t, HDA>*>(lds_u),
+                                        args.prog, args.p[0].nt, code, args.err);
+      return;
+    } else {
+      const int li = bi - args.items0 - args.n_attn;
+      const int it = (li % kSkXcds) * args.per1 + li / kSkXcds;
+      if (it >= args.items - args.items0) return;
+      item0 = args.items0 + it;
+    }
+  } else {
+    item0 = (int)(blockIdx.x % kSkXcds) * args.per_xcd + (int)(blockIdx.x / kSkXcds);
+    if (item0 >= args.items) return;
+  }
   const bool second = item0 >= args.items0;
   const SkProb& P = second ? args.p[1] : args.p[0];
   const GemmParams& p = P.g;
@@ -120,9 +155,11 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(SkArgs args) {
   const int nch = (kend - kbeg + C::KC - 1) / C::KC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rpos = p.rope_q ? *gbl(p.d_pos) : 0;   // RoPE epilogue: the position (used at the end)
+  // attention in the launch: the code the QKV tiles publish
+  const uint32_t pcode = HDA != 0 && p.rope_q ? (uint32_t)*gbl(args.at.d_epoch) * kSeqCodeStride + (uint32_t)args.tag : 0u;
 
-  __shared__ __align__(16) uint16_t xs[2][2][C::ROWS * C::LDX];   // [buffer][hi, lo][row][k]
-  __shared__ __align__(16) uint16_t wt[4][16 * C::KC];            // per wave: one 16-row unit
+  auto& xs = reinterpret_cast<SkL*>(lds_u)->xs;
+  auto& wt = reinterpret_cast<SkL*>(lds_u)->wt;
   __shared__ float inv_s[kSkMaxM];
   __shared__ int last_s;
 
@@ -352,15 +389,22 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(SkArgs args) {
         rope_rot(o.x, o.y, rcs[jj].x, rcs[jj].y);
         rope_rot(o.z, o.w, rcs[jj].z, rcs[jj].w);
       }
+      // with the attention in the launch its readers are other workgroups: coherent stores
       if (n < rq) {
-        *(float4*)(p.rope_q + (size_t)m * rq + n) = o;
+        float* dq = p.rope_q + (size_t)m * rq + n;
+        if constexpr (HDA != 0) st_coh16(dq, o);
+        else *(float4*)dq = o;
       } else {
         const bool isk = n < rq + rk;
         const int r = isk ? n - rq : n - rq - rk, kvh = r / p.hd, d = r % p.hd;
         uint16_t* cache = (uint16_t*)(isk ? p.k_cache : p.v_cache);
-        *(uint2*)(cache + (((size_t)m * p.nkv + kvh) * p.max_seq + rpos) * p.hd + d) =
-            make_uint2((uint32_t)f32_to_bf16(o.x) | ((uint32_t)f32_to_bf16(o.y) << 16),
-                       (uint32_t)f32_to_bf16(o.z) | ((uint32_t)f32_to_bf16(o.w) << 16));
+        uint2* dc = (uint2*)(cache + (((size_t)m * p.nkv + kvh) * p.max_seq + rpos) * p.hd + d);
+        const uint2 v = make_uint2((uint32_t)f32_to_bf16(o.x) | ((uint32_t)f32_to_bf16(o.y) << 16),
+                                   (uint32_t)f32_to_bf16(o.z) | ((uint32_t)f32_to_bf16(o.w) << 16));
+        if constexpr (HDA != 0)
+          __hip_atomic_store(gbl((unsigned long long*)dc), __builtin_bit_cast(unsigned long long, v), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        else *dc = v;
       }
     } else if (p.swiglu) {
       *(float2*)(p.C + (size_t)m * p.ldc + n / 2) = make_float2(silu(o.x) * o.y, silu(o.z) * o.w);
@@ -374,6 +418,9 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(SkArgs args) {
         *(float4*)(p.C2 + (size_t)m * p.ldc + n) = make_float4(o.x + v1.x, o.y + v1.y, o.z + v1.z, o.w + v1.w);
     }
   }
+  // the QKV tile's q and K/V rows are in memory: tell the attention workgroups
+  if constexpr (HDA != 0)
+    if (p.rope_q) prog_publish(args.prog + tile, pcode);
 }
 
 // Slices of one K part: about 512 workgroups (two per CU) for its tiles, at least two
@@ -449,6 +496,41 @@ hipError_t launch_skinny(const GemmParams& p, hipStream_t s) {
 
 bool skinny_pair_supported(const GemmParams& a, const GemmParams& b) {
   return sk_ok(a) && sk_ok(b) && a.M == b.M && (a.gain != nullptr) == (b.gain != nullptr);
+}
+
+bool skinny_pair_attn_supported(const GemmParams& a, const GemmParams& b, const AttnDecodeParams& at) {
+  if (!skinny_pair_supported(a, b) || !a.rope_q || !a.gain || b.rope_q) return false;
+  const int nt = (a.N + kSkRows - 1) / kSkRows;
+  return nt <= kSeqProgWords && at.wdtype == W_BF16 && at.q == a.rope_q && at.k_cache == a.k_cache &&
+         at.v_cache == a.v_cache && at.d_pos == a.d_pos && at.B == a.M && at.nq == a.nq && at.nkv == a.nkv &&
+         at.hd == a.hd && at.max_seq == a.max_seq && (at.hd == 64 || at.hd == 128) && at.nq % at.nkv == 0 &&
+         at.nq / at.nkv <= kAttnMaxGroup && at.n_split >= 1 && at.n_split <= kAttnMaxSplits && at.part &&
+         at.counters && at.out && at.d_epoch && !at.done_flag;
+}
+
+hipError_t launch_skinny_pair_attn(const GemmParams& a, const GemmParams& b, const AttnDecodeParams& at,
+                                   uint32_t* prog, int tag, int* err, hipStream_t s) {
+  if (!skinny_pair_attn_supported(a, b, at) || !prog || !err || tag < 1 || tag >= (int)kSeqCodeStride)
+    return hipErrorInvalidValue;
+  const SkProb q[2] = {sk_prob(a), sk_prob(b)};
+  SkArgs g{};
+  g.p[0] = q[0];
+  g.p[1] = q[1];
+  g.items0 = q[0].nt * (q[0].S0 + q[0].S1);
+  g.items = g.items0 + q[1].nt * (q[1].S0 + q[1].S1);
+  g.per_xcd = 0;
+  g.at = at;
+  g.n_attn = at.n_split * at.nkv * at.B;
+  g.per1 = (g.items - g.items0 + kSkXcds - 1) / kSkXcds;
+  g.tag = tag;
+  g.prog = prog;
+  g.err = err;
+  const dim3 grid(g.items0 + g.n_attn + g.per1 * kSkXcds), block(256);
+  if (a.M <= 16)
+    launch_timed(at.hd == 128 ? skinny_kernel<1, true, 128> : skinny_kernel<1, true, 64>, grid, block, 0, s, g);
+  else
+    launch_timed(at.hd == 128 ? skinny_kernel<2, true, 128> : skinny_kernel<2, true, 64>, grid, block, 0, s, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_skinny_pair(const GemmParams& a, const GemmParams& b, hipStream_t s) {
