@@ -425,6 +425,14 @@ GemvParams qkv_params(const ladder_ctx* ctx, int l, int B, const float* xin, con
   return p;
 }
 
+// Key chunks of the matrix-core route's decode attention: at most kDecodeAttnFill / (B *
+// kv heads) workgroups' worth (and at most the context's own split), the same rule on every
+// path so that the schedules give the same bits.  With the attention inside the
+// [QKV | gate/up] launch its workgroups wait there beside the gate/up rows: 128 measured
+// 2578 tok/s at batch 16 on the 70B shard against 2446 with 256 and 2458 with 64 (batches 8
+// and 32 within 0.2% of 256).
+constexpr int kDecodeAttnFill = 128;
+
 AttnDecodeParams attn_params(const ladder_ctx* ctx, int l, int B, const StreamScratch& sc) {
   const ladder_config& g = ctx->cfg;
   AttnDecodeParams a{};
@@ -733,9 +741,8 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
     if (ctx->gemm_step) {
       // a decode step (one query per sequence at *pos_dev): the split-KV decode attention
       AttnDecodeParams a = attn_params(ctx, l, B, sc);
-      // key chunks: about 256 workgroups in all (batch 16, one kv head: 16 chunks; batch
-      // 32: 8, which measured 4% faster per step than 16 on the 70B shard)
-      const int fill = 256 / (B * g.n_kv_heads);
+      // key chunks: the rule of every matrix-core decode path (kDecodeAttnFill)
+      const int fill = kDecodeAttnFill / (B * g.n_kv_heads);
       a.n_split = std::max(1, std::min(a.n_split, fill));
       a.q = sc.qr;
       a.out = sc.ob;
@@ -1151,7 +1158,7 @@ ladder_status decode_layer_skinny(ladder_ctx* ctx, int l, int B, hipStream_t s) 
   GemmParams qg[2], od;
   skinny_layer_params(ctx, l, B, qg, &od);
   AttnDecodeParams at = attn_params(ctx, l, B, sc);
-  at.n_split = std::max(1, std::min(at.n_split, 256 / (B * g.n_kv_heads)));
+  at.n_split = std::max(1, std::min(at.n_split, kDecodeAttnFill / (B * g.n_kv_heads)));
   at.q = sc.qr;
   at.out = sc.ob;
   TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
@@ -1545,7 +1552,7 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
         for (int l = 0; l < g.n_layers; ++l, ++launches) {
           if (kind == LADDER_KERNEL_ATTN) {
             AttnDecodeParams at = attn_params(ctx, l, B, sc);
-            at.n_split = std::max(1, std::min(at.n_split, 256 / (B * g.n_kv_heads)));
+            at.n_split = std::max(1, std::min(at.n_split, kDecodeAttnFill / (B * g.n_kv_heads)));
             at.q = sc.qr;
             at.out = sc.ob;
             HIPCHK(launch_attn_decode(at, s));
@@ -1555,7 +1562,7 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
           skinny_layer_params(ctx, l, B, qg, &od);
           if (kind == LADDER_KERNEL_QKV_GATEUP) {
             AttnDecodeParams at = attn_params(ctx, l, B, sc);
-            at.n_split = std::max(1, std::min(at.n_split, 256 / (B * g.n_kv_heads)));
+            at.n_split = std::max(1, std::min(at.n_split, kDecodeAttnFill / (B * g.n_kv_heads)));
             at.q = sc.qr;
             at.out = sc.ob;
             if (skinny_pair_attn_supported(qg[0], qg[1], at)) {
