@@ -30,14 +30,15 @@ CSRC = "ladder_residual_transformer_amd/csrc/"
 DOMINANT = {
     "fused": ("qkv_attn_gateup", "front launch of a ladder layer [RMSNorm+QKV+RoPE+KV, then RMSNorm+gate/up+"
               "SwiGLU, in every workgroup | split-KV GQA attention chunks once their kv group's QKV outputs "
-              "arrive]; at batch 1 the streaming launch (stream.hip), else the row-wave one",
+              "arrive]; at batch 1 the streaming launch (stream.hip), at batches 3-32 the skinny "
+              "[QKV | attention | gate/up] launch (skinny.hip), else the row-wave one",
               "traffic_qkv_attn_gateup_70b_b1.json",
-              ("stream.hip", "gemv_rw.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
+              ("stream.hip", "gemv_rw.hip", "gemv_rw.hpp", "skinny.hip", "attn_decode.hpp", "common.hpp")),
     # FUSED without the bf16 two-launch layers, and the schedule with the attention in the
     # down projection's launch: the [QKV | gate/up] launch
     "fused3": ("qkv_gateup", "fused ladder launch [RMSNorm+QKV | RMSNorm+gate/up+SwiGLU]: the row-wave launch "
-               "(RoPE+KV in its epilogue) or, at batches on the matrix cores, the skinny weight-streaming "
-               "launch (skinny.hip)",
+               "(RoPE+KV in its epilogue) or, at batches on the matrix cores without the attention in the "
+               "launch, the skinny weight-streaming launch (skinny.hip)",
                "traffic_qkv_gateup_70b_b1.json",
                ("gemv_rw.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
     "persistent": ("layer_stack", "persistent decode launch of the whole layer stack (every projection, "
@@ -284,7 +285,7 @@ def main():
     # of that kernel with a pair of HIP events on the stream it runs on, taken from its
     # dispatch's own begin/end timestamps (traced steps are launched eagerly).  Fused
     # schedule: the [QKV, then gate/up | attention] launch of every layer (~80% of the
-    # step's bytes; [QKV | gate/up] where layers take three launches, and under the
+    # step's bytes; [QKV | gate/up] where the attention has a launch of its own, and under the
     # schedule with the attention in the down projection's launch); persistent schedule:
     # the one launch of the whole layer stack.  Which of them a step launches depends on
     # the shape (the two-launch layers need the staged input rows to fit in LDS), so the

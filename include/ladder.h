@@ -175,9 +175,9 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
  * n_q_heads * head_dim; at B = 3 and 4 only up to 65 KB, two workgroups per CU) run the
  * schedule's GEMV launches; other bf16 batches run one token per sequence on the matrix
  * cores (with the split-KV decode attention), under every schedule: up to 32 sequences
- * through skinny weight-streaming launches (a ladder layer in four launches under the
- * FUSED schedules, module by module otherwise, with the same bits), beyond that through
- * tiled GEMMs. */
+ * through skinny weight-streaming launches (a ladder layer in two launches under the
+ * FUSED schedules, [QKV + RoPE/KV | attention | gate/up] and [O + down], module by module
+ * otherwise, with the same bits), beyond that through tiled GEMMs. */
 ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t pos,
                                  float* d_logits, int32_t* d_next, float* d_hidden);
 
@@ -251,10 +251,12 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 #define LADDER_KERNEL_LAYER_STACK 9  /* persistent launch of a decode step's whole layer stack
                                         (LADDER_SCHED_PERSISTENT); ladder_time_kernels stores
                                         -1 where that launch is not available */
-#define LADDER_KERNEL_QKV_ATTN_GATEUP 10 /* fused ladder launch (FUSED, bf16, row-wave batches
-                                        with two workgroups per CU): QKV (+RoPE/KV) in half of
-                                        the workgroups, then gate/up (+SwiGLU) in all | the
-                                        split-KV attention once every QKV share is done; -1
+#define LADDER_KERNEL_QKV_ATTN_GATEUP 10 /* fused ladder launch (FUSED, bf16): QKV (+RoPE/KV),
+                                        gate/up (+SwiGLU) and the split-KV attention once the
+                                        QKV outputs are done: at batch 1 the streaming front
+                                        launch, at row-wave batches with two workgroups per CU
+                                        the sequential launch, at batches 3-32 on the matrix
+                                        cores the skinny [QKV | attention | gate/up] launch; -1
                                         from ladder_time_kernels where not available */
 #define LADDER_KERNEL_DOWN_OPROJ 11  /* fused ladder launch (the same layers): down rows, then
                                         the O rows + both residual adds; -1 where not
@@ -267,8 +269,10 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 /* Profiling aid.  For each kernel kind, enqueue it on the context's stream exactly as
  * a decode step at batch B launches it (once per layer; the LM head once), once untimed
  * and then reps times (the GEMV kinds at B <= 16 only; -1 beyond; at a batch that runs on
- * the matrix cores only the kinds such a step launches: QKV_GATEUP and DOWN_OPROJ as its
- * [QKV | gate/up] and [O + down] launches, ATTN, LMHEAD and SAMPLE, -1 for the others),
+ * the matrix cores only the kinds such a step launches: QKV_ATTN_GATEUP as its
+ * [QKV | attention | gate/up] launch (batches up to 32), QKV_GATEUP as the same launch
+ * without the attention, DOWN_OPROJ as its [O + down] launch, ATTN as the attention launched
+ * alone, LMHEAD and SAMPLE, -1 for the others),
  * (the fused kinds use each layer as if it were a ladder layer),
  * between two HIP events, and store the mean duration of one launch in microseconds
  * in us_out[kind] (host array of LADDER_N_KERNELS floats).  Works on the context's

@@ -1161,12 +1161,13 @@ ladder_status decode_layer_skinny(ladder_ctx* ctx, int l, int B, hipStream_t s) 
   at.n_split = std::max(1, std::min(at.n_split, kDecodeAttnFill / (B * g.n_kv_heads)));
   at.q = sc.qr;
   at.out = sc.ob;
-  TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
   if (skinny_pair_attn_supported(qg[0], qg[1], at)) {
     // the attention waits for the QKV tiles inside the same launch, beside the gate/up rows
+    TRACE(LADDER_KERNEL_QKV_ATTN_GATEUP, s, false);
     HIPCHK(launch_skinny_pair_attn(qg[0], qg[1], at, ctx->seq_prog, l + 1, ctx->err_word, s));
-    TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
+    TRACE(LADDER_KERNEL_QKV_ATTN_GATEUP, s, true);
   } else {
+    TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
     HIPCHK(launch_skinny_pair(qg[0], qg[1], s));
     TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
     HIPCHK(launch_attn_decode(at, s));
@@ -1547,7 +1548,8 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
           continue;
         }
         const bool ok = kind == LADDER_KERNEL_ATTN ||
-                        (mc_layers && (kind == LADDER_KERNEL_QKV_GATEUP || kind == LADDER_KERNEL_DOWN_OPROJ));
+                        (mc_layers && (kind == LADDER_KERNEL_QKV_GATEUP || kind == LADDER_KERNEL_QKV_ATTN_GATEUP ||
+                                       kind == LADDER_KERNEL_DOWN_OPROJ));
         if (!ok) break;
         for (int l = 0; l < g.n_layers; ++l, ++launches) {
           if (kind == LADDER_KERNEL_ATTN) {
@@ -1560,18 +1562,17 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
           }
           GemmParams qg[2], od;
           skinny_layer_params(ctx, l, B, qg, &od);
-          if (kind == LADDER_KERNEL_QKV_GATEUP) {
+          if (kind == LADDER_KERNEL_QKV_ATTN_GATEUP) {
             AttnDecodeParams at = attn_params(ctx, l, B, sc);
             at.n_split = std::max(1, std::min(at.n_split, kDecodeAttnFill / (B * g.n_kv_heads)));
             at.q = sc.qr;
             at.out = sc.ob;
-            if (skinny_pair_attn_supported(qg[0], qg[1], at)) {
-              // codes as in a decode step: a new epoch per pass over the layers, tag l + 1
-              if (l == 0) HIPCHK(launch_epoch_bump(ctx->epoch, s));
-              HIPCHK(launch_skinny_pair_attn(qg[0], qg[1], at, ctx->seq_prog, l + 1, ctx->err_word, s));
-            } else {
-              HIPCHK(launch_skinny_pair(qg[0], qg[1], s));
-            }
+            if (!skinny_pair_attn_supported(qg[0], qg[1], at)) break;
+            // codes as in a decode step: a new epoch per pass over the layers, tag l + 1
+            if (l == 0) HIPCHK(launch_epoch_bump(ctx->epoch, s));
+            HIPCHK(launch_skinny_pair_attn(qg[0], qg[1], at, ctx->seq_prog, l + 1, ctx->err_word, s));
+          } else if (kind == LADDER_KERNEL_QKV_GATEUP) {
+            HIPCHK(launch_skinny_pair(qg[0], qg[1], s));
           } else {
             HIPCHK(launch_skinny(od, s));
           }

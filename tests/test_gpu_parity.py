@@ -389,6 +389,29 @@ def test_kernel_tracing_keeps_results_and_counts_launches(edge):
         assert np.array_equal(a, b)
 
 
+def test_matrix_core_layer_launch_is_traced_with_its_attention(edge):
+    """Batch 5 decodes on the matrix cores: the first launch of each ladder layer is the
+    skinny [QKV + RoPE/KV | attention | gate/up] launch, whose attention workgroups wait for
+    the QKV tiles' progress words; it is traced as the qkv_attn_gateup kind once per ladder
+    layer, no wait gives up (sync reports one that did), and tracing leaves every result
+    unchanged."""
+    cfg, w = edge
+    B = 5
+    prompt = synth.gen_ids(B, 9, cfg.vocab, seed=13)
+    cont = synth.gen_ids(B, 3, cfg.vocab, seed=13, stream=1)
+    m = make_model(cfg, w, B, 16)
+    plain = gpu_teacher_forced(m, prompt, cont)
+    m.free()
+    m = make_model(cfg, w, B, 16)
+    m.trace_kernel("qkv_attn_gateup")
+    traced = gpu_teacher_forced(m, prompt, cont)
+    us, n = m.trace_result()
+    assert n == sum(1 for v in cfg.ladder_mask if v) and us > 0.0
+    m.free()
+    for a, b in zip(plain, traced):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("B, T, max_seq, n_dec", [(2, 150, 256, 6), (1, 2100, 2200, 3)])
 def test_long_context_split_kv(edge, B, T, max_seq, n_dec):
     """Decode attention over several key chunks (150 keys in 64-key chunks, merged across
