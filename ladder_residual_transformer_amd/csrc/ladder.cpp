@@ -425,13 +425,14 @@ GemvParams qkv_params(const ladder_ctx* ctx, int l, int B, const float* xin, con
   return p;
 }
 
-// Key chunks of the matrix-core route's decode attention: at most kDecodeAttnFill / (B *
-// kv heads) workgroups' worth (and at most the context's own split), the same rule on every
-// path so that the schedules give the same bits.  With the attention inside the
-// [QKV | gate/up] launch its workgroups wait there beside the gate/up rows: 128 measured
-// 2578 tok/s at batch 16 on the 70B shard against 2446 with 256 and 2458 with 64 (batches 8
-// and 32 within 0.2% of 256).
-constexpr int kDecodeAttnFill = 128;
+// Key chunks of the matrix-core route's decode attention: at most decode_attn_fill(B) / (B *
+// kv heads) workgroups' worth (and at most the context's own split), a function of the batch
+// only, so that every schedule gives the same bits.  Up to 32 sequences the attention runs
+// inside the [QKV | gate/up] launch, its workgroups waiting there beside the gate/up rows:
+// 128 measured 2578 tok/s at batch 16 on the 70B shard against 2446 with 256 and 2458 with 64
+// (batches 8 and 32 within 0.2% of 256).  Beyond, the attention has a launch of its own,
+// where 256 measured 4474 / 1961 tok/s (70B / 405B shard, batch 64) against 4383 / 1869.
+constexpr int decode_attn_fill(int B) { return B <= 32 ? 128 : 256; }
 
 AttnDecodeParams attn_params(const ladder_ctx* ctx, int l, int B, const StreamScratch& sc) {
   const ladder_config& g = ctx->cfg;
@@ -741,8 +742,8 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
     if (ctx->gemm_step) {
       // a decode step (one query per sequence at *pos_dev): the split-KV decode attention
       AttnDecodeParams a = attn_params(ctx, l, B, sc);
-      // key chunks: the rule of every matrix-core decode path (kDecodeAttnFill)
-      const int fill = kDecodeAttnFill / (B * g.n_kv_heads);
+      // key chunks: the rule of every matrix-core decode path (decode_attn_fill)
+      const int fill = decode_attn_fill(B) / (B * g.n_kv_heads);
       a.n_split = std::max(1, std::min(a.n_split, fill));
       a.q = sc.qr;
       a.out = sc.ob;
@@ -1158,7 +1159,7 @@ ladder_status decode_layer_skinny(ladder_ctx* ctx, int l, int B, hipStream_t s) 
   GemmParams qg[2], od;
   skinny_layer_params(ctx, l, B, qg, &od);
   AttnDecodeParams at = attn_params(ctx, l, B, sc);
-  at.n_split = std::max(1, std::min(at.n_split, kDecodeAttnFill / (B * g.n_kv_heads)));
+  at.n_split = std::max(1, std::min(at.n_split, decode_attn_fill(B) / (B * g.n_kv_heads)));
   at.q = sc.qr;
   at.out = sc.ob;
   if (skinny_pair_attn_supported(qg[0], qg[1], at)) {
@@ -1554,7 +1555,7 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
         for (int l = 0; l < g.n_layers; ++l, ++launches) {
           if (kind == LADDER_KERNEL_ATTN) {
             AttnDecodeParams at = attn_params(ctx, l, B, sc);
-            at.n_split = std::max(1, std::min(at.n_split, kDecodeAttnFill / (B * g.n_kv_heads)));
+            at.n_split = std::max(1, std::min(at.n_split, decode_attn_fill(B) / (B * g.n_kv_heads)));
             at.q = sc.qr;
             at.out = sc.ob;
             HIPCHK(launch_attn_decode(at, s));
@@ -1564,7 +1565,7 @@ ladder_status ladder_time_kernels(ladder_ctx* ctx, int32_t B, int32_t reps, floa
           skinny_layer_params(ctx, l, B, qg, &od);
           if (kind == LADDER_KERNEL_QKV_ATTN_GATEUP) {
             AttnDecodeParams at = attn_params(ctx, l, B, sc);
-            at.n_split = std::max(1, std::min(at.n_split, kDecodeAttnFill / (B * g.n_kv_heads)));
+            at.n_split = std::max(1, std::min(at.n_split, decode_attn_fill(B) / (B * g.n_kv_heads)));
             at.q = sc.qr;
             at.out = sc.ob;
             if (!skinny_pair_attn_supported(qg[0], qg[1], at)) break;
