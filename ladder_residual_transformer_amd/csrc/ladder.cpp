@@ -1048,17 +1048,22 @@ ladder_status enqueue_decode(ladder_ctx* ctx, int B) {
 // staged input rows of any projection, the widest of hidden, ffn and the attention rows,
 // beyond their LDS budget): one token per sequence on the matrix cores (the K-sliced GEMV
 // kernels leave most of the HBM bandwidth unused at those batches), through the skinny
-// projections up to 32 sequences (a ladder layer in four launches, decode_layer_skinny;
+// projections up to 32 sequences (a ladder layer in two launches, decode_layer_skinny;
 // standard layers module by module) and the tiled GEMMs beyond, with the split-KV decode
 // attention, then the LM head with the final RMSNorm folded in and a row argmax.  Every
 // kernel of the route takes the position from the device (the prologue's pos_dev), so it
 // is replayed as a graph too.  Batches 3 and 4 also take it where the row-wave launches
 // would hold one workgroup per CU (the 70B shard at batch 3: 498 against 335 tok/s; the 1B
-// model at batch 3: 2290 against 2065).
+// model at batch 3: 2290 against 2065), and batch 2 for wide models whose layers are all
+// ladder or parallel blocks (70B shard: 394 against 378 tok/s; the 8B hybrid, half of its
+// layers standard, stays on the row-wave launches: 459 against 429).
 bool gemm_decode(const ladder_ctx* ctx, int B) {
   const int kmax = std::max(ctx->cfg.hidden, std::max(ctx->cfg.ffn, ctx->qrows));
   if (ctx->wdt != W_BF16) return false;
-  return !gemv_rw_supported(ctx->wdt, kmax, B) || (B >= 3 && !gemv_rw_two_per_cu(ctx->wdt, kmax, B));
+  bool no_standard = true;
+  for (int l = 0; l < ctx->cfg.n_layers; ++l) no_standard = no_standard && ctx->mask[l] != 0;
+  return !gemv_rw_supported(ctx->wdt, kmax, B) || (B >= 3 && !gemv_rw_two_per_cu(ctx->wdt, kmax, B)) ||
+         (B == 2 && no_standard && ctx->cfg.hidden >= 8192);
 }
 
 // The skinny parameters of a decode step's projections on the matrix cores, as the

@@ -97,13 +97,11 @@ def test_8b_hybrid_widths(B, T, n_dec):
                                   (33, 16)])
 def test_70b_tp8_shard_widths_batches(B, T):
     """70B TP=8 shard widths (hidden 8192), four ladder layers.  Batch 1: the two streaming
-    launches per layer.  Batch 2: the staged input rows (65.6 KB) just keep two row-wave
-    workgroups per CU.  Batch 3: one workgroup per CU, and the attention (48 workgroups)
-    runs in the down projection's launch.  Batch 4, 6, 8, 16 and 32: the decode steps run
-    on the matrix cores, whose 32-row GEMMs split K over up to 32 slices at these widths
-    (the QKV projection: 10 tiles, 32 slices) with the RMSNorm folded in (batch 6: 26 of
-    the 32 tile rows are padding; batch 32: the last batch the fold takes).  Batch 33: the
-    64-row tiles with the RMSNorm kernel ahead of them (31 rows of padding)."""
+    launches per layer.  Batches 2-32: the skinny launches on the matrix cores, two per
+    layer ([QKV with RoPE + KV | attention | gate/up], [O + down]), both RMSNorms folded in,
+    16-row tiles up to batch 16 (batch 6: 10 of 16 rows padding) and 32-row tiles beyond
+    (batch 32: the last batch they take).  Batch 33: the tiled GEMMs with 64-row tiles, the
+    RMSNorm kernel ahead of them (31 rows of padding) and the attention in its own launch."""
     base = synth.CONFIGS["70b_tp8_shard"]
     cfg = synth.scaled_config(base, 4)
     w = synth.gen_weights(cfg, seed=8)
