@@ -172,7 +172,8 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
  * captured HIP graph per (B, schedule, next-token rule) when graphs are enabled.
  * Batches whose staged projection inputs fit the row-wave GEMV (B <= 4 and
  * B * (K + 8) * 4 bytes <= 150 KB for K the widest of hidden, ffn and
- * n_q_heads * head_dim; at B = 3 and 4 only up to 65 KB, two workgroups per CU) run the
+ * n_q_heads * head_dim; at B = 3 and 4 only up to 65 KB, two workgroups per CU; not B = 2
+ * for models of hidden >= 8192 whose layers are all ladder or parallel blocks) run the
  * schedule's GEMV launches; other bf16 batches run one token per sequence on the matrix
  * cores (with the split-KV decode attention), under every schedule: up to 32 sequences
  * through skinny weight-streaming launches (a ladder layer in two launches under the
