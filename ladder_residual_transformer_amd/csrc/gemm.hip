@@ -61,11 +61,15 @@ constexpr int kStages = 4;   // K steps whose global loads are in flight (even: 
 
 // TM x TN workgroup tile (128x128, or 64x64 when the big tiles would not fill the
 // device), 4 waves of (TM/2) x (TN/2), i.e. (TM/32) x (TN/32) MFMA tiles of 16x16 each.
-// Slice blockIdx.y covers K range [blockIdx.y * kchunk, + kchunk); with more than one
+// Slice s of S covers K range [s * kchunk, + kchunk); with more than one
 // slice the raw partial tile goes to p.ws[slice][M][N].
+// Register caps: two waves per SIMD for 128-row tiles (two workgroups per CU instead of
+// one: the 70B shard's 1024-token prefill 52.8 against 54.3 ms), three for 64-row tiles
+// (with or without the folded RMSNorm; batch 64 decode 4923 against 4817 tok/s on the 70B
+// shard, 2177 against 2132 on the 405B shard) and four for 32-row tiles, all without spills.
 template <int TM, int TN, bool NORM = false>
-__global__ __launch_bounds__(256) void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd,
-                                                         int kchunk) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 128 ? 2 : TM == 64 ? 3 : 4)))
+void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, int kchunk) {
   constexpr int FM = TM / 32, FN = TN / 32;       // MFMA tiles per wave
   constexpr int AV = TM * BK / 4 / 256;           // float4 of A per thread per K step
   constexpr int BV = TN * BK / 8 / 256;           // 16-byte W chunks per thread per K step
@@ -74,11 +78,12 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(GemmParams p, int n_ti
   __shared__ __attribute__((aligned(16))) uint16_t Al[2][TM][BK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TN][BK];
   const int tile = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int slice = blockIdx.y, S = gridDim.y;
   if (tile >= n_tiles) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int m0 = (tile % n_tiles_m) * TM, n0 = (tile / n_tiles_m) * TN;
-  const int kbase = (int)blockIdx.y * kchunk;
+  const int kbase = slice * kchunk;
   const float* A = (const float*)p.A + kbase;
 
   // per K step a thread moves AV float4 of A (rows c/8, columns 4*(c%8)) and BV 16-byte
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(GemmParams p, int n_ti
 
   if (sum_sq) {
     // the 8 threads of a row (consecutive lanes) hold its squares over 4 columns of each
-    // K step; slice blockIdx.y's sum of row m goes to ws[S*M*N + blockIdx.y*M + m]
+    // K step; the slice's sum of row m goes to ws[S*M*N + slice*M + m]
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
       float v = sq[i];
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(GemmParams p, int n_ti
       v += __shfl_xor(v, 4, 64);
       const int row = m0 + ar[i];
       if ((tid & 7) == 0 && row < p.M)
-        p.ws[(size_t)gridDim.y * p.M * p.N + (size_t)blockIdx.y * p.M + row] = v;
+        p.ws[(size_t)S * p.M * p.N + (size_t)slice * p.M + row] = v;
     }
   }
 
@@ -230,8 +235,8 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(GemmParams p, int n_ti
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + wm * (TM / 2) + i * 16 + (lane >> 4) * 4 + r;
         float v = acc[i][j][r];
-        if (gridDim.y > 1) {
-          if (row < p.M && col < p.N) p.ws[((size_t)blockIdx.y * p.M + row) * p.N + col] = v;
+        if (S > 1) {
+          if (row < p.M && col < p.N) p.ws[((size_t)slice * p.M + row) * p.N + col] = v;
         } else if (p.swiglu) {
           const float up = __shfl_xor(v, 1, 64);
           if (!(col & 1) && row < p.M && col < p.N) p.C[(size_t)row * p.ldc + (col >> 1)] = silu(v) * up;
@@ -358,10 +363,9 @@ int gemm_splits(const GemmParams& p) {
 }
 
 // The fused RMSNorm: split launches of the 32- and 64-row tiles (decode steps of up to 64
-// sequences).  The gain's registers take the 64-row tile from three workgroups per CU to
-// two, and the fold still saves the two RMSNorm launches per layer: 4794 against 4483
-// tok/s at batch 64 on the 70B shard, 2129 against 1958 on the 405B shard.  The 128-row
-// tiles keep the RMSNorm kernel.
+// sequences); it saves the two RMSNorm launches per layer: 4794 against 4483 tok/s at
+// batch 64 on the 70B shard, 2129 against 1958 on the 405B shard (both measured before the
+// register caps below).  The 128-row tiles keep the RMSNorm kernel.
 bool gemm_norm_fusable(const GemmParams& p) {
   if (skinny_supported(p)) return true;
   return p.wdtype == W_BF16 && p.M <= 64 && p.lda % 4 == 0 && p.K % BK == 0 && gemm_splits(p) > 1;
