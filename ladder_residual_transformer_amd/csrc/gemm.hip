@@ -34,10 +34,15 @@
 // (deterministic) and applies the epilogue.
 //
 // fp32 models (small correctness-only models): a plain LDS-tiled VALU GEMM.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.h"
 
 namespace ladder {
+
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
@@ -64,11 +69,13 @@ constexpr int kStages = 4;   // K steps whose global loads are in flight (even: 
 // Slice s of S covers K range [s * kchunk, + kchunk); with more than one
 // slice the raw partial tile goes to p.ws[slice][M][N].
 // Register caps: two waves per SIMD for 128-row tiles (two workgroups per CU instead of
-// one: the 70B shard's 1024-token prefill 52.8 against 54.3 ms), three for 64-row tiles
-// (with or without the folded RMSNorm; batch 64 decode 4923 against 4817 tok/s on the 70B
-// shard, 2177 against 2132 on the 405B shard) and four for 32-row tiles, all without spills.
+// one) and for 64-row tiles with the folded RMSNorm, three for the other 64-row tiles and
+// four for 32-row tiles; each the tightest that keeps the four-stage ring in registers
+// without spills.  With the caps and the unconditional loads (the ring actually in
+// flight): the 70B shard's 1024-token prefill 51.0 against 54.3 ms, batch-64 decode 4991
+// against 4817 tok/s on the 70B shard and 2313 against 2132 on the 405B shard.
 template <int TM, int TN, bool NORM = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 128 ? 2 : TM == 64 ? 3 : 4)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 128 || (TM == 64 && NORM) ? 2 : TM == 64 ? 3 : 4)))
 void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, int kchunk) {
   constexpr int FM = TM / 32, FN = TN / 32;       // MFMA tiles per wave
   constexpr int AV = TM * BK / 4 / 256;           // float4 of A per thread per K step
@@ -87,7 +94,11 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
   const float* A = (const float*)p.A + kbase;
 
   // per K step a thread moves AV float4 of A (rows c/8, columns 4*(c%8)) and BV 16-byte
-  // chunks of W (rows c/4, columns 8*(c%4))
+  // chunks of W (rows c/4, columns 8*(c%4)).  Rows past M (N) read row M-1 (N-1): they
+  // only feed output rows (columns) that are never stored, and every load is
+  // unconditional, so that the wait before each step's LDS stores covers that step's
+  // loads only (with loads under branches the compiler waits for all of them, and the
+  // ring holds nothing in flight).
   const float* arow[AV];
   const uint16_t* brow[BV];
   int ar[AV], ac[AV], br[BV], bc[BV];
@@ -97,7 +108,7 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
     ar[i] = c >> 3;
     ac[i] = (c & 7) * 4;
     const int m = m0 + ar[i];
-    arow[i] = m < p.M ? A + (size_t)m * p.lda + ac[i] : nullptr;
+    arow[i] = A + (size_t)min(m, p.M - 1) * p.lda + ac[i];
   }
 #pragma unroll
   for (int i = 0; i < BV; ++i) {
@@ -105,7 +116,7 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
     br[i] = c >> 2;
     bc[i] = (c & 3) * 8;
     const int n = n0 + br[i];
-    brow[i] = n < p.N ? gemm_row<uint16_t>(p.rows, n, p.K) + kbase + bc[i] : nullptr;
+    brow[i] = gemm_row<uint16_t>(p.rows, min(n, p.N - 1), p.K) + kbase + bc[i];
   }
   // register ring: stage st holds the global loads of one K step
   float4 ra[kStages][AV];
@@ -116,18 +127,29 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
   float sq[AV];
 #pragma unroll
   for (int i = 0; i < AV; ++i) sq[i] = 0.f;
-  auto gload = [&](int st, int k0) {
+  const int nk = kchunk / BK;
+  const int nkp = (nk + kStages - 1) / kStages * kStages;   // steps padded to whole ring turns
+  // Stage indices are compile-time constants (std::integral_constant), so that the ring
+  // stays in registers.  Step kt's loads into stage ST (steps past the slice load its last
+  // step again).
+  auto gload = [&](auto STC, int kt) {
+    constexpr int st = decltype(STC)::value;
+    const int k0 = min(kt, nk - 1) * BK;
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
-      ra[st][i] = arow[i] ? *(const float4*)(arow[i] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      ra[st][i] = ldg4(arow[i] + k0);
       if constexpr (NORM) rg[st][i] = *(const uint2*)(gain + k0 + ac[i]);
     }
 #pragma unroll
-    for (int i = 0; i < BV; ++i) rb[st][i] = brow[i] ? *(const uint4*)(brow[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < BV; ++i) rb[st][i] = ldg4u(brow[i] + k0);
   };
-  auto sstore = [&](int st, int buf) {
+  // stage st (step kt) into LDS buffer buf; the A of a padding step (kt >= nk) is zero,
+  // so that its products add nothing
+  auto sstore = [&](auto STC, int buf, int kt) {
+    constexpr int st = decltype(STC)::value;
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
+      if (kt >= nk) ra[st][i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (NORM) {
         float4& a = ra[st][i];
         if (sum_sq) {
@@ -159,26 +181,25 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = kchunk / BK;
   // prologue: steps 0 .. kStages-1 in flight, step 0 into LDS buffer 0, then stage 0
   // refilled with step kStages
-#pragma unroll
-  for (int st = 0; st < kStages; ++st)
-    if (st < nk) gload(st, st * BK);
-  sstore(0, 0);
-  if (kStages < nk) gload(0, kStages * BK);
+  static_assert(kStages == 4, "the ring below is written out for four stages");
+  gload(IC<0>{}, 0);
+  gload(IC<1>{}, 1);
+  gload(IC<2>{}, 2);
+  gload(IC<3>{}, 3);
+  sstore(IC<0>{}, 0, 0);
+  gload(IC<0>{}, kStages);
   __syncthreads();
   // 16x16x32 fragments: lane holds row (A) / column (W) lane%16, k = 8*(lane/16) .. +8
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   // step kt reads LDS buffer kt & 1 and register stage kt % kStages holds (in flight)
   // step kt + kStages; after the MFMAs, step kt + 1 goes from its stage into the other
   // LDS buffer and that stage is refilled with step kt + 1 + kStages
-  for (int k0 = 0; k0 < nk; k0 += kStages) {
-#pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      const int kt = k0 + u;
-      if (kt < nk) {
-        const int cur = u & 1;
+  auto step = [&](auto UC, int kt) {
+    constexpr int u = decltype(UC)::value;
+      {
+        constexpr int cur = u & 1;
         bf16x8 ah[FM], al[FM], b[FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -198,14 +219,19 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], b[j], acc[i][j], 0, 0, 0);
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], b[j], acc[i][j], 0, 0, 0);
           }
-        if (kt + 1 < nk) {
-          const int nxt = (u + 1) % kStages;       // a constant once the loop is unrolled
-          sstore(nxt, cur ^ 1);
-          if (kt + 1 + kStages < nk) gload(nxt, (kt + 1 + kStages) * BK);
-        }
+        // (after the last step too: the stores go to the idle buffer, the loads repeat the
+        // last step, and nothing reads either)
+        using Nxt = IC<(u + 1) % kStages>;
+        sstore(Nxt{}, cur ^ 1, kt + 1);
+        gload(Nxt{}, kt + 1 + kStages);
         __syncthreads();
       }
-    }
+  };
+  for (int k0 = 0; k0 < nkp; k0 += kStages) {
+    step(IC<0>{}, k0);
+    step(IC<1>{}, k0 + 1);
+    step(IC<2>{}, k0 + 2);
+    step(IC<3>{}, k0 + 3);
   }
 
   if (sum_sq) {
