@@ -96,6 +96,39 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int ldx, c
   }
 }
 
+// rmsnorm_kernel's output (bf16 gains, H and ldx multiples of 4) split into bf16 pairs
+// hi = bf16(y), lo = bf16(y - hi), 16 bytes per 4 columns: their 4 hi, then their 4 lo.
+__global__ __launch_bounds__(256) void rmsnorm_pairs_kernel(const float* x, int ldx, const uint16_t* gain, float eps,
+                                                            int H, uint16_t* out) {
+  __shared__ float part[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float* xr = x + (size_t)m * ldx;
+  const int n4 = H / 4;
+  float s = 0.f;
+  for (int i = tid; i < n4; i += 256) {
+    const float4 v = *(const float4*)(xr + 4 * i);
+    s = fmaf(v.x, v.x, s);
+    s = fmaf(v.y, v.y, s);
+    s = fmaf(v.z, v.z, s);
+    s = fmaf(v.w, v.w, s);
+  }
+  s = wave_sum(s);
+  if ((tid & 63) == 0) part[tid >> 6] = s;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  uint4* o = (uint4*)(out + (size_t)m * 2 * H);
+  for (int i = tid; i < n4; i += 256) {
+    const float4 v = *(const float4*)(xr + 4 * i);
+    const float y0 = v.x * inv * load_w<uint16_t>(gain + 4 * i), y1 = v.y * inv * load_w<uint16_t>(gain + 4 * i + 1);
+    const float y2 = v.z * inv * load_w<uint16_t>(gain + 4 * i + 2), y3 = v.w * inv * load_w<uint16_t>(gain + 4 * i + 3);
+    uint32_t h0, l0, h1, l1;
+    split_bf2(y0, y1, h0, l0);
+    split_bf2(y2, y3, h1, l1);
+    o[i] = make_uint4(h0, h1, l0, l1);
+  }
+}
+
 // Row m = b*T + t of qkv holds token t of sequence b at position start_pos + t.
 template <typename WT>
 __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int T, int start_pos, const int* d_pos, int nq,
@@ -199,6 +232,14 @@ hipError_t launch_rmsnorm(int wdtype, const float* x, int ldx, const void* gain,
     hipLaunchKernelGGL(rmsnorm_kernel<uint16_t>, dim3(M), dim3(256), 0, s, x, ldx, (const uint16_t*)gain, eps, H, out);
   else
     hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, s, x, ldx, (const float*)gain, eps, H, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_pairs(const float* x, int ldx, const void* gain, float eps, int M, int H, void* out,
+                                hipStream_t s) {
+  if (M < 1 || H < 4 || H % 4 != 0 || ldx % 4 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rmsnorm_pairs_kernel, dim3(M), dim3(256), 0, s, x, ldx, (const uint16_t*)gain, eps, H,
+                     (uint16_t*)out);
   return hipGetLastError();
 }
 

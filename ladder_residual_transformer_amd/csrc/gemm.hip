@@ -2,7 +2,10 @@
 //
 // bf16 models: a dense contraction, so it runs on the CDNA4 matrix cores
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  A arrives in fp32 and is split on
-// its way into LDS into a pair of bf16 values, hi = bf16(a) and lo = bf16(a - hi),
+// its way into LDS into a pair of bf16 values, hi = bf16(a) and lo = bf16(a - hi) (the
+// prefill projections fed by an RMSNorm get A already split by the RMSNorm kernel: 50.0
+// against 52.1 ms for the 70B shard's 1024-token prefill, since each of the 56 column
+// tiles of its gate/up GEMM would otherwise split the same rows again),
 // which together carry about 16 significant bits over fp32's range; the stored bf16
 // weights feed the matrix cores as they are.  Each product is then two MFMAs, hi.W and
 // lo.W, into one fp32 accumulator: a single 16-bit rounding of the activations perturbs
@@ -74,9 +77,13 @@ constexpr int kStages = 4;   // K steps whose global loads are in flight (even: 
 // without spills.  With the caps and the unconditional loads (the ring actually in
 // flight): the 70B shard's 1024-token prefill 51.0 against 54.3 ms, batch-64 decode 4991
 // against 4817 tok/s on the 70B shard and 2313 against 2132 on the 405B shard.
-template <int TM, int TN, bool NORM = false>
+// APAIR: A arrives already split into bf16 pairs (p.a_pairs: 16 bytes per 4 columns, their
+// 4 hi then their 4 lo values) and goes into LDS as it is (the split is done once by A's
+// producer instead of once per column tile).
+template <int TM, int TN, bool NORM = false, bool APAIR = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 128 || (TM == 64 && NORM) ? 2 : TM == 64 ? 3 : 4)))
 void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, int kchunk) {
+  static_assert(!(NORM && APAIR), "the folded RMSNorm takes fp32 rows");
   constexpr int FM = TM / 32, FN = TN / 32;       // MFMA tiles per wave
   constexpr int AV = TM * BK / 4 / 256;           // float4 of A per thread per K step
   constexpr int BV = TN * BK / 8 / 256;           // 16-byte W chunks per thread per K step
@@ -92,6 +99,7 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
   const int m0 = (tile % n_tiles_m) * TM, n0 = (tile / n_tiles_m) * TN;
   const int kbase = slice * kchunk;
   const float* A = (const float*)p.A + kbase;
+  const uint16_t* Ap = (const uint16_t*)p.A + 2 * kbase;                      // APAIR
 
   // per K step a thread moves AV float4 of A (rows c/8, columns 4*(c%8)) and BV 16-byte
   // chunks of W (rows c/4, columns 8*(c%4)).  Rows past M (N) read row M-1 (N-1): they
@@ -100,6 +108,7 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
   // loads only (with loads under branches the compiler waits for all of them, and the
   // ring holds nothing in flight).
   const float* arow[AV];
+  const uint16_t* aprow[AV];   // APAIR
   const uint16_t* brow[BV];
   int ar[AV], ac[AV], br[BV], bc[BV];
 #pragma unroll
@@ -108,7 +117,8 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
     ar[i] = c >> 3;
     ac[i] = (c & 7) * 4;
     const int m = m0 + ar[i];
-    arow[i] = A + (size_t)min(m, p.M - 1) * p.lda + ac[i];
+    if constexpr (APAIR) aprow[i] = Ap + 2 * ((size_t)min(m, p.M - 1) * p.lda + ac[i]);
+    else arow[i] = A + (size_t)min(m, p.M - 1) * p.lda + ac[i];
   }
 #pragma unroll
   for (int i = 0; i < BV; ++i) {
@@ -120,6 +130,7 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
   }
   // register ring: stage st holds the global loads of one K step
   float4 ra[kStages][AV];
+  uint4 rp[kStages][AV];       // APAIR: 4 bf16 of the hi plane (x, y), 4 of the lo plane (z, w)
   uint4 rb[kStages][BV];
   uint2 rg[kStages][AV];                          // NORM: the gain of each A float4 (4 x bf16)
   const uint16_t* gain = NORM ? (const uint16_t*)p.gain + kbase : nullptr;
@@ -137,6 +148,10 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
     const int k0 = min(kt, nk - 1) * BK;
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
+      if constexpr (APAIR) {
+        rp[st][i] = ldg4u(aprow[i] + 2 * k0);
+        continue;
+      }
       ra[st][i] = ldg4(arow[i] + k0);
       if constexpr (NORM) rg[st][i] = *(const uint2*)(gain + k0 + ac[i]);
     }
@@ -149,6 +164,13 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
     constexpr int st = decltype(STC)::value;
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
+      if constexpr (APAIR) {
+        const uint4 v = kt >= nk ? make_uint4(0u, 0u, 0u, 0u) : rp[st][i];
+        const int ak = gsw(ar[i], ac[i] >> 3) + (ac[i] & 7);
+        *(uint2*)&Ah[buf][ar[i]][ak] = make_uint2(v.x, v.y);
+        *(uint2*)&Al[buf][ar[i]][ak] = make_uint2(v.z, v.w);
+        continue;
+      }
       if (kt >= nk) ra[st][i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (NORM) {
         float4& a = ra[st][i];
@@ -392,6 +414,11 @@ int gemm_splits(const GemmParams& p) {
 // sequences); it saves the two RMSNorm launches per layer: 4794 against 4483 tok/s at
 // batch 64 on the 70B shard, 2129 against 1958 on the 405B shard (both measured before the
 // register caps below).  The 128-row tiles keep the RMSNorm kernel.
+bool gemm_takes_pairs(const GemmParams& p) {
+  return p.wdtype == W_BF16 && !p.gain && !p.A2 && p.M > 64 && p.K % BK == 0 && p.lda % 4 == 0 &&
+         (!p.swiglu || (p.N % 2 == 0 && !p.res));
+}
+
 bool gemm_norm_fusable(const GemmParams& p) {
   if (skinny_supported(p)) return true;
   return p.wdtype == W_BF16 && p.M <= 64 && p.lda % 4 == 0 && p.K % BK == 0 && gemm_splits(p) > 1;
@@ -401,6 +428,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.M < 1 || p.N < 1 || p.K < 1) return hipErrorInvalidValue;
   if (skinny_supported(p)) return launch_skinny(p, s);
   if (p.A2) return hipErrorInvalidValue;   // a second K part: skinny launches only
+  if (p.a_pairs && !gemm_takes_pairs(p)) return hipErrorInvalidValue;
   if (p.wdtype == W_BF16) {
     if (p.K % BK != 0 || p.lda % 4 != 0 || (p.swiglu && (p.N % 2 != 0 || p.res))) return hipErrorInvalidValue;
     // 128x128 tiles (32x128 / 64x128 for at most 32 / 64 rows) when they give the device at
@@ -419,14 +447,16 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
         launch_timed(p.gain ? gemm_bf16x2_kernel<64, 128, true> : gemm_bf16x2_kernel<64, 128>, grid, dim3(256), 0, s,
                      p, tm, tiles, per, p.K / S);
       else
-        launch_timed(gemm_bf16x2_kernel<128, 128>, grid, dim3(256), 0, s, p, tm, tiles, per, p.K / S);
+        launch_timed(p.a_pairs ? gemm_bf16x2_kernel<128, 128, false, true> : gemm_bf16x2_kernel<128, 128>, grid,
+                     dim3(256), 0, s, p, tm, tiles, per, p.K / S);
       if (S > 1) {
         const size_t n_out = (size_t)p.M * (p.swiglu ? p.N / 2 : p.N);
         launch_timed(gemm_splitk_reduce_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, p, S);
       }
     } else {
       const int tm = (p.M + 63) / 64, tiles = tm * ((p.N + 63) / 64), per = (tiles + kXcds - 1) / kXcds;
-      launch_timed(gemm_bf16x2_kernel<64, 64>, dim3(per * kXcds), dim3(256), 0, s, p, tm, tiles, per, p.K);
+      launch_timed(p.a_pairs ? gemm_bf16x2_kernel<64, 64, false, true> : gemm_bf16x2_kernel<64, 64>, dim3(per * kXcds),
+                   dim3(256), 0, s, p, tm, tiles, per, p.K);
     }
   } else if (p.swiglu || p.gain) {
     return hipErrorInvalidValue;

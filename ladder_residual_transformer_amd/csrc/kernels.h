@@ -229,8 +229,12 @@ hipError_t launch_attn_prefill(const AttnPrefillParams& p, hipStream_t s);
 // swiglu (bf16 models, N even, rows interleaved gate/up): C[M][N/2] = silu(c[2n]) * c[2n+1].
 struct GemmParams {
   int wdtype;                          // W_BF16: MFMA on bf16 pairs of A and the bf16 weights; W_F32: VALU
-  // A: fp32 [M][lda] (lda a multiple of 4 for bf16 models)
+  // A: fp32 [M][lda] (lda a multiple of 4 for bf16 models); or, with a_pairs (bf16
+  // models, where gemm_takes_pairs() holds), A already split into bf16 pairs hi = bf16(a),
+  // lo = bf16(a - hi): row m holds lda / 4 groups of 16 bytes, the 4 hi then the 4 lo
+  // values of 4 consecutive columns (the bytes of an fp32 row)
   const void* A; int lda;
+  int a_pairs;
   RowSrc rows;
   int M, N, K;
   float* C; int ldc;
@@ -289,6 +293,9 @@ hipError_t launch_skinny_pair_attn(const GemmParams& a, const GemmParams& b, con
 size_t skinny_ws_floats(const GemmParams& p);
 // K slices launch_gemm uses for p (1: no split).
 int gemm_splits(const GemmParams& p);
+// Whether a launch can take A as bf16 pairs (GemmParams::a_pairs): bf16 weights,
+// more than 64 rows (the 128-row tiles), no folded RMSNorm.
+bool gemm_takes_pairs(const GemmParams& p);
 bool gemm_norm_fusable(const GemmParams& p);
 
 // ------------------------------------------------------------ launch timing
@@ -302,6 +309,12 @@ hipError_t launch_embed(int wdtype, const void* table, int V, int H, const int* 
 // out[m][:] = RMSNorm(x[m*ldx + :]) * gain (fp32)
 hipError_t launch_rmsnorm(int wdtype, const float* x, int ldx, const void* gain, float eps, int M, int H,
                           float* out, hipStream_t s);
+// The same RMSNorm with bf16 gains, its output split into bf16 pairs for a GEMM's a_pairs
+// input ([M][H / 4] groups of 4 hi then 4 lo values, the bytes of an fp32 [M][H] output);
+// each value is the fp32 RMSNorm output split as the GEMM would split it.  H and ldx
+// multiples of 4.
+hipError_t launch_rmsnorm_pairs(const float* x, int ldx, const void* gain, float eps, int M, int H, void* out,
+                                hipStream_t s);
 // qkv [B*T][q_rows + 2 kv_rows] -> q (rotated, fp32) and KV cache rows p0..p0+T-1, with
 // p0 = *d_pos when d_pos is set (read when the kernel runs), else start_pos
 hipError_t launch_rope_kv(int wdtype, const float* qkv, int B, int T, int start_pos, const int* d_pos, int nq, int nkv, int hd,

@@ -723,6 +723,17 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
         return LADDER_OK;
       }
     }
+    if (ctx->wdt == W_BF16) {
+      // A as bf16 pairs, split once here instead of once per column tile of the GEMM
+      GemmParams t = gp;
+      t.A = sc.u;
+      t.a_pairs = 1;
+      if (gemm_takes_pairs(t)) {
+        HIPCHK(launch_rmsnorm_pairs(xin, g.hidden, gain, g.norm_eps, M, g.hidden, sc.u, s));
+        gp = t;
+        return LADDER_OK;
+      }
+    }
     HIPCHK(launch_rmsnorm(ctx->wdt, xin, g.hidden, gain, g.norm_eps, M, g.hidden, sc.u, s));
     gp.A = sc.u;
     return LADDER_OK;
