@@ -287,7 +287,20 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
           if (row < p.M && col < p.N) p.ws[((size_t)slice * p.M + row) * p.N + col] = v;
         } else if (p.swiglu) {
           const float up = __shfl_xor(v, 1, 64);
-          if (!(col & 1) && row < p.M && col < p.N) p.C[(size_t)row * p.ldc + (col >> 1)] = silu(v) * up;
+          const float y = silu(v) * up;
+          if (p.c_pairs) {
+            // the output as bf16 pairs: lanes fr = 0 and 8 of each row gather the values of
+            // the three even lanes after them (four consecutive outputs) and store one group
+            const float y1 = __shfl(y, lane + 2, 64), y2 = __shfl(y, lane + 4, 64), y3 = __shfl(y, lane + 6, 64);
+            if ((fr & 7) == 0 && row < p.M && col < p.N) {
+              uint32_t h0, l0, h1, l1;
+              split_bf2(y, y1, h0, l0);
+              split_bf2(y2, y3, h1, l1);
+              *(uint4*)((uint16_t*)p.C + 2 * ((size_t)row * p.ldc + (col >> 1))) = make_uint4(h0, h1, l0, l1);
+            }
+          } else if (!(col & 1) && row < p.M && col < p.N) {
+            p.C[(size_t)row * p.ldc + (col >> 1)] = y;
+          }
         } else if (row < p.M && col < p.N) {
           if (p.res) v = p.res[(size_t)row * p.ldr + col] + v;
           p.C[(size_t)row * p.ldc + col] = v;
@@ -419,6 +432,11 @@ bool gemm_takes_pairs(const GemmParams& p) {
          (!p.swiglu || (p.N % 2 == 0 && !p.res));
 }
 
+bool gemm_writes_pairs(const GemmParams& p) {
+  return p.wdtype == W_BF16 && p.swiglu && !p.gain && !p.A2 && !p.res && p.M > 64 && p.N % 16 == 0 &&
+         p.ldc % 4 == 0 && p.K % BK == 0 && p.lda % 4 == 0 && gemm_splits(p) == 1;
+}
+
 bool gemm_norm_fusable(const GemmParams& p) {
   if (skinny_supported(p)) return true;
   return p.wdtype == W_BF16 && p.M <= 64 && p.lda % 4 == 0 && p.K % BK == 0 && gemm_splits(p) > 1;
@@ -429,6 +447,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (skinny_supported(p)) return launch_skinny(p, s);
   if (p.A2) return hipErrorInvalidValue;   // a second K part: skinny launches only
   if (p.a_pairs && !gemm_takes_pairs(p)) return hipErrorInvalidValue;
+  if (p.c_pairs && !gemm_writes_pairs(p)) return hipErrorInvalidValue;
   if (p.wdtype == W_BF16) {
     if (p.K % BK != 0 || p.lda % 4 != 0 || (p.swiglu && (p.N % 2 != 0 || p.res))) return hipErrorInvalidValue;
     // 128x128 tiles (32x128 / 64x128 for at most 32 / 64 rows) when they give the device at

@@ -240,6 +240,9 @@ struct GemmParams {
   float* C; int ldc;
   const float* res; int ldr;
   int swiglu;
+  // c_pairs (SwiGLU launches where gemm_writes_pairs() holds): C is written as bf16 pairs
+  // in a_pairs' layout, ready to be the A of the next projection ([M][ldc / 4] groups)
+  int c_pairs;
   // split-K partials (nullable: no split); kGemmSplitWsFloats floats cover any split the
   // launcher chooses
   float* ws; size_t ws_floats;
@@ -296,6 +299,9 @@ int gemm_splits(const GemmParams& p);
 // Whether a launch can take A as bf16 pairs (GemmParams::a_pairs): bf16 weights,
 // more than 64 rows (the 128-row tiles), no folded RMSNorm.
 bool gemm_takes_pairs(const GemmParams& p);
+// Whether a SwiGLU launch can write its output as bf16 pairs (GemmParams::c_pairs): the
+// tiled kernel without split K, more than 64 rows.
+bool gemm_writes_pairs(const GemmParams& p);
 bool gemm_norm_fusable(const GemmParams& p);
 
 // ------------------------------------------------------------ launch timing

@@ -790,6 +790,14 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
       gp.swiglu = 1;
       gp.C = sc.ab;
       gp.ldc = g.ffn;
+      // its output as bf16 pairs where the down projection takes them (prefill)
+      GemmParams d{};
+      d.wdtype = ctx->wdt;
+      d.M = M;
+      d.N = g.hidden;
+      d.K = g.ffn;
+      d.lda = g.ffn;
+      gp.c_pairs = gemm_writes_pairs(gp) && gemm_takes_pairs(d);
       if (T == 1) TRACE(LADDER_KERNEL_GATEUP, s, false);   // a decode step on the matrix cores
       HIPCHK(launch_gemm(gp, s));
       if (T == 1) TRACE(LADDER_KERNEL_GATEUP, s, true);
@@ -809,6 +817,7 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
   op.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
   op.cnt = sc.skcnt;
   op.A = proj_in;
+  op.a_pairs = proj_in == sc.ab && gp.c_pairs;
   op.lda = proj_k;
   op.rows = RowSrc{{proj_w, nullptr, nullptr}, g.hidden, g.hidden, 0};
   op.M = M;
