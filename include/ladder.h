@@ -79,7 +79,7 @@ typedef int32_t ladder_status;
                                     + both residual adds] while the first launch keeps two
                                     workgroups per CU, else as FUSED_LATE_ATTN; fp32:
                                     [QKV | gate/up], [attention | down], [O + both adds]
-                                    (default) */
+                                    (default); prefill as DUAL */
 #define LADDER_SCHED_PERSISTENT 4 /* decode: the whole layer stack in one launch of resident
                                     workgroups that signal each other (every layer ladder,
                                     bf16, a batch the row-wave GEMV takes, see
