@@ -444,7 +444,8 @@ bool gemm_norm_fusable(const GemmParams& p) {
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.M < 1 || p.N < 1 || p.K < 1) return hipErrorInvalidValue;
-  if (skinny_supported(p)) return launch_skinny(p, s);
+  // (bf16 pairs in or out: the tiled kernel, for more than 64 rows)
+  if (!p.a_pairs && !p.c_pairs && skinny_supported(p)) return launch_skinny(p, s);
   if (p.A2) return hipErrorInvalidValue;   // a second K part: skinny launches only
   if (p.a_pairs && !gemm_takes_pairs(p)) return hipErrorInvalidValue;
   if (p.c_pairs && !gemm_writes_pairs(p)) return hipErrorInvalidValue;

@@ -455,7 +455,7 @@ size_t sk_need(const SkProb& q) {
 bool sk_rows_ok(const RowSrc& r) { return r.interleave || (r.n0 % 16 == 0 && r.n1 % 16 == 0); }
 
 bool sk_ok(const GemmParams& p) {
-  if (p.wdtype != W_BF16 || p.a_pairs || p.c_pairs || p.M < 1 || p.M > kSkMaxM || !p.cnt || !p.ws || p.N % 16 || p.K % 64 || p.lda % 4 ||
+  if (p.wdtype != W_BF16 || p.M < 1 || p.M > kSkMaxM || !p.cnt || !p.ws || p.N % 16 || p.K % 64 || p.lda % 4 ||
       !sk_rows_ok(p.rows) || (p.A2 && !sk_rows_ok(p.rows2)) ||
       (p.res && p.ldr % 4) || (!p.swiglu && p.ldc % 4) || (p.swiglu && (p.ldc % 2 || p.res)))
     return false;
