@@ -69,7 +69,7 @@ constexpr int kStages = 4;   // K steps whose global loads are in flight (even: 
 
 // TM x TN workgroup tile (128x128, or 64x64 when the big tiles would not fill the
 // device), 4 waves of (TM/2) x (TN/2), i.e. (TM/32) x (TN/32) MFMA tiles of 16x16 each.
-// Slice s of S covers K range [s * kchunk, + kchunk); with more than one
+// Slice s of S covers K steps [s * nst / S, (s + 1) * nst / S) of the nst = K / 32; with more than one
 // slice the raw partial tile goes to p.ws[slice][M][N].
 // Register caps: two waves per SIMD for 128-row tiles (two workgroups per CU instead of
 // one) and for 64-row tiles with the folded RMSNorm, three for the other 64-row tiles and
@@ -82,7 +82,7 @@ constexpr int kStages = 4;   // K steps whose global loads are in flight (even: 
 // producer instead of once per column tile).
 template <int TM, int TN, bool NORM = false, bool APAIR = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 128 || (TM == 64 && NORM) ? 2 : TM == 64 ? 3 : 4)))
-void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, int kchunk) {
+void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, int nst) {
   static_assert(!(NORM && APAIR), "the folded RMSNorm takes fp32 rows");
   constexpr int FM = TM / 32, FN = TN / 32;       // MFMA tiles per wave
   constexpr int AV = TM * BK / 4 / 256;           // float4 of A per thread per K step
@@ -97,7 +97,8 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int m0 = (tile % n_tiles_m) * TM, n0 = (tile / n_tiles_m) * TN;
-  const int kbase = slice * kchunk;
+  const int st0 = slice * nst / S;
+  const int kbase = st0 * BK;
   const float* A = (const float*)p.A + kbase;
   const uint16_t* Ap = (const uint16_t*)p.A + 2 * kbase;                      // APAIR
 
@@ -138,7 +139,7 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
   float sq[AV];
 #pragma unroll
   for (int i = 0; i < AV; ++i) sq[i] = 0.f;
-  const int nk = kchunk / BK;
+  const int nk = (slice + 1) * nst / S - st0;
   const int nkp = (nk + kStages - 1) / kStages * kStages;   // steps padded to whole ring turns
   // Stage indices are compile-time constants (std::integral_constant), so that the ring
   // stays in registers.  Step kt's loads into stage ST (steps past the slice load its last
@@ -410,6 +411,9 @@ int gemm_splits(const GemmParams& p) {
   // steps long, partials (and the fused norm's row sums) within the workspace
   const int tmr = gemm_tile_rows(p);
   const int big = ((p.M + tmr - 1) / tmr) * ((p.N + 127) / 128);
+  // (slices of unequal length, as many as fill one round at the register caps' occupancy,
+  // measured 5057 against 4926 tok/s at batch 64 on the 70B shard but 2257 against 2297 on
+  // the 405B shard and a slower prefill: not taken)
   const int want = tmr < 128 ? 512 : 256;
   int S = 1;
   if (big < 256) {
@@ -462,13 +466,13 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
       const dim3 grid(per * kXcds, S);
       if (tmr == 32)
         launch_timed(p.gain ? gemm_bf16x2_kernel<32, 128, true> : gemm_bf16x2_kernel<32, 128>, grid, dim3(256), 0, s, p,
-                     tm, tiles, per, p.K / S);
+                     tm, tiles, per, p.K / BK);
       else if (tmr == 64)
         launch_timed(p.gain ? gemm_bf16x2_kernel<64, 128, true> : gemm_bf16x2_kernel<64, 128>, grid, dim3(256), 0, s,
-                     p, tm, tiles, per, p.K / S);
+                     p, tm, tiles, per, p.K / BK);
       else
         launch_timed(p.a_pairs ? gemm_bf16x2_kernel<128, 128, false, true> : gemm_bf16x2_kernel<128, 128>, grid,
-                     dim3(256), 0, s, p, tm, tiles, per, p.K / S);
+                     dim3(256), 0, s, p, tm, tiles, per, p.K / BK);
       if (S > 1) {
         const size_t n_out = (size_t)p.M * (p.swiglu ? p.N / 2 : p.N);
         launch_timed(gemm_splitk_reduce_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, p, S);
@@ -476,7 +480,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     } else {
       const int tm = (p.M + 63) / 64, tiles = tm * ((p.N + 63) / 64), per = (tiles + kXcds - 1) / kXcds;
       launch_timed(p.a_pairs ? gemm_bf16x2_kernel<64, 64, false, true> : gemm_bf16x2_kernel<64, 64>, dim3(per * kXcds),
-                   dim3(256), 0, s, p, tm, tiles, per, p.K);
+                   dim3(256), 0, s, p, tm, tiles, per, p.K / BK);
     }
   } else if (p.swiglu || p.gain) {
     return hipErrorInvalidValue;
