@@ -38,7 +38,8 @@ DOMINANT = {
     # down projection's launch: the [QKV | gate/up] launch
     "fused3": ("qkv_gateup", "fused ladder launch [RMSNorm+QKV | RMSNorm+gate/up+SwiGLU]: the row-wave launch "
                "(RoPE+KV in its epilogue) or, at batches on the matrix cores without the attention in the "
-               "launch, the skinny weight-streaming launch (skinny.hip)",
+               "launch, the skinny weight-streaming launch (skinny.hip), or at 33-64 sequences the tiled "
+               "split-K launch of both projections with their two reductions (gemm.hip)",
                "traffic_qkv_gateup_70b_b1.json",
                ("gemv_rw.hip", "gemv_rw.hpp", "attn_decode.hpp", "common.hpp")),
     "persistent": ("layer_stack", "persistent decode launch of the whole layer stack (every projection, "

@@ -80,9 +80,9 @@ constexpr int kStages = 4;   // K steps whose global loads are in flight (even: 
 // APAIR: A arrives already split into bf16 pairs (p.a_pairs: 16 bytes per 4 columns, their
 // 4 hi then their 4 lo values) and goes into LDS as it is (the split is done once by A's
 // producer instead of once per column tile).
-template <int TM, int TN, bool NORM = false, bool APAIR = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 128 || (TM == 64 && NORM) ? 2 : TM == 64 ? 3 : 4)))
-void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, int nst) {
+// One workgroup's tile (tile, slice of S) of problem p.
+template <int TM, int TN, bool NORM, bool APAIR>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int slice, int S, int n_tiles_m, int nst) {
   static_assert(!(NORM && APAIR), "the folded RMSNorm takes fp32 rows");
   constexpr int FM = TM / 32, FN = TN / 32;       // MFMA tiles per wave
   constexpr int AV = TM * BK / 4 / 256;           // float4 of A per thread per K step
@@ -91,9 +91,6 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
   __shared__ __attribute__((aligned(16))) uint16_t Ah[2][TM][BK];
   __shared__ __attribute__((aligned(16))) uint16_t Al[2][TM][BK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TN][BK];
-  const int tile = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int slice = blockIdx.y, S = gridDim.y;
-  if (tile >= n_tiles) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int m0 = (tile % n_tiles_m) * TM, n0 = (tile / n_tiles_m) * TN;
@@ -310,6 +307,36 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
     }
 }
 
+template <int TM, int TN, bool NORM = false, bool APAIR = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 128 || (TM == 64 && NORM) ? 2 : TM == 64 ? 3 : 4)))
+void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, int nst) {
+  const int tile = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (tile >= n_tiles) return;
+  gemm_tile<TM, TN, NORM, APAIR>(p, tile, blockIdx.y, gridDim.y, n_tiles_m, nst);
+}
+
+// Two split-K problems of one row tile (64 rows) in one launch: items [0, items0) are the
+// first problem's (column run x of its tile list on XCD x, then slice), the rest the
+// second's; each problem's tiles, slices and partials are those of its own launch.
+struct GemmPairArgs {
+  GemmParams p[2];
+  int n_tiles[2], per_xcd[2], S[2], nst[2];
+  int items0;
+};
+
+template <bool NORM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NORM ? 2 : 3)))
+void gemm_pair_kernel(GemmPairArgs a) {
+  int b = (int)blockIdx.x;
+  const int q = b >= a.items0 ? 1 : 0;
+  if (q) b -= a.items0;
+  const int W = a.per_xcd[q] * kXcds;
+  const int x = b % W;
+  const int tile = (x % kXcds) * a.per_xcd[q] + x / kXcds;
+  if (tile >= a.n_tiles[q]) return;
+  gemm_tile<64, 128, NORM, false>(a.p[q], tile, b / W, a.S[q], 1, a.nst[q]);
+}
+
 // C = (res +) sum over the S slices of ws[s] in slice order, or with swiglu
 // C[m][n] = silu(g) * u of the summed columns 2n, 2n+1.  One thread per output element.
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmParams p, int S) {
@@ -444,6 +471,40 @@ bool gemm_writes_pairs(const GemmParams& p) {
 bool gemm_norm_fusable(const GemmParams& p) {
   if (skinny_supported(p)) return true;
   return p.wdtype == W_BF16 && p.M <= 64 && p.lda % 4 == 0 && p.K % BK == 0 && gemm_splits(p) > 1;
+}
+
+bool gemm_pair_ok(const GemmParams& a, const GemmParams& b) {
+  auto one = [](const GemmParams& p) {
+    return p.wdtype == W_BF16 && !p.A2 && !p.a_pairs && !p.c_pairs && p.M > 32 && p.M <= 64 && p.K % BK == 0 &&
+           p.lda % 4 == 0 && (!p.swiglu || (p.N % 2 == 0 && !p.res)) && p.ws && gemm_splits(p) > 1 &&
+           !skinny_supported(p);
+  };
+  return one(a) && one(b) && a.M == b.M && (a.gain != nullptr) == (b.gain != nullptr) && a.ws != b.ws;
+}
+
+hipError_t launch_gemm_pair(const GemmParams& a, const GemmParams& b, hipStream_t s) {
+  if (!gemm_pair_ok(a, b)) return hipErrorInvalidValue;
+  GemmPairArgs g{};
+  const GemmParams* q[2] = {&a, &b};
+  int items = 0;
+  for (int i = 0; i < 2; ++i) {
+    const GemmParams& p = *q[i];
+    g.p[i] = p;
+    g.n_tiles[i] = (p.N + 127) / 128;
+    g.per_xcd[i] = (g.n_tiles[i] + kXcds - 1) / kXcds;
+    g.S[i] = gemm_splits(p);
+    g.nst[i] = p.K / BK;
+    if (i == 0) g.items0 = g.per_xcd[0] * kXcds * g.S[0];
+    items += g.per_xcd[i] * kXcds * g.S[i];
+  }
+  if (a.gain) launch_timed(gemm_pair_kernel<true>, dim3(items), dim3(256), 0, s, g);
+  else launch_timed(gemm_pair_kernel<false>, dim3(items), dim3(256), 0, s, g);
+  for (int i = 0; i < 2; ++i) {
+    const GemmParams& p = *q[i];
+    const size_t n_out = (size_t)p.M * (p.swiglu ? p.N / 2 : p.N);
+    launch_timed(gemm_splitk_reduce_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, p, g.S[i]);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {

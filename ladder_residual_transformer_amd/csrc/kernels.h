@@ -299,6 +299,12 @@ int gemm_splits(const GemmParams& p);
 // Whether a launch can take A as bf16 pairs (GemmParams::a_pairs): bf16 weights,
 // more than 64 rows (the 128-row tiles), no folded RMSNorm.
 bool gemm_takes_pairs(const GemmParams& p);
+// Two projections of 33-64 rows that each take a split-K tiled launch (gemm_splits() > 1,
+// their own workspaces), with or without the folded RMSNorm in both: one launch of both
+// problems' workgroups, then each problem's reduction; the same bits as launch_gemm of
+// each.
+bool gemm_pair_ok(const GemmParams& a, const GemmParams& b);
+hipError_t launch_gemm_pair(const GemmParams& a, const GemmParams& b, hipStream_t s);
 // Whether a SwiGLU launch can write its output as bf16 pairs (GemmParams::c_pairs): the
 // tiled kernel without split K, more than 64 rows.
 bool gemm_writes_pairs(const GemmParams& p);

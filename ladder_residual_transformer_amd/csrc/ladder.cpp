@@ -133,6 +133,11 @@ struct ladder_ctx {
   int sched = LADDER_SCHED_FUSED;
   int use_graph = 1;
   bool gemm_step = false;            // a decode step is running through the prefill modules
+  // a decode step of 33-64 sequences through the tiled GEMMs: the next attention module's
+  // QKV launch also runs its layer's gate/up projection (pair_gu, ready when pair_next),
+  // and the MLP module then skips it (skip_gateup)
+  GemmParams pair_gu{};
+  bool pair_next = false, skip_gateup = false;
   // next-token rule: greedy, or a draw (temperature > 0) with an optional top-k cut
   float temperature = 0.f;
   int top_k = 0;
@@ -747,7 +752,15 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
     gp.C = sc.qkv;
     gp.ldc = nqkv;
     if ((nst = norm_input(L.attn_norm))) return nst;
-    HIPCHK(launch_gemm(gp, s));
+    if (ctx->pair_next && gemm_pair_ok(gp, ctx->pair_gu)) {
+      TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
+      HIPCHK(launch_gemm_pair(gp, ctx->pair_gu, s));
+      TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
+      ctx->skip_gateup = true;
+    } else {
+      HIPCHK(launch_gemm(gp, s));
+    }
+    ctx->pair_next = false;
     HIPCHK(launch_rope_kv(ctx->wdt, sc.qkv, B, T, start_pos, ctx->gemm_step ? ctx->pos_dev : nullptr, g.n_q_heads, g.n_kv_heads, g.head_dim, ctx->rope_cos,
                           ctx->rope_sin, sc.qr, layer_k(ctx, l), layer_v(ctx, l), g.max_seq, s));
     if (ctx->gemm_step) {
@@ -798,9 +811,13 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
       d.K = g.ffn;
       d.lda = g.ffn;
       gp.c_pairs = gemm_writes_pairs(gp) && gemm_takes_pairs(d);
-      if (T == 1) TRACE(LADDER_KERNEL_GATEUP, s, false);   // a decode step on the matrix cores
-      HIPCHK(launch_gemm(gp, s));
-      if (T == 1) TRACE(LADDER_KERNEL_GATEUP, s, true);
+      if (ctx->skip_gateup) {
+        ctx->skip_gateup = false;           // run with the layer's QKV projection
+      } else {
+        if (T == 1) TRACE(LADDER_KERNEL_GATEUP, s, false);   // a decode step on the matrix cores
+        HIPCHK(launch_gemm(gp, s));
+        if (T == 1) TRACE(LADDER_KERNEL_GATEUP, s, true);
+      }
     } else {
       gp.C = sc.gu;
       gp.ldc = 2 * g.ffn;
@@ -1204,6 +1221,35 @@ ladder_status decode_layer_skinny(ladder_ctx* ctx, int l, int B, hipStream_t s) 
   return LADDER_OK;
 }
 
+// The gate/up projection of layer l's MLP module in a decode step on the matrix cores, as
+// prefill_module builds it (RMSNorm folded in), with its split-K partials in the second
+// stream scratch's workspace (the QKV launch beside it uses the first's); false where the
+// fold does not apply (the module then runs it alone).
+bool gateup_pair_params(ladder_ctx* ctx, int l, int B, const float* xin, GemmParams* out) {
+  const ladder_config& g = ctx->cfg;
+  const ladder_layer_weights& L = ctx->layers[l];
+  if (ctx->wdt != W_BF16 || !ctx->sc[1].gk) return false;
+  GemmParams t{};
+  t.wdtype = ctx->wdt;
+  t.M = B;
+  t.ws = ctx->sc[1].gk;
+  t.ws_floats = kGemmSplitWsFloats;
+  t.cnt = ctx->sc[1].skcnt;
+  t.rows = RowSrc{{L.w_gate, L.w_up, nullptr}, 0, 0, 1};
+  t.N = 2 * g.ffn;
+  t.K = g.hidden;
+  t.swiglu = 1;
+  t.lda = g.hidden;
+  t.A = xin;
+  t.gain = L.mlp_norm;
+  t.eps = g.norm_eps;
+  t.C = module_scratch(ctx, 2 * l + 1).ab;
+  t.ldc = g.ffn;
+  if (!gemm_norm_fusable(t)) return false;
+  *out = t;
+  return true;
+}
+
 ladder_status enqueue_decode_gemm(ladder_ctx* ctx, int B) {
   const int pos = 0;   // unused: every kernel reads the position from pos_dev
   const ladder_config& g = ctx->cfg;
@@ -1225,6 +1271,16 @@ ladder_status enqueue_decode_gemm(ladder_ctx* ctx, int B) {
         for (int m = 2 * l; m < 2 * l + 2 && !st; ++m)
           st = mod(m, X[module_src(ctx, m) % 2], X[m % 2], X[(m + 1) % 2], nullptr, ctx->s0, false, nullptr);
       }
+    }
+  } else if (fused) {
+    // module order (the adds in the GEMM epilogues); a ladder or parallel layer's gate/up
+    // projection (its input exists when the layer starts) shares the QKV launch
+    float* const* X = ctx->dx;
+    for (int l = 0; l < g.n_layers && !st; ++l) {
+      if (ctx->mask[l]) ctx->pair_next = gateup_pair_params(ctx, l, B, X[module_src(ctx, 2 * l + 1) % 2], &ctx->pair_gu);
+      for (int m = 2 * l; m < 2 * l + 2 && !st; ++m)
+        st = mod(m, X[module_src(ctx, m) % 2], X[m % 2], X[(m + 1) % 2], nullptr, ctx->s0, false, nullptr);
+      ctx->pair_next = ctx->skip_gateup = false;
     }
   } else {
     st = run_modules(ctx, ctx->dx, ctx->dout, (size_t)B * g.hidden, mod, fused);
