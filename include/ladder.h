@@ -178,7 +178,8 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
  * cores (with the split-KV decode attention), under every schedule: up to 32 sequences
  * through skinny weight-streaming launches (a ladder layer in two launches under the
  * FUSED schedules, [QKV + RoPE/KV | attention | gate/up] and [O + down], module by module
- * otherwise, with the same bits), beyond that through tiled GEMMs. */
+ * otherwise, with the same bits), beyond that through tiled GEMMs (under the FUSED
+ * schedules a ladder or parallel layer's QKV and gate/up projections in one launch). */
 ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t pos,
                                  float* d_logits, int32_t* d_next, float* d_hidden);
 
@@ -243,7 +244,10 @@ ladder_status ladder_sync(ladder_ctx* ctx);
 #define LADDER_KERNEL_GATEUP 3   /* RMSNorm + [Wgate,Wup] GEMV + SwiGLU */
 #define LADDER_KERNEL_DOWN 4     /* Wdown GEMV + fused residual add */
 #define LADDER_KERNEL_LMHEAD 5   /* final RMSNorm + LM head GEMV + greedy argmax */
-#define LADDER_KERNEL_QKV_GATEUP 6  /* fused ladder launch: QKV (+RoPE/KV) | gate/up (+SwiGLU) */
+#define LADDER_KERNEL_QKV_GATEUP 6  /* fused ladder launch: QKV (+RoPE/KV) | gate/up (+SwiGLU); at
+                                       33-64 sequences on the matrix cores the tiled split-K launch
+                                       of both projections with their reductions (traced, not
+                                       replayed by ladder_time_kernels) */
 #define LADDER_KERNEL_ATTN_DOWN 7   /* fused ladder launch: decode attention | down projection; with
                                        bf16 weights and a row-wave batch followed, in the same launch, by
                                        the O projection + both residual adds */
