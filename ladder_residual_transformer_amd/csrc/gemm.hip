@@ -317,7 +317,8 @@ void gemm_bf16x2_kernel(GemmParams p, int n_tiles_m, int n_tiles, int per_xcd, i
 
 // Two split-K problems of one row tile (64 rows) in one launch: items [0, items0) are the
 // first problem's (column run x of its tile list on XCD x, then slice), the rest the
-// second's; each problem's tiles, slices and partials are those of its own launch.
+// second's; each problem's tiles, slices and partials are those of its own launch, and
+// one reduction launch then serves both.
 struct GemmPairArgs {
   GemmParams p[2];
   int n_tiles[2], per_xcd[2], S[2], nst[2];
@@ -339,9 +340,8 @@ void gemm_pair_kernel(GemmPairArgs a) {
 
 // C = (res +) sum over the S slices of ws[s] in slice order, or with swiglu
 // C[m][n] = silu(g) * u of the summed columns 2n, 2n+1.  One thread per output element.
-__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmParams p, int S) {
+__device__ __forceinline__ void splitk_reduce(const GemmParams& p, int S, size_t e) {
   const int NO = p.swiglu ? p.N / 2 : p.N;
-  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= (size_t)p.M * NO) return;
   const int m = (int)(e / NO), n = (int)(e % NO);
   const size_t plane = (size_t)p.M * p.N;
@@ -375,6 +375,18 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmParams p, i
     if (p.res) v = p.res[(size_t)m * p.ldr + n] + v;
     p.C[(size_t)m * p.ldc + n] = v;
   }
+}
+
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmParams p, int S) {
+  splitk_reduce(p, S, (size_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+// The reductions of a pair launch in one launch: blocks [0, blocks0) reduce problem a.
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_pair_kernel(GemmParams a, int Sa, GemmParams b, int Sb,
+                                                                      int blocks0) {
+  const int bi = (int)blockIdx.x;
+  if (bi < blocks0) splitk_reduce(a, Sa, (size_t)bi * 256 + threadIdx.x);
+  else splitk_reduce(b, Sb, (size_t)(bi - blocks0) * 256 + threadIdx.x);
 }
 
 constexpr int FT = 64, FK = 16;
@@ -499,11 +511,13 @@ hipError_t launch_gemm_pair(const GemmParams& a, const GemmParams& b, hipStream_
   }
   if (a.gain) launch_timed(gemm_pair_kernel<true>, dim3(items), dim3(256), 0, s, g);
   else launch_timed(gemm_pair_kernel<false>, dim3(items), dim3(256), 0, s, g);
+  unsigned blocks[2];
   for (int i = 0; i < 2; ++i) {
     const GemmParams& p = *q[i];
-    const size_t n_out = (size_t)p.M * (p.swiglu ? p.N / 2 : p.N);
-    launch_timed(gemm_splitk_reduce_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, p, g.S[i]);
+    blocks[i] = (unsigned)(((size_t)p.M * (p.swiglu ? p.N / 2 : p.N) + 255) / 256);
   }
+  launch_timed(gemm_splitk_reduce_pair_kernel, dim3(blocks[0] + blocks[1]), dim3(256), 0, s, a, g.S[0], b, g.S[1],
+               (int)blocks[0]);
   return hipGetLastError();
 }
 
