@@ -377,16 +377,66 @@ __device__ __forceinline__ void splitk_reduce(const GemmParams& p, int S, size_t
   }
 }
 
+// The reduction of a decode step's QKV projection with rope_kv's epilogue (bf16 caches): a
+// thread sums the partials of two neighbouring outputs (n even) as splitk_reduce does, then
+// rotates the q and k pairs (d, d + 1) and writes q to rope_q, k and v to the caches at
+// position *d_pos, with rope_kv's arithmetic on the same fp32 values.
+__device__ __forceinline__ void splitk_reduce_rope(const GemmParams& p, int S, size_t e) {
+  const int NP = p.N / 2;
+  if (e >= (size_t)p.M * NP) return;
+  const int m = (int)(e / NP), n = 2 * (int)(e % NP);
+  const size_t plane = (size_t)p.M * p.N;
+  float inv = 1.f;
+  if (p.gain) {
+    const float* q = p.ws + (size_t)S * plane + m;
+    float t = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) t += q[(size_t)s * p.M];
+    inv = 1.0f / sqrtf(t / (float)p.K + p.eps);
+  }
+  const float* w = p.ws + (size_t)m * p.N + n;
+  float v0 = 0.f, v1 = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < S; ++s) {
+    v0 += w[s * plane];
+    v1 += w[s * plane + 1];
+  }
+  if (p.gain) {
+    v0 *= inv;
+    v1 *= inv;
+  }
+  const int qr = p.nq * p.hd, kr = p.nkv * p.hd, pos = *gbl(p.d_pos);
+  uint16_t* dst;
+  if (n < qr + kr) {
+    const int d = (n < qr ? n : n - qr) % p.hd;
+    const float c = p.rope_cos[(size_t)pos * (p.hd / 2) + d / 2], sn = p.rope_sin[(size_t)pos * (p.hd / 2) + d / 2];
+    rope_rot(v0, v1, c, sn);
+    if (n < qr) {
+      p.rope_q[(size_t)m * qr + n] = v0;
+      p.rope_q[(size_t)m * qr + n + 1] = v1;
+      return;
+    }
+    dst = (uint16_t*)p.k_cache + (((size_t)m * p.nkv + (n - qr) / p.hd) * p.max_seq + pos) * p.hd + d;
+  } else {
+    const int i = n - qr - kr;
+    dst = (uint16_t*)p.v_cache + (((size_t)m * p.nkv + i / p.hd) * p.max_seq + pos) * p.hd + i % p.hd;
+  }
+  store_w<uint16_t>(dst, v0);
+  store_w<uint16_t>(dst + 1, v1);
+}
+
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmParams p, int S) {
   splitk_reduce(p, S, (size_t)blockIdx.x * 256 + threadIdx.x);
 }
 
-// The reductions of a pair launch in one launch: blocks [0, blocks0) reduce problem a.
+// The reductions of a pair launch in one launch: blocks [0, blocks0) reduce problem a
+// (with the RoPE + KV epilogue where a.rope_q is set).
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_pair_kernel(GemmParams a, int Sa, GemmParams b, int Sb,
                                                                       int blocks0) {
   const int bi = (int)blockIdx.x;
-  if (bi < blocks0) splitk_reduce(a, Sa, (size_t)bi * 256 + threadIdx.x);
-  else splitk_reduce(b, Sb, (size_t)(bi - blocks0) * 256 + threadIdx.x);
+  if (bi >= blocks0) splitk_reduce(b, Sb, (size_t)(bi - blocks0) * 256 + threadIdx.x);
+  else if (a.rope_q) splitk_reduce_rope(a, Sa, (size_t)bi * 256 + threadIdx.x);
+  else splitk_reduce(a, Sa, (size_t)bi * 256 + threadIdx.x);
 }
 
 constexpr int FT = 64, FK = 16;
@@ -491,7 +541,13 @@ bool gemm_pair_ok(const GemmParams& a, const GemmParams& b) {
            p.lda % 4 == 0 && (!p.swiglu || (p.N % 2 == 0 && !p.res)) && p.ws && gemm_splits(p) > 1 &&
            !skinny_supported(p);
   };
-  return one(a) && one(b) && a.M == b.M && (a.gain != nullptr) == (b.gain != nullptr) && a.ws != b.ws;
+  // a.rope_q: the first problem is a decode step's QKV projection whose reduction runs
+  // rope_kv's epilogue (bf16 caches, the skinny launches' conditions on the rope fields)
+  const bool rope_ok = !a.rope_q || (!a.swiglu && !a.res && a.k_cache && a.v_cache && a.rope_cos && a.rope_sin &&
+                                     a.d_pos && a.hd >= 2 && a.hd % 2 == 0 && a.nq >= 1 && a.nkv >= 1 &&
+                                     a.max_seq >= 1 && a.N == (a.nq + 2 * a.nkv) * a.hd);
+  return one(a) && one(b) && !b.rope_q && rope_ok && a.M == b.M && (a.gain != nullptr) == (b.gain != nullptr) &&
+         a.ws != b.ws;
 }
 
 hipError_t launch_gemm_pair(const GemmParams& a, const GemmParams& b, hipStream_t s) {
@@ -514,7 +570,7 @@ hipError_t launch_gemm_pair(const GemmParams& a, const GemmParams& b, hipStream_
   unsigned blocks[2];
   for (int i = 0; i < 2; ++i) {
     const GemmParams& p = *q[i];
-    blocks[i] = (unsigned)(((size_t)p.M * (p.swiglu ? p.N / 2 : p.N) + 255) / 256);
+    blocks[i] = (unsigned)(((size_t)p.M * (p.swiglu || (i == 0 && p.rope_q) ? p.N / 2 : p.N) + 255) / 256);
   }
   launch_timed(gemm_splitk_reduce_pair_kernel, dim3(blocks[0] + blocks[1]), dim3(256), 0, s, a, g.S[0], b, g.S[1],
                (int)blocks[0]);

@@ -752,16 +752,31 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
     gp.C = sc.qkv;
     gp.ldc = nqkv;
     if ((nst = norm_input(L.attn_norm))) return nst;
-    if (ctx->pair_next && gemm_pair_ok(gp, ctx->pair_gu)) {
-      TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
-      HIPCHK(launch_gemm_pair(gp, ctx->pair_gu, s));
-      TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
-      ctx->skip_gateup = true;
-    } else {
-      HIPCHK(launch_gemm(gp, s));
+    bool paired = false;
+    if (ctx->pair_next && ctx->gemm_step) {
+      // with the layer's gate/up projection, RoPE + KV append in the QKV reduction
+      GemmParams r = gp;
+      r.rope_q = sc.qr;
+      r.k_cache = layer_k(ctx, l);
+      r.v_cache = layer_v(ctx, l);
+      r.rope_cos = ctx->rope_cos;
+      r.rope_sin = ctx->rope_sin;
+      r.d_pos = ctx->pos_dev;
+      r.nq = g.n_q_heads;
+      r.nkv = g.n_kv_heads;
+      r.hd = g.head_dim;
+      r.max_seq = g.max_seq;
+      if (gemm_pair_ok(r, ctx->pair_gu)) {
+        TRACE(LADDER_KERNEL_QKV_GATEUP, s, false);
+        HIPCHK(launch_gemm_pair(r, ctx->pair_gu, s));
+        TRACE(LADDER_KERNEL_QKV_GATEUP, s, true);
+        ctx->skip_gateup = true;
+        paired = true;
+      }
     }
     ctx->pair_next = false;
-    HIPCHK(launch_rope_kv(ctx->wdt, sc.qkv, B, T, start_pos, ctx->gemm_step ? ctx->pos_dev : nullptr, g.n_q_heads, g.n_kv_heads, g.head_dim, ctx->rope_cos,
+    if (!paired) HIPCHK(launch_gemm(gp, s));
+    if (!paired) HIPCHK(launch_rope_kv(ctx->wdt, sc.qkv, B, T, start_pos, ctx->gemm_step ? ctx->pos_dev : nullptr, g.n_q_heads, g.n_kv_heads, g.head_dim, ctx->rope_cos,
                           ctx->rope_sin, sc.qr, layer_k(ctx, l), layer_v(ctx, l), g.max_seq, s));
     if (ctx->gemm_step) {
       // a decode step (one query per sequence at *pos_dev): the split-KV decode attention
