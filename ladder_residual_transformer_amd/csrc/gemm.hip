@@ -439,6 +439,27 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_pair_kernel(GemmParams
   else splitk_reduce(a, Sa, (size_t)bi * 256 + threadIdx.x);
 }
 
+// The reduction of a chained pair (a: the O projection with its residual, b: the down
+// projection whose residual is a's output): per element x1 = res + sum(a) written to a.C,
+// then x1 + sum(b) to b.C, each sum in slice order as splitk_reduce adds it.
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_chain_kernel(GemmParams a, int Sa, GemmParams b, int Sb) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (size_t)a.M * a.N) return;
+  const int m = (int)(e / a.N), n = (int)(e % a.N);
+  const size_t plane = (size_t)a.M * a.N;
+  const float* wa = a.ws + (size_t)m * a.N + n;
+  float o = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < Sa; ++s) o += wa[s * plane];
+  const float x1 = a.res[(size_t)m * a.ldr + n] + o;
+  a.C[(size_t)m * a.ldc + n] = x1;
+  const float* wb = b.ws + (size_t)m * b.N + n;
+  float d = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < Sb; ++s) d += wb[s * plane];
+  b.C[(size_t)m * b.ldc + n] = x1 + d;
+}
+
 constexpr int FT = 64, FK = 16;
 
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
@@ -574,6 +595,32 @@ hipError_t launch_gemm_pair(const GemmParams& a, const GemmParams& b, hipStream_
   }
   launch_timed(gemm_splitk_reduce_pair_kernel, dim3(blocks[0] + blocks[1]), dim3(256), 0, s, a, g.S[0], b, g.S[1],
                (int)blocks[0]);
+  return hipGetLastError();
+}
+
+bool gemm_chain_ok(const GemmParams& a, const GemmParams& b) {
+  return !a.rope_q && !b.rope_q && !a.gain && !b.gain && !a.swiglu && !b.swiglu && gemm_pair_ok(a, b) &&
+         a.N == b.N && a.res && a.C && b.res == a.C && b.ldr == a.ldc && b.C && b.C != a.C && a.ws != b.ws;
+}
+
+hipError_t launch_gemm_chain(const GemmParams& a, const GemmParams& b, hipStream_t s) {
+  if (!gemm_chain_ok(a, b)) return hipErrorInvalidValue;
+  GemmPairArgs g{};
+  const GemmParams* q[2] = {&a, &b};
+  int items = 0;
+  for (int i = 0; i < 2; ++i) {
+    const GemmParams& p = *q[i];
+    g.p[i] = p;
+    g.n_tiles[i] = (p.N + 127) / 128;
+    g.per_xcd[i] = (g.n_tiles[i] + kXcds - 1) / kXcds;
+    g.S[i] = gemm_splits(p);
+    g.nst[i] = p.K / BK;
+    if (i == 0) g.items0 = g.per_xcd[0] * kXcds * g.S[0];
+    items += g.per_xcd[i] * kXcds * g.S[i];
+  }
+  launch_timed(gemm_pair_kernel<false>, dim3(items), dim3(256), 0, s, g);
+  launch_timed(gemm_splitk_reduce_chain_kernel, dim3((unsigned)(((size_t)a.M * a.N + 255) / 256)), dim3(256), 0, s, a,
+               g.S[0], b, g.S[1]);
   return hipGetLastError();
 }
 

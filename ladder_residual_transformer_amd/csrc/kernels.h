@@ -305,6 +305,11 @@ bool gemm_takes_pairs(const GemmParams& p);
 // each.
 bool gemm_pair_ok(const GemmParams& a, const GemmParams& b);
 hipError_t launch_gemm_pair(const GemmParams& a, const GemmParams& b, hipStream_t s);
+// A pair whose second problem adds onto the first's output (a: C = res + A.W^T, b: C =
+// a.C + A.W^T, the same N, no gain or SwiGLU): one launch of both, then one reduction
+// writing both outputs; the same bits as launch_gemm of a, then of b.
+bool gemm_chain_ok(const GemmParams& a, const GemmParams& b);
+hipError_t launch_gemm_chain(const GemmParams& a, const GemmParams& b, hipStream_t s);
 // Whether a SwiGLU launch can write its output as bf16 pairs (GemmParams::c_pairs): the
 // tiled kernel without split K, more than 64 rows.
 bool gemm_writes_pairs(const GemmParams& p);

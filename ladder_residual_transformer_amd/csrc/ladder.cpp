@@ -138,6 +138,9 @@ struct ladder_ctx {
   // and the MLP module then skips it (skip_gateup)
   GemmParams pair_gu{};
   bool pair_next = false, skip_gateup = false;
+  // and its O projection waits for the down projection (pair_o, when o_deferred)
+  GemmParams pair_o{};
+  bool o_deferred = false;
   // next-token rule: greedy, or a draw (temperature > 0) with an optional top-k cut
   float temperature = 0.f;
   int top_k = 0;
@@ -864,6 +867,26 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
   } else {
     op.C = out_store;
   }
+  if (m % 2 == 0 && ctx->skip_gateup && ctx->gemm_step && out_x && !wait_xm) {
+    // a paired layer's O projection waits for the down projection: one launch of both,
+    // and one reduction writing x_{2l+1} = x_{2l} + o and x_{2l+2} = x_{2l+1} + d
+    ctx->pair_o = op;
+    ctx->o_deferred = true;
+    return LADDER_OK;
+  }
+  if (m % 2 == 1 && ctx->o_deferred) {
+    ctx->o_deferred = false;
+    GemmParams d = op;
+    d.ws = ctx->sc[1].gk;             // the O partials take the first workspace
+    d.cnt = ctx->sc[1].skcnt;
+    if (gemm_chain_ok(ctx->pair_o, d)) {
+      TRACE(LADDER_KERNEL_DOWN_OPROJ, s, false);
+      HIPCHK(launch_gemm_chain(ctx->pair_o, d, s));
+      TRACE(LADDER_KERNEL_DOWN_OPROJ, s, true);
+      return LADDER_OK;
+    }
+    HIPCHK(launch_gemm(ctx->pair_o, s));
+  }
   HIPCHK(launch_gemm(op, s));
   return LADDER_OK;
 }
@@ -1296,6 +1319,10 @@ ladder_status enqueue_decode_gemm(ladder_ctx* ctx, int B) {
       for (int m = 2 * l; m < 2 * l + 2 && !st; ++m)
         st = mod(m, X[module_src(ctx, m) % 2], X[m % 2], X[(m + 1) % 2], nullptr, ctx->s0, false, nullptr);
       ctx->pair_next = ctx->skip_gateup = false;
+      if (ctx->o_deferred) {                // (not taken: the MLP module launches it)
+        ctx->o_deferred = false;
+        HIPCHK(launch_gemm(ctx->pair_o, ctx->s0));
+      }
     }
   } else {
     st = run_modules(ctx, ctx->dx, ctx->dout, (size_t)B * g.hidden, mod, fused);
