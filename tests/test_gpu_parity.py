@@ -412,6 +412,37 @@ def test_matrix_core_layer_launch_is_traced_with_its_attention(edge):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("B", [40, 64])
+def test_tiled_paired_launches_match_module_order(B):
+    """Batches 33-64 decode through the tiled split-K GEMMs.  Under the fused schedule a
+    ladder layer's [QKV | gate/up] run in one launch with one reduction (RMSNorm, RoPE + KV,
+    SwiGLU) and [O | down] in one launch whose reduction writes both residual adds; module
+    order (serial) launches each GEMM and its reduction alone.  The two must give the same
+    bits (70B shard widths, two ladder layers, so that K splits), the paired launch must be
+    traced once per layer, and tracing must leave every result unchanged."""
+    cfg = synth.scaled_config(synth.CONFIGS["70b_tp8_shard"], 2)
+    w = synth.gen_weights(cfg, seed=21)
+    prompt = synth.gen_ids(B, 6, cfg.vocab, seed=22)
+    cont = synth.gen_ids(B, 3, cfg.vocab, seed=22, stream=1)
+    outs = {}
+    for sched in (SERIAL, FUSED):
+        model = make_model(cfg, w, B, 16)
+        model.set_schedule(sched, True)
+        outs[sched] = gpu_teacher_forced(model, prompt, cont)
+        model.free()
+    for a, b in zip(outs[SERIAL], outs[FUSED]):
+        assert np.array_equal(a, b), "paired launches differ from module order"
+    model = make_model(cfg, w, B, 16)
+    model.trace_kernel("qkv_gateup")
+    traced = gpu_teacher_forced(model, prompt, cont)
+    us, n = model.trace_result()
+    log(f"tiled pairs B={B}: qkv_gateup launch {us:.1f} us over {n} launches")
+    assert n == cfg.n_layers and us > 0.0
+    model.free()
+    for a, b in zip(outs[FUSED], traced):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("B, T, max_seq, n_dec", [(2, 150, 256, 6), (1, 2100, 2200, 3)])
 def test_long_context_split_kv(edge, B, T, max_seq, n_dec):
     """Decode attention over several key chunks (150 keys in 64-key chunks, merged across
