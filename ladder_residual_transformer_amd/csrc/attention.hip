@@ -172,8 +172,9 @@ constexpr int kPkTile = 64;                  // keys per LDS tile
 template <int HD>
 struct PrefillLds {
   uint16_t ks[kPkTile][HD + 8];     // K tile, row = key (fp16)
-  uint16_t vt[HD][kPkTile + 8];     // V tile transposed, row = head dim (fp16)
+  uint16_t vt[HD][kPkTile + 8];     // V tile transposed, row = head dim (fp16), keys at vt_col
 };
+static_assert(kPkTile == kAttnKeyTile, "vt_col permutes the 16 key groups of a 64-key row");
 
 // MFMA 32x32x16 operand/result layout (lane l): A row l%32, B column l%32, k-slots
 // 8*(l/32)..+8; C column l%32, rows 8*(r/4) + 4*(l/32) + r%4 for result r = 0..15.
@@ -260,8 +261,8 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillParam
       const uint32_t* v1 = (const uint32_t*)&vr[i][1];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        *(uint32_t*)&L.vt[c * 8 + 2 * q][2 * j] = pack_h2(bf16_lo(v0[q]), bf16_lo(v1[q]));
-        *(uint32_t*)&L.vt[c * 8 + 2 * q + 1][2 * j] = pack_h2(bf16_hi(v0[q]), bf16_hi(v1[q]));
+        *(uint32_t*)&L.vt[c * 8 + 2 * q][vt_col(c * 8, 2 * j)] = pack_h2(bf16_lo(v0[q]), bf16_lo(v1[q]));
+        *(uint32_t*)&L.vt[c * 8 + 2 * q + 1][vt_col(c * 8, 2 * j)] = pack_h2(bf16_hi(v0[q]), bf16_hi(v1[q]));
       }
     }
   };
@@ -341,8 +342,8 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnPrefillParam
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
         const uint16_t* vrow = &L.vt[d * 32 + col][0];
-        const uint2 lo = *(const uint2*)(vrow + kbase);
-        const uint2 hi = *(const uint2*)(vrow + kbase + 8);
+        const uint2 lo = *(const uint2*)(vrow + vt_col(d * 32 + col, kbase));
+        const uint2 hi = *(const uint2*)(vrow + vt_col(d * 32 + col, kbase + 8));
         const half8 vf = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pfl, o[d], 0, 0, 0);
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pfh, o[d], 0, 0, 0);

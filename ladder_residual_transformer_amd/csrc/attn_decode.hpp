@@ -64,6 +64,13 @@ struct AttnLds<uint16_t, HD> {
   int is_last;
 };
 
+// Position of key k in row `dim` of the V^T tile: the 4-key groups of a row are permuted by
+// XOR with (dim / 8) % 16.  The transposing stores of a wave write one key pair into 16
+// rows 8 apart, whose unpermuted row starts (72 halves apart) all fall in one LDS bank (a
+// 16-way conflict, three quarters of the attention's LDS cycles); permuted, they spread
+// over the banks.  Reads of 4 keys (one group) stay contiguous.
+__device__ __forceinline__ int vt_col(int dim, int k) { return ((((k >> 2) ^ (dim >> 3)) & 15) << 2) | (k & 3); }
+
 // Keys per chunk at length len: whole tiles, the fewest that cover len with n_split chunks.
 __host__ __device__ inline int attn_chunk(int len, int n_split) {
   const int per = (len + n_split - 1) / n_split;
@@ -379,8 +386,8 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
       const uint32_t* v1 = (const uint32_t*)&vr[i][1];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        *(uint32_t*)&L.vt[c * 8 + 2 * q][2 * j] = pack_h2(bf16_lo(v0[q]), bf16_lo(v1[q]));
-        *(uint32_t*)&L.vt[c * 8 + 2 * q + 1][2 * j] = pack_h2(bf16_hi(v0[q]), bf16_hi(v1[q]));
+        *(uint32_t*)&L.vt[c * 8 + 2 * q][vt_col(c * 8, 2 * j)] = pack_h2(bf16_lo(v0[q]), bf16_lo(v1[q]));
+        *(uint32_t*)&L.vt[c * 8 + 2 * q + 1][vt_col(c * 8, 2 * j)] = pack_h2(bf16_hi(v0[q]), bf16_hi(v1[q]));
       }
     }
     __syncthreads();
@@ -434,7 +441,8 @@ __device__ void attn_decode_block_mfma(const AttnDecodeParams& p, int blk, AttnL
       const half4 bl = __builtin_bit_cast(half4, *(const uint2*)&L.ptl[col][16 * ks + 4 * grp]);
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
-        const half4 av = __builtin_bit_cast(half4, *(const uint2*)&L.vt[w * DPW + 16 * d + col][16 * ks + 4 * grp]);
+        const int vr = w * DPW + 16 * d + col;
+        const half4 av = __builtin_bit_cast(half4, *(const uint2*)&L.vt[vr][vt_col(vr, 16 * ks + 4 * grp)]);
         o[d] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bl, o[d], 0, 0, 0);
         o[d] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bh, o[d], 0, 0, 0);
       }
