@@ -54,8 +54,10 @@ template <int HD>
 struct AttnLds<uint16_t, HD> {
   __attribute__((aligned(16))) uint16_t ks[kAttnKeyTile][HD + 8];   // K, row = key
   __attribute__((aligned(16))) uint16_t vt[HD][kAttnKeyTile + 8];   // V^T, row = head dim
-  __attribute__((aligned(16))) uint16_t pth[16][kAttnKeyTile + 8];  // P^T hi, row = head
-  __attribute__((aligned(16))) uint16_t ptl[16][kAttnKeyTile + 8];  // P^T lo
+  // P^T hi and lo, row = head; rows of 68 halves (34 dwords): the 16 rows a pass of 8-byte
+  // accesses touches start 2 banks apart (with 72 halves, rows r and r + 8 shared banks)
+  __attribute__((aligned(16))) uint16_t pth[16][kAttnKeyTile + 4];
+  __attribute__((aligned(16))) uint16_t ptl[16][kAttnKeyTile + 4];
   float wmax[4][16];                                               // per wave and head
   float wsum[4][16];
   float wsc[kAttnMaxGroup][kAttnMaxSplits];
