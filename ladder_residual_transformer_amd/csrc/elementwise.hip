@@ -98,19 +98,40 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int ldx, c
 
 // rmsnorm_kernel's output (bf16 gains, H and ldx multiples of 4) split into bf16 pairs
 // hi = bf16(y), lo = bf16(y - hi), 16 bytes per 4 columns: their 4 hi, then their 4 lo.
+// V > 0: the row is read once into registers (V float4 per thread, H <= 1024 V); V = 0: a
+// second pass re-reads it.  The same sums in the same order either way.
+template <int V>
 __global__ __launch_bounds__(256) void rmsnorm_pairs_kernel(const float* x, int ldx, const uint16_t* gain, float eps,
                                                             int H, uint16_t* out) {
   __shared__ float part[4];
   const int m = blockIdx.x, tid = threadIdx.x;
   const float* xr = x + (size_t)m * ldx;
   const int n4 = H / 4;
+  float4 r[V > 0 ? V : 1];
   float s = 0.f;
-  for (int i = tid; i < n4; i += 256) {
-    const float4 v = *(const float4*)(xr + 4 * i);
-    s = fmaf(v.x, v.x, s);
-    s = fmaf(v.y, v.y, s);
-    s = fmaf(v.z, v.z, s);
-    s = fmaf(v.w, v.w, s);
+  if constexpr (V > 0) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const int i = tid + 256 * k;
+      r[k] = i < n4 ? ldg4(xr + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      if (tid + 256 * k < n4) {
+        s = fmaf(r[k].x, r[k].x, s);
+        s = fmaf(r[k].y, r[k].y, s);
+        s = fmaf(r[k].z, r[k].z, s);
+        s = fmaf(r[k].w, r[k].w, s);
+      }
+    }
+  } else {
+    for (int i = tid; i < n4; i += 256) {
+      const float4 v = *(const float4*)(xr + 4 * i);
+      s = fmaf(v.x, v.x, s);
+      s = fmaf(v.y, v.y, s);
+      s = fmaf(v.z, v.z, s);
+      s = fmaf(v.w, v.w, s);
+    }
   }
   s = wave_sum(s);
   if ((tid & 63) == 0) part[tid >> 6] = s;
@@ -118,14 +139,20 @@ __global__ __launch_bounds__(256) void rmsnorm_pairs_kernel(const float* x, int 
   const float tot = part[0] + part[1] + part[2] + part[3];
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
   uint4* o = (uint4*)(out + (size_t)m * 2 * H);
-  for (int i = tid; i < n4; i += 256) {
-    const float4 v = *(const float4*)(xr + 4 * i);
+  auto emit = [&](int i, const float4& v) {
     const float y0 = v.x * inv * load_w<uint16_t>(gain + 4 * i), y1 = v.y * inv * load_w<uint16_t>(gain + 4 * i + 1);
     const float y2 = v.z * inv * load_w<uint16_t>(gain + 4 * i + 2), y3 = v.w * inv * load_w<uint16_t>(gain + 4 * i + 3);
     uint32_t h0, l0, h1, l1;
     split_bf2(y0, y1, h0, l0);
     split_bf2(y2, y3, h1, l1);
     o[i] = make_uint4(h0, h1, l0, l1);
+  };
+  if constexpr (V > 0) {
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+      if (tid + 256 * k < n4) emit(tid + 256 * k, r[k]);
+  } else {
+    for (int i = tid; i < n4; i += 256) emit(i, *(const float4*)(xr + 4 * i));
   }
 }
 
@@ -238,8 +265,15 @@ hipError_t launch_rmsnorm(int wdtype, const float* x, int ldx, const void* gain,
 hipError_t launch_rmsnorm_pairs(const float* x, int ldx, const void* gain, float eps, int M, int H, void* out,
                                 hipStream_t s) {
   if (M < 1 || H < 4 || H % 4 != 0 || ldx % 4 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rmsnorm_pairs_kernel, dim3(M), dim3(256), 0, s, x, ldx, (const uint16_t*)gain, eps, H,
-                     (uint16_t*)out);
+  if (H <= 8192)
+    hipLaunchKernelGGL(rmsnorm_pairs_kernel<8>, dim3(M), dim3(256), 0, s, x, ldx, (const uint16_t*)gain, eps, H,
+                       (uint16_t*)out);
+  else if (H <= 16384)
+    hipLaunchKernelGGL(rmsnorm_pairs_kernel<16>, dim3(M), dim3(256), 0, s, x, ldx, (const uint16_t*)gain, eps, H,
+                       (uint16_t*)out);
+  else
+    hipLaunchKernelGGL(rmsnorm_pairs_kernel<0>, dim3(M), dim3(256), 0, s, x, ldx, (const uint16_t*)gain, eps, H,
+                       (uint16_t*)out);
   return hipGetLastError();
 }
 
