@@ -179,9 +179,9 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
  * through skinny weight-streaming launches (a ladder layer in two launches under the
  * FUSED schedules, [QKV + RoPE/KV | attention | gate/up] and [O + down], module by module
  * otherwise, with the same bits), beyond that through tiled GEMMs (under the FUSED
- * schedules a ladder or parallel layer in five launches: [QKV | gate/up], their split-K
- * reduction with RoPE + KV and SwiGLU, the attention, [O | down], their reduction with
- * both residual adds). */
+ * schedules a ladder or parallel layer in four launches: [QKV | gate/up], their split-K
+ * reduction with RoPE + KV and SwiGLU, [attention | down | O once the attention has
+ * signalled], their reduction with both residual adds). */
 ladder_status ladder_decode_step(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t pos,
                                  float* d_logits, int32_t* d_next, float* d_hidden);
 
@@ -267,8 +267,9 @@ ladder_status ladder_sync(ladder_ctx* ctx);
                                         from ladder_time_kernels where not available */
 #define LADDER_KERNEL_DOWN_OPROJ 11  /* fused ladder launch (the same layers): down rows, then
                                         the O rows + both residual adds (at 33-64 sequences on
-                                        the matrix cores the tiled [O | down] launch and its
-                                        reduction, traced only); -1 where not available */
+                                        the matrix cores the tiled [attention | down | O] launch
+                                        and its reduction, traced only); -1 where not
+                                        available */
 #define LADDER_KERNEL_SAMPLE 12   /* stochastic draw from the logits (ladder_set_sampling); timed
                                         with the context's sampling settings, or temperature 1
                                         and no top-k cut when sampling is off */

@@ -39,6 +39,7 @@
 // fp32 models (small correctness-only models): a plain LDS-tiled VALU GEMM.
 #include <type_traits>
 
+#include "attn_decode.hpp"
 #include "common.hpp"
 #include "kernels.h"
 
@@ -439,6 +440,37 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_pair_kernel(GemmParams
   else splitk_reduce(a, Sa, (size_t)bi * 256 + threadIdx.x);
 }
 
+// A chained pair with the decode attention that feeds its first problem in the same launch:
+// blocks [0, n_attn) run the split-KV attention (coherent records and output, and the
+// completion signal at.done_flag = step epoch after the last merge), the next ones the
+// second problem (the down projection, which needs no attention), the last ones the first
+// problem (O), whose workgroups wait for the signal before loading their A (the attention
+// output: nothing in the launch reads it earlier, so no cache holds a stale copy).  The
+// attention workgroups come first in dispatch order and wait for nothing.
+template <int HD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_attn_chain_kernel(GemmPairArgs g, AttnDecodeParams at, int n_attn, int* err) {
+  __shared__ AttnLds<uint16_t, HD> L;
+  int b = (int)blockIdx.x;
+  if (b < n_attn) {
+    attn_decode_block_mfma<HD, true>(at, b, L);
+    return;
+  }
+  b -= n_attn;
+  const int items1 = g.per_xcd[1] * kXcds * g.S[1];
+  int q = 1;
+  if (b >= items1) {
+    q = 0;
+    b -= items1;
+    wg_wait_coh(at.done_flag, *gbl(at.d_epoch), err);
+  }
+  const int W = g.per_xcd[q] * kXcds;
+  const int x = b % W;
+  const int tile = (x % kXcds) * g.per_xcd[q] + x / kXcds;
+  if (tile >= g.n_tiles[q]) return;
+  gemm_tile<64, 128, false, false>(g.p[q], tile, b / W, g.S[q], 1, g.nst[q]);
+}
+
 // The reduction of a chained pair (a: the O projection with its residual, b: the down
 // projection whose residual is a's output): per element x1 = res + sum(a) written to a.C,
 // then x1 + sum(b) to b.C, each sum in slice order as splitk_reduce adds it.
@@ -619,6 +651,39 @@ hipError_t launch_gemm_chain(const GemmParams& a, const GemmParams& b, hipStream
     items += g.per_xcd[i] * kXcds * g.S[i];
   }
   launch_timed(gemm_pair_kernel<false>, dim3(items), dim3(256), 0, s, g);
+  launch_timed(gemm_splitk_reduce_chain_kernel, dim3((unsigned)(((size_t)a.M * a.N + 255) / 256)), dim3(256), 0, s, a,
+               g.S[0], b, g.S[1]);
+  return hipGetLastError();
+}
+
+bool gemm_attn_chain_ok(const AttnDecodeParams& at, const GemmParams& a, const GemmParams& b) {
+  return gemm_chain_ok(a, b) && at.wdtype == W_BF16 && (at.hd == 64 || at.hd == 128) && at.nkv >= 1 &&
+         at.nq % at.nkv == 0 && at.nq / at.nkv <= kAttnMaxGroup && at.n_split >= 1 && at.n_split <= kAttnMaxSplits &&
+         at.B == a.M && at.out == a.A && !a.a_pairs && at.done_cnt && at.done_flag && at.d_epoch && at.part &&
+         at.counters && at.q && at.d_pos;
+}
+
+hipError_t launch_gemm_attn_chain(const AttnDecodeParams& at, const GemmParams& a, const GemmParams& b, int* err,
+                                  hipStream_t s) {
+  if (!gemm_attn_chain_ok(at, a, b) || !err) return hipErrorInvalidValue;
+  GemmPairArgs g{};
+  const GemmParams* q[2] = {&a, &b};
+  int items = 0;
+  for (int i = 0; i < 2; ++i) {
+    const GemmParams& p = *q[i];
+    g.p[i] = p;
+    g.n_tiles[i] = (p.N + 127) / 128;
+    g.per_xcd[i] = (g.n_tiles[i] + kXcds - 1) / kXcds;
+    g.S[i] = gemm_splits(p);
+    g.nst[i] = p.K / BK;
+    items += g.per_xcd[i] * kXcds * g.S[i];
+  }
+  g.items0 = 0;   // (unused: the kernel takes the second problem first)
+  const int n_attn = at.n_split * at.nkv * at.B;
+  if (at.hd == 128)
+    launch_timed(gemm_attn_chain_kernel<128>, dim3(n_attn + items), dim3(256), 0, s, g, at, n_attn, err);
+  else
+    launch_timed(gemm_attn_chain_kernel<64>, dim3(n_attn + items), dim3(256), 0, s, g, at, n_attn, err);
   launch_timed(gemm_splitk_reduce_chain_kernel, dim3((unsigned)(((size_t)a.M * a.N + 255) / 256)), dim3(256), 0, s, a,
                g.S[0], b, g.S[1]);
   return hipGetLastError();

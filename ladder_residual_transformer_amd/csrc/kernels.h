@@ -310,6 +310,13 @@ hipError_t launch_gemm_pair(const GemmParams& a, const GemmParams& b, hipStream_
 // writing both outputs; the same bits as launch_gemm of a, then of b.
 bool gemm_chain_ok(const GemmParams& a, const GemmParams& b);
 hipError_t launch_gemm_chain(const GemmParams& a, const GemmParams& b, hipStream_t s);
+// The same chained pair with the decode attention whose output is a's A in the same launch
+// (bf16; the attention with its completion signal: done_cnt, done_flag, d_epoch): the
+// attention and b's workgroups run side by side, a's wait for the signal (bounded; a wait
+// that gives up sets *err).  The same bits as launch_attn_decode, then launch_gemm_chain.
+bool gemm_attn_chain_ok(const AttnDecodeParams& at, const GemmParams& a, const GemmParams& b);
+hipError_t launch_gemm_attn_chain(const AttnDecodeParams& at, const GemmParams& a, const GemmParams& b, int* err,
+                                  hipStream_t s);
 // Whether a SwiGLU launch can write its output as bf16 pairs (GemmParams::c_pairs): the
 // tiled kernel without split K, more than 64 rows.
 bool gemm_writes_pairs(const GemmParams& p);

@@ -141,6 +141,9 @@ struct ladder_ctx {
   // and its O projection waits for the down projection (pair_o, when o_deferred)
   GemmParams pair_o{};
   bool o_deferred = false;
+  // and its attention runs in that launch too (pair_at, when at_deferred)
+  AttnDecodeParams pair_at{};
+  bool at_deferred = false;
   // next-token rule: greedy, or a draw (temperature > 0) with an optional top-k cut
   float temperature = 0.f;
   int top_k = 0;
@@ -441,6 +444,7 @@ GemvParams qkv_params(const ladder_ctx* ctx, int l, int B, const float* xin, con
 // (batches 8 and 32 within 0.2% of 256).  Beyond, the attention has a launch of its own,
 // where 256 measured 4474 / 1961 tok/s (70B / 405B shard, batch 64) against 4383 / 1869.
 constexpr int decode_attn_fill(int B) { return B <= 32 ? 128 : 256; }
+constexpr bool kAttnInOutLaunch = true;
 
 AttnDecodeParams attn_params(const ladder_ctx* ctx, int l, int B, const StreamScratch& sc) {
   const ladder_config& g = ctx->cfg;
@@ -789,7 +793,13 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
       a.n_split = std::max(1, std::min(a.n_split, fill));
       a.q = sc.qr;
       a.out = sc.ob;
-      HIPCHK(launch_attn_decode(a, s));
+      if (ctx->skip_gateup && kAttnInOutLaunch) {
+        // a paired layer: the attention runs in the [O | down] launch (with its signal)
+        ctx->pair_at = signalled(ctx, a, l);
+        ctx->at_deferred = true;
+      } else {
+        HIPCHK(launch_attn_decode(a, s));
+      }
     } else {
       AttnPrefillParams ap{};
       ap.wdtype = ctx->wdt;
@@ -874,11 +884,25 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
     ctx->o_deferred = true;
     return LADDER_OK;
   }
+  if (m % 2 == 0 && ctx->at_deferred) {      // (not taken: the O projection needs it now)
+    ctx->at_deferred = false;
+    HIPCHK(launch_attn_decode(ctx->pair_at, s));
+  }
   if (m % 2 == 1 && ctx->o_deferred) {
     ctx->o_deferred = false;
     GemmParams d = op;
     d.ws = ctx->sc[1].gk;             // the O partials take the first workspace
     d.cnt = ctx->sc[1].skcnt;
+    if (ctx->at_deferred) {
+      ctx->at_deferred = false;
+      if (gemm_attn_chain_ok(ctx->pair_at, ctx->pair_o, d)) {
+        TRACE(LADDER_KERNEL_DOWN_OPROJ, s, false);
+        HIPCHK(launch_gemm_attn_chain(ctx->pair_at, ctx->pair_o, d, ctx->err_word, s));
+        TRACE(LADDER_KERNEL_DOWN_OPROJ, s, true);
+        return LADDER_OK;
+      }
+      HIPCHK(launch_attn_decode(ctx->pair_at, s));
+    }
     if (gemm_chain_ok(ctx->pair_o, d)) {
       TRACE(LADDER_KERNEL_DOWN_OPROJ, s, false);
       HIPCHK(launch_gemm_chain(ctx->pair_o, d, s));
@@ -1319,7 +1343,11 @@ ladder_status enqueue_decode_gemm(ladder_ctx* ctx, int B) {
       for (int m = 2 * l; m < 2 * l + 2 && !st; ++m)
         st = mod(m, X[module_src(ctx, m) % 2], X[m % 2], X[(m + 1) % 2], nullptr, ctx->s0, false, nullptr);
       ctx->pair_next = ctx->skip_gateup = false;
-      if (ctx->o_deferred) {                // (not taken: the MLP module launches it)
+      if (ctx->at_deferred) {               // (not taken: the MLP module launches these)
+        ctx->at_deferred = false;
+        HIPCHK(launch_attn_decode(ctx->pair_at, ctx->s0));
+      }
+      if (ctx->o_deferred) {
         ctx->o_deferred = false;
         HIPCHK(launch_gemm(ctx->pair_o, ctx->s0));
       }

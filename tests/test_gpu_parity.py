@@ -416,8 +416,9 @@ def test_matrix_core_layer_launch_is_traced_with_its_attention(edge):
 def test_tiled_paired_launches_match_module_order(B):
     """Batches 33-64 decode through the tiled split-K GEMMs.  Under the fused schedule a
     ladder layer's [QKV | gate/up] run in one launch with one reduction (RMSNorm, RoPE + KV,
-    SwiGLU) and [O | down] in one launch whose reduction writes both residual adds; module
-    order (serial) launches each GEMM and its reduction alone.  The two must give the same
+    SwiGLU) and [attention | down | O] in one launch (the O workgroups wait for the
+    attention's signal) whose reduction writes both residual adds; module order (serial)
+    launches the attention, each GEMM and its reduction alone.  The two must give the same
     bits (70B shard widths, two ladder layers, so that K splits), the paired launch must be
     traced once per layer, and tracing must leave every result unchanged."""
     cfg = synth.scaled_config(synth.CONFIGS["70b_tp8_shard"], 2)

@@ -101,8 +101,8 @@ def test_70b_tp8_shard_widths_batches(B, T):
     layer ([QKV with RoPE + KV | attention | gate/up], [O + down]), both RMSNorms folded in,
     16-row tiles up to batch 16 (batch 6: 10 of 16 rows padding) and 32-row tiles beyond
     (batch 32: the last batch they take).  Batch 33: the tiled GEMMs with 64-row tiles and
-    the RMSNorm folded into them (31 rows of padding), five launches per layer ([QKV |
-    gate/up], their reduction with RoPE + KV and SwiGLU, the attention, [O | down], their
+    the RMSNorm folded into them (31 rows of padding), four launches per layer ([QKV |
+    gate/up], their reduction with RoPE + KV and SwiGLU, [attention | down | O], their
     reduction with both residual adds)."""
     base = synth.CONFIGS["70b_tp8_shard"]
     cfg = synth.scaled_config(base, 4)
@@ -160,8 +160,8 @@ def test_405b_tp16_shard_widths():
     """405B-shape TP=16 shard widths (hidden 16384: the staged input exceeds 64 KB of
     LDS), four ladder layers; batch 1, 16 and 64 (the workload's batches).  Batch 64 runs
     the 64-row GEMM tiles with the RMSNorm folded into them in paired launches ([QKV |
-    gate/up], [O | down]) with one reduction each, the split-KV attention over 4 key chunks
-    per sequence and the row argmax over 64 rows."""
+    gate/up], [attention | down | O]) with one reduction each, the split-KV attention over
+    4 key chunks per sequence and the row argmax over 64 rows."""
     base = synth.CONFIGS["405b_tp16_shard"]
     cfg = synth.scaled_config(base, 4)
     w = synth.gen_weights(cfg, seed=6)
