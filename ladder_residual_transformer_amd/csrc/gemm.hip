@@ -546,8 +546,7 @@ static int gemm_tile_rows(const GemmParams& p) { return p.M <= 32 ? 32 : p.M <= 
 
 int gemm_splits(const GemmParams& p) {
   if (p.wdtype != W_BF16 || !p.ws || p.M < 1 || p.N < 1 || p.K < 1) return 1;
-  // the fewest slices that give one round of workgroups (two rounds, two per CU, for
-  // skinny tiles, which stream weights with little work per byte: more of them in flight);
+  // the fewest slices that give one round of workgroups;
   // at most 32 slices (64 made the 10-tile QKV projection of a 70B shard's decode step
   // slower: slices of 4 K steps and 64 partials per output); each slice at least kStages
   // steps long, partials (and the fused norm's row sums) within the workspace
@@ -556,7 +555,11 @@ int gemm_splits(const GemmParams& p) {
   // (slices of unequal length, as many as fill one round at the register caps' occupancy,
   // measured 5057 against 4926 tok/s at batch 64 on the 70B shard but 2257 against 2297 on
   // the 405B shard and a slower prefill: not taken)
-  const int want = tmr < 128 ? 512 : 256;
+  // (two rounds for the 32- and 64-row tiles, so that more of their weight streams are in
+  // flight, was the rule before those projections ran in pairs: one round measured 6711
+  // against 5848 tok/s at batch 64 on the 70B shard, 2881 against 2680 on the 405B shard,
+  // 3694 against 3467 at batch 32)
+  const int want = 256;
   int S = 1;
   if (big < 256) {
     for (int c = 2; c <= 32; c *= 2) {
