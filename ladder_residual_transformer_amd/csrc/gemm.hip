@@ -546,8 +546,9 @@ static int gemm_tile_rows(const GemmParams& p) { return p.M <= 32 ? 32 : p.M <= 
 
 int gemm_splits(const GemmParams& p) {
   if (p.wdtype != W_BF16 || !p.ws || p.M < 1 || p.N < 1 || p.K < 1) return 1;
-  // the fewest slices that give one round of workgroups;
-  // at most 32 slices (64 made the 10-tile QKV projection of a 70B shard's decode step
+  // the fewest slices that give one round of workgroups (half a round for the 32- and
+  // 64-row tiles: decode steps, whose projections mostly run two to a launch); at most 32
+  // slices (64 made the 10-tile QKV projection of a 70B shard's decode step
   // slower: slices of 4 K steps and 64 partials per output); each slice at least kStages
   // steps long, partials (and the fused norm's row sums) within the workspace
   const int tmr = gemm_tile_rows(p);
@@ -555,18 +556,21 @@ int gemm_splits(const GemmParams& p) {
   // (slices of unequal length, as many as fill one round at the register caps' occupancy,
   // measured 5057 against 4926 tok/s at batch 64 on the 70B shard but 2257 against 2297 on
   // the 405B shard and a slower prefill: not taken)
-  // (two rounds for the 32- and 64-row tiles, so that more of their weight streams are in
-  // flight, was the rule before those projections ran in pairs: one round measured 6711
-  // against 5848 tok/s at batch 64 on the 70B shard, 2881 against 2680 on the 405B shard,
-  // 3694 against 3467 at batch 32)
-  const int want = 256;
+  // (for the 32- and 64-row tiles two rounds, so that more weight streams are in flight,
+  // was the rule before their projections ran in pairs; tok/s on the 70B shard at batch
+  // 64 / 32 / 24 and on the 405B shard at batch 64, two rounds -> one -> half: 5848 ->
+  // 6729 -> 7231, 3467 -> 3687 -> 4027, 2682 -> 2872 -> 3097, 2680 -> 2877 -> 2989; a
+  // quarter round: 6057, 3256, 2477, 2311)
+  const int fill = tmr < 128 ? 128 : 256;
   int S = 1;
-  if (big < 256) {
+  if (big < 256) {   // (under a round of tiles: at least two slices, or none)
     for (int c = 2; c <= 32; c *= 2) {
       const size_t ws = (size_t)c * p.M * p.N + (p.gain ? (size_t)c * p.M : 0);
       if (p.K % (c * BK) != 0 || p.K / c < kStages * BK || ws > p.ws_floats) break;
-      if ((long long)big * c >= 256) S = c;            // a valid split that fills one round
-      if ((long long)big * c >= want) break;
+      if ((long long)big * c >= fill) {
+        S = c;
+        break;
+      }
     }
   }
   return S;
