@@ -423,14 +423,18 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(SkArgs args) {
     if (p.rope_q) prog_publish(args.prog + tile, pcode);
 }
 
-// Slices of one K part: about 512 workgroups (two per CU) for its tiles, at least two
-// whole chunks per slice (so that a workgroup has a chunk in flight while it multiplies
-// one); a function of the shape only, so a problem gives the same bits in every launch.
+// Slices of one K part: about 128 workgroups for its tiles (half a round: the projections
+// run two to a launch, or two K parts to a problem), at least two whole chunks per slice
+// (so that a workgroup has a chunk in flight while it multiplies one); a function of the
+// shape only, so a problem gives the same bits in every launch.  (Aimed at 512 / 192 /
+// 96 / 64 workgroups, the 70B shard decoded 1459 / 1452 / 1335 / 1170 tok/s at batch 8
+// against 1534 at 128; at 512 / 256 / 192 / 96 / 64, 2566 / 2532 / 2468 / 2511 / 2217 at
+// batch 16 against 2774.)
 void sk_part_plan(int M, int N, int K, int* S, int* ks) {
   const int KC = M <= 16 ? 256 : 128;
   const int nt = (N + kSkRows - 1) / kSkRows;
   const int nkc = (K + KC - 1) / KC;
-  const int s = std::max(1, std::min(std::min(nkc / 2, sk_max_slices(M)), (512 + nt - 1) / nt));
+  const int s = std::max(1, std::min(std::min(nkc / 2, sk_max_slices(M)), (128 + nt - 1) / nt));
   const int k = (nkc + s - 1) / s * KC;
   *S = (K + k - 1) / k;
   *ks = k;
