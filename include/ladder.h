@@ -176,7 +176,7 @@ ladder_status ladder_prefill(ladder_ctx* ctx, const int32_t* d_ids, int32_t B, i
  * for models of hidden >= 8192 whose layers are all ladder or parallel blocks) run the
  * schedule's GEMV launches; other bf16 batches run one token per sequence on the matrix
  * cores (with the split-KV decode attention), under every schedule: up to 32 sequences
- * (16 on models narrower than 16384) through skinny weight-streaming launches (a ladder layer in two launches under the
+ * through skinny weight-streaming launches (a ladder layer in two launches under the
  * FUSED schedules, [QKV + RoPE/KV | attention | gate/up] and [O + down], module by module
  * otherwise, with the same bits), beyond that through tiled GEMMs (under the FUSED
  * schedules a ladder or parallel layer in four launches: [QKV | gate/up], their split-K

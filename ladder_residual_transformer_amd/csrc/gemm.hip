@@ -591,15 +591,15 @@ bool gemm_writes_pairs(const GemmParams& p) {
 }
 
 bool gemm_norm_fusable(const GemmParams& p) {
-  if (!p.no_skinny && skinny_supported(p)) return true;
+  if (skinny_supported(p)) return true;
   return p.wdtype == W_BF16 && p.M <= 64 && p.lda % 4 == 0 && p.K % BK == 0 && gemm_splits(p) > 1;
 }
 
 bool gemm_pair_ok(const GemmParams& a, const GemmParams& b) {
   auto one = [](const GemmParams& p) {
-    return p.wdtype == W_BF16 && !p.A2 && !p.a_pairs && !p.c_pairs && (p.M > 32 || (p.no_skinny && p.M > 16)) &&
+    return p.wdtype == W_BF16 && !p.A2 && !p.a_pairs && !p.c_pairs && p.M > 32 &&
            p.M <= 64 && p.K % BK == 0 && p.lda % 4 == 0 && (!p.swiglu || (p.N % 2 == 0 && !p.res)) && p.ws &&
-           gemm_splits(p) > 1 && (p.no_skinny || !skinny_supported(p));
+           gemm_splits(p) > 1 && !skinny_supported(p);
   };
   // a.rope_q: the first problem is a decode step's QKV projection whose reduction runs
   // rope_kv's epilogue (bf16 caches, the skinny launches' conditions on the rope fields)
@@ -699,7 +699,7 @@ hipError_t launch_gemm_attn_chain(const AttnDecodeParams& at, const GemmParams& 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.M < 1 || p.N < 1 || p.K < 1) return hipErrorInvalidValue;
   // (bf16 pairs in or out: the tiled kernel, for more than 64 rows)
-  if (!p.no_skinny && !p.a_pairs && !p.c_pairs && skinny_supported(p)) return launch_skinny(p, s);
+  if (!p.a_pairs && !p.c_pairs && skinny_supported(p)) return launch_skinny(p, s);
   if (p.A2) return hipErrorInvalidValue;   // a second K part: skinny launches only
   if (p.a_pairs && !gemm_takes_pairs(p)) return hipErrorInvalidValue;
   if (p.c_pairs && !gemm_writes_pairs(p)) return hipErrorInvalidValue;

@@ -240,9 +240,6 @@ struct GemmParams {
   float* C; int ldc;
   const float* res; int ldr;
   int swiglu;
-  // no_skinny: the tiled kernel even where a skinny launch could take the rows (the decode
-  // steps of 17-32 sequences of models narrower than 16384, in every schedule)
-  int no_skinny;
   // c_pairs (SwiGLU launches where gemm_writes_pairs() holds): C is written as bf16 pairs
   // in a_pairs' layout, ready to be the A of the next projection ([M][ldc / 4] groups)
   int c_pairs;

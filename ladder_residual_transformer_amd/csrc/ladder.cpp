@@ -444,13 +444,11 @@ GemvParams qkv_params(const ladder_ctx* ctx, int l, int B, const float* xin, con
 // (batches 8 and 32 within 0.2% of 256).  Beyond, the attention has a launch of its own,
 // where 256 measured 4474 / 1961 tok/s (70B / 405B shard, batch 64) against 4383 / 1869.
 constexpr int decode_attn_fill(int B) { return B <= 32 ? 128 : 256; }
-// Decode steps of 17-32 sequences on models narrower than 16384 take the tiled GEMMs (the
-// paired launches below) instead of the skinny launches: 70B shard 3472 against 3077 tok/s
-// at batch 32, 2684 against 2532 at batch 24; the 405B shard keeps the skinny launches
-// (1685 against 1557 at batch 32).  Every schedule routes the same way.
-inline bool tiled_mid_batch(const ladder_ctx* ctx, int B) {
-  return ctx->wdt == W_BF16 && B > 16 && B <= 32 && ctx->cfg.hidden < 16384;
-}
+// (Decode steps of 17-32 sequences on models narrower than 16384 took the tiled GEMMs'
+// paired launches for a while: 3472 against 3077 tok/s at batch 32 on the 70B shard.  With
+// the skinny launches' K cut for about 128 items per K part the skinny launches measured
+// 2723 / 3712 / 4559 against 2293 / 3106 / 4020 tok/s at batch 17 / 24 / 32, the 8B model
+// 4309 against 3789 at batch 24, so every batch up to 32 takes them again.)
 constexpr bool kAttnInOutLaunch = true;
 
 AttnDecodeParams attn_params(const ladder_ctx* ctx, int l, int B, const StreamScratch& sc) {
@@ -721,7 +719,6 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
   GemmParams gp{};
   gp.wdtype = ctx->wdt;
   gp.M = M;
-  gp.no_skinny = ctx->gemm_step && tiled_mid_batch(ctx, M);
   gp.ws = sc.gk;
   gp.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
   gp.cnt = sc.skcnt;
@@ -866,7 +863,6 @@ ladder_status prefill_module(ladder_ctx* ctx, int m, int B, int T, int start_pos
   }
   GemmParams op{};
   op.wdtype = ctx->wdt;
-  op.no_skinny = gp.no_skinny;
   op.ws = sc.gk;
   op.ws_floats = sc.gk ? kGemmSplitWsFloats : 0;
   op.cnt = sc.skcnt;
@@ -1259,7 +1255,7 @@ void skinny_layer_params(const ladder_ctx* ctx, int l, int B, GemmParams qg[2], 
 
 bool skinny_layer_ok(const ladder_ctx* ctx, int B) {
   const StreamScratch& sc = ctx->sc[0];
-  if (ctx->wdt != W_BF16 || !sc.gk || !sc.skcnt || tiled_mid_batch(ctx, B)) return false;
+  if (ctx->wdt != W_BF16 || !sc.gk || !sc.skcnt) return false;
   GemmParams qg[2], od;
   skinny_layer_params(ctx, 0, B, qg, &od);
   const int tiles = (qg[0].N + 127) / 128 + (qg[1].N + 127) / 128;
@@ -1303,7 +1299,6 @@ bool gateup_pair_params(ladder_ctx* ctx, int l, int B, const float* xin, GemmPar
   GemmParams t{};
   t.wdtype = ctx->wdt;
   t.M = B;
-  t.no_skinny = tiled_mid_batch(ctx, B);
   t.ws = ctx->sc[1].gk;
   t.ws_floats = kGemmSplitWsFloats;
   t.cnt = ctx->sc[1].skcnt;

@@ -99,9 +99,9 @@ def test_70b_tp8_shard_widths_batches(B, T):
     """70B TP=8 shard widths (hidden 8192), four ladder layers.  Batch 1: the two streaming
     launches per layer.  Batches 2-32: the skinny launches on the matrix cores, two per
     layer ([QKV with RoPE + KV | attention | gate/up], [O + down]), both RMSNorms folded in,
-    16-row tiles up to batch 16 (batch 6: 10 of 16 rows padding).  Batch 32 (a model of
-    hidden 8192) and batch 33: the tiled GEMMs with 32-row / 64-row tiles and
-    the RMSNorm folded into them (31 rows of padding), four launches per layer ([QKV |
+    16-row tiles up to batch 16 (batch 6: 10 of 16 rows padding), 32-row tiles beyond.
+    Batch 33: the tiled GEMMs with 64-row tiles and the RMSNorm folded into them (31 rows
+    of padding), four launches per layer ([QKV |
     gate/up], their reduction with RoPE + KV and SwiGLU, [attention | down | O], their
     reduction with both residual adds)."""
     base = synth.CONFIGS["70b_tp8_shard"]
