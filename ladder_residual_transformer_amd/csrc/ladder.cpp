@@ -439,11 +439,14 @@ GemvParams qkv_params(const ladder_ctx* ctx, int l, int B, const float* xin, con
 // Key chunks of the matrix-core route's decode attention: at most decode_attn_fill(B) / (B *
 // kv heads) workgroups' worth (and at most the context's own split), a function of the batch
 // only, so that every schedule gives the same bits.  Up to 32 sequences the attention runs
-// inside the [QKV | gate/up] launch, its workgroups waiting there beside the gate/up rows:
-// 128 measured 2578 tok/s at batch 16 on the 70B shard against 2446 with 256 and 2458 with 64
-// (batches 8 and 32 within 0.2% of 256).  Beyond, the attention has a launch of its own,
-// where 256 measured 4474 / 1961 tok/s (70B / 405B shard, batch 64) against 4383 / 1869.
-constexpr int decode_attn_fill(int B) { return B <= 32 ? 128 : 256; }
+// inside the skinny [QKV | gate/up] launch, its workgroups waiting there beside the gate/up
+// rows: 128 measured 2766 tok/s at batch 16 on the 70B shard against 2514 with 256 and 2681
+// with 64 (batch 8 within 0.3%); 256 at 17-32 sequences: 4862 / 3668 / 2762 against 4552
+// / 3703 / 2716 with 128 at batch 32 / 24 / 17, the 405B shard 2007 against 1897 at batch
+// 32, the 8B model at batch 24 within 0.1%.  Beyond,
+// the attention shares the tiled [down | O] launch, where 256 measured 4474 / 1961 tok/s
+// (70B / 405B shard, batch 64, in a launch of its own then) against 4383 / 1869.
+constexpr int decode_attn_fill(int B) { return B <= 16 ? 128 : 256; }
 // (Decode steps of 17-32 sequences on models narrower than 16384 took the tiled GEMMs'
 // paired launches for a while: 3472 against 3077 tok/s at batch 32 on the 70B shard.  With
 // the skinny launches' K cut for about 128 items per K part the skinny launches measured
